@@ -1,0 +1,192 @@
+"""Benchmark of the small-M decode GEMM on one MI355X.
+
+Workload: the unpooler shard GEMM sweep y[M, 1024] = x[M, 4096] @ W[1024,
+4096]^T for M = 1, 2, 4, 8, 16 (unpooler page, module description), BF16 in
+and out, FP32 accumulation, at the chooser's launch shapes.  One step is one
+pass of the sweep: five GEMM launches, each on the next weight of a ring of
+distinct layers (60 layers = 480 MiB, twice the 256 MiB Infinity Cache, so no
+call finds its weights in a cache).  Inputs are seeded synthetic tensors
+already resident in HBM: x ~ N(0, 1), W ~ N(0, 1/K).
+
+Steps run as HIP-graph replays (the decode loop records its calls once and
+replays them: the calls allocate nothing and never synchronize).  Timing uses
+HIP events on the stream the kernels run on.
+
+Output: one JSON line.  `value` is achieved HBM GB/s over the step
+(algorithmic bytes 2NK + 2MK + 2MN per call / step time).  `roofline` is for
+the dominant kernel (the launch with the largest share of the step), with its
+average duration measured here from graph replays of that launch alone over
+the ring.  `cpu_baseline` times the oracle on the host for a bounded sample of
+the same workload.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+N, K = 1024, 4096
+MS = (1, 2, 4, 8, 16)
+RING = 60
+PEAK_GBS = 8000.0  # MI355X HBM3E, published
+
+
+def algorithmic_bytes(M: int, n: int = N, k: int = K) -> int:
+    return 2 * n * k + 2 * M * k + 2 * M * n
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def cpu_baseline(budget_s: float = 12.0):
+    """The oracle (plain C, binary64) on the host cores for a bounded sample of
+    the same sweep: whole steps until the budget is spent."""
+    import numpy as np
+
+    import oracle
+    import synthetic
+
+    threads = min(16, len(os.sched_getaffinity(0)))
+    x, w = synthetic.gemm_inputs(N=N, K=K, seed=0)
+    oracle.gemm_bf16(x[:1], w[:16], threads)  # load the library
+    steps, t0 = 0, time.perf_counter()
+    while True:
+        for M in MS:
+            oracle.gemm_bf16(x[:M], w, threads)
+        steps += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s or steps >= 200:
+            break
+    per_step = el / steps
+    gbs = sum(algorithmic_bytes(M) for M in MS) / per_step / 1e9
+    return {"value": round(gbs, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
+            "sample": f"{steps} steps of the M=1,2,4,8,16 sweep on one weight "
+                      f"({el:.1f} s, {per_step * 1e3:.1f} ms/step)"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=600)
+    ap.add_argument("--warmup", type=int, default=60)
+    ap.add_argument("--kernel-reps", type=int, default=20,
+                    help="ring passes per launch shape for the per-kernel timing")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py runs on one GPU only: this GEMM is one GPU's shard and the "
+              "build has no multi-GPU path (use --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import moe_decode_skinny_amd as sk
+    import synthetic
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    sk.skinny_init(0)
+    log(f"device {torch.cuda.get_device_name(dev)}; building the {RING}-layer ring")
+    ring = synthetic.device_weight_ring(RING, N, K, dev)
+    x_bits, _ = synthetic.gemm_inputs(N=16, K=K, seed=0)
+    xs = {M: synthetic.to_device(x_bits[:M], dev) for M in MS}
+    ys = {M: torch.empty((M, N), dtype=torch.bfloat16, device=dev) for M in MS}
+    launches = {M: sk.skinny_choose(M, N, K, 0) for M in MS}
+    stream = torch.cuda.Stream(dev)
+
+    # One graph per group of five ring layers: step i replays graph i % 12,
+    # which runs the sweep M = 1..16 on layers 5 (i % 12) .. + 4.
+    groups = RING // len(MS)
+    graphs = []
+    with torch.cuda.stream(stream):
+        for M in MS:  # eager warm-up of every launch
+            sk.skinny_gemm_bf16(xs[M], ring[0], ys[M], 0)
+        torch.cuda.synchronize()
+        for gi in range(groups):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=stream):
+                for j, M in enumerate(MS):
+                    sk.skinny_gemm_bf16(xs[M], ring[gi * len(MS) + j], ys[M], 0)
+            graphs.append(g)
+        torch.cuda.synchronize()
+
+        for i in range(args.warmup):
+            graphs[i % groups].replay()
+        torch.cuda.synchronize()
+        start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t0 = time.perf_counter()
+        start.record(stream)
+        for i in range(args.steps):
+            graphs[i % groups].replay()
+        end.record(stream)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        ms_step = start.elapsed_time(end) / args.steps
+
+        # Per-launch durations: a graph of one launch shape over the whole ring.
+        per_kernel = {}
+        for M in MS:
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=stream):
+                for l in range(RING):
+                    sk.skinny_gemm_bf16(xs[M], ring[l], ys[M], 0)
+            g.replay()
+            torch.cuda.synchronize()
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            for _ in range(args.kernel_reps):
+                g.replay()
+            b.record(stream)
+            torch.cuda.synchronize()
+            us = a.elapsed_time(b) * 1e3 / (args.kernel_reps * RING)
+            per_kernel[M] = us
+            del g
+
+    step_bytes = sum(algorithmic_bytes(M) for M in MS)
+    value = step_bytes / (ms_step * 1e-3) / 1e9
+    dom = max(MS, key=lambda M: per_kernel[M])
+    ach = algorithmic_bytes(dom) / (per_kernel[dom] * 1e-6) / 1e9
+    detail = {str(M): {"launch": dict(launches[M]._asdict()),
+                       "us_per_call": round(per_kernel[M], 3),
+                       "GBs": round(algorithmic_bytes(M) / (per_kernel[M] * 1e-6) / 1e9, 1),
+                       "pct_peak": round(100 * algorithmic_bytes(M) / (per_kernel[M] * 1e-6)
+                                         / 1e9 / PEAK_GBS, 2)}
+              for M in MS}
+    out = {
+        "metric": "achieved HBM GB/s (and us/call) of the M=1..16 skinny BF16 GEMM sweep",
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "unpooler shard GEMM sweep M=1,2,4,8,16, N=1024, K=4096, "
+                               f"{RING}-layer weight ring, chooser launch shapes",
+                   "global_batch": list(MS), "parallelism": "single GPU shard"},
+        "roofline": {"bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_GBS,
+                     "unit": "GB/s", "frac": round(ach / PEAK_GBS, 4), "traffic": None,
+                     "kernel": f"M={dom} {dict(launches[dom]._asdict())}",
+                     "bytes_per_launch": algorithmic_bytes(dom),
+                     "us_per_launch": round(per_kernel[dom], 3)},
+        "per_m": detail,
+        "wall_s": round(wall, 3),
+    }
+    if not args.no_cpu:
+        log("timing the CPU oracle baseline")
+        out["cpu_baseline"] = cpu_baseline()
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    sys.path.insert(0, os.path.dirname(os.path.abspath(__file__)))
+    main()

@@ -1,0 +1,155 @@
+/*
+ * libskinny — the small-M decode GEMM and its NVFP4 expert-input epilogue for
+ * AMD Instinct MI355X (gfx950).
+ *
+ * What is computed follows three vLLM API pages on the Muse Spark specialized
+ * decode:
+ *   - "vllm.models.muse_spark.nvidia.specialized_decode.cutedsl.gemm.unpooler"
+ *     (module description; Unpooler.run; Unpooler.unsupported;
+ *     launch_unsupported): y[M, N] = x[M, K] @ W[N, K]^T, BF16 in and out,
+ *     FP32 accumulation, 1 <= M <= 16, split-K partials summed in an order
+ *     fixed by the launch shape so that runs are bitwise reproducible.
+ *   - "vllm.models.muse_spark.nvidia.specialized_decode.cutedsl.moe.pooler_gather"
+ *     (module description; compile_norm_quant; cvt_e2m1x8_f32;
+ *     cvt_f32_to_e4m3; nvfp4_compute_output_scale): RMSNorm with a gain
+ *     center, then block-16 NVFP4 quantization.
+ *   - "vllm.models.muse_spark.nvidia.specialized_decode.cutedsl.oproj.batt"
+ *     (OProjection): the o_proj shard runs on the same small-M GEMM.
+ *
+ * Conventions for every entry point:
+ *   - Tensor arguments are DEVICE pointers owned by the caller.  The library
+ *     never allocates, frees or keeps them.  Row-major, contiguous.
+ *   - bfloat16 data is passed as its 16-bit patterns.
+ *   - `stream` is a hipStream_t (NULL = the default stream).  Work is only
+ *     enqueued; no call synchronizes with the host.
+ *   - Arguments are checked on the host before anything is enqueued.  A bad
+ *     argument returns a negative skinny_status and enqueues nothing;
+ *     skinny_last_error() then gives the reason (thread-local string).
+ *   - After skinny_init(), the compute calls allocate nothing, compile nothing
+ *     and never synchronize, so they may be recorded into a HIP graph.
+ */
+#ifndef SKINNY_H
+#define SKINNY_H
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum skinny_status {
+  SKINNY_OK = 0,
+  SKINNY_EINVAL = -1,      /* null or misaligned pointer, bad M/N/K/P, overlap */
+  SKINNY_EUNSUPPORTED = -2,/* valid problem, but no launch for this shape      */
+  SKINNY_EDEVICE = -3,     /* no device, or the device is not gfx950          */
+  SKINNY_ELAUNCH = -4,     /* the HIP runtime refused the launch              */
+  SKINNY_ENOTINIT = -5     /* compute call on a device before skinny_init()   */
+} skinny_status;
+
+/* Kernel families of the GEMM. */
+enum {
+  SKINNY_PATH_DOT2 = 0, /* VALU bf16 dot2: lanes run along K, any row count  */
+  SKINNY_PATH_MFMA = 1  /* bf16 MFMA 16x16x32: 16 weight rows x 16 tokens    */
+};
+
+/* A launch shape of the GEMM: the counterpart of the unpooler page's
+ * UnpoolerShape (splits, kw, accs) and the pooler page's PoolerGemmShape.
+ * The launch is fully determined by (M, N, K, skinny_launch); the summation
+ * order depends only on it.
+ *
+ *   MFMA: a workgroup owns 16 output features (one MFMA tile) and one of
+ *         `splits` K ranges; each of its `waves` waves owns kw = 32 * chunks
+ *         consecutive K of that range and keeps `accs` FP32 accumulators.
+ *   DOT2: a workgroup owns `rows` output features; each wave owns
+ *         kw = 512 * chunks consecutive K (64 lanes x 8 bf16 per chunk).
+ * In both, wave partials are summed in LDS in wave order, and with
+ * splits > 1 the workgroup partials of one tile are summed in split order by
+ * whichever workgroup of the tile finishes last. */
+typedef struct skinny_launch {
+  int path;   /* SKINNY_PATH_MFMA or SKINNY_PATH_DOT2                       */
+  int splits; /* S in {1, 2, 4, 8}: workgroups along K per output tile        */
+  int waves;  /* waves per workgroup, 1..16; waves = ceil(K / (splits * kw))  */
+  int chunks; /* K chunks per wave (MFMA 1..16, DOT2 1..4)                   */
+  int accs;   /* MFMA: accumulators per wave, 1, 2 or 4; DOT2: 1           */
+  int rows;   /* output features per workgroup: 16 (MFMA) or 2..16 (DOT2)    */
+} skinny_launch;
+
+/* Prepare `device` (a HIP ordinal) for the compute calls: checks that it is a
+ * gfx950 GPU and allocates the library's split-K workspace on it (8 MiB of
+ * FP32 partials and 256 KiB of self-resetting tile counters).  Call it before
+ * any graph capture.  Idempotent.  Returns SKINNY_OK, SKINNY_EDEVICE or
+ * SKINNY_ELAUNCH (allocation failure). */
+int skinny_init(int device);
+
+/* y[M, N] = bf16( x[M, K] @ W[N, K]^T ), FP32 accumulation (unpooler page,
+ * module description and Unpooler.run).
+ *   x       bf16 [M, K], 16-byte aligned
+ *   W       bf16 [N, K], 16-byte aligned
+ *   y       bf16 [M, N], 16-byte aligned; only these M rows are written
+ *   M       1..16 tokens
+ *   N       output features, N > 0, N % 16 == 0
+ *   K       reduction length, K > 0, K % 8 == 0 (16-byte rows)
+ *   splits  0 = let the chooser pick; otherwise S in {1, 2, 4, 8}
+ * x, W and y must not overlap.  The result is bitwise identical for the same
+ * (M, N, K, launch) on one device.  Calls with splits > 1 on the same device
+ * share the workspace: the caller must not run two of them concurrently on
+ * different streams.  Errors: SKINNY_EINVAL, SKINNY_EUNSUPPORTED,
+ * SKINNY_ENOTINIT, SKINNY_ELAUNCH. */
+int skinny_gemm_bf16(const void *x, const void *W, void *y, int M, int N,
+                     int K, int splits, void *stream);
+
+/* The same GEMM at an explicit launch shape (for sweeps and tests). */
+int skinny_gemm_bf16_launch(const void *x, const void *W, void *y, int M,
+                            int N, int K, const skinny_launch *launch,
+                            void *stream);
+
+/* The chooser: the launch shape skinny_gemm_bf16 uses for (M, N, K, splits).
+ * Pure host function of its arguments.  Returns SKINNY_OK and fills *out, or
+ * SKINNY_EINVAL / SKINNY_EUNSUPPORTED with the reason in skinny_last_error(). */
+int skinny_choose(int M, int N, int K, int splits, skinny_launch *out);
+
+/* Why there is no launch for (M, N, K, splits): the status the GEMM would
+ * return for valid pointers (the unpooler page's Unpooler.unsupported and
+ * launch_unsupported).  SKINNY_OK when supported; the reason otherwise in
+ * skinny_last_error().  Host only. */
+int skinny_gemm_unsupported(int M, int N, int K, int splits);
+
+/* Why (M, N, K) cannot run at `launch`; SKINNY_OK when it can.  Host only. */
+int skinny_launch_unsupported(int M, int N, int K, const skinny_launch *launch);
+
+/* The NVFP4 expert input (pooler_gather page, module description and
+ * compile_norm_quant; nvfp4_compute_output_scale; cvt_e2m1x8_f32;
+ * cvt_f32_to_e4m3), for each of the M rows of r:
+ *   yn   = bf16( r * rsqrt(mean(r^2) + eps) * (norm_w + gain_center) )
+ *   per 16-column block b:  sf_b = e4m3fn_rn_satfinite(gs * amax_b(|yn|) / 6)
+ *                           os_b = gs / dec(sf_b), 0 when dec(sf_b) == 0
+ *                           q_j  = e2m1_rn_satfinite(yn_j * os_b)
+ *   r            bf16 [M, P], 16-byte aligned
+ *   norm_w       bf16 [P], 16-byte aligned
+ *   gain_center, eps   FP32 scalars (host values)
+ *   global_scale FP32 [1] on the device, 4-byte aligned
+ *   a            u8 [M, P / 2]: byte i = q_{2i} | q_{2i+1} << 4 (even column in
+ *                the low nibble), 8-byte aligned
+ *   a_sf         u8 [M, P / 16]: e4m3fn scale bytes, row-major, not swizzled
+ *   M >= 1 rows; P > 0, P % 16 == 0
+ * r and the outputs must not overlap.  Errors: SKINNY_EINVAL,
+ * SKINNY_ENOTINIT, SKINNY_ELAUNCH. */
+int skinny_rmsnorm_nvfp4(const void *r, const void *norm_w, float gain_center,
+                         float eps, const float *global_scale, void *a,
+                         void *a_sf, int M, int P, void *stream);
+
+/* The BF16 edge-layer form of the same norm (pooler_gather page, module
+ * description, "BF16 edge layers"): y = yn above, bf16 [M, P], 16-byte
+ * aligned, with no quantization.  Same arguments and errors otherwise. */
+int skinny_rmsnorm_bf16(const void *r, const void *norm_w, float gain_center,
+                        float eps, void *y, int M, int P, void *stream);
+
+/* The reason for the last non-OK status on this thread ("" if none). */
+const char *skinny_last_error(void);
+
+/* Library ABI version: major * 100 + minor. */
+int skinny_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SKINNY_H */

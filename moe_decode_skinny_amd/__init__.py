@@ -1,0 +1,222 @@
+"""moe_decode_skinny_amd: the small-M decode GEMM and its NVFP4 expert-input
+epilogue on AMD Instinct MI355X (gfx950).
+
+A thin ctypes binding over the C ABI of ``libskinny.so`` (declared in
+``include/skinny.h``).  It only marshals arguments: every step runs in the HIP
+kernels of the library.  PyTorch provides device memory and streams.  If the
+library has not been built this module raises ImportError; there is no
+fallback.
+
+Same names as the C ABI:
+  skinny_init, skinny_gemm_bf16, skinny_gemm_bf16_launch, skinny_choose,
+  skinny_gemm_unsupported, skinny_launch_unsupported, skinny_rmsnorm_nvfp4,
+  skinny_rmsnorm_bf16, skinny_last_error, skinny_version
+Status codes map to exceptions as on the unpooler page (Unpooler.run /
+Unpooler.unsupported): EINVAL and EUNSUPPORTED raise ValueError, the others
+RuntimeError.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import NamedTuple, Optional
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libskinny.so")
+
+SKINNY_OK = 0
+SKINNY_EINVAL = -1
+SKINNY_EUNSUPPORTED = -2
+SKINNY_EDEVICE = -3
+SKINNY_ELAUNCH = -4
+SKINNY_ENOTINIT = -5
+SKINNY_PATH_DOT2 = 0
+SKINNY_PATH_MFMA = 1
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(
+        f"{LIB_PATH} is not built; run `python -m moe_decode_skinny_amd.build` "
+        "(there is no CPU fallback)")
+
+_lib = ctypes.CDLL(LIB_PATH)
+
+
+class _CLaunch(ctypes.Structure):
+    _fields_ = [("path", ctypes.c_int), ("splits", ctypes.c_int), ("waves", ctypes.c_int),
+                ("chunks", ctypes.c_int), ("accs", ctypes.c_int), ("rows", ctypes.c_int)]
+
+
+class Launch(NamedTuple):
+    """skinny_launch: path (0 DOT2, 1 MFMA), splits, waves, chunks, accs, rows."""
+    path: int
+    splits: int
+    waves: int
+    chunks: int
+    accs: int
+    rows: int
+
+    def _c(self) -> _CLaunch:
+        return _CLaunch(*self)
+
+
+_vp = ctypes.c_void_p
+_i = ctypes.c_int
+_f = ctypes.c_float
+_sig = {
+    "skinny_init": ([_i], _i),
+    "skinny_gemm_bf16": ([_vp, _vp, _vp, _i, _i, _i, _i, _vp], _i),
+    "skinny_gemm_bf16_launch": ([_vp, _vp, _vp, _i, _i, _i, ctypes.POINTER(_CLaunch), _vp], _i),
+    "skinny_choose": ([_i, _i, _i, _i, ctypes.POINTER(_CLaunch)], _i),
+    "skinny_gemm_unsupported": ([_i, _i, _i, _i], _i),
+    "skinny_launch_unsupported": ([_i, _i, _i, ctypes.POINTER(_CLaunch)], _i),
+    "skinny_rmsnorm_nvfp4": ([_vp, _vp, _f, _f, _vp, _vp, _vp, _i, _i, _vp], _i),
+    "skinny_rmsnorm_bf16": ([_vp, _vp, _f, _f, _vp, _i, _i, _vp], _i),
+    "skinny_last_error": ([], ctypes.c_char_p),
+    "skinny_version": ([], _i),
+}
+for _name, (_args, _res) in _sig.items():
+    _fn = getattr(_lib, _name)
+    _fn.argtypes = _args
+    _fn.restype = _res
+
+
+def skinny_last_error() -> str:
+    return _lib.skinny_last_error().decode()
+
+
+def skinny_version() -> int:
+    return _lib.skinny_version()
+
+
+def _check(status: int) -> None:
+    if status == SKINNY_OK:
+        return
+    msg = skinny_last_error()
+    if status in (SKINNY_EINVAL, SKINNY_EUNSUPPORTED):
+        raise ValueError(msg)
+    raise RuntimeError(f"libskinny status {status}: {msg}")
+
+
+def _stream(stream, device) -> Optional[int]:
+    import torch
+
+    if stream is None:
+        stream = torch.cuda.current_stream(device)
+    return getattr(stream, "cuda_stream", stream)
+
+
+def _dev_tensor(t, name, dtype):
+    import torch
+
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be on a GPU")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t.data_ptr()
+
+
+def skinny_init(device: int = 0) -> None:
+    """Check that `device` is gfx950 and allocate the split-K workspace."""
+    _check(_lib.skinny_init(int(device)))
+
+
+def init(device: int = 0) -> None:
+    skinny_init(device)
+
+
+def skinny_choose(M: int, N: int, K: int, splits: int = 0) -> Launch:
+    out = _CLaunch()
+    _check(_lib.skinny_choose(M, N, K, splits, ctypes.byref(out)))
+    return Launch(out.path, out.splits, out.waves, out.chunks, out.accs, out.rows)
+
+
+def skinny_gemm_unsupported(M: int, N: int, K: int, splits: int = 0) -> Optional[str]:
+    st = _lib.skinny_gemm_unsupported(M, N, K, splits)
+    return None if st == SKINNY_OK else skinny_last_error()
+
+
+def skinny_launch_unsupported(M: int, N: int, K: int, launch: Launch) -> Optional[str]:
+    c = Launch(*launch)._c()
+    st = _lib.skinny_launch_unsupported(M, N, K, ctypes.byref(c))
+    return None if st == SKINNY_OK else skinny_last_error()
+
+
+def _gemm_args(x, w, y):
+    import torch
+
+    xp = _dev_tensor(x, "x", torch.bfloat16)
+    wp = _dev_tensor(w, "W", torch.bfloat16)
+    yp = _dev_tensor(y, "y", torch.bfloat16)
+    if x.dim() != 2 or w.dim() != 2 or y.dim() != 2:
+        raise ValueError("x, W and y must be 2-D")
+    M, K = x.shape
+    N = w.shape[0]
+    if w.shape[1] != K or tuple(y.shape) != (M, N):
+        raise ValueError(f"shapes x{tuple(x.shape)} W{tuple(w.shape)} y{tuple(y.shape)}")
+    return xp, wp, yp, M, N, K
+
+
+def skinny_gemm_bf16(x, w, y, splits: int = 0, stream=None):
+    """y[M, N] = x[M, K] @ W[N, K]^T into the caller's y; returns y."""
+    xp, wp, yp, M, N, K = _gemm_args(x, w, y)
+    _check(_lib.skinny_gemm_bf16(xp, wp, yp, M, N, K, splits, _stream(stream, x.device)))
+    return y
+
+
+def skinny_gemm_bf16_launch(x, w, y, launch: Launch, stream=None):
+    """The GEMM at an explicit launch shape; returns y."""
+    xp, wp, yp, M, N, K = _gemm_args(x, w, y)
+    c = Launch(*launch)._c()
+    _check(_lib.skinny_gemm_bf16_launch(xp, wp, yp, M, N, K, ctypes.byref(c),
+                                        _stream(stream, x.device)))
+    return y
+
+
+def skinny_rmsnorm_nvfp4(r, norm_w, gain_center: float, eps: float, global_scale, a, a_sf,
+                         stream=None):
+    """NVFP4 expert input of the rows of r into a [M, P/2] u8 and a_sf [M, P/16] u8."""
+    import torch
+
+    rp = _dev_tensor(r, "r", torch.bfloat16)
+    wp = _dev_tensor(norm_w, "norm_w", torch.bfloat16)
+    gp = _dev_tensor(global_scale, "global_scale", torch.float32)
+    ap = _dev_tensor(a, "a", torch.uint8)
+    sp = _dev_tensor(a_sf, "a_sf", torch.uint8)
+    if r.dim() != 2:
+        raise ValueError("r must be 2-D")
+    M, P = r.shape
+    if (tuple(norm_w.shape) != (P,) or global_scale.numel() != 1
+            or tuple(a.shape) != (M, P // 2) or tuple(a_sf.shape) != (M, P // 16)):
+        raise ValueError("norm_w [P], global_scale [1], a [M, P/2], a_sf [M, P/16]")
+    _check(_lib.skinny_rmsnorm_nvfp4(rp, wp, float(gain_center), float(eps), gp, ap, sp,
+                                     M, P, _stream(stream, r.device)))
+    return a, a_sf
+
+
+def skinny_rmsnorm_bf16(r, norm_w, gain_center: float, eps: float, y, stream=None):
+    """BF16 edge-layer norm of the rows of r into y [M, P]."""
+    import torch
+
+    rp = _dev_tensor(r, "r", torch.bfloat16)
+    wp = _dev_tensor(norm_w, "norm_w", torch.bfloat16)
+    yp = _dev_tensor(y, "y", torch.bfloat16)
+    if r.dim() != 2 or tuple(y.shape) != tuple(r.shape):
+        raise ValueError("r and y must be [M, P]")
+    M, P = r.shape
+    if tuple(norm_w.shape) != (P,):
+        raise ValueError("norm_w must be [P]")
+    _check(_lib.skinny_rmsnorm_bf16(rp, wp, float(gain_center), float(eps), yp, M, P,
+                                    _stream(stream, r.device)))
+    return y
+
+
+__all__ = [
+    "Launch", "init", "skinny_init", "skinny_gemm_bf16", "skinny_gemm_bf16_launch",
+    "skinny_choose", "skinny_gemm_unsupported", "skinny_launch_unsupported",
+    "skinny_rmsnorm_nvfp4", "skinny_rmsnorm_bf16", "skinny_last_error", "skinny_version",
+    "LIB_PATH",
+]

@@ -1,0 +1,220 @@
+// The DOT2 (VALU) path of the small-M decode GEMM y[M, N] = x[M, K] @ W[N, K]^T
+// (unpooler page, module description), for few tokens.
+//
+// At M = 1 a 16-token MFMA tile wastes 15/16 of its work and forces 16
+// features per workgroup; here lanes run along K instead, so a workgroup can
+// own any number of rows and a wave-wide load is 1 KiB of one weight row:
+//   wave w of workgroup (group, s) owns K range (s * waves + w) * kw,
+//   kw = 512 * CHUNKS; lane l reads W[row][k + 8 l .. + 8] for each of the
+//   workgroup's ROWS rows (weights first, as the pages order their loads),
+//   then x[t][same k] for t < M, and accumulates 8 products per (row, token)
+//   with four v_dot2_f32_bf16 (FP32 accumulation of exact bf16 products).
+// Reduction in an order fixed by the launch shape (module description):
+//   a butterfly over the 64 lanes (xor 32, 16, .., 1: every lane ends with the
+//   same bits), waves 0..waves-1 in order through LDS, and with S > 1 the
+//   workgroup partials s = 0..S-1 in order by the last workgroup to arrive at
+//   the group's counter (which it resets).
+#include "internal.h"
+
+namespace skinny {
+namespace {
+
+__device__ __forceinline__ float dot8(u32x4 a, u32x4 b, float c) {
+  c = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a.x),
+                                      __builtin_bit_cast(bf16x2, b.x), c, false);
+  c = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a.y),
+                                      __builtin_bit_cast(bf16x2, b.y), c, false);
+  c = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a.z),
+                                      __builtin_bit_cast(bf16x2, b.z), c, false);
+  c = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a.w),
+                                      __builtin_bit_cast(bf16x2, b.w), c, false);
+  return c;
+}
+
+constexpr int kDot2MaxThreads = 512;
+
+template <int ROWS, int CHUNKS, int MT>
+__global__ __launch_bounds__(kDot2MaxThreads) void gemm_dot2_kernel(
+    const uint16_t *__restrict__ x, const uint16_t *__restrict__ w,
+    uint16_t *__restrict__ y, float *__restrict__ partials,
+    unsigned *__restrict__ counters, int M, int N, int K, int S, int groups,
+    int kw) {
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int waves = blockDim.x >> 6;
+
+  int group, s;
+  const int b = blockIdx.x;
+  if ((groups & 7) == 0) {  // the S workgroups of a group share an XCD
+    const int xcd = b & 7, slot = b >> 3;
+    group = (slot / S) * 8 + xcd;
+    s = slot % S;
+  } else {
+    group = b / S;
+    s = b % S;
+  }
+  const int f0 = group * ROWS;
+  // K offset of this lane's 8 elements in chunk 0 of its slice; lanes past K
+  // and tokens >= M read past their buffer resource and get zeros.
+  const int k0 = (s * waves + wave) * kw + lane * 8;
+  const __amdgpu_buffer_rsrc_t wres =
+      buffer_rsrc(w + (size_t)f0 * K, (unsigned)(ROWS * K * 2));
+  const __amdgpu_buffer_rsrc_t xres = buffer_rsrc(x, (unsigned)(M * K * 2));
+
+  u32x4 wv[ROWS][CHUNKS];
+#pragma unroll
+  for (int c = 0; c < CHUNKS; ++c) {
+    const bool in = k0 + c * kDot2K < K;
+#pragma unroll
+    for (int r = 0; r < ROWS; ++r)
+      wv[r][c] = __builtin_amdgcn_raw_buffer_load_b128(
+          wres, in ? (r * K + k0 + c * kDot2K) * 2 : kOutOfRange, 0, kCacheNT);
+  }
+  // All loads in flight before the first wait (no sinking below the math).
+  __builtin_amdgcn_sched_barrier(0);
+  u32x4 xv[MT][CHUNKS];
+#pragma unroll
+  for (int c = 0; c < CHUNKS; ++c) {
+    const bool in = k0 + c * kDot2K < K;
+#pragma unroll
+    for (int t = 0; t < MT; ++t)
+      xv[t][c] = __builtin_amdgcn_raw_buffer_load_b128(
+          xres, in ? (t * K + k0 + c * kDot2K) * 2 : kOutOfRange, 0, 0);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+
+  float acc[ROWS][MT];
+#pragma unroll
+  for (int r = 0; r < ROWS; ++r)
+#pragma unroll
+    for (int t = 0; t < MT; ++t) acc[r][t] = 0.f;
+#pragma unroll
+  for (int c = 0; c < CHUNKS; ++c)
+#pragma unroll
+    for (int r = 0; r < ROWS; ++r)
+#pragma unroll
+      for (int t = 0; t < MT; ++t) acc[r][t] = dot8(wv[r][c], xv[t][c], acc[r][t]);
+
+  // Lane butterfly: afterwards every lane holds the wave's sums.
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1)
+#pragma unroll
+    for (int r = 0; r < ROWS; ++r)
+#pragma unroll
+      for (int t = 0; t < MT; ++t) acc[r][t] += __shfl_xor(acc[r][t], off);
+
+  // Waves in order through LDS; lane i < ROWS * MT then owns (row i % ROWS,
+  // token i / ROWS).
+  constexpr int kOut = ROWS * MT;
+  __shared__ float red[kDot2MaxThreads / 64][kOut];
+  if (lane == 0) {
+#pragma unroll
+    for (int r = 0; r < ROWS; ++r)
+#pragma unroll
+      for (int t = 0; t < MT; ++t) red[wave][t * ROWS + r] = acc[r][t];
+  }
+  __syncthreads();
+  if (wave != 0) return;
+  const int r = lane % ROWS, t = lane / ROWS;
+  const bool live = lane < kOut && t < M;
+  float part = 0.f;
+  if (lane < kOut) {
+    part = red[0][lane];
+    for (int v = 1; v < waves; ++v) part += red[v][lane];
+  }
+
+  if (S > 1) {
+    float *ws = partials + (size_t)group * S * kOut;
+    if (live) ws[s * kOut + lane] = part;
+    __threadfence();
+    unsigned prev = 0;
+    if (lane == 0) prev = atomicAdd(&counters[group], 1u);
+    prev = __builtin_amdgcn_readfirstlane(prev);
+    if (prev != (unsigned)(S - 1)) return;
+    __threadfence();
+    if (live) {
+      float sum = s == 0 ? part : ws[lane];
+      for (int j = 1; j < S; ++j) sum += (j == s) ? part : ws[j * kOut + lane];
+      part = sum;
+    }
+    if (lane == 0)
+      __hip_atomic_store(&counters[group], 0u, __ATOMIC_RELAXED,
+                         __HIP_MEMORY_SCOPE_AGENT);
+  }
+  if (live) y[(size_t)t * N + f0 + r] = (uint16_t)f32_to_bf16(part);
+}
+
+using Dot2Kernel = void (*)(const uint16_t *, const uint16_t *, uint16_t *,
+                            float *, unsigned *, int, int, int, int, int, int);
+
+// Register budget per lane: weights 4 * ROWS * CHUNKS, activations
+// 4 * MT * CHUNKS, sums ROWS * MT.  Variants above the budget are not built.
+constexpr bool fits(int rows, int chunks, int mt) {
+  return 4 * rows * chunks + 4 * mt * chunks + rows * mt <= 160;
+}
+
+template <int R, int C, int T>
+constexpr Dot2Kernel variant() {
+  if constexpr (fits(R, C, T)) return gemm_dot2_kernel<R, C, T>;
+  else return nullptr;
+}
+
+template <int R, int C>
+Dot2Kernel pick_mt(int mt) {
+  switch (mt) {
+    case 1: return variant<R, C, 1>();
+    case 2: return variant<R, C, 2>();
+    case 4: return variant<R, C, 4>();
+    case 8: return variant<R, C, 8>();
+  }
+  return nullptr;
+}
+
+template <int R>
+Dot2Kernel pick_chunks(int chunks, int mt) {
+  switch (chunks) {
+    case 1: return pick_mt<R, 1>(mt);
+    case 2: return pick_mt<R, 2>(mt);
+    case 4: return pick_mt<R, 4>(mt);
+  }
+  return nullptr;
+}
+
+Dot2Kernel pick(int rows, int chunks, int mt) {
+  switch (rows) {
+    case 2: return pick_chunks<2>(chunks, mt);
+    case 4: return pick_chunks<4>(chunks, mt);
+    case 8: return pick_chunks<8>(chunks, mt);
+    case 16: return pick_chunks<16>(chunks, mt);
+  }
+  return nullptr;
+}
+
+}  // namespace
+
+int dot2_token_tile(int M) {
+  if (M <= 1) return 1;
+  if (M <= 2) return 2;
+  if (M <= 4) return 4;
+  if (M <= 8) return 8;
+  return 0;
+}
+
+bool dot2_variant_exists(int rows, int chunks, int mt) {
+  return pick(rows, chunks, mt) != nullptr;
+}
+
+int dot2_max_waves() { return kDot2MaxThreads / 64; }
+
+hipError_t launch_gemm_dot2(const uint16_t *x, const uint16_t *w, uint16_t *y,
+                            int M, int N, int K, const skinny_launch &l,
+                            DeviceState &st, hipStream_t stream) {
+  Dot2Kernel k = pick(l.rows, l.chunks, dot2_token_tile(M));
+  const int groups = N / l.rows;
+  dim3 grid(groups * l.splits), block(64 * l.waves);
+  hipLaunchKernelGGL(k, grid, block, 0, stream, x, w, y, st.partials, st.counters,
+                     M, N, K, l.splits, groups, kDot2K * l.chunks);
+  return hipGetLastError();
+}
+
+}  // namespace skinny

@@ -1,0 +1,93 @@
+// Internal declarations shared by the libskinny translation units: device
+// helpers, the per-device state and the kernel launchers.  Not installed.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "skinny.h"
+
+namespace skinny {
+
+// ---------------------------------------------------------------- limits
+constexpr int kMaxM = 16;          // tokens (unpooler page: 1 <= M <= 16)
+constexpr int kTileN = 16;         // features per MFMA tile (grid N / 16)
+constexpr int kMfmaK = 32;         // K per v_mfma_f32_16x16x32_bf16
+constexpr int kDot2K = 512;        // K per DOT2 chunk: 64 lanes x 8 bf16
+constexpr int kMaxWaves = 16;      // 1024 threads per workgroup
+constexpr int kMaxMfmaChunks = 16;
+constexpr int kMaxDot2Chunks = 4;
+// Split-K workspace owned by the library (per device, from skinny_init).
+constexpr size_t kWorkspaceFloats = size_t(2) << 20;  // 8 MiB of FP32 partials
+constexpr int kMaxCounters = 65536;                   // one per output tile
+
+struct DeviceState {
+  bool ready = false;
+  float *partials = nullptr;   // kWorkspaceFloats
+  unsigned *counters = nullptr;  // kMaxCounters, zero between launches
+  int cus = 0;
+};
+
+// The state of the current HIP device, or nullptr (and a reason) if the
+// device has not been initialised.
+DeviceState *current_state(int *status);
+
+void set_error(const char *fmt, ...);
+
+// ------------------------------------------------------------- launchers
+// Each returns hipSuccess or the launch error; arguments are already valid.
+hipError_t launch_gemm_mfma(const uint16_t *x, const uint16_t *w, uint16_t *y,
+                            int M, int N, int K, const skinny_launch &l,
+                            DeviceState &st, hipStream_t stream);
+hipError_t launch_gemm_dot2(const uint16_t *x, const uint16_t *w, uint16_t *y,
+                            int M, int N, int K, const skinny_launch &l,
+                            DeviceState &st, hipStream_t stream);
+hipError_t launch_rmsnorm(const uint16_t *r, const uint16_t *w, float gain_center,
+                          float eps, const float *global_scale, uint8_t *a,
+                          uint8_t *a_sf, uint16_t *y, int M, int P, bool quant,
+                          hipStream_t stream);
+
+// Instantiation tables (which template variants exist), used by validation.
+bool mfma_variant_exists(int chunks, int accs);
+int mfma_max_waves(int chunks);  // waves per MFMA workgroup (launch bound)
+bool dot2_variant_exists(int rows, int chunks, int mt);
+int dot2_token_tile(int M);  // smallest compiled token count >= M, 0 if none
+int dot2_max_waves();        // waves per DOT2 workgroup (launch bound)
+
+}  // namespace skinny
+
+// ------------------------------------------------------------ device helpers
+#if defined(__HIPCC__)
+namespace skinny {
+
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// FP32 -> bfloat16 bits, round to nearest even; NaN stays a quiet NaN.
+__device__ __forceinline__ unsigned f32_to_bf16(float f) {
+  unsigned u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+
+__device__ __forceinline__ float bf16_lo(unsigned u) { return __uint_as_float(u << 16); }
+
+// Raw buffer resource over [base, base + bytes): loads at offsets >= bytes
+// return zeros instead of touching memory, which gives token padding and
+// ragged-K tails without branches.  bytes must be < 2^31.
+constexpr unsigned kBufferFlags = 0x00020000u;  // gfx9 dword3: 32-bit data format
+constexpr int kOutOfRange = 0x7FFFF000;         // an offset past any resource used here
+constexpr int kCacheNT = 2;                     // nontemporal (streaming) load policy
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void *base, unsigned bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes,
+                                           (int)kBufferFlags);
+}
+__device__ __forceinline__ float bf16_hi(unsigned u) { return __uint_as_float(u & 0xffff0000u); }
+
+}  // namespace skinny
+#endif

@@ -1,0 +1,164 @@
+// RMSNorm with gain center and the block-16 NVFP4 expert input
+// (pooler_gather page, module description and compile_norm_quant):
+//   yn = bf16( r * rsqrt(mean(r^2) + eps) * (w + gain_center) )
+//   a, a_sf = nvfp4(yn, global_scale, block 16)
+// with the conversions of cvt_e2m1x8_f32 / cvt_f32_to_e4m3 (round to nearest
+// even, saturate to the largest finite value) and the output scale of
+// nvfp4_compute_output_scale (the reciprocal of dec(sf) / global_scale, zero
+// when dec(sf) is zero).
+//
+// gfx950 design: one workgroup of 256 threads per row; thread t owns whole
+// 16-column blocks (t, t + 256, ...), so a block's amax, scale and codes stay
+// in one thread and its 8 code bytes leave as one 8-byte store.  The sum of
+// squares is reduced in a fixed order: per thread in column order, a lane
+// butterfly inside each wave, then the four wave sums in wave order.
+// The e4m3 and e2m1 encoders are written out in integer/compare form here
+// (no vendor conversion instruction), so rounding and saturation are exactly
+// the round-to-nearest-even + satfinite the pages specify.
+// Readings (the norm/quant kernel body is not printed): the block scale is
+// e4m3(global_scale * amax / 6); the FP32 output scale is global_scale /
+// dec(sf) rounded once; a negative value that rounds to zero keeps its sign.
+#include "internal.h"
+
+namespace skinny {
+namespace {
+
+constexpr int kNormThreads = 256;
+
+// |v| -> e4m3fn code, round to nearest even, saturating at 448 (0x7E).
+__device__ __forceinline__ unsigned e4m3_rn_satfinite(float v) {
+  const unsigned sign = (__float_as_uint(v) >> 24) & 0x80u;
+  const float a = fabsf(v);
+  if (a != a) return 0x7Fu;
+  if (a >= 448.0f) return sign | 0x7Eu;
+  if (a < 0.015625f) {                              // below 2^-6: step 2^-9
+    return sign | (unsigned)rintf(a * 512.0f);      // 8 -> 0x08 = 2^-6
+  }
+  unsigned b = __float_as_uint(a);
+  b += 0x7FFFFu + ((b >> 20) & 1u);                 // keep 3 mantissa bits, RNE
+  const unsigned exp = (b >> 23) - 127u + 7u;       // 1..15
+  return sign | (exp << 3) | ((b >> 20) & 7u);
+}
+
+// e4m3fn code (finite, non-negative) -> its value (exact in FP32).
+__device__ __forceinline__ float e4m3_value(unsigned c) {
+  const unsigned exp = (c >> 3) & 15u, man = c & 7u;
+  if (exp == 0) return (float)man * 0.001953125f;  // man * 2^-9
+  return __uint_as_float(((exp + 120u) << 23) | (man << 20));
+}
+
+// v -> e2m1 code: magnitudes 0, .5, 1, 1.5, 2, 3, 4, 6 by index; ties to the
+// even index (the comparison is >= where the upper neighbour is even);
+// anything above 5 saturates to 6; the sign bit is kept.
+__device__ __forceinline__ unsigned e2m1_rn_satfinite(float v) {
+  const float a = fabsf(v);
+  const unsigned idx = (a > 0.25f) + (a >= 0.75f) + (a > 1.25f) + (a >= 1.75f) +
+                       (a > 2.5f) + (a >= 3.5f) + (a > 5.0f);
+  return ((__float_as_uint(v) >> 28) & 8u) | idx;
+}
+
+__device__ __forceinline__ void load16(const uint16_t *p, float (&v)[16]) {
+  const u32x4 a = *reinterpret_cast<const u32x4 *>(p);
+  const u32x4 b = *reinterpret_cast<const u32x4 *>(p + 8);
+  const unsigned u[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    v[2 * i] = bf16_lo(u[i]);
+    v[2 * i + 1] = bf16_hi(u[i]);
+  }
+}
+
+template <bool QUANT>
+__global__ __launch_bounds__(kNormThreads) void rmsnorm_kernel(
+    const uint16_t *__restrict__ r, const uint16_t *__restrict__ w, float gain_center,
+    float eps, const float *__restrict__ global_scale, uint8_t *__restrict__ a,
+    uint8_t *__restrict__ a_sf, uint16_t *__restrict__ y, int P) {
+  const int row = blockIdx.x;
+  const int tid = threadIdx.x;
+  const int blocks = P / 16;
+  const uint16_t *rrow = r + (size_t)row * P;
+
+  // Sum of squares in a fixed order; the first block stays in registers.
+  float first[16];
+  float ss = 0.f;
+  if (tid < blocks) {
+    load16(rrow + tid * 16, first);
+#pragma unroll
+    for (int j = 0; j < 16; ++j) ss += first[j] * first[j];
+  }
+  for (int blk = tid + kNormThreads; blk < blocks; blk += kNormThreads) {
+    float v[16];
+    load16(rrow + blk * 16, v);
+#pragma unroll
+    for (int j = 0; j < 16; ++j) ss += v[j] * v[j];
+  }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) ss += __shfl_xor(ss, off);
+  __shared__ float wave_ss[kNormThreads / 64];
+  if ((tid & 63) == 0) wave_ss[tid >> 6] = ss;
+  __syncthreads();
+  float total = wave_ss[0];
+#pragma unroll
+  for (int i = 1; i < kNormThreads / 64; ++i) total += wave_ss[i];
+  // correctly rounded division and square root (hipcc's default for FP32)
+  const float inv = 1.0f / sqrtf(total / (float)P + eps);
+  const float gs = QUANT ? *global_scale : 0.f;
+
+  for (int blk = tid; blk < blocks; blk += kNormThreads) {
+    float v[16], g[16];
+    if (blk == tid) {
+#pragma unroll
+      for (int j = 0; j < 16; ++j) v[j] = first[j];
+    } else {
+      load16(rrow + blk * 16, v);
+    }
+    load16(w + blk * 16, g);
+    unsigned yb[16];
+    float amax = 0.f;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      yb[j] = f32_to_bf16((v[j] * inv) * (g[j] + gain_center));
+      amax = fmaxf(amax, fabsf(__uint_as_float(yb[j] << 16)));
+    }
+    if constexpr (QUANT) {
+      const unsigned sf = e4m3_rn_satfinite(gs * amax / 6.0f);
+      const float dec = e4m3_value(sf);
+      const float os = dec == 0.f ? 0.f : gs / dec;
+      unsigned lo = 0, hi = 0;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        lo |= e2m1_rn_satfinite(__uint_as_float(yb[j] << 16) * os) << (4 * j);
+        hi |= e2m1_rn_satfinite(__uint_as_float(yb[j + 8] << 16) * os) << (4 * j);
+      }
+      *reinterpret_cast<uint2 *>(a + (size_t)row * (P / 2) + blk * 8) = make_uint2(lo, hi);
+      a_sf[(size_t)row * blocks + blk] = (uint8_t)sf;
+    } else {
+      u32x4 o0, o1;
+      o0.x = yb[0] | (yb[1] << 16);   o0.y = yb[2] | (yb[3] << 16);
+      o0.z = yb[4] | (yb[5] << 16);   o0.w = yb[6] | (yb[7] << 16);
+      o1.x = yb[8] | (yb[9] << 16);   o1.y = yb[10] | (yb[11] << 16);
+      o1.z = yb[12] | (yb[13] << 16); o1.w = yb[14] | (yb[15] << 16);
+      u32x4 *dst = reinterpret_cast<u32x4 *>(y + (size_t)row * P + blk * 16);
+      dst[0] = o0;
+      dst[1] = o1;
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_rmsnorm(const uint16_t *r, const uint16_t *w, float gain_center,
+                          float eps, const float *global_scale, uint8_t *a,
+                          uint8_t *a_sf, uint16_t *y, int M, int P, bool quant,
+                          hipStream_t stream) {
+  dim3 grid(M), block(kNormThreads);
+  if (quant)
+    hipLaunchKernelGGL(rmsnorm_kernel<true>, grid, block, 0, stream, r, w, gain_center,
+                       eps, global_scale, a, a_sf, y, P);
+  else
+    hipLaunchKernelGGL(rmsnorm_kernel<false>, grid, block, 0, stream, r, w, gain_center,
+                       eps, global_scale, a, a_sf, y, P);
+  return hipGetLastError();
+}
+
+}  // namespace skinny

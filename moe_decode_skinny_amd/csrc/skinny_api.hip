@@ -1,0 +1,341 @@
+// The C ABI of libskinny: argument checks, the launch-shape chooser, the
+// per-device workspace and dispatch to the kernels.
+//
+// The checks restate, for gfx950, the unpooler page's Unpooler.unsupported,
+// Unpooler.run and launch_unsupported: N % 16 == 0, 16-byte aligned
+// contiguous BF16 operands, 1 <= M <= 16, splits in {1, 2, 4, 8}, and a K that
+// divides into splits x waves x kw with at most a workgroup's worth of waves.
+// Their reasons come back as strings through skinny_last_error(), like the
+// pages' ValueError(reason).
+#include <stdarg.h>
+#include <stdio.h>
+#include <stdlib.h>
+#include <string.h>
+
+#include <mutex>
+
+#include "internal.h"
+
+namespace skinny {
+namespace {
+
+thread_local char g_error[512] = "";
+
+constexpr int kMaxDevices = 64;
+DeviceState g_state[kMaxDevices];
+std::mutex g_init_mutex;
+
+bool aligned(const void *p, size_t n) { return ((uintptr_t)p % n) == 0; }
+
+// [p, p + bytes) and [q, q + qbytes) intersect
+bool overlap(const void *p, size_t bytes, const void *q, size_t qbytes) {
+  const uintptr_t a = (uintptr_t)p, b = (uintptr_t)q;
+  return a < b + qbytes && b < a + bytes;
+}
+
+int fail(int status, const char *fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_error, sizeof g_error, fmt, ap);
+  va_end(ap);
+  return status;
+}
+
+int check_problem(int M, int N, int K) {
+  if (M < 1 || M > kMaxM)
+    return fail(SKINNY_EINVAL, "M=%d: needs 1 <= M <= %d", M, kMaxM);
+  if (N <= 0 || N % kTileN)
+    return fail(SKINNY_EINVAL, "N=%d: needs N > 0 and N %% %d == 0", N, kTileN);
+  if (K <= 0 || K % 8)
+    return fail(SKINNY_EINVAL, "K=%d: needs K > 0 and K %% 8 == 0 (16-byte rows)", K);
+  if (K > (1 << 25))
+    return fail(SKINNY_EUNSUPPORTED, "K=%d: at most %d (32-bit buffer offsets)", K, 1 << 25);
+  if (N / kTileN > kMaxCounters)
+    return fail(SKINNY_EUNSUPPORTED, "N=%d: more than %d output tiles", N, kMaxCounters);
+  return SKINNY_OK;
+}
+
+int ceil_div(long a, long b) { return (int)((a + b - 1) / b); }
+
+}  // namespace
+
+void set_error(const char *fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_error, sizeof g_error, fmt, ap);
+  va_end(ap);
+}
+
+DeviceState *current_state(int *status) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+    *status = fail(SKINNY_EDEVICE, "no current HIP device");
+    return nullptr;
+  }
+  if (!g_state[dev].ready) {
+    *status = fail(SKINNY_ENOTINIT, "skinny_init(%d) has not been called", dev);
+    return nullptr;
+  }
+  *status = SKINNY_OK;
+  return &g_state[dev];
+}
+
+// Validity of (M, N, K) at an explicit launch shape; the gfx950 restatement
+// of launch_unsupported.
+static int launch_check(int M, int N, int K, const skinny_launch &l) {
+  int st = check_problem(M, N, K);
+  if (st) return st;
+  if (l.splits != 1 && l.splits != 2 && l.splits != 4 && l.splits != 8)
+    return fail(SKINNY_EUNSUPPORTED, "splits=%d: needs 1, 2, 4 or 8", l.splits);
+  if (l.path == SKINNY_PATH_MFMA) {
+    if (l.rows != kTileN)
+      return fail(SKINNY_EUNSUPPORTED, "MFMA launch owns %d rows per workgroup, not %d",
+                  kTileN, l.rows);
+    if (!mfma_variant_exists(l.chunks, l.accs))
+      return fail(SKINNY_EUNSUPPORTED, "no MFMA kernel with chunks=%d accs=%d "
+                  "(chunks 1, 2, 4, 8, 16; accs 1, 2, 4)", l.chunks, l.accs);
+    const long kw = (long)kMfmaK * l.chunks;
+    const int need = ceil_div(K, (long)l.splits * kw);
+    if (l.waves != need)
+      return fail(SKINNY_EUNSUPPORTED, "K=%d does not split into %d x %d waves x %ld "
+                  "(needs %d waves)", K, l.splits, l.waves, kw, need);
+    if (l.waves < 1 || l.waves > mfma_max_waves(l.chunks))
+      return fail(SKINNY_EUNSUPPORTED, "%d waves per workgroup (1..%d at chunks=%d)", l.waves,
+                  mfma_max_waves(l.chunks), l.chunks);
+    const long tiles = N / kTileN;
+    if (l.splits > 1 && tiles * l.splits * 256 > (long)kWorkspaceFloats)
+      return fail(SKINNY_EUNSUPPORTED, "split-K workspace too small for %ld tiles x %d splits",
+                  tiles, l.splits);
+    return SKINNY_OK;
+  }
+  if (l.path == SKINNY_PATH_DOT2) {
+    const int mt = dot2_token_tile(M);
+    if (mt == 0) return fail(SKINNY_EUNSUPPORTED, "DOT2 path takes M <= 8, got %d", M);
+    if (l.accs != 1) return fail(SKINNY_EUNSUPPORTED, "DOT2 launch has accs=1");
+    if (l.rows <= 0 || N % l.rows)
+      return fail(SKINNY_EUNSUPPORTED, "N=%d is not a multiple of rows=%d", N, l.rows);
+    if (!dot2_variant_exists(l.rows, l.chunks, mt))
+      return fail(SKINNY_EUNSUPPORTED, "no DOT2 kernel with rows=%d chunks=%d tokens=%d",
+                  l.rows, l.chunks, mt);
+    const long kw = (long)kDot2K * l.chunks;
+    const int need = ceil_div(K, (long)l.splits * kw);
+    if (l.waves != need)
+      return fail(SKINNY_EUNSUPPORTED, "K=%d does not split into %d x %d waves x %ld "
+                  "(needs %d waves)", K, l.splits, l.waves, kw, need);
+    if (l.waves < 1 || l.waves > dot2_max_waves())
+      return fail(SKINNY_EUNSUPPORTED, "%d waves per workgroup (DOT2: 1..%d)", l.waves,
+                  dot2_max_waves());
+    const long groups = N / l.rows;
+    if (groups > kMaxCounters)
+      return fail(SKINNY_EUNSUPPORTED, "%ld row groups (max %d)", groups, kMaxCounters);
+    if (l.splits > 1 && groups * l.splits * l.rows * mt > (long)kWorkspaceFloats)
+      return fail(SKINNY_EUNSUPPORTED, "split-K workspace too small");
+    return SKINNY_OK;
+  }
+  return fail(SKINNY_EUNSUPPORTED, "unknown path %d", l.path);
+}
+
+// The chooser: a pure function of (M, N, K, splits).
+//   - M <= 2 and N divisible by the row count: DOT2, lanes along K, enough
+//     row groups that the grid covers the 256 CUs without split-K;
+//   - otherwise MFMA: S picked so that tiles * S >= 256 workgroups (capped at
+//     8), then the fewest chunks per wave (1..16, most memory parallelism per
+//     wave) that keep waves <= 16; 2 accumulators when a wave has >= 4 chunks.
+static int choose(int M, int N, int K, int splits, skinny_launch *out) {
+  int st = check_problem(M, N, K);
+  if (st) return st;
+  if (splits != 0 && splits != 1 && splits != 2 && splits != 4 && splits != 8)
+    return fail(SKINNY_EINVAL, "splits=%d: needs 0 (auto), 1, 2, 4 or 8", splits);
+  skinny_launch l{};
+  if (M <= 2) {
+    // DOT2: 1 KiB of a weight row per wave-wide load.
+    const long row_bytes = 2L * K;
+    static const int kRows[] = {16, 8, 4, 2};
+    for (int rows : kRows) {
+      if (N % rows) continue;
+      const long groups = N / rows;
+      if (groups < 256 && rows > 2) continue;  // prefer >= 256 workgroups
+      const int S = splits ? splits : 1;
+      for (int chunks = 1; chunks <= kMaxDot2Chunks; chunks *= 2) {
+        skinny_launch c{SKINNY_PATH_DOT2, S, ceil_div(K, (long)S * kDot2K * chunks), chunks, 1, rows};
+        if (c.waves > dot2_max_waves()) continue;
+        if (!dot2_variant_exists(rows, chunks, dot2_token_tile(M))) continue;
+        (void)row_bytes;
+        l = c;
+        break;
+      }
+      if (l.waves) break;
+    }
+    if (l.waves && launch_check(M, N, K, l) == SKINNY_OK) {
+      *out = l;
+      return SKINNY_OK;
+    }
+    l = skinny_launch{};
+  }
+  const long tiles = N / kTileN;
+  int S = splits;
+  if (S == 0) {
+    S = 1;
+    while (S < 8 && tiles * S < 256 && K >= (long)kMfmaK * 2 * S) S *= 2;
+  }
+  for (;;) {
+    for (int chunks = 1; chunks <= kMaxMfmaChunks; chunks *= 2) {
+      const int waves = ceil_div(K, (long)S * kMfmaK * chunks);
+      if (waves > mfma_max_waves(chunks)) continue;
+      l = skinny_launch{SKINNY_PATH_MFMA, S, waves, chunks, chunks >= 4 ? 2 : 1, kTileN};
+      break;
+    }
+    // an automatic S grows until one workgroup's waves can hold its K range
+    if (l.waves || splits != 0 || S == 8) break;
+    S *= 2;
+  }
+  if (!l.waves)
+    return fail(SKINNY_EUNSUPPORTED, "K=%d too long for %d splits x %d waves x %d",
+                K, S, mfma_max_waves(kMaxMfmaChunks), kMfmaK * kMaxMfmaChunks);
+  st = launch_check(M, N, K, l);
+  if (st) return st;
+  *out = l;
+  return SKINNY_OK;
+}
+
+static int gemm_common(const void *x, const void *W, void *y, int M, int N, int K,
+                       const skinny_launch &l, void *stream) {
+  if (!x || !W || !y) return fail(SKINNY_EINVAL, "null pointer");
+  if (!aligned(x, 16) || !aligned(W, 16) || !aligned(y, 16))
+    return fail(SKINNY_EINVAL, "x, W and y must be 16-byte aligned");
+  const size_t xb = 2ul * M * K, wb = 2ul * N * K, yb = 2ul * M * N;
+  if (overlap(y, yb, x, xb) || overlap(y, yb, W, wb))
+    return fail(SKINNY_EINVAL, "y overlaps x or W");
+  int st = SKINNY_OK;
+  DeviceState *ds = current_state(&st);
+  if (!ds) return st;
+  const uint16_t *xp = static_cast<const uint16_t *>(x);
+  const uint16_t *wp = static_cast<const uint16_t *>(W);
+  uint16_t *yp = static_cast<uint16_t *>(y);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = l.path == SKINNY_PATH_MFMA ? launch_gemm_mfma(xp, wp, yp, M, N, K, l, *ds, s)
+                                            : launch_gemm_dot2(xp, wp, yp, M, N, K, l, *ds, s);
+  if (e != hipSuccess) return fail(SKINNY_ELAUNCH, "launch failed: %s", hipGetErrorString(e));
+  return SKINNY_OK;
+}
+
+static int norm_common(const void *r, const void *norm_w, float gain_center, float eps,
+                       const float *global_scale, void *a, void *a_sf, void *y, int M,
+                       int P, bool quant, void *stream) {
+  if (M < 1 || M > 65535) return fail(SKINNY_EINVAL, "M=%d: needs 1 <= M <= 65535", M);
+  if (P <= 0 || P % 16) return fail(SKINNY_EINVAL, "P=%d: needs P > 0 and P %% 16 == 0", P);
+  if (!r || !norm_w) return fail(SKINNY_EINVAL, "null pointer");
+  if (!aligned(r, 16) || !aligned(norm_w, 16))
+    return fail(SKINNY_EINVAL, "r and norm_w must be 16-byte aligned");
+  const size_t rb = 2ul * M * P;
+  if (quant) {
+    if (!global_scale || !a || !a_sf) return fail(SKINNY_EINVAL, "null pointer");
+    if (!aligned(global_scale, 4)) return fail(SKINNY_EINVAL, "global_scale must be 4-byte aligned");
+    if (!aligned(a, 8)) return fail(SKINNY_EINVAL, "a must be 8-byte aligned");
+    const size_t ab = (size_t)M * P / 2, sb = (size_t)M * P / 16;
+    if (overlap(a, ab, r, rb) || overlap(a_sf, sb, r, rb) || overlap(a, ab, a_sf, sb))
+      return fail(SKINNY_EINVAL, "outputs overlap each other or r");
+  } else {
+    if (!y) return fail(SKINNY_EINVAL, "null pointer");
+    if (!aligned(y, 16)) return fail(SKINNY_EINVAL, "y must be 16-byte aligned");
+    if (overlap(y, rb, r, rb)) return fail(SKINNY_EINVAL, "y overlaps r");
+  }
+  int st = SKINNY_OK;
+  if (!current_state(&st)) return st;
+  hipError_t e = launch_rmsnorm(static_cast<const uint16_t *>(r),
+                                static_cast<const uint16_t *>(norm_w), gain_center, eps,
+                                global_scale, static_cast<uint8_t *>(a),
+                                static_cast<uint8_t *>(a_sf), static_cast<uint16_t *>(y), M,
+                                P, quant, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(SKINNY_ELAUNCH, "launch failed: %s", hipGetErrorString(e));
+  return SKINNY_OK;
+}
+
+}  // namespace skinny
+
+using namespace skinny;
+
+extern "C" {
+
+int skinny_version(void) { return 100; }
+
+const char *skinny_last_error(void) { return g_error; }
+
+int skinny_init(int device) {
+  std::lock_guard<std::mutex> lock(g_init_mutex);
+  int count = 0;
+  if (hipGetDeviceCount(&count) != hipSuccess || count <= 0)
+    return fail(SKINNY_EDEVICE, "no HIP device");
+  if (device < 0 || device >= count || device >= kMaxDevices)
+    return fail(SKINNY_EDEVICE, "device %d out of range (0..%d)", device, count - 1);
+  DeviceState &st = g_state[device];
+  if (st.ready) return SKINNY_OK;
+  hipDeviceProp_t prop;
+  if (hipGetDeviceProperties(&prop, device) != hipSuccess)
+    return fail(SKINNY_EDEVICE, "cannot query device %d", device);
+  if (strncmp(prop.gcnArchName, "gfx950", 6) != 0)
+    return fail(SKINNY_EDEVICE, "device %d is %s; the kernels are built for gfx950",
+                device, prop.gcnArchName);
+  int prev = device;
+  if (hipGetDevice(&prev) != hipSuccess) prev = device;
+  if (hipSetDevice(device) != hipSuccess) return fail(SKINNY_EDEVICE, "cannot select device %d", device);
+  int status = SKINNY_OK;
+  if (hipMalloc(&st.partials, kWorkspaceFloats * sizeof(float)) != hipSuccess ||
+      hipMalloc(&st.counters, kMaxCounters * sizeof(unsigned)) != hipSuccess ||
+      hipMemset(st.counters, 0, kMaxCounters * sizeof(unsigned)) != hipSuccess ||
+      hipDeviceSynchronize() != hipSuccess) {
+    status = fail(SKINNY_ELAUNCH, "workspace allocation failed on device %d", device);
+  } else {
+    st.cus = prop.multiProcessorCount;
+    st.ready = true;
+  }
+  if (hipSetDevice(prev) != hipSuccess && status == SKINNY_OK)
+    status = fail(SKINNY_EDEVICE, "cannot restore device %d", prev);
+  return status;
+}
+
+int skinny_choose(int M, int N, int K, int splits, skinny_launch *out) {
+  if (!out) return fail(SKINNY_EINVAL, "null output");
+  return choose(M, N, K, splits, out);
+}
+
+int skinny_gemm_unsupported(int M, int N, int K, int splits) {
+  skinny_launch l;
+  return choose(M, N, K, splits, &l);
+}
+
+int skinny_launch_unsupported(int M, int N, int K, const skinny_launch *launch) {
+  if (!launch) return fail(SKINNY_EINVAL, "null launch");
+  return launch_check(M, N, K, *launch);
+}
+
+int skinny_gemm_bf16(const void *x, const void *W, void *y, int M, int N, int K,
+                     int splits, void *stream) {
+  skinny_launch l;
+  int st = choose(M, N, K, splits, &l);
+  if (st) return st;
+  return gemm_common(x, W, y, M, N, K, l, stream);
+}
+
+int skinny_gemm_bf16_launch(const void *x, const void *W, void *y, int M, int N, int K,
+                            const skinny_launch *launch, void *stream) {
+  if (!launch) return fail(SKINNY_EINVAL, "null launch");
+  int st = launch_check(M, N, K, *launch);
+  if (st) return st;
+  return gemm_common(x, W, y, M, N, K, *launch, stream);
+}
+
+int skinny_rmsnorm_nvfp4(const void *r, const void *norm_w, float gain_center, float eps,
+                         const float *global_scale, void *a, void *a_sf, int M, int P,
+                         void *stream) {
+  return norm_common(r, norm_w, gain_center, eps, global_scale, a, a_sf, nullptr, M, P,
+                     true, stream);
+}
+
+int skinny_rmsnorm_bf16(const void *r, const void *norm_w, float gain_center, float eps,
+                        void *y, int M, int P, void *stream) {
+  return norm_common(r, norm_w, gain_center, eps, nullptr, nullptr, nullptr, y, M, P,
+                     false, stream);
+}
+
+}  // extern "C"

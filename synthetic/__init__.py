@@ -74,6 +74,14 @@ def exact_integer_inputs(M: int, N: int, K: int, seed: int = 0, nnz: int = 64):
     return to_bf16_bits(x), to_bf16_bits(w)
 
 
+def to_device(bits: np.ndarray, device="cuda"):
+    """bfloat16 bit patterns (uint16) -> a torch bfloat16 tensor on device."""
+    import torch
+
+    t = torch.from_numpy(np.ascontiguousarray(bits, dtype=np.uint16).view(np.int16))
+    return t.view(torch.bfloat16).to(device)
+
+
 def device_weight_ring(layers: int, N: int, K: int, device, w_std: float | None = None,
                        base_seed: int = 1000):
     """``layers`` distinct W [N, K] bfloat16 tensors on ``device``, layer l

@@ -1,0 +1,120 @@
+"""Host-only checks of the C ABI: the library loads, exports every entry point
+that include/skinny.h declares, and its host logic (argument checks, the
+launch-shape chooser, error reasons) behaves as documented.  No compute call
+is made here: these tests run without a GPU.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared_symbols():
+    names = set()
+    for fn in os.listdir(os.path.join(ROOT, "include")):
+        if fn.endswith(".h"):
+            text = open(os.path.join(ROOT, "include", fn)).read()
+            text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+            names |= set(re.findall(r"\b(skinny_\w+)\s*\(", text))
+    return sorted(names)
+
+
+@pytest.fixture(scope="module")
+def sk():
+    import moe_decode_skinny_amd as sk
+
+    return sk
+
+
+def test_header_declares_the_entry_points():
+    names = _declared_symbols()
+    for n in ["skinny_init", "skinny_gemm_bf16", "skinny_rmsnorm_nvfp4", "skinny_choose",
+              "skinny_last_error"]:
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol(sk):
+    lib = ctypes.CDLL(sk.LIB_PATH)
+    missing = [n for n in _declared_symbols() if not hasattr(lib, n)]
+    assert not missing, missing
+
+
+def test_binding_has_the_same_names(sk):
+    for n in _declared_symbols():
+        assert hasattr(sk, n), n
+
+
+def test_version(sk):
+    assert sk.skinny_version() >= 100
+
+
+@pytest.mark.parametrize("M,N,K", [(m, 1024, 4096) for m in (1, 2, 4, 8, 16)]
+                         + [(m, 8192, 1024) for m in (1, 8, 16)]
+                         + [(m, 512, 8192) for m in (1, 8, 16)]
+                         + [(m, 4096, 8192) for m in (1, 8, 16)]
+                         + [(3, 48, 40), (16, 16, 8), (1, 16, 8), (5, 208, 1000)])
+@pytest.mark.parametrize("splits", [0, 1, 2, 4, 8])
+def test_chooser_gives_valid_launches(sk, M, N, K, splits):
+    reason = sk.skinny_gemm_unsupported(M, N, K, splits)
+    if reason is not None:
+        # only an explicit split count too small for a long K may be refused
+        assert splits in (1, 2) and "too long" in reason, reason
+        return
+    launch = sk.skinny_choose(M, N, K, splits)
+    assert sk.skinny_launch_unsupported(M, N, K, launch) is None
+    assert sk.skinny_gemm_unsupported(M, N, K, splits) is None
+    if splits:
+        assert launch.splits == splits
+    # waves = ceil(K / (splits * kw)), kw = 32 * chunks (MFMA) or 512 * chunks (DOT2)
+    kw = (32 if launch.path == sk.SKINNY_PATH_MFMA else 512) * launch.chunks
+    assert launch.waves == -(-K // (launch.splits * kw))
+    # pure: the same arguments give the same launch
+    assert sk.skinny_choose(M, N, K, splits) == launch
+
+
+@pytest.mark.parametrize(
+    "M,N,K,splits,needle",
+    [(0, 1024, 4096, 0, "M=0"), (17, 1024, 4096, 0, "M=17"), (1, 1000, 4096, 0, "N=1000"),
+     (1, 0, 4096, 0, "N=0"), (1, 1024, 4095, 0, "K=4095"), (1, 1024, 0, 0, "K=0"),
+     (1, 1024, 4096, 3, "splits=3"), (1, 1024, 4096, 16, "splits=16")],
+)
+def test_unsupported_reasons(sk, M, N, K, splits, needle):
+    reason = sk.skinny_gemm_unsupported(M, N, K, splits)
+    assert reason is not None and needle in reason
+    with pytest.raises(ValueError, match=re.escape(needle)):
+        sk.skinny_choose(M, N, K, splits)
+
+
+def test_launch_unsupported_reasons(sk):
+    L = sk.Launch
+    assert "splits" in sk.skinny_launch_unsupported(1, 1024, 4096, L(1, 3, 8, 4, 1, 16))
+    assert "chunks" in sk.skinny_launch_unsupported(1, 1024, 4096, L(1, 4, 8, 3, 1, 16))
+    assert "waves" in sk.skinny_launch_unsupported(1, 1024, 4096, L(1, 4, 4, 4, 1, 16))
+    assert "rows" in sk.skinny_launch_unsupported(1, 1024, 4096, L(1, 4, 8, 4, 1, 8))
+    assert "DOT2" in sk.skinny_launch_unsupported(16, 1024, 4096, L(0, 1, 8, 1, 1, 4))
+    assert "multiple" in sk.skinny_launch_unsupported(1, 1040, 4096, L(0, 1, 8, 1, 1, 32))
+    assert sk.skinny_launch_unsupported(1, 1024, 4096, L(0, 1, 8, 1, 1, 4)) is None
+    assert sk.skinny_launch_unsupported(16, 1024, 4096, L(1, 4, 8, 4, 2, 16)) is None
+
+
+def test_compute_calls_without_device_fail_cleanly(sk):
+    # Pointer checks come before any device access: null pointers are EINVAL.
+    lib = ctypes.CDLL(sk.LIB_PATH)
+    lib.skinny_gemm_bf16.argtypes = [ctypes.c_void_p] * 3 + [ctypes.c_int] * 4 + [ctypes.c_void_p]
+    assert lib.skinny_gemm_bf16(None, None, None, 1, 1024, 4096, 0, None) == sk.SKINNY_EINVAL
+    assert lib.skinny_gemm_bf16(16, 32, 48, 17, 1024, 4096, 0, None) == sk.SKINNY_EINVAL
+    # misaligned
+    assert lib.skinny_gemm_bf16(18, 4096, 1 << 20, 1, 1024, 4096, 0, None) == sk.SKINNY_EINVAL
+    assert "aligned" in sk.skinny_last_error()
+    # y overlapping W
+    assert lib.skinny_gemm_bf16(0x10000, 0x100000, 0x100010, 1, 16, 64, 0, None) == sk.SKINNY_EINVAL
+    assert "overlap" in sk.skinny_last_error()
+    lib.skinny_rmsnorm_nvfp4.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_float,
+                                         ctypes.c_float] + [ctypes.c_void_p] * 3 + \
+                                        [ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
+    assert lib.skinny_rmsnorm_nvfp4(0x1000, 0x2000, 1.0, 1e-6, 0x3000, 0x4000, 0x5000, 8, 4100,
+                                    None) == sk.SKINNY_EINVAL
+    assert "P=4100" in sk.skinny_last_error()

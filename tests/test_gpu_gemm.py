@@ -1,0 +1,195 @@
+"""GPU parity of skinny_gemm_bf16 against the oracle, through the C ABI.
+
+Workloads (synthetic, seeded; the shard shapes of the three API pages):
+  unpooler shard  N=1024, K=4096 (unpooler page, module description)
+  o_proj shard    N=8192, K=1024 (oproj.batt page, OProjection)
+  pooler shard    N=512,  K=8192 and the full pooler N=4096, K=8192
+                  (pooler_gather page, module description)
+x ~ N(0, 1), W ~ N(0, 1/K).  Acceptance: |err| <= 2^-7 |ref| + 2^-10 rms(ref)
+per element (tests/helpers.py), bitwise determinism per launch shape
+(unpooler page: the summation order depends only on the launch shape), and
+bit-exactness on integer inputs whose sums are exact in any order.
+"""
+import os
+import sys
+
+import numpy as np
+import pytest
+
+import oracle
+import synthetic
+from tests.helpers import assert_gemm_close, from_dev, to_dev
+
+pytestmark = pytest.mark.gpu
+
+THREADS = min(16, os.cpu_count() or 1)
+
+
+def _say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def _run(sk, x_bits, w_bits, M, splits=0, launch=None, poison=True):
+    import torch
+
+    N, K = w_bits.shape
+    x = to_dev(x_bits[:M])
+    w = to_dev(w_bits)
+    # y sits inside a larger buffer whose other bytes are poisoned; rows >= M
+    # and the guard regions must come back untouched.
+    guard = 64
+    buf = torch.full((2 * guard + 16 * N,), -12345.0, dtype=torch.bfloat16, device="cuda")
+    y = buf[guard:guard + M * N].view(M, N)
+    if launch is None:
+        sk.skinny_gemm_bf16(x, w, y, splits)
+    else:
+        sk.skinny_gemm_bf16_launch(x, w, y, launch)
+    torch.cuda.synchronize()
+    b = from_dev(buf)
+    poison_bits = from_dev(torch.tensor([-12345.0], dtype=torch.bfloat16))[0]
+    if poison:
+        assert np.all(b[:guard] == poison_bits) and np.all(b[guard + M * N:] == poison_bits), \
+            "write outside y"
+    return from_dev(y)
+
+
+@pytest.fixture(scope="module")
+def unpooler_inputs():
+    return synthetic.gemm_inputs(N=1024, K=4096, seed=0)
+
+
+def test_unpooler_m1_s1(gpu_lib, unpooler_inputs):
+    x, w = unpooler_inputs
+    _say("unpooler M=1 N=1024 K=4096 S=1")
+    y = _run(gpu_lib, x, w, 1, splits=1)
+    assert_gemm_close(y, oracle.gemm_bf16(x[:1], w, THREADS), "unpooler M=1 S=1")
+
+
+@pytest.mark.parametrize("M", [1, 2, 4, 8, 16])
+@pytest.mark.parametrize("splits", [1, 2, 4])
+def test_unpooler_sweep_parity_and_determinism(gpu_lib, unpooler_inputs, M, splits):
+    x, w = unpooler_inputs
+    _say(f"unpooler M={M} S={splits}")
+    ref = oracle.gemm_bf16(x[:M], w, THREADS)
+    first = _run(gpu_lib, x, w, M, splits=splits)
+    assert_gemm_close(first, ref, f"unpooler M={M} S={splits}")
+    for _ in range(9):
+        again = _run(gpu_lib, x, w, M, splits=splits, poison=False)
+        assert np.array_equal(again, first), "not bitwise reproducible"
+
+
+@pytest.mark.parametrize("M", [1, 8, 16])
+def test_oproj_shard(gpu_lib, M):
+    x, w = synthetic.gemm_inputs(N=8192, K=1024, seed=3)
+    _say(f"o_proj M={M}")
+    assert_gemm_close(_run(gpu_lib, x, w, M), oracle.gemm_bf16(x[:M], w, THREADS), f"o_proj M={M}")
+
+
+@pytest.mark.parametrize("N", [512, 4096])
+@pytest.mark.parametrize("M", [1, 8, 16])
+def test_pooler_shards(gpu_lib, N, M):
+    x, w = synthetic.gemm_inputs(N=N, K=8192, seed=4)
+    _say(f"pooler N={N} M={M}")
+    assert_gemm_close(_run(gpu_lib, x, w, M), oracle.gemm_bf16(x[:M], w, THREADS),
+                      f"pooler N={N} M={M}")
+
+
+def test_pooler_weight_ring_layers(gpu_lib):
+    """60 distinct W on the device (the pooler ring); layers 0 and 59 checked."""
+    import torch
+
+    N, K, M = 512, 8192, 8
+    _say("pooler ring 60 layers")
+    ring = synthetic.device_weight_ring(60, N, K, "cuda")
+    x_bits, _ = synthetic.gemm_inputs(N=16, K=K, seed=5)
+    x = to_dev(x_bits[:M])
+    ys = [torch.empty((M, N), dtype=torch.bfloat16, device="cuda") for _ in ring]
+    for w, y in zip(ring, ys):
+        gpu_lib.skinny_gemm_bf16(x, w, y, 0)
+    torch.cuda.synchronize()
+    for l in (0, 59):
+        ref = oracle.gemm_bf16(x_bits[:M], from_dev(ring[l]), THREADS)
+        assert_gemm_close(from_dev(ys[l]), ref, f"ring layer {l}")
+
+
+def _all_launches(sk, M, N, K):
+    out = []
+    for path in (sk.SKINNY_PATH_MFMA, sk.SKINNY_PATH_DOT2):
+        for splits in (1, 2, 4, 8):
+            for chunks in (1, 2, 4, 8, 16):
+                for accs in (1, 2, 4):
+                    for rows in ((16,) if path == sk.SKINNY_PATH_MFMA else (2, 4, 8, 16)):
+                        kw = (32 if path == sk.SKINNY_PATH_MFMA else 512) * chunks
+                        waves = -(-K // (splits * kw))
+                        l = sk.Launch(path, splits, waves, chunks, accs, rows)
+                        if sk.skinny_launch_unsupported(M, N, K, l) is None:
+                            out.append(l)
+    return out
+
+
+@pytest.mark.parametrize("M,N,K", [(1, 64, 1024), (3, 48, 1000), (7, 128, 2048), (16, 32, 520)])
+def test_every_launch_shape(gpu_lib, M, N, K):
+    """Every compiled variant the validator accepts, on a small ragged case
+    (N with tiles % 8 != 0, K not a multiple of the chunk)."""
+    x, w = synthetic.gemm_inputs(N=N, K=K, seed=6)
+    ref = oracle.gemm_bf16(x[:M], w, THREADS)
+    launches = _all_launches(gpu_lib, M, N, K)
+    assert launches
+    for l in launches:
+        _say(f"M={M} N={N} K={K} {l}")
+        assert_gemm_close(_run(gpu_lib, x, w, M, launch=l), ref, f"{l}")
+
+
+@pytest.mark.parametrize("M", [1, 2, 3, 4, 5, 7, 8, 9, 13, 16])
+def test_exact_integer_inputs_bit_exact(gpu_lib, M):
+    """Integer inputs whose every partial sum is exact in FP32: each launch
+    shape must reproduce the oracle bit for bit."""
+    N, K = 256, 2048
+    x, w = synthetic.exact_integer_inputs(M=16, N=N, K=K, seed=M)
+    ref = oracle.gemm_bf16(x[:M], w, THREADS)
+    for l in _all_launches(gpu_lib, M, N, K):
+        y = _run(gpu_lib, x, w, M, launch=l, poison=False)
+        assert np.array_equal(y, ref), f"{l} not bit-exact at M={M}"
+
+
+@pytest.mark.parametrize("M,N,K", [(1, 16, 8), (16, 16, 8), (2, 16, 32), (5, 80, 8), (16, 16, 4104)])
+def test_edge_shapes(gpu_lib, M, N, K):
+    x, w = synthetic.gemm_inputs(N=N, K=K, seed=7)
+    _say(f"edge M={M} N={N} K={K}")
+    assert_gemm_close(_run(gpu_lib, x, w, M), oracle.gemm_bf16(x[:M], w, THREADS), "edge")
+
+
+def test_graph_capture_replay(gpu_lib):
+    """The GEMM recorded in a HIP graph (allocates nothing, no host sync),
+    replayed with new inputs and eager work between replays."""
+    import torch
+
+    N, K = 1024, 4096
+    x_bits, w_bits = synthetic.gemm_inputs(N=N, K=K, seed=8)
+    x2_bits, _ = synthetic.gemm_inputs(N=16, K=K, seed=9)
+    for M, splits in ((1, 0), (8, 4), (16, 0)):
+        _say(f"graph M={M} S={splits}")
+        x = to_dev(x_bits[:M])
+        w = to_dev(w_bits)
+        y = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+        gpu_lib.skinny_gemm_bf16(x, w, y, splits)  # warm
+        torch.cuda.synchronize()
+        eager = from_dev(y).copy()
+        g = torch.cuda.CUDAGraph()
+        s = torch.cuda.Stream()
+        with torch.cuda.stream(s):
+            with torch.cuda.graph(g, stream=s):
+                gpu_lib.skinny_gemm_bf16(x, w, y, splits)
+        torch.cuda.synchronize()
+        for rep in range(4):
+            y.fill_(7.0)
+            src = x_bits if rep % 2 == 0 else x2_bits
+            x.copy_(to_dev(src[:M]))
+            g.replay()
+            torch.cuda.synchronize()
+            expect = eager if rep % 2 == 0 else oracle.gemm_bf16(x2_bits[:M], w_bits, THREADS)
+            if rep % 2 == 0:
+                assert np.array_equal(from_dev(y), expect)
+            else:
+                assert_gemm_close(from_dev(y), expect, "graph replay with new x")
