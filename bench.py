@@ -43,6 +43,37 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
+HERE = os.path.dirname(os.path.abspath(__file__))
+KERNEL_SOURCES = ["moe_decode_skinny_amd/csrc/gemm_mfma.hip", "moe_decode_skinny_amd/csrc/gemm_dot2.hip",
+                  "moe_decode_skinny_amd/csrc/split_reduce.hip", "moe_decode_skinny_amd/csrc/internal.h"]
+
+
+def kernel_source_digest() -> str:
+    import hashlib
+
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(HERE, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(M: int):
+    """HBM bytes per launch of the M=<M> sweep kernel from the committed
+    counter summary (FETCH_SIZE + WRITE_SIZE, scaled by the plain-copy
+    reference), or None when the kernels changed since it was taken."""
+    path = os.path.join(HERE, "profiles", "hbm_traffic_unpooler_sweep.json")
+    try:
+        with open(path) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if rec.get("kernel_source_digest") != kernel_source_digest():
+        return None
+    per_m = rec.get("per_m", {}).get(str(M))
+    return None if per_m is None else per_m.get("hbm_bytes_per_launch")
+
+
 def cpu_baseline(budget_s: float = 12.0):
     """The oracle (plain C, binary64) on the host cores for a bounded sample of
     the same sweep: whole steps until the budget is spent."""
@@ -77,6 +108,9 @@ def main():
     ap.add_argument("--kernel-reps", type=int, default=20,
                     help="ring passes per launch shape for the per-kernel timing")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--copy-mib", type=int, default=0,
+                    help="first run one plain device copy of this many MiB (the reference "
+                         "kernel that scales hardware byte counters in a counter run)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py runs on one GPU only: this GEMM is one GPU's shard and the "
@@ -91,6 +125,12 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     sk.skinny_init(0)
+    if args.copy_mib:
+        src = torch.empty(args.copy_mib << 20, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     log(f"device {torch.cuda.get_device_name(dev)}; building the {RING}-layer ring")
     ring = synthetic.device_weight_ring(RING, N, K, dev)
     x_bits, _ = synthetic.gemm_inputs(N=16, K=K, seed=0)
@@ -174,7 +214,8 @@ def main():
                                f"{RING}-layer weight ring, chooser launch shapes",
                    "global_batch": list(MS), "parallelism": "single GPU shard"},
         "roofline": {"bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_GBS,
-                     "unit": "GB/s", "frac": round(ach / PEAK_GBS, 4), "traffic": None,
+                     "unit": "GB/s", "frac": round(ach / PEAK_GBS, 4),
+                     "traffic": measured_traffic(dom),
                      "kernel": f"M={dom} {dict(launches[dom]._asdict())}",
                      "bytes_per_launch": algorithmic_bytes(dom),
                      "us_per_launch": round(per_kernel[dom], 3)},

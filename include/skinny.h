@@ -55,28 +55,31 @@ enum {
  * The launch is fully determined by (M, N, K, skinny_launch); the summation
  * order depends only on it.
  *
- *   MFMA: a workgroup owns 16 output features (one MFMA tile) and one of
- *         `splits` K ranges; each of its `waves` waves owns kw = 32 * chunks
- *         consecutive K of that range and keeps `accs` FP32 accumulators.
+ *   MFMA: a workgroup owns rows = 16 F output features (F = 1, 2 or 4 MFMA
+ *         tiles sharing one LDS copy of the activations) and one of `splits`
+ *         K ranges; the range is cut into KW pieces of kw = 32 * chunks
+ *         consecutive K, and waves = F * KW (one wave per tile and piece),
+ *         each keeping `accs` FP32 accumulators.
  *   DOT2: a workgroup owns `rows` output features; each wave owns
- *         kw = 512 * chunks consecutive K (64 lanes x 8 bf16 per chunk).
- * In both, wave partials are summed in LDS in wave order, and with
- * splits > 1 the workgroup partials of one tile are summed in split order by
- * whichever workgroup of the tile finishes last. */
+ *         kw = 512 * chunks consecutive K (64 lanes x 8 bf16 per chunk);
+ *         waves = ceil(K / (splits * kw)).
+ * In both, wave partials are summed in LDS in wave order; with splits > 1
+ * each workgroup writes an FP32 partial and a second kernel on the same
+ * stream sums splits 0..S-1 in order. */
 typedef struct skinny_launch {
   int path;   /* SKINNY_PATH_MFMA or SKINNY_PATH_DOT2                       */
-  int splits; /* S in {1, 2, 4, 8}: workgroups along K per output tile        */
-  int waves;  /* waves per workgroup, 1..16; waves = ceil(K / (splits * kw))  */
-  int chunks; /* K chunks per wave (MFMA 1..16, DOT2 1..4)                   */
-  int accs;   /* MFMA: accumulators per wave, 1, 2 or 4; DOT2: 1           */
-  int rows;   /* output features per workgroup: 16 (MFMA) or 2..16 (DOT2)    */
+  int splits; /* S in {1, 2, 4, 8, 16}: workgroups along K per output block   */
+  int waves;  /* waves per workgroup (see above)                             */
+  int chunks; /* K chunks per wave (MFMA 1, 2, 4, 8, 16; DOT2 1, 2, 4)        */
+  int accs;   /* MFMA: accumulators per wave, 1, 2 or 4; DOT2: 1             */
+  int rows;   /* output features per workgroup: MFMA 16, 32, 64; DOT2 2..16  */
 } skinny_launch;
 
 /* Prepare `device` (a HIP ordinal) for the compute calls: checks that it is a
- * gfx950 GPU and allocates the library's split-K workspace on it (8 MiB of
- * FP32 partials and 256 KiB of self-resetting tile counters).  Call it before
- * any graph capture.  Idempotent.  Returns SKINNY_OK, SKINNY_EDEVICE or
- * SKINNY_ELAUNCH (allocation failure). */
+ * gfx950 GPU, allocates the library's split-K workspace on it (8 MiB of FP32
+ * partials, enough for S * M * N <= 2^21) and sets the kernels' LDS limits.
+ * Call it before any graph capture.  Idempotent.  Returns SKINNY_OK,
+ * SKINNY_EDEVICE or SKINNY_ELAUNCH (allocation failure). */
 int skinny_init(int device);
 
 /* y[M, N] = bf16( x[M, K] @ W[N, K]^T ), FP32 accumulation (unpooler page,
@@ -87,12 +90,12 @@ int skinny_init(int device);
  *   M       1..16 tokens
  *   N       output features, N > 0, N % 16 == 0
  *   K       reduction length, K > 0, K % 8 == 0 (16-byte rows)
- *   splits  0 = let the chooser pick; otherwise S in {1, 2, 4, 8}
+ *   splits  0 = let the chooser pick; otherwise S in {1, 2, 4, 8, 16}
  * x, W and y must not overlap.  The result is bitwise identical for the same
- * (M, N, K, launch) on one device.  Calls with splits > 1 on the same device
- * share the workspace: the caller must not run two of them concurrently on
- * different streams.  Errors: SKINNY_EINVAL, SKINNY_EUNSUPPORTED,
- * SKINNY_ENOTINIT, SKINNY_ELAUNCH. */
+ * (M, N, K, launch) on one device.  A launch with S > 1 enqueues two kernels
+ * and uses the device's workspace: two such calls must not run concurrently
+ * on different streams of one device (calls on one stream are ordered).
+ * Errors: SKINNY_EINVAL, SKINNY_EUNSUPPORTED, SKINNY_ENOTINIT, SKINNY_ELAUNCH. */
 int skinny_gemm_bf16(const void *x, const void *W, void *y, int M, int N,
                      int K, int splits, void *stream);
 

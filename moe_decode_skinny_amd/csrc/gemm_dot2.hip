@@ -11,23 +11,27 @@
 //   with four v_dot2_f32_bf16 (FP32 accumulation of exact bf16 products).
 // Reduction in an order fixed by the launch shape (module description):
 //   a butterfly over the 64 lanes (xor 32, 16, .., 1: every lane ends with the
-//   same bits), waves 0..waves-1 in order through LDS, and with S > 1 the
-//   workgroup partials s = 0..S-1 in order by the last workgroup to arrive at
-//   the group's counter (which it resets).
+//   same bits), waves 0..waves-1 in order through LDS, and with S > 1 an FP32
+//   partial per split that split_reduce.hip sums s = 0..S-1 in order.
 #include "internal.h"
 
 namespace skinny {
 namespace {
 
+// Eight bf16 products accumulated in FP32 by four v_dot2_f32_bf16.  The
+// operands are split with vector shuffles of a whole-vector bit cast (a bit
+// cast of a single vector element does not lower correctly).
 __device__ __forceinline__ float dot8(u32x4 a, u32x4 b, float c) {
-  c = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a.x),
-                                      __builtin_bit_cast(bf16x2, b.x), c, false);
-  c = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a.y),
-                                      __builtin_bit_cast(bf16x2, b.y), c, false);
-  c = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a.z),
-                                      __builtin_bit_cast(bf16x2, b.z), c, false);
-  c = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a.w),
-                                      __builtin_bit_cast(bf16x2, b.w), c, false);
+  const bf16x8 av = __builtin_bit_cast(bf16x8, a);
+  const bf16x8 bv = __builtin_bit_cast(bf16x8, b);
+  c = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(av, av, 0, 1),
+                                      __builtin_shufflevector(bv, bv, 0, 1), c, false);
+  c = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(av, av, 2, 3),
+                                      __builtin_shufflevector(bv, bv, 2, 3), c, false);
+  c = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(av, av, 4, 5),
+                                      __builtin_shufflevector(bv, bv, 4, 5), c, false);
+  c = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(av, av, 6, 7),
+                                      __builtin_shufflevector(bv, bv, 6, 7), c, false);
   return c;
 }
 
@@ -36,9 +40,8 @@ constexpr int kDot2MaxThreads = 512;
 template <int ROWS, int CHUNKS, int MT>
 __global__ __launch_bounds__(kDot2MaxThreads) void gemm_dot2_kernel(
     const uint16_t *__restrict__ x, const uint16_t *__restrict__ w,
-    uint16_t *__restrict__ y, float *__restrict__ partials,
-    unsigned *__restrict__ counters, int M, int N, int K, int S, int groups,
-    int kw) {
+    uint16_t *__restrict__ y, float *__restrict__ partials, int M, int N, int K,
+    int S, int groups, int kw) {
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int waves = blockDim.x >> 6;
@@ -123,29 +126,15 @@ __global__ __launch_bounds__(kDot2MaxThreads) void gemm_dot2_kernel(
     for (int v = 1; v < waves; ++v) part += red[v][lane];
   }
 
-  if (S > 1) {
-    float *ws = partials + (size_t)group * S * kOut;
-    if (live) ws[s * kOut + lane] = part;
-    __threadfence();
-    unsigned prev = 0;
-    if (lane == 0) prev = atomicAdd(&counters[group], 1u);
-    prev = __builtin_amdgcn_readfirstlane(prev);
-    if (prev != (unsigned)(S - 1)) return;
-    __threadfence();
-    if (live) {
-      float sum = s == 0 ? part : ws[lane];
-      for (int j = 1; j < S; ++j) sum += (j == s) ? part : ws[j * kOut + lane];
-      part = sum;
-    }
-    if (lane == 0)
-      __hip_atomic_store(&counters[group], 0u, __ATOMIC_RELAXED,
-                         __HIP_MEMORY_SCOPE_AGENT);
-  }
-  if (live) y[(size_t)t * N + f0 + r] = (uint16_t)f32_to_bf16(part);
+  if (!live) return;
+  if (S == 1)
+    y[(size_t)t * N + f0 + r] = (uint16_t)f32_to_bf16(part);
+  else  // FP32 partial of split s: partials[s][token][feature]
+    partials[((size_t)s * M + t) * N + f0 + r] = part;
 }
 
 using Dot2Kernel = void (*)(const uint16_t *, const uint16_t *, uint16_t *,
-                            float *, unsigned *, int, int, int, int, int, int);
+                            float *, int, int, int, int, int, int);
 
 // Register budget per lane: weights 4 * ROWS * CHUNKS, activations
 // 4 * MT * CHUNKS, sums ROWS * MT.  Variants above the budget are not built.
@@ -166,6 +155,7 @@ Dot2Kernel pick_mt(int mt) {
     case 2: return variant<R, C, 2>();
     case 4: return variant<R, C, 4>();
     case 8: return variant<R, C, 8>();
+    case 16: return variant<R, C, 16>();
   }
   return nullptr;
 }
@@ -197,6 +187,7 @@ int dot2_token_tile(int M) {
   if (M <= 2) return 2;
   if (M <= 4) return 4;
   if (M <= 8) return 8;
+  if (M <= 16) return 16;
   return 0;
 }
 
@@ -212,9 +203,11 @@ hipError_t launch_gemm_dot2(const uint16_t *x, const uint16_t *w, uint16_t *y,
   Dot2Kernel k = pick(l.rows, l.chunks, dot2_token_tile(M));
   const int groups = N / l.rows;
   dim3 grid(groups * l.splits), block(64 * l.waves);
-  hipLaunchKernelGGL(k, grid, block, 0, stream, x, w, y, st.partials, st.counters,
-                     M, N, K, l.splits, groups, kDot2K * l.chunks);
-  return hipGetLastError();
+  hipLaunchKernelGGL(k, grid, block, 0, stream, x, w, y, st.partials, M, N, K, l.splits,
+                     groups, kDot2K * l.chunks);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || l.splits == 1) return e;
+  return launch_split_reduce(st.partials, y, M, N, l.splits, stream);
 }
 
 }  // namespace skinny

@@ -13,18 +13,21 @@
 //
 // Work split (unpooler page, module description: CTA (t, s) owns features
 // [16 t, 16 t + 16) and the K slice s; each warp owns consecutive K):
-//   workgroup (tile, s), s < S, owns features [16 tile, 16 tile + 16);
-//   its wave w owns the K range of slice (s * waves + w), kw = 32 * CHUNKS
-//   consecutive K.  All of a wave's weight loads are issued first (the pages
-//   load weights before their dependency wait), then its activation loads,
-//   then the MFMAs, chunk i into accumulator i % ACCS.
+//   workgroup (group, s), s < S, owns F = rows / 16 tiles of 16 features and
+//   the K slice s of length kslice = KW * kw; its waves are (tile f, quarter
+//   q), q < KW, and wave (f, q) owns K [s kslice + q kw, + kw), kw = 32 CHUNKS.
+//   All of a wave's weight loads are issued first (the pages load weights
+//   before their dependency wait); then the workgroup reads its x slice once,
+//   along K, into LDS, where the F tiles share it (activation traffic is
+//   M / (16 F) of the weight traffic); then each wave runs its MFMAs, chunk i
+//   into accumulator i % ACCS, with B fragments read from LDS.
 // Reduction, in an order fixed by the launch shape (module description:
 // partials summed in a fixed order, so runs are bitwise reproducible):
-//   accumulators 0..ACCS-1 in order -> waves 0..waves-1 in order through LDS
-//   -> with S > 1, the workgroup partials of a tile s = 0..S-1 in order, by
-//   the workgroup that arrives last at the tile's counter (agent-scope
-//   release/acquire; the counter is reset by that workgroup, so no memset
-//   is needed between launches or graph replays).
+//   accumulators 0..ACCS-1 in order -> waves q = 0..KW-1 of a tile in order
+//   through LDS -> with S = 1 the BF16 store; with S > 1 an FP32 partial per
+//   split, which a second kernel (split_reduce.hip) sums s = 0..S-1 in order.
+//   The kernel boundary orders the two, so no workgroup waits on another and
+//   no counter or fence is needed.
 #include "internal.h"
 
 namespace skinny {
@@ -37,40 +40,41 @@ constexpr int mfma_max_threads(int chunks) { return chunks >= 16 ? 512 : 1024; }
 template <int CHUNKS, int ACCS>
 __global__ __launch_bounds__(mfma_max_threads(CHUNKS)) void gemm_mfma_kernel(
     const uint16_t *__restrict__ x, const uint16_t *__restrict__ w,
-    uint16_t *__restrict__ y, float *__restrict__ partials,
-    unsigned *__restrict__ counters, int M, int N, int K, int S, int tiles,
-    int kw) {
+    uint16_t *__restrict__ y, float *__restrict__ partials, int M, int N, int K,
+    int S, int groups, int F, int kw) {
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int waves = blockDim.x >> 6;
+  const int KW = waves / F;
+  const int f = wave / KW, q = wave - f * KW;
   const int row = lane & 15;  // weight row (A) / token (B) of this lane
   const int grp = lane >> 4;  // which 8-wide K group of a 32-wide chunk
 
-  // Workgroup -> (tile, split).  Workgroups are dispatched to the 8 XCDs
-  // round-robin, so ids congruent mod 8 share an XCD (and its L2); when the
-  // tile count allows, the S workgroups of a tile get ids that share one.
-  int tile, s;
+  // Workgroup -> (group, split).  Workgroups are dispatched to the 8 XCDs
+  // round-robin, so ids congruent mod 8 share an XCD and its L2; when the
+  // group count allows, the S workgroups of a group (which read the same
+  // weight rows' neighbourhood and write one partial block) share one.
+  int group, s;
   const int b = blockIdx.x;
-  if ((tiles & 7) == 0) {
+  if ((groups & 7) == 0) {
     const int xcd = b & 7, slot = b >> 3;
-    tile = (slot / S) * 8 + xcd;
+    group = (slot / S) * 8 + xcd;
     s = slot % S;
   } else {
-    tile = b / S;
+    group = b / S;
     s = b % S;
   }
+  const int tile = group * F + f;
 
-  // K offset of this lane's 8 elements in chunk 0 of its slice.
-  const int k0 = (s * waves + wave) * kw + grp * 8;
-  // Byte offsets inside the 16-row weight block of this tile and inside x.
-  // Lanes whose chunk lies past K, or whose token row is >= M, read past the
-  // end of their buffer resource and get zeros.
+  // This workgroup's K range is [kbase, kbase + kslice).  Reads past K, or
+  // past row M of x, fall outside their buffer resource and return zeros.
+  const int kslice = KW * kw;
+  const int kbase = s * kslice;
+  const int k0 = kbase + q * kw + grp * 8;
   const __amdgpu_buffer_rsrc_t wres =
       buffer_rsrc(w + (size_t)tile * kTileN * K, (unsigned)(kTileN * K * 2));
   const __amdgpu_buffer_rsrc_t xres = buffer_rsrc(x, (unsigned)(M * K * 2));
   const int woff = (row * K + k0) * 2;
-  const int xoff = (row * K + k0) * 2;
-  const bool token = row < M;
 
   // Weight stream first: every W byte of the slice is read exactly once.
   u32x4 wv[CHUNKS];
@@ -82,67 +86,82 @@ __global__ __launch_bounds__(mfma_max_threads(CHUNKS)) void gemm_mfma_kernel(
   // Keep the compiler from sinking loads below the MFMAs: the whole slice
   // must be in flight before the first wait.
   __builtin_amdgcn_sched_barrier(0);
-  // Activations: zero past row M (token padding in registers) and past K.
+
+  // Activations: the workgroup's x[0..M)[kbase .. kbase + kslice) is read
+  // once, with 16-byte loads running along K (a wave-wide load covers 1 KiB
+  // of one token row), into LDS rows padded by 16 bytes so that the B-operand
+  // reads below (16 tokens at one K offset) hit 16 different bank groups.
+  // Segment j of the slice is token j / (kslice / 8), K offset 8 (j % ..);
+  // a thread takes segments tid, tid + threads, ...: at most CHUNKS of them.
+  extern __shared__ __align__(16) uint16_t lds[];
+  uint16_t *xs = lds;
+  const int xstride = kslice + 8;
+  const int seg_row = kslice / 8;
+  const int segs = M * seg_row;
+  const int iters = (segs + (int)blockDim.x - 1) / (int)blockDim.x;
   u32x4 xv[CHUNKS];
 #pragma unroll
   for (int i = 0; i < CHUNKS; ++i) {
-    const int off = k0 + i * kMfmaK < K ? xoff + i * kMfmaK * 2 : kOutOfRange;
-    xv[i] = __builtin_amdgcn_raw_buffer_load_b128(xres, off, 0, 0);
+    if (i < iters) {
+      const int j = threadIdx.x + i * blockDim.x;
+      const int t = j / seg_row, k = kbase + (j - t * seg_row) * 8;
+      xv[i] = __builtin_amdgcn_raw_buffer_load_b128(
+          xres, (j < segs && k < K) ? (t * K + k) * 2 : kOutOfRange, 0, 0);
+    }
   }
   __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int i = 0; i < CHUNKS; ++i) {
+    if (i < iters) {
+      const int j = threadIdx.x + i * blockDim.x;
+      const int t = j / seg_row, c = j - t * seg_row;
+      if (j < segs) *reinterpret_cast<u32x4 *>(xs + t * xstride + c * 8) = xv[i];
+    }
+  }
+  __syncthreads();
 
+  const bool token = row < M;
+  const uint16_t *xsrow = xs + row * xstride + q * kw + grp * 8;
   f32x4 acc[ACCS];
 #pragma unroll
   for (int a = 0; a < ACCS; ++a) acc[a] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-  for (int i = 0; i < CHUNKS; ++i)
+  for (int i = 0; i < CHUNKS; ++i) {
+    const u32x4 bv = token ? *reinterpret_cast<const u32x4 *>(xsrow + i * kMfmaK)
+                           : u32x4{0, 0, 0, 0};
     acc[i % ACCS] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-        __builtin_bit_cast(bf16x8, wv[i]), __builtin_bit_cast(bf16x8, xv[i]),
-        acc[i % ACCS], 0, 0, 0);
+        __builtin_bit_cast(bf16x8, wv[i]), __builtin_bit_cast(bf16x8, bv), acc[i % ACCS], 0, 0, 0);
+  }
   f32x4 part = acc[0];
 #pragma unroll
   for (int a = 1; a < ACCS; ++a) part += acc[a];
 
-  // Waves 0..waves-1 in order, through LDS.
-  __shared__ f32x4 red[kMaxWaves][64];
-  if (waves > 1) {
-    red[wave][lane] = part;
+  // Waves q = 0..KW-1 of each tile in order, through LDS (the x slice is no
+  // longer needed: the same LDS holds one 1 KiB partial per wave).
+  if (KW > 1) {
+    f32x4 *red = reinterpret_cast<f32x4 *>(lds);
     __syncthreads();
-    if (wave != 0) return;
-    part = red[0][lane];
-    for (int v = 1; v < waves; ++v) part += red[v][lane];
+    red[wave * 64 + lane] = part;
+    __syncthreads();
+    if (q != 0) return;
+    part = red[(f * KW) * 64 + lane];
+    for (int v = 1; v < KW; ++v) part += red[(f * KW + v) * 64 + lane];
   }
 
-  if (S > 1) {
-    // Workgroup partial of split s -> workspace; last arriver sums s in order.
-    f32x4 *ws = reinterpret_cast<f32x4 *>(partials) + (size_t)tile * S * 64;
-    if (token) ws[s * 64 + lane] = part;
-    __threadfence();  // release: partial visible device-wide before the count
-    unsigned prev = 0;
-    if (lane == 0) prev = atomicAdd(&counters[tile], 1u);
-    prev = __builtin_amdgcn_readfirstlane(prev);
-    if (prev != (unsigned)(S - 1)) return;
-    __threadfence();  // acquire: the other splits' partials
-    if (token) {
-      f32x4 sum = s == 0 ? part : ws[lane];
-      for (int j = 1; j < S; ++j) sum += (j == s) ? part : ws[j * 64 + lane];
-      part = sum;
-    }
-    if (lane == 0)
-      __hip_atomic_store(&counters[tile], 0u, __ATOMIC_RELAXED,
-                         __HIP_MEMORY_SCOPE_AGENT);
-  }
-
-  if (token) {
+  if (!token) return;
+  const int col = tile * kTileN + grp * 4;
+  if (S == 1) {
     const unsigned lo = f32_to_bf16(part[0]) | (f32_to_bf16(part[1]) << 16);
     const unsigned hi = f32_to_bf16(part[2]) | (f32_to_bf16(part[3]) << 16);
-    uint2 *dst = reinterpret_cast<uint2 *>(y + (size_t)row * N + tile * kTileN + grp * 4);
-    *dst = make_uint2(lo, hi);
+    *reinterpret_cast<uint2 *>(y + (size_t)row * N + col) = make_uint2(lo, hi);
+  } else {
+    // FP32 partial of split s: partials[s][token][feature]
+    *reinterpret_cast<f32x4 *>(partials + ((size_t)s * M + row) * N + col) = part;
   }
 }
 
 using MfmaKernel = void (*)(const uint16_t *, const uint16_t *, uint16_t *,
-                            float *, unsigned *, int, int, int, int, int, int);
+                            float *, int, int, int, int, int, int, int);
 
 template <int C>
 MfmaKernel pick_accs(int accs) {
@@ -171,15 +190,39 @@ bool mfma_variant_exists(int chunks, int accs) { return pick(chunks, accs) != nu
 
 int mfma_max_waves(int chunks) { return mfma_max_threads(chunks) / 64; }
 
+// Allow every variant the largest dynamic LDS a launch may ask for.  Called
+// once per device from skinny_init, outside any graph capture.
+hipError_t mfma_prepare() {
+  static const int kChunks[] = {1, 2, 4, 8, 16}, kAccs[] = {1, 2, 4};
+  for (int c : kChunks)
+    for (int a : kAccs) {
+      hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(pick(c, a)),
+                                         hipFuncAttributeMaxDynamicSharedMemorySize,
+                                         (int)kMaxDynamicLds);
+      if (e != hipSuccess) return e;
+    }
+  return hipSuccess;
+}
+
+size_t mfma_lds_bytes(int M, const skinny_launch &l) {
+  const int F = l.rows / kTileN, KW = l.waves / F;
+  const size_t xbytes = (size_t)M * (KW * kMfmaK * l.chunks + 8) * sizeof(uint16_t);
+  const size_t rbytes = (size_t)l.waves * 64 * sizeof(f32x4);
+  return xbytes > rbytes ? xbytes : rbytes;
+}
+
 hipError_t launch_gemm_mfma(const uint16_t *x, const uint16_t *w, uint16_t *y,
                             int M, int N, int K, const skinny_launch &l,
                             DeviceState &st, hipStream_t stream) {
   MfmaKernel k = pick(l.chunks, l.accs);
-  const int tiles = N / kTileN;
-  dim3 grid(tiles * l.splits), block(64 * l.waves);
-  hipLaunchKernelGGL(k, grid, block, 0, stream, x, w, y, st.partials, st.counters,
-                     M, N, K, l.splits, tiles, kMfmaK * l.chunks);
-  return hipGetLastError();
+  const int F = l.rows / kTileN;
+  const int groups = N / l.rows;
+  dim3 grid(groups * l.splits), block(64 * l.waves);
+  hipLaunchKernelGGL(k, grid, block, mfma_lds_bytes(M, l), stream, x, w, y, st.partials, M, N,
+                     K, l.splits, groups, F, kMfmaK * l.chunks);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || l.splits == 1) return e;
+  return launch_split_reduce(st.partials, y, M, N, l.splits, stream);
 }
 
 }  // namespace skinny

@@ -18,14 +18,14 @@ constexpr int kDot2K = 512;        // K per DOT2 chunk: 64 lanes x 8 bf16
 constexpr int kMaxWaves = 16;      // 1024 threads per workgroup
 constexpr int kMaxMfmaChunks = 16;
 constexpr int kMaxDot2Chunks = 4;
-// Split-K workspace owned by the library (per device, from skinny_init).
-constexpr size_t kWorkspaceFloats = size_t(2) << 20;  // 8 MiB of FP32 partials
-constexpr int kMaxCounters = 65536;                   // one per output tile
+constexpr int kMaxSplits = 16;
+// Split-K workspace owned by the library (per device, from skinny_init):
+// FP32 partials [split][token][feature], S * M * N floats at most.
+constexpr size_t kWorkspaceFloats = size_t(2) << 20;  // 8 MiB
 
 struct DeviceState {
   bool ready = false;
-  float *partials = nullptr;   // kWorkspaceFloats
-  unsigned *counters = nullptr;  // kMaxCounters, zero between launches
+  float *partials = nullptr;  // kWorkspaceFloats
   int cus = 0;
 };
 
@@ -43,6 +43,8 @@ hipError_t launch_gemm_mfma(const uint16_t *x, const uint16_t *w, uint16_t *y,
 hipError_t launch_gemm_dot2(const uint16_t *x, const uint16_t *w, uint16_t *y,
                             int M, int N, int K, const skinny_launch &l,
                             DeviceState &st, hipStream_t stream);
+hipError_t launch_split_reduce(const float *partials, uint16_t *y, int M, int N, int S,
+                               hipStream_t stream);
 hipError_t launch_rmsnorm(const uint16_t *r, const uint16_t *w, float gain_center,
                           float eps, const float *global_scale, uint8_t *a,
                           uint8_t *a_sf, uint16_t *y, int M, int P, bool quant,
@@ -51,6 +53,9 @@ hipError_t launch_rmsnorm(const uint16_t *r, const uint16_t *w, float gain_cente
 // Instantiation tables (which template variants exist), used by validation.
 bool mfma_variant_exists(int chunks, int accs);
 int mfma_max_waves(int chunks);  // waves per MFMA workgroup (launch bound)
+size_t mfma_lds_bytes(int M, const skinny_launch &l);  // dynamic LDS of a launch
+hipError_t mfma_prepare();  // per-device kernel attributes (skinny_init)
+constexpr size_t kMaxDynamicLds = 160 * 1024;  // all of a gfx950 CU's LDS
 bool dot2_variant_exists(int rows, int chunks, int mt);
 int dot2_token_tile(int M);  // smallest compiled token count >= M, 0 if none
 int dot2_max_waves();        // waves per DOT2 workgroup (launch bound)

@@ -9,15 +9,21 @@
 //
 // gfx950 design: one workgroup of 256 threads per row; thread t owns whole
 // 16-column blocks (t, t + 256, ...), so a block's amax, scale and codes stay
-// in one thread and its 8 code bytes leave as one 8-byte store.  The sum of
-// squares is reduced in a fixed order: per thread in column order, a lane
-// butterfly inside each wave, then the four wave sums in wave order.
-// The e4m3 and e2m1 encoders are written out in integer/compare form here
-// (no vendor conversion instruction), so rounding and saturation are exactly
-// the round-to-nearest-even + satfinite the pages specify.
+// in one thread and its 8 code bytes leave as one 8-byte store.
+// Arithmetic is binary64 (gfx950 has full-rate FP64 vector units and the
+// kernel is latency-bound, so this costs nothing measurable): the sum of
+// squares, the reciprocal root, the product r * inv * (w + gain_center), the
+// block scale global_scale * amax / 6, the output scale and the scaled values
+// are all exact or rounded once in binary64, and every narrowing (to
+// bfloat16, e4m3fn, e2m1) is a single round-to-nearest-even from binary64.
+// The sum of squares is reduced in a fixed order: per thread in column order,
+// a lane butterfly inside each wave, then the four wave sums in wave order.
+// The e4m3 and e2m1 encoders are written out in integer/compare form (no
+// vendor conversion instruction), so rounding and saturation are exactly the
+// round-to-nearest-even + satfinite the pages specify.
 // Readings (the norm/quant kernel body is not printed): the block scale is
-// e4m3(global_scale * amax / 6); the FP32 output scale is global_scale /
-// dec(sf) rounded once; a negative value that rounds to zero keeps its sign.
+// e4m3(global_scale * amax / 6); the output scale is global_scale / dec(sf);
+// a negative value that rounds to zero keeps its sign.
 #include "internal.h"
 
 namespace skinny {
@@ -25,46 +31,59 @@ namespace {
 
 constexpr int kNormThreads = 256;
 
-// |v| -> e4m3fn code, round to nearest even, saturating at 448 (0x7E).
-__device__ __forceinline__ unsigned e4m3_rn_satfinite(float v) {
-  const unsigned sign = (__float_as_uint(v) >> 24) & 0x80u;
-  const float a = fabsf(v);
-  if (a != a) return 0x7Fu;
-  if (a >= 448.0f) return sign | 0x7Eu;
-  if (a < 0.015625f) {                              // below 2^-6: step 2^-9
-    return sign | (unsigned)rintf(a * 512.0f);      // 8 -> 0x08 = 2^-6
+// binary64 -> bfloat16 bits, round to nearest even (finite inputs; overflow
+// gives infinity).
+__device__ __forceinline__ unsigned f64_to_bf16(double v) {
+  const unsigned long long u = (unsigned long long)__double_as_longlong(v);
+  const unsigned sign = (unsigned)(u >> 48) & 0x8000u;
+  const double a = fabs(v);
+  if (a < 0x1p-126) {                       // bfloat16 subnormals: step 2^-133
+    return sign | (unsigned)rint(a * 0x1p133);  // 128 -> smallest normal
   }
-  unsigned b = __float_as_uint(a);
-  b += 0x7FFFFu + ((b >> 20) & 1u);                 // keep 3 mantissa bits, RNE
-  const unsigned exp = (b >> 23) - 127u + 7u;       // 1..15
-  return sign | (exp << 3) | ((b >> 20) & 7u);
+  unsigned long long b = u & 0x7fffffffffffffffull;
+  b += 0xfffffffffffull + ((b >> 45) & 1ull);   // keep 7 of 52 mantissa bits
+  const int exp = (int)(b >> 52) - 1023 + 127;
+  if (exp >= 255) return sign | 0x7f80u;
+  return sign | ((unsigned)exp << 7) | (unsigned)((b >> 45) & 0x7full);
 }
 
-// e4m3fn code (finite, non-negative) -> its value (exact in FP32).
-__device__ __forceinline__ float e4m3_value(unsigned c) {
+// |v| -> e4m3fn code, round to nearest even, saturating at 448 (0x7E).
+__device__ __forceinline__ unsigned e4m3_rn_satfinite(double v) {
+  const double a = fabs(v);
+  if (a != a) return 0x7Fu;
+  if (a >= 448.0) return 0x7Eu;
+  if (a < 0x1p-6) return (unsigned)rint(a * 512.0);   // step 2^-9; 8 -> 0x08
+  unsigned long long b = (unsigned long long)__double_as_longlong(a);
+  b += 0xffffffffffffull + ((b >> 49) & 1ull);        // keep 3 mantissa bits
+  const unsigned exp = (unsigned)(b >> 52) - 1023u + 7u;  // 1..15
+  return (exp << 3) | (unsigned)((b >> 49) & 7ull);
+}
+
+// e4m3fn code (finite, non-negative) -> its value.
+__device__ __forceinline__ double e4m3_value(unsigned c) {
   const unsigned exp = (c >> 3) & 15u, man = c & 7u;
-  if (exp == 0) return (float)man * 0.001953125f;  // man * 2^-9
-  return __uint_as_float(((exp + 120u) << 23) | (man << 20));
+  if (exp == 0) return (double)man * 0x1p-9;
+  return ldexp(1.0 + man * 0.125, (int)exp - 7);
 }
 
 // v -> e2m1 code: magnitudes 0, .5, 1, 1.5, 2, 3, 4, 6 by index; ties to the
 // even index (the comparison is >= where the upper neighbour is even);
 // anything above 5 saturates to 6; the sign bit is kept.
-__device__ __forceinline__ unsigned e2m1_rn_satfinite(float v) {
-  const float a = fabsf(v);
-  const unsigned idx = (a > 0.25f) + (a >= 0.75f) + (a > 1.25f) + (a >= 1.75f) +
-                       (a > 2.5f) + (a >= 3.5f) + (a > 5.0f);
-  return ((__float_as_uint(v) >> 28) & 8u) | idx;
+__device__ __forceinline__ unsigned e2m1_rn_satfinite(double v) {
+  const double a = fabs(v);
+  const unsigned idx = (a > 0.25) + (a >= 0.75) + (a > 1.25) + (a >= 1.75) +
+                       (a > 2.5) + (a >= 3.5) + (a > 5.0);
+  return (signbit(v) ? 8u : 0u) | idx;
 }
 
-__device__ __forceinline__ void load16(const uint16_t *p, float (&v)[16]) {
+__device__ __forceinline__ void load16(const uint16_t *p, double (&v)[16]) {
   const u32x4 a = *reinterpret_cast<const u32x4 *>(p);
   const u32x4 b = *reinterpret_cast<const u32x4 *>(p + 8);
   const unsigned u[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
-    v[2 * i] = bf16_lo(u[i]);
-    v[2 * i + 1] = bf16_hi(u[i]);
+    v[2 * i] = (double)bf16_lo(u[i]);
+    v[2 * i + 1] = (double)bf16_hi(u[i]);
   }
 }
 
@@ -79,33 +98,33 @@ __global__ __launch_bounds__(kNormThreads) void rmsnorm_kernel(
   const uint16_t *rrow = r + (size_t)row * P;
 
   // Sum of squares in a fixed order; the first block stays in registers.
-  float first[16];
-  float ss = 0.f;
+  double first[16];
+  double ss = 0.0;
   if (tid < blocks) {
     load16(rrow + tid * 16, first);
 #pragma unroll
     for (int j = 0; j < 16; ++j) ss += first[j] * first[j];
   }
   for (int blk = tid + kNormThreads; blk < blocks; blk += kNormThreads) {
-    float v[16];
+    double v[16];
     load16(rrow + blk * 16, v);
 #pragma unroll
     for (int j = 0; j < 16; ++j) ss += v[j] * v[j];
   }
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) ss += __shfl_xor(ss, off);
-  __shared__ float wave_ss[kNormThreads / 64];
+  __shared__ double wave_ss[kNormThreads / 64];
   if ((tid & 63) == 0) wave_ss[tid >> 6] = ss;
   __syncthreads();
-  float total = wave_ss[0];
+  double total = wave_ss[0];
 #pragma unroll
   for (int i = 1; i < kNormThreads / 64; ++i) total += wave_ss[i];
-  // correctly rounded division and square root (hipcc's default for FP32)
-  const float inv = 1.0f / sqrtf(total / (float)P + eps);
-  const float gs = QUANT ? *global_scale : 0.f;
+  const double inv = 1.0 / sqrt(total / (double)P + (double)eps);
+  const double gc = (double)gain_center;
+  const double gs = QUANT ? (double)*global_scale : 0.0;
 
   for (int blk = tid; blk < blocks; blk += kNormThreads) {
-    float v[16], g[16];
+    double v[16], g[16];
     if (blk == tid) {
 #pragma unroll
       for (int j = 0; j < 16; ++j) v[j] = first[j];
@@ -114,21 +133,21 @@ __global__ __launch_bounds__(kNormThreads) void rmsnorm_kernel(
     }
     load16(w + blk * 16, g);
     unsigned yb[16];
-    float amax = 0.f;
+    double amax = 0.0;
 #pragma unroll
     for (int j = 0; j < 16; ++j) {
-      yb[j] = f32_to_bf16((v[j] * inv) * (g[j] + gain_center));
-      amax = fmaxf(amax, fabsf(__uint_as_float(yb[j] << 16)));
+      yb[j] = f64_to_bf16(v[j] * inv * (g[j] + gc));
+      amax = fmax(amax, fabs((double)__uint_as_float(yb[j] << 16)));
     }
     if constexpr (QUANT) {
-      const unsigned sf = e4m3_rn_satfinite(gs * amax / 6.0f);
-      const float dec = e4m3_value(sf);
-      const float os = dec == 0.f ? 0.f : gs / dec;
+      const unsigned sf = e4m3_rn_satfinite(gs * amax / 6.0);
+      const double dec = e4m3_value(sf);
+      const double os = dec == 0.0 ? 0.0 : gs / dec;
       unsigned lo = 0, hi = 0;
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
-        lo |= e2m1_rn_satfinite(__uint_as_float(yb[j] << 16) * os) << (4 * j);
-        hi |= e2m1_rn_satfinite(__uint_as_float(yb[j + 8] << 16) * os) << (4 * j);
+        lo |= e2m1_rn_satfinite((double)__uint_as_float(yb[j] << 16) * os) << (4 * j);
+        hi |= e2m1_rn_satfinite((double)__uint_as_float(yb[j + 8] << 16) * os) << (4 * j);
       }
       *reinterpret_cast<uint2 *>(a + (size_t)row * (P / 2) + blk * 8) = make_uint2(lo, hi);
       a_sf[(size_t)row * blocks + blk] = (uint8_t)sf;

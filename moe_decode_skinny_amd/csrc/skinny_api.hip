@@ -50,8 +50,8 @@ int check_problem(int M, int N, int K) {
     return fail(SKINNY_EINVAL, "K=%d: needs K > 0 and K %% 8 == 0 (16-byte rows)", K);
   if (K > (1 << 25))
     return fail(SKINNY_EUNSUPPORTED, "K=%d: at most %d (32-bit buffer offsets)", K, 1 << 25);
-  if (N / kTileN > kMaxCounters)
-    return fail(SKINNY_EUNSUPPORTED, "N=%d: more than %d output tiles", N, kMaxCounters);
+  if (N > (1 << 24))
+    return fail(SKINNY_EUNSUPPORTED, "N=%d: at most %d", N, 1 << 24);
   return SKINNY_OK;
 }
 
@@ -81,36 +81,43 @@ DeviceState *current_state(int *status) {
 }
 
 // Validity of (M, N, K) at an explicit launch shape; the gfx950 restatement
-// of launch_unsupported.
+// of launch_unsupported (splits, K per wave, waves per workgroup) plus this
+// build's own limits (compiled variants, LDS, workspace).
 static int launch_check(int M, int N, int K, const skinny_launch &l) {
   int st = check_problem(M, N, K);
   if (st) return st;
-  if (l.splits != 1 && l.splits != 2 && l.splits != 4 && l.splits != 8)
-    return fail(SKINNY_EUNSUPPORTED, "splits=%d: needs 1, 2, 4 or 8", l.splits);
+  if (l.splits < 1 || l.splits > kMaxSplits || (l.splits & (l.splits - 1)))
+    return fail(SKINNY_EUNSUPPORTED, "splits=%d: needs 1, 2, 4, 8 or 16", l.splits);
+  if (l.splits > 1 && (size_t)l.splits * M * N > kWorkspaceFloats)
+    return fail(SKINNY_EUNSUPPORTED, "split-K workspace too small for %d x %d x %d partials",
+                l.splits, M, N);
   if (l.path == SKINNY_PATH_MFMA) {
-    if (l.rows != kTileN)
-      return fail(SKINNY_EUNSUPPORTED, "MFMA launch owns %d rows per workgroup, not %d",
-                  kTileN, l.rows);
+    if (l.rows != 16 && l.rows != 32 && l.rows != 64)
+      return fail(SKINNY_EUNSUPPORTED, "MFMA rows=%d: needs 16, 32 or 64 (1, 2 or 4 tiles)",
+                  l.rows);
+    if (N % l.rows)
+      return fail(SKINNY_EUNSUPPORTED, "N=%d is not a multiple of rows=%d", N, l.rows);
     if (!mfma_variant_exists(l.chunks, l.accs))
       return fail(SKINNY_EUNSUPPORTED, "no MFMA kernel with chunks=%d accs=%d "
                   "(chunks 1, 2, 4, 8, 16; accs 1, 2, 4)", l.chunks, l.accs);
+    const int F = l.rows / kTileN;
     const long kw = (long)kMfmaK * l.chunks;
-    const int need = ceil_div(K, (long)l.splits * kw);
+    const int need = F * ceil_div(K, (long)l.splits * kw);
     if (l.waves != need)
       return fail(SKINNY_EUNSUPPORTED, "K=%d does not split into %d x %d waves x %ld "
-                  "(needs %d waves)", K, l.splits, l.waves, kw, need);
+                  "(needs %d waves: %d tiles x %d along K)", K, l.splits, l.waves, kw, need, F,
+                  need / F);
     if (l.waves < 1 || l.waves > mfma_max_waves(l.chunks))
       return fail(SKINNY_EUNSUPPORTED, "%d waves per workgroup (1..%d at chunks=%d)", l.waves,
                   mfma_max_waves(l.chunks), l.chunks);
-    const long tiles = N / kTileN;
-    if (l.splits > 1 && tiles * l.splits * 256 > (long)kWorkspaceFloats)
-      return fail(SKINNY_EUNSUPPORTED, "split-K workspace too small for %ld tiles x %d splits",
-                  tiles, l.splits);
+    if (mfma_lds_bytes(M, l) > kMaxDynamicLds)
+      return fail(SKINNY_EUNSUPPORTED, "K slice of %ld per workgroup needs %zu bytes of LDS "
+                  "(max %zu)", (long)(l.waves / F) * kw, mfma_lds_bytes(M, l), kMaxDynamicLds);
     return SKINNY_OK;
   }
   if (l.path == SKINNY_PATH_DOT2) {
     const int mt = dot2_token_tile(M);
-    if (mt == 0) return fail(SKINNY_EUNSUPPORTED, "DOT2 path takes M <= 8, got %d", M);
+    if (mt == 0) return fail(SKINNY_EUNSUPPORTED, "DOT2 path takes M <= 16, got %d", M);
     if (l.accs != 1) return fail(SKINNY_EUNSUPPORTED, "DOT2 launch has accs=1");
     if (l.rows <= 0 || N % l.rows)
       return fail(SKINNY_EUNSUPPORTED, "N=%d is not a multiple of rows=%d", N, l.rows);
@@ -125,73 +132,71 @@ static int launch_check(int M, int N, int K, const skinny_launch &l) {
     if (l.waves < 1 || l.waves > dot2_max_waves())
       return fail(SKINNY_EUNSUPPORTED, "%d waves per workgroup (DOT2: 1..%d)", l.waves,
                   dot2_max_waves());
-    const long groups = N / l.rows;
-    if (groups > kMaxCounters)
-      return fail(SKINNY_EUNSUPPORTED, "%ld row groups (max %d)", groups, kMaxCounters);
-    if (l.splits > 1 && groups * l.splits * l.rows * mt > (long)kWorkspaceFloats)
-      return fail(SKINNY_EUNSUPPORTED, "split-K workspace too small");
     return SKINNY_OK;
   }
   return fail(SKINNY_EUNSUPPORTED, "unknown path %d", l.path);
 }
 
-// The chooser: a pure function of (M, N, K, splits).
-//   - M <= 2 and N divisible by the row count: DOT2, lanes along K, enough
-//     row groups that the grid covers the 256 CUs without split-K;
-//   - otherwise MFMA: S picked so that tiles * S >= 256 workgroups (capped at
-//     8), then the fewest chunks per wave (1..16, most memory parallelism per
-//     wave) that keep waves <= 16; 2 accumulators when a wave has >= 4 chunks.
+// DOT2 candidate with `rows` rows per workgroup: the fewest waves (largest
+// chunks) that cover a split's K range, waves <= the launch bound.
+static skinny_launch dot2_candidate(int M, int N, int K, int S, int rows) {
+  for (int chunks = kMaxDot2Chunks; chunks >= 1; chunks /= 2) {
+    skinny_launch c{SKINNY_PATH_DOT2, S, ceil_div(K, (long)S * kDot2K * chunks), chunks, 1, rows};
+    if (chunks > 1 && c.waves < 2) continue;  // keep at least two waves per workgroup
+    if (launch_check(M, N, K, c) == SKINNY_OK) return c;
+  }
+  return skinny_launch{};
+}
+
+// MFMA candidate: F tiles per workgroup, S splits, the chunk count whose
+// waves fit the variant's launch bound and the LDS.
+static skinny_launch mfma_candidate(int M, int N, int K, int S, int F, int chunks) {
+  const int KW = ceil_div(K, (long)S * kMfmaK * chunks);
+  skinny_launch c{SKINNY_PATH_MFMA, S, F * KW, chunks, chunks >= 4 ? 2 : 1, F * kTileN};
+  return launch_check(M, N, K, c) == SKINNY_OK ? c : skinny_launch{};
+}
+
+// The chooser: a pure function of (M, N, K, splits), from launch-shape sweeps
+// on MI355X (rule of thumb: about 256-512 workgroups of 16-64 KiB of weights
+// each; DOT2 while its activation traffic, M / rows of the weight traffic,
+// stays small; MFMA with split-K partials beyond).
 static int choose(int M, int N, int K, int splits, skinny_launch *out) {
   int st = check_problem(M, N, K);
   if (st) return st;
-  if (splits != 0 && splits != 1 && splits != 2 && splits != 4 && splits != 8)
-    return fail(SKINNY_EINVAL, "splits=%d: needs 0 (auto), 1, 2, 4 or 8", splits);
+  if (splits != 0 && (splits < 1 || splits > kMaxSplits || (splits & (splits - 1))))
+    return fail(SKINNY_EINVAL, "splits=%d: needs 0 (auto), 1, 2, 4, 8 or 16", splits);
   skinny_launch l{};
-  if (M <= 2) {
-    // DOT2: 1 KiB of a weight row per wave-wide load.
-    const long row_bytes = 2L * K;
-    static const int kRows[] = {16, 8, 4, 2};
-    for (int rows : kRows) {
+  const long tiles = N / kTileN;
+  const bool dot2 = M <= 4 || (M <= 8 && tiles < 512);
+  if (dot2) {
+    for (int rows : {2, 4, 8, 16}) {
       if (N % rows) continue;
-      const long groups = N / rows;
-      if (groups < 256 && rows > 2) continue;  // prefer >= 256 workgroups
-      const int S = splits ? splits : 1;
-      for (int chunks = 1; chunks <= kMaxDot2Chunks; chunks *= 2) {
-        skinny_launch c{SKINNY_PATH_DOT2, S, ceil_div(K, (long)S * kDot2K * chunks), chunks, 1, rows};
-        if (c.waves > dot2_max_waves()) continue;
-        if (!dot2_variant_exists(rows, chunks, dot2_token_tile(M))) continue;
-        (void)row_bytes;
-        l = c;
-        break;
+      l = dot2_candidate(M, N, K, splits ? splits : 1, rows);
+      if (l.waves) break;
+    }
+  }
+  if (!l.waves) {
+    // MFMA: F tiles share the x slice; S so that (tiles / F) * S >= 256.
+    for (int F : {4, 2, 1}) {
+      if (F > 1 && (tiles % F || tiles / F < 32)) continue;
+      int S = splits;
+      if (S == 0) {
+        S = 1;
+        while (S < kMaxSplits && (tiles / F) * S < 256 && K >= (long)kMfmaK * 2 * S) S *= 2;
+      }
+      for (; !l.waves && S <= kMaxSplits; S *= 2) {
+        for (int chunks = 4; chunks <= kMaxMfmaChunks && !l.waves; chunks *= 2)
+          l = mfma_candidate(M, N, K, S, F, chunks);
+        for (int chunks = 2; chunks >= 1 && !l.waves; chunks /= 2)
+          l = mfma_candidate(M, N, K, S, F, chunks);
+        if (splits) break;
       }
       if (l.waves) break;
     }
-    if (l.waves && launch_check(M, N, K, l) == SKINNY_OK) {
-      *out = l;
-      return SKINNY_OK;
-    }
-    l = skinny_launch{};
-  }
-  const long tiles = N / kTileN;
-  int S = splits;
-  if (S == 0) {
-    S = 1;
-    while (S < 8 && tiles * S < 256 && K >= (long)kMfmaK * 2 * S) S *= 2;
-  }
-  for (;;) {
-    for (int chunks = 1; chunks <= kMaxMfmaChunks; chunks *= 2) {
-      const int waves = ceil_div(K, (long)S * kMfmaK * chunks);
-      if (waves > mfma_max_waves(chunks)) continue;
-      l = skinny_launch{SKINNY_PATH_MFMA, S, waves, chunks, chunks >= 4 ? 2 : 1, kTileN};
-      break;
-    }
-    // an automatic S grows until one workgroup's waves can hold its K range
-    if (l.waves || splits != 0 || S == 8) break;
-    S *= 2;
   }
   if (!l.waves)
-    return fail(SKINNY_EUNSUPPORTED, "K=%d too long for %d splits x %d waves x %d",
-                K, S, mfma_max_waves(kMaxMfmaChunks), kMfmaK * kMaxMfmaChunks);
+    return fail(SKINNY_EUNSUPPORTED, "no launch for M=%d N=%d K=%d splits=%d (K too long "
+                "for the requested splits)", M, N, K, splits);
   st = launch_check(M, N, K, l);
   if (st) return st;
   *out = l;
@@ -281,8 +286,7 @@ int skinny_init(int device) {
   if (hipSetDevice(device) != hipSuccess) return fail(SKINNY_EDEVICE, "cannot select device %d", device);
   int status = SKINNY_OK;
   if (hipMalloc(&st.partials, kWorkspaceFloats * sizeof(float)) != hipSuccess ||
-      hipMalloc(&st.counters, kMaxCounters * sizeof(unsigned)) != hipSuccess ||
-      hipMemset(st.counters, 0, kMaxCounters * sizeof(unsigned)) != hipSuccess ||
+      mfma_prepare() != hipSuccess ||
       hipDeviceSynchronize() != hipSuccess) {
     status = fail(SKINNY_ELAUNCH, "workspace allocation failed on device %d", device);
   } else {

@@ -1,0 +1,44 @@
+// The split-K reduction of the small-M decode GEMM: y[t][n] = bf16( sum over
+// s = 0..S-1, in that order, of partials[s][t][n] ) (unpooler page, module
+// description: the partials are summed in a fixed order that depends only on
+// the launch shape, then rounded to BF16 and stored).
+//
+// It runs as the second kernel of a split launch, on the same stream, so the
+// kernel boundary orders it after every partial store of the first: no
+// workgroup ever waits for another.  One thread per four consecutive outputs
+// of a token row: S 16-byte loads (coalesced across the row) and one 8-byte
+// store.
+#include "internal.h"
+
+namespace skinny {
+namespace {
+
+constexpr int kReduceThreads = 256;
+
+__global__ __launch_bounds__(kReduceThreads) void split_reduce_kernel(
+    const float *__restrict__ partials, uint16_t *__restrict__ y, int M, int N, int S) {
+  const int i = blockIdx.x * kReduceThreads + threadIdx.x;
+  const int quads = M * (N / 4);
+  if (i >= quads) return;
+  const int t = i / (N / 4), n = (i - t * (N / 4)) * 4;
+  const size_t plane = (size_t)M * N;
+  const f32x4 *p = reinterpret_cast<const f32x4 *>(partials + (size_t)t * N + n);
+  f32x4 sum = p[0];
+  for (int s = 1; s < S; ++s) sum += *reinterpret_cast<const f32x4 *>(
+      partials + s * plane + (size_t)t * N + n);
+  const unsigned lo = f32_to_bf16(sum[0]) | (f32_to_bf16(sum[1]) << 16);
+  const unsigned hi = f32_to_bf16(sum[2]) | (f32_to_bf16(sum[3]) << 16);
+  *reinterpret_cast<uint2 *>(y + (size_t)t * N + n) = make_uint2(lo, hi);
+}
+
+}  // namespace
+
+hipError_t launch_split_reduce(const float *partials, uint16_t *y, int M, int N, int S,
+                               hipStream_t stream) {
+  const int quads = M * (N / 4);
+  dim3 grid((quads + kReduceThreads - 1) / kReduceThreads), block(kReduceThreads);
+  hipLaunchKernelGGL(split_reduce_kernel, grid, block, 0, stream, partials, y, M, N, S);
+  return hipGetLastError();
+}
+
+}  // namespace skinny

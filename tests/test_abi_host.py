@@ -56,7 +56,7 @@ def test_version(sk):
                          + [(m, 512, 8192) for m in (1, 8, 16)]
                          + [(m, 4096, 8192) for m in (1, 8, 16)]
                          + [(3, 48, 40), (16, 16, 8), (1, 16, 8), (5, 208, 1000)])
-@pytest.mark.parametrize("splits", [0, 1, 2, 4, 8])
+@pytest.mark.parametrize("splits", [0, 1, 2, 4, 8, 16])
 def test_chooser_gives_valid_launches(sk, M, N, K, splits):
     reason = sk.skinny_gemm_unsupported(M, N, K, splits)
     if reason is not None:
@@ -68,9 +68,12 @@ def test_chooser_gives_valid_launches(sk, M, N, K, splits):
     assert sk.skinny_gemm_unsupported(M, N, K, splits) is None
     if splits:
         assert launch.splits == splits
-    # waves = ceil(K / (splits * kw)), kw = 32 * chunks (MFMA) or 512 * chunks (DOT2)
-    kw = (32 if launch.path == sk.SKINNY_PATH_MFMA else 512) * launch.chunks
-    assert launch.waves == -(-K // (launch.splits * kw))
+    # waves = F * ceil(K / (splits * kw)): kw = 32 * chunks and F = rows / 16
+    # tiles (MFMA), or kw = 512 * chunks and F = 1 (DOT2)
+    mfma = launch.path == sk.SKINNY_PATH_MFMA
+    kw = (32 if mfma else 512) * launch.chunks
+    F = launch.rows // 16 if mfma else 1
+    assert launch.waves == F * -(-K // (launch.splits * kw))
     # pure: the same arguments give the same launch
     assert sk.skinny_choose(M, N, K, splits) == launch
 
@@ -79,7 +82,7 @@ def test_chooser_gives_valid_launches(sk, M, N, K, splits):
     "M,N,K,splits,needle",
     [(0, 1024, 4096, 0, "M=0"), (17, 1024, 4096, 0, "M=17"), (1, 1000, 4096, 0, "N=1000"),
      (1, 0, 4096, 0, "N=0"), (1, 1024, 4095, 0, "K=4095"), (1, 1024, 0, 0, "K=0"),
-     (1, 1024, 4096, 3, "splits=3"), (1, 1024, 4096, 16, "splits=16")],
+     (1, 1024, 4096, 3, "splits=3"), (1, 1024, 4096, 32, "splits=32")],
 )
 def test_unsupported_reasons(sk, M, N, K, splits, needle):
     reason = sk.skinny_gemm_unsupported(M, N, K, splits)
@@ -94,7 +97,11 @@ def test_launch_unsupported_reasons(sk):
     assert "chunks" in sk.skinny_launch_unsupported(1, 1024, 4096, L(1, 4, 8, 3, 1, 16))
     assert "waves" in sk.skinny_launch_unsupported(1, 1024, 4096, L(1, 4, 4, 4, 1, 16))
     assert "rows" in sk.skinny_launch_unsupported(1, 1024, 4096, L(1, 4, 8, 4, 1, 8))
-    assert "DOT2" in sk.skinny_launch_unsupported(16, 1024, 4096, L(0, 1, 8, 1, 1, 4))
+    assert "waves" in sk.skinny_launch_unsupported(1, 1024, 4096, L(1, 4, 8, 4, 1, 32))
+    assert sk.skinny_launch_unsupported(1, 1024, 4096, L(1, 4, 16, 4, 1, 32)) is None
+    assert "workspace" in sk.skinny_launch_unsupported(16, 16384, 4096, L(1, 16, 8, 1, 1, 16))
+    assert sk.skinny_launch_unsupported(16, 1024, 4096, L(1, 1, 16, 8, 1, 16)) is None
+    assert "DOT2" in sk.skinny_launch_unsupported(16, 1024, 4096, L(0, 1, 8, 1, 1, 16))
     assert "multiple" in sk.skinny_launch_unsupported(1, 1040, 4096, L(0, 1, 8, 1, 1, 32))
     assert sk.skinny_launch_unsupported(1, 1024, 4096, L(0, 1, 8, 1, 1, 4)) is None
     assert sk.skinny_launch_unsupported(16, 1024, 4096, L(1, 4, 8, 4, 2, 16)) is None

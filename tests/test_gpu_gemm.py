@@ -116,12 +116,13 @@ def test_pooler_weight_ring_layers(gpu_lib):
 def _all_launches(sk, M, N, K):
     out = []
     for path in (sk.SKINNY_PATH_MFMA, sk.SKINNY_PATH_DOT2):
-        for splits in (1, 2, 4, 8):
+        for splits in (1, 2, 4, 8, 16):
             for chunks in (1, 2, 4, 8, 16):
                 for accs in (1, 2, 4):
-                    for rows in ((16,) if path == sk.SKINNY_PATH_MFMA else (2, 4, 8, 16)):
-                        kw = (32 if path == sk.SKINNY_PATH_MFMA else 512) * chunks
-                        waves = -(-K // (splits * kw))
+                    mfma = path == sk.SKINNY_PATH_MFMA
+                    for rows in ((16, 32, 64) if mfma else (2, 4, 8, 16)):
+                        kw = (32 if mfma else 512) * chunks
+                        waves = (rows // 16 if mfma else 1) * -(-K // (splits * kw))
                         l = sk.Launch(path, splits, waves, chunks, accs, rows)
                         if sk.skinny_launch_unsupported(M, N, K, l) is None:
                             out.append(l)
@@ -193,3 +194,37 @@ def test_graph_capture_replay(gpu_lib):
                 assert np.array_equal(from_dev(y), expect)
             else:
                 assert_gemm_close(from_dev(y), expect, "graph replay with new x")
+
+
+@pytest.mark.parametrize("path", ["mfma", "mfma4", "dot2"])
+@pytest.mark.parametrize("splits", [2, 4, 8, 16])
+def test_split_k_handoff_alternating_inputs(gpu_lib, path, splits):
+    """Back-to-back split calls on alternating weights share the partials
+    workspace: a partial left from the previous call would show up as a wrong
+    or non-reproducible result."""
+    import torch
+
+    N, K, M = 1024, 4096, 4
+    xa, wa = synthetic.gemm_inputs(N=N, K=K, seed=21)
+    _, wb = synthetic.gemm_inputs(N=N, K=K, seed=22)
+    refs = [oracle.gemm_bf16(xa[:M], wa, THREADS), oracle.gemm_bf16(xa[:M], wb, THREADS)]
+    if path == "mfma":
+        launch = gpu_lib.Launch(1, splits, -(-K // (splits * 32 * 4)), 4, 2, 16)
+    elif path == "mfma4":
+        launch = gpu_lib.Launch(1, splits, 4 * -(-K // (splits * 32 * 4)), 4, 2, 64)
+    else:
+        launch = gpu_lib.Launch(0, splits, -(-K // (splits * 512)), 1, 1, 4)
+    if gpu_lib.skinny_launch_unsupported(M, N, K, launch) is not None:
+        pytest.skip(gpu_lib.skinny_launch_unsupported(M, N, K, launch))
+    _say(f"alternating {path} S={splits} {launch}")
+    x = to_dev(xa[:M])
+    ws = [to_dev(wa), to_dev(wb)]
+    ys = [torch.empty((M, N), dtype=torch.bfloat16, device="cuda") for _ in range(40)]
+    for i, y in enumerate(ys):
+        gpu_lib.skinny_gemm_bf16_launch(x, ws[i % 2], y, launch)
+    torch.cuda.synchronize()
+    first = [from_dev(ys[0]), from_dev(ys[1])]
+    for j in range(2):
+        assert_gemm_close(first[j], refs[j], f"alternating {path} S={splits} weight {j}")
+    for i, y in enumerate(ys):
+        assert np.array_equal(from_dev(y), first[i % 2]), f"call {i} differs"
