@@ -100,6 +100,47 @@ def cpu_baseline(budget_s: float = 12.0):
                       f"({el:.1f} s, {per_step * 1e3:.1f} ms/step)"}
 
 
+def epilogue_timing(sk, synthetic, dev, stream, reps: int = 50):
+    """us/call of the full pooler GEMM (M=8, N=4096, K=8192, on a 16-layer
+    ring) and of RMSNorm -> NVFP4 on [8, 4096] (latency-bound: ~92 KB)."""
+    import torch
+
+    M, N2, K2 = 8, 4096, 8192
+    ring = synthetic.device_weight_ring(16, N2, K2, dev, base_seed=5000)
+    xb, _ = synthetic.gemm_inputs(N=16, K=K2, seed=1)
+    x = synthetic.to_device(xb[:M], dev)
+    y = torch.empty((M, N2), dtype=torch.bfloat16, device=dev)
+    nw = synthetic.to_device(synthetic.norm_weight(N2, seed=1), dev)
+    gs = torch.tensor([100.0], dtype=torch.float32, device=dev)
+    a = torch.empty((M, N2 // 2), dtype=torch.uint8, device=dev)
+    sf = torch.empty((M, N2 // 16), dtype=torch.uint8, device=dev)
+
+    def timed(fns):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=stream):
+            for f in fns:
+                f()
+        g.replay()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            g.replay()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e3 / (reps * len(fns))
+
+    gemm_us = timed([lambda w=w: sk.skinny_gemm_bf16(x, w, y, 0) for w in ring])
+    norm_us = timed([lambda: sk.skinny_rmsnorm_nvfp4(y, nw, 1.0, 1e-6, gs, a, sf)] * 16)
+    del ring
+    gbytes = algorithmic_bytes(M, N2, K2)
+    return {"workload": "full pooler GEMM M=8 N=4096 K=8192 -> RMSNorm -> NVFP4 [8, 4096]",
+            "gemm_us_per_call": round(gemm_us, 3),
+            "gemm_GBs": round(gbytes / (gemm_us * 1e-6) / 1e9, 1),
+            "gemm_launch": dict(sk.skinny_choose(M, N2, K2, 0)._asdict()),
+            "norm_nvfp4_us_per_call": round(norm_us, 3)}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -187,6 +228,10 @@ def main():
             per_kernel[M] = us
             del g
 
+        # The expert-input epilogue (pooler page): full-pooler GEMM at M=8,
+        # then RMSNorm -> NVFP4 on its output, both timed per call.
+        epi = epilogue_timing(sk, synthetic, dev, stream)
+
     step_bytes = sum(algorithmic_bytes(M) for M in MS)
     value = step_bytes / (ms_step * 1e-3) / 1e9
     dom = max(MS, key=lambda M: per_kernel[M])
@@ -220,6 +265,7 @@ def main():
                      "bytes_per_launch": algorithmic_bytes(dom),
                      "us_per_launch": round(per_kernel[dom], 3)},
         "per_m": detail,
+        "epilogue": epi,
         "wall_s": round(wall, 3),
     }
     if not args.no_cpu:

@@ -137,63 +137,96 @@ static int launch_check(int M, int N, int K, const skinny_launch &l) {
   return fail(SKINNY_EUNSUPPORTED, "unknown path %d", l.path);
 }
 
-// DOT2 candidate with `rows` rows per workgroup: the fewest waves (largest
-// chunks) that cover a split's K range, waves <= the launch bound.
-static skinny_launch dot2_candidate(int M, int N, int K, int S, int rows) {
-  for (int chunks = kMaxDot2Chunks; chunks >= 1; chunks /= 2) {
-    skinny_launch c{SKINNY_PATH_DOT2, S, ceil_div(K, (long)S * kDot2K * chunks), chunks, 1, rows};
-    if (chunks > 1 && c.waves < 2) continue;  // keep at least two waves per workgroup
-    if (launch_check(M, N, K, c) == SKINNY_OK) return c;
+// Launch shapes measured best on MI355X for the pages' shard shapes (sweeps
+// of every valid launch, weights cycling through a ring larger than the
+// Infinity Cache): {N, K, M_lo, M_hi, launch}.
+struct TableEntry {
+  int N, K, m_lo, m_hi;
+  skinny_launch l;
+};
+static const TableEntry kTable[] = {
+    // unpooler shard
+    {1024, 4096, 1, 1, {SKINNY_PATH_DOT2, 1, 2, 4, 1, 2}},
+    {1024, 4096, 2, 2, {SKINNY_PATH_DOT2, 1, 4, 2, 1, 2}},
+    {1024, 4096, 3, 4, {SKINNY_PATH_DOT2, 1, 2, 4, 1, 2}},
+    {1024, 4096, 5, 8, {SKINNY_PATH_DOT2, 1, 4, 2, 1, 2}},
+    {1024, 4096, 9, 16, {SKINNY_PATH_MFMA, 4, 16, 2, 2, 16}},
+    // o_proj shard
+    {8192, 1024, 1, 4, {SKINNY_PATH_DOT2, 1, 1, 2, 1, 2}},
+    {8192, 1024, 5, 8, {SKINNY_PATH_MFMA, 1, 16, 4, 1, 32}},
+    {8192, 1024, 9, 16, {SKINNY_PATH_MFMA, 1, 16, 4, 2, 32}},
+    // pooler shard
+    {512, 8192, 1, 4, {SKINNY_PATH_DOT2, 1, 4, 4, 1, 2}},
+    {512, 8192, 5, 8, {SKINNY_PATH_DOT2, 1, 8, 2, 1, 2}},
+    {512, 8192, 9, 16, {SKINNY_PATH_MFMA, 8, 16, 2, 1, 16}},
+    // full pooler
+    {4096, 8192, 1, 2, {SKINNY_PATH_DOT2, 1, 8, 2, 1, 2}},
+    {4096, 8192, 3, 4, {SKINNY_PATH_DOT2, 1, 4, 4, 1, 4}},
+    {4096, 8192, 5, 16, {SKINNY_PATH_MFMA, 8, 8, 8, 1, 32}},
+};
+
+// The general rule the table follows (used for any other shape, or when an
+// explicit split count is asked for):
+//   DOT2 (lanes along K, activation traffic M / rows of the weight traffic)
+//   while M <= 4, or M <= 8 on narrow shards (< 256 MFMA tiles); 2 rows per
+//   workgroup, 4 chunks per wave for <= 4 tokens when K allows, else 2.
+//   MFMA otherwise: 2 tiles per workgroup on wide shards (>= 256 tiles), the
+//   split count that gives each workgroup about 32 KiB of weights (64 KiB
+//   past 16 MiB of weights), and the fewest chunks per wave that keep a
+//   workgroup within 16 waves.
+static skinny_launch rule(int M, int N, int K, int splits) {
+  const long tiles = N / kTileN;
+  const long units = ceil_div(K, kDot2K);
+  if (M <= 4 || (M <= 8 && tiles < 256)) {
+    const int chunks = (dot2_token_tile(M) <= 4 && units >= 8) ? 4 : (units >= 2 ? 2 : 1);
+    for (int S = splits ? splits : 1; S <= kMaxSplits; S *= 2) {
+      for (int c = chunks; c >= 1; c /= 2) {
+        const skinny_launch l{SKINNY_PATH_DOT2, S, ceil_div(K, (long)S * kDot2K * c), c, 1, 2};
+        if (launch_check(M, N, K, l) == SKINNY_OK) return l;
+      }
+      if (splits) break;
+    }
+  }
+  const int F = (tiles >= 256 && tiles % 2 == 0) ? 2 : 1;
+  const long groups = tiles / F;
+  const double wbytes = 2.0 * N * K;
+  const double target = wbytes > 16.0 * (1 << 20) ? 65536.0 : 32768.0;
+  int S = 1;
+  while (S < kMaxSplits && wbytes / (groups * S) > target && K >= (long)kMfmaK * 2 * S) S *= 2;
+  if (splits) S = splits;
+  for (; S <= kMaxSplits; S *= 2) {
+    for (int chunks = 2; chunks <= kMaxMfmaChunks; chunks *= 2) {
+      const int KW = ceil_div(K, (long)S * kMfmaK * chunks);
+      const skinny_launch l{SKINNY_PATH_MFMA, S, F * KW, chunks, 1, F * kTileN};
+      if (launch_check(M, N, K, l) == SKINNY_OK) return l;
+    }
+    for (int Fs : {1}) {  // a single tile per workgroup fits more waves' K
+      for (int chunks = 1; chunks <= kMaxMfmaChunks; chunks *= 2) {
+        const int KW = ceil_div(K, (long)S * kMfmaK * chunks);
+        const skinny_launch l{SKINNY_PATH_MFMA, S, Fs * KW, chunks, 1, Fs * kTileN};
+        if (launch_check(M, N, K, l) == SKINNY_OK) return l;
+      }
+    }
+    if (splits) break;
   }
   return skinny_launch{};
 }
 
-// MFMA candidate: F tiles per workgroup, S splits, the chunk count whose
-// waves fit the variant's launch bound and the LDS.
-static skinny_launch mfma_candidate(int M, int N, int K, int S, int F, int chunks) {
-  const int KW = ceil_div(K, (long)S * kMfmaK * chunks);
-  skinny_launch c{SKINNY_PATH_MFMA, S, F * KW, chunks, chunks >= 4 ? 2 : 1, F * kTileN};
-  return launch_check(M, N, K, c) == SKINNY_OK ? c : skinny_launch{};
-}
-
-// The chooser: a pure function of (M, N, K, splits), from launch-shape sweeps
-// on MI355X (rule of thumb: about 256-512 workgroups of 16-64 KiB of weights
-// each; DOT2 while its activation traffic, M / rows of the weight traffic,
-// stays small; MFMA with split-K partials beyond).
+// The chooser: a pure function of (M, N, K, splits): the measured table for
+// the shard shapes, the rule above otherwise.
 static int choose(int M, int N, int K, int splits, skinny_launch *out) {
   int st = check_problem(M, N, K);
   if (st) return st;
   if (splits != 0 && (splits < 1 || splits > kMaxSplits || (splits & (splits - 1))))
     return fail(SKINNY_EINVAL, "splits=%d: needs 0 (auto), 1, 2, 4, 8 or 16", splits);
   skinny_launch l{};
-  const long tiles = N / kTileN;
-  const bool dot2 = M <= 4 || (M <= 8 && tiles < 512);
-  if (dot2) {
-    for (int rows : {2, 4, 8, 16}) {
-      if (N % rows) continue;
-      l = dot2_candidate(M, N, K, splits ? splits : 1, rows);
-      if (l.waves) break;
+  for (const TableEntry &e : kTable)
+    if (e.N == N && e.K == K && M >= e.m_lo && M <= e.m_hi &&
+        (splits == 0 || splits == e.l.splits) && launch_check(M, N, K, e.l) == SKINNY_OK) {
+      l = e.l;
+      break;
     }
-  }
-  if (!l.waves) {
-    // MFMA: F tiles share the x slice; S so that (tiles / F) * S >= 256.
-    for (int F : {4, 2, 1}) {
-      if (F > 1 && (tiles % F || tiles / F < 32)) continue;
-      int S = splits;
-      if (S == 0) {
-        S = 1;
-        while (S < kMaxSplits && (tiles / F) * S < 256 && K >= (long)kMfmaK * 2 * S) S *= 2;
-      }
-      for (; !l.waves && S <= kMaxSplits; S *= 2) {
-        for (int chunks = 4; chunks <= kMaxMfmaChunks && !l.waves; chunks *= 2)
-          l = mfma_candidate(M, N, K, S, F, chunks);
-        for (int chunks = 2; chunks >= 1 && !l.waves; chunks /= 2)
-          l = mfma_candidate(M, N, K, S, F, chunks);
-        if (splits) break;
-      }
-      if (l.waves) break;
-    }
-  }
+  if (!l.waves) l = rule(M, N, K, splits);
   if (!l.waves)
     return fail(SKINNY_EUNSUPPORTED, "no launch for M=%d N=%d K=%d splits=%d (K too long "
                 "for the requested splits)", M, N, K, splits);
