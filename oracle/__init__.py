@@ -38,7 +38,14 @@ def _load():
         from . import build as _build  # compiling the checker is not using it
 
         _build.build()
-    lib = ctypes.CDLL(_LIB_PATH)
+    _lib = load_library(_LIB_PATH)
+    return _lib
+
+
+def load_library(path: str):
+    """ctypes handle of a compiled oracle with every signature declared (the
+    mutation tests load deliberately broken copies this way)."""
+    lib = ctypes.CDLL(path)
     lib.oracle_bf16_value.argtypes = [ctypes.c_uint16]
     lib.oracle_bf16_value.restype = ctypes.c_double
     lib.oracle_bf16_round.argtypes = [ctypes.c_double]
@@ -68,8 +75,25 @@ def _load():
         ctypes.c_int, ctypes.c_int, _u8p, _u8p, ctypes.c_void_p, ctypes.c_void_p,
         ctypes.c_void_p]
     lib.oracle_rmsnorm_nvfp4.restype = None
-    _lib = lib
     return lib
+
+
+class use_library:
+    """Context manager: route this module's functions to another compiled
+    oracle (a planted-mistake copy) for the duration of the block."""
+
+    def __init__(self, lib):
+        self.lib, self.saved = lib, None
+
+    def __enter__(self):
+        global _lib
+        self.saved, _lib = _lib, self.lib
+        return self.lib
+
+    def __exit__(self, *exc):
+        global _lib
+        _lib = self.saved
+        return False
 
 
 def _ptr(a):

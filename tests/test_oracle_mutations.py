@@ -1,0 +1,106 @@
+"""The oracle's pins catch planted mistakes.
+
+Each case copies oracle/skinny_oracle.c, plants one plausible mistake (a
+dropped term, a transposed operand, a wrong tie rule, bias, divisor, nibble
+order, ...), compiles the copy with gcc and runs the pin battery of
+tests/test_oracle_*.py against it.  At least one pin must fail for every
+mistake; the unmodified copy must pass them all.  Everything here runs on
+the CPU.
+"""
+import os
+import subprocess
+
+import pytest
+
+import oracle
+from tests import test_oracle_formats as F
+from tests import test_oracle_gemm as G
+from tests import test_oracle_norm as Nm
+
+SRC = os.path.join(os.path.dirname(oracle.__file__), "skinny_oracle.c")
+
+# (name, text in the source, replacement)
+MUTATIONS = [
+    ("gemm_drops_last_term",
+     "      for (int k = 0; k < K; ++k)\n        acc += oracle_bf16_value(x[(size_t)m * K + k]) *",
+     "      for (int k = 0; k < K - 1; ++k)\n        acc += oracle_bf16_value(x[(size_t)m * K + k]) *"),
+    ("gemm_transposed_w", "oracle_bf16_value(w[(size_t)n * K + k]);\n      y[",
+     "oracle_bf16_value(w[(size_t)k * N + n]);\n      y["),
+    ("gemm_output_transposed", "y[(size_t)m * N + n] = oracle_bf16_round(acc);",
+     "y[(size_t)n * M + m] = oracle_bf16_round(acc);"),
+    ("bf16_ties_away", "double q = nearbyint(ldexp(a, 8 - e));", "double q = round(ldexp(a, 8 - e));"),
+    ("bf16_truncates", "double q = nearbyint(ldexp(a, 8 - e));", "double q = floor(ldexp(a, 8 - e));"),
+    ("ties_to_odd_code", "(c & 1) == 0 && (best & 1) == 1", "(c & 1) == 1 && (best & 1) == 0"),
+    ("e4m3_wrong_bias", "mag = ldexp(1.0 + man / 8.0, exp - 7);", "mag = ldexp(1.0 + man / 8.0, exp - 8);"),
+    ("e2m1_drops_sign", "return (uint8_t)(signbit(v) ? 0x8 | mag : mag);", "return (uint8_t)mag;"),
+    ("block_scale_over_4", "global_scale * amax / 6.0", "global_scale * amax / 4.0"),
+    ("output_scale_inverted", "global_scale / dec; /* [oscale] */", "dec / global_scale; /* [oscale] */"),
+    ("signed_amax", "if (fabs(yn[j]) > amax) amax = fabs(yn[j]);", "if (yn[j] > amax) amax = yn[j];"),
+    ("nibbles_swapped", "(uint8_t)(codes[2 * i] | (codes[2 * i + 1] << 4));",
+     "(uint8_t)(codes[2 * i + 1] | (codes[2 * i] << 4));"),
+    ("mean_over_p_minus_1", "double inv = 1.0 / sqrt(ss / P + eps);",
+     "double inv = 1.0 / sqrt(ss / (P - 1) + eps);"),
+    ("eps_outside_root", "double inv = 1.0 / sqrt(ss / P + eps);",
+     "double inv = 1.0 / (sqrt(ss / P) + eps);"),
+    ("gain_center_dropped", "(oracle_bf16_value(w[j]) + gain_center)", "oracle_bf16_value(w[j])"),
+]
+
+# The pins (test functions that raise AssertionError on a mismatch).
+BATTERY = [
+    lambda: [G.test_gemm_brute_force_rational(s) for s in range(4)],
+    G.test_gemm_midpoint_ties,
+    G.test_gemm_identity_and_one_hot,
+    G.test_gemm_non_square_orientation,
+    G.test_gemm_exact_sums_match_numpy_float64,
+    G.test_gemm_exact_integer_inputs,
+    F.test_bf16_roundtrip_every_pattern,
+    F.test_bf16_round_matches_torch_from_float32,
+    F.test_bf16_round_exact_rational_midpoints,
+    F.test_e4m3_decode_matches_torch,
+    F.test_e4m3_encode_matches_torch_in_range,
+    F.test_e4m3_saturates_and_roundtrips,
+    F.test_e2m1_decode_table,
+    lambda: [F.test_e2m1_ties_and_saturation(v, c) for v, c in
+             [(0.25, 0x0), (0.75, 0x2), (1.25, 0x2), (1.75, 0x4), (2.5, 0x4), (3.5, 0x6),
+              (5.0, 0x6), (1e9, 0x7), (-0.25, 0x8), (-5.0, 0xE)]],
+    lambda: [Nm.test_golden_worked_blocks(c) for c in Nm._parse_golden()],
+    Nm.test_rmsnorm_constant_row_closed_form,
+    Nm.test_rmsnorm_one_hot_closed_form,
+    Nm.test_global_max_block_hits_the_largest_codes,
+    Nm.test_all_zero_block,
+    Nm.test_packing_low_nibble_even_column,
+]
+
+
+def _build(tmp_path, name, text=None, repl=None):
+    src = open(SRC).read()
+    if text is not None:
+        assert src.count(text) >= 1, f"mutation {name}: pattern not in the oracle source"
+        src = src.replace(text, repl)
+    c = tmp_path / f"{name}.c"
+    c.write_text(src)
+    so = tmp_path / f"lib{name}.so"
+    subprocess.run(["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-fopenmp", "-ffp-contract=off",
+                    str(c), "-o", str(so), "-lm"], check=True)
+    return oracle.load_library(str(so))
+
+
+def _failures(lib):
+    failed = []
+    with oracle.use_library(lib):
+        for i, pin in enumerate(BATTERY):
+            try:
+                pin()
+            except AssertionError:
+                failed.append(i)
+    return failed
+
+
+def test_unmodified_copy_passes_every_pin(tmp_path):
+    assert _failures(_build(tmp_path, "unmodified")) == []
+
+
+@pytest.mark.parametrize("name,text,repl", MUTATIONS, ids=[m[0] for m in MUTATIONS])
+def test_planted_mistake_is_caught(tmp_path, name, text, repl):
+    failed = _failures(_build(tmp_path, name, text, repl))
+    assert failed, f"no pin catches the planted mistake '{name}'"
