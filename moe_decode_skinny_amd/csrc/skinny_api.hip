@@ -148,28 +148,31 @@ static const TableEntry kTable[] = {
     // unpooler shard
     {1024, 4096, 1, 1, {SKINNY_PATH_DOT2, 1, 2, 4, 1, 2}},
     {1024, 4096, 2, 2, {SKINNY_PATH_DOT2, 1, 4, 2, 1, 2}},
-    {1024, 4096, 3, 4, {SKINNY_PATH_DOT2, 1, 2, 4, 1, 2}},
-    {1024, 4096, 5, 8, {SKINNY_PATH_DOT2, 1, 4, 2, 1, 2}},
-    {1024, 4096, 9, 16, {SKINNY_PATH_MFMA, 4, 16, 2, 2, 16}},
+    {1024, 4096, 3, 8, {SKINNY_PATH_DOT2, 1, 4, 2, 1, 4}},
+    {1024, 4096, 9, 16, {SKINNY_PATH_DOT2, 1, 8, 1, 1, 4}},
     // o_proj shard
-    {8192, 1024, 1, 4, {SKINNY_PATH_DOT2, 1, 1, 2, 1, 2}},
-    {8192, 1024, 5, 8, {SKINNY_PATH_MFMA, 1, 16, 4, 1, 32}},
-    {8192, 1024, 9, 16, {SKINNY_PATH_MFMA, 1, 16, 4, 2, 32}},
+    {8192, 1024, 1, 1, {SKINNY_PATH_DOT2, 1, 1, 2, 1, 2}},
+    {8192, 1024, 2, 2, {SKINNY_PATH_DOT2, 1, 1, 2, 1, 4}},
+    {8192, 1024, 3, 4, {SKINNY_PATH_DOT2, 1, 1, 2, 1, 2}},
+    {8192, 1024, 5, 8, {SKINNY_PATH_DOT2, 1, 2, 1, 1, 4}},
+    {8192, 1024, 9, 16, {SKINNY_PATH_MFMA, 1, 16, 4, 1, 32}},
     // pooler shard
     {512, 8192, 1, 4, {SKINNY_PATH_DOT2, 1, 4, 4, 1, 2}},
     {512, 8192, 5, 8, {SKINNY_PATH_DOT2, 1, 8, 2, 1, 2}},
-    {512, 8192, 9, 16, {SKINNY_PATH_MFMA, 8, 16, 2, 1, 16}},
+    {512, 8192, 9, 16, {SKINNY_PATH_DOT2, 2, 8, 1, 1, 4}},
     // full pooler
-    {4096, 8192, 1, 2, {SKINNY_PATH_DOT2, 1, 8, 2, 1, 2}},
-    {4096, 8192, 3, 4, {SKINNY_PATH_DOT2, 1, 4, 4, 1, 4}},
-    {4096, 8192, 5, 16, {SKINNY_PATH_MFMA, 8, 8, 8, 1, 32}},
+    {4096, 8192, 1, 1, {SKINNY_PATH_DOT2, 1, 8, 2, 1, 2}},
+    {4096, 8192, 2, 4, {SKINNY_PATH_DOT2, 1, 8, 2, 1, 8}},
+    {4096, 8192, 5, 8, {SKINNY_PATH_DOT2, 1, 8, 2, 1, 4}},
+    {4096, 8192, 9, 16, {SKINNY_PATH_MFMA, 8, 16, 4, 2, 32}},
 };
 
 // The general rule the table follows (used for any other shape, or when an
 // explicit split count is asked for):
-//   DOT2 (lanes along K, activation traffic M / rows of the weight traffic)
-//   while M <= 4, or M <= 8 on narrow shards (< 256 MFMA tiles); 2 rows per
-//   workgroup, 4 chunks per wave for <= 4 tokens when K allows, else 2.
+//   DOT2 (lanes along K; activation traffic M / rows of the weight traffic;
+//   no split-K) for M <= 8, and for M <= 16 on narrow shards (< 256 MFMA
+//   tiles); 2 rows per workgroup for M <= 2, else 4; 4 chunks per wave for
+//   <= 4 tokens when K allows, else 2 (1 at 16 tokens).
 //   MFMA otherwise: 2 tiles per workgroup on wide shards (>= 256 tiles), the
 //   split count that gives each workgroup about 32 KiB of weights (64 KiB
 //   past 16 MiB of weights), and the fewest chunks per wave that keep a
@@ -177,11 +180,13 @@ static const TableEntry kTable[] = {
 static skinny_launch rule(int M, int N, int K, int splits) {
   const long tiles = N / kTileN;
   const long units = ceil_div(K, kDot2K);
-  if (M <= 4 || (M <= 8 && tiles < 256)) {
-    const int chunks = (dot2_token_tile(M) <= 4 && units >= 8) ? 4 : (units >= 2 ? 2 : 1);
+  if (M <= 8 || tiles < 256) {
+    const int rows = M <= 2 ? 2 : 4;
+    const int mt = dot2_token_tile(M);
+    const int chunks = mt >= 16 ? 1 : (mt <= 4 && units >= 8) ? 4 : (units >= 2 ? 2 : 1);
     for (int S = splits ? splits : 1; S <= kMaxSplits; S *= 2) {
       for (int c = chunks; c >= 1; c /= 2) {
-        const skinny_launch l{SKINNY_PATH_DOT2, S, ceil_div(K, (long)S * kDot2K * c), c, 1, 2};
+        const skinny_launch l{SKINNY_PATH_DOT2, S, ceil_div(K, (long)S * kDot2K * c), c, 1, rows};
         if (launch_check(M, N, K, l) == SKINNY_OK) return l;
       }
       if (splits) break;
