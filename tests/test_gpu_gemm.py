@@ -67,8 +67,9 @@ def test_unpooler_m1_s1(gpu_lib, unpooler_inputs):
 
 
 @pytest.mark.parametrize("M", [1, 2, 4, 8, 16])
-@pytest.mark.parametrize("splits", [1, 2, 4])
+@pytest.mark.parametrize("splits", [0, 1, 2, 4])
 def test_unpooler_sweep_parity_and_determinism(gpu_lib, unpooler_inputs, M, splits):
+    """splits=0 is the chooser's launch, the one bench.py times."""
     x, w = unpooler_inputs
     _say(f"unpooler M={M} S={splits}")
     ref = oracle.gemm_bf16(x[:M], w, THREADS)
