@@ -15,7 +15,6 @@ constexpr int kMaxM = 16;          // tokens (unpooler page: 1 <= M <= 16)
 constexpr int kTileN = 16;         // features per MFMA tile (grid N / 16)
 constexpr int kMfmaK = 32;         // K per v_mfma_f32_16x16x32_bf16
 constexpr int kDot2K = 512;        // K per DOT2 chunk: 64 lanes x 8 bf16
-constexpr int kMaxWaves = 16;      // 1024 threads per workgroup
 constexpr int kMaxMfmaChunks = 16;
 constexpr int kMaxDot2Chunks = 4;
 constexpr int kMaxSplits = 16;
@@ -26,14 +25,12 @@ constexpr size_t kWorkspaceFloats = size_t(2) << 20;  // 8 MiB
 struct DeviceState {
   bool ready = false;
   float *partials = nullptr;  // kWorkspaceFloats
-  int cus = 0;
 };
 
 // The state of the current HIP device, or nullptr (and a reason) if the
 // device has not been initialised.
 DeviceState *current_state(int *status);
 
-void set_error(const char *fmt, ...);
 
 // ------------------------------------------------------------- launchers
 // Each returns hipSuccess or the launch error; arguments are already valid.

@@ -59,13 +59,6 @@ int ceil_div(long a, long b) { return (int)((a + b - 1) / b); }
 
 }  // namespace
 
-void set_error(const char *fmt, ...) {
-  va_list ap;
-  va_start(ap, fmt);
-  vsnprintf(g_error, sizeof g_error, fmt, ap);
-  va_end(ap);
-}
-
 DeviceState *current_state(int *status) {
   int dev = -1;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
@@ -205,12 +198,11 @@ static skinny_launch rule(int M, int N, int K, int splits) {
       const skinny_launch l{SKINNY_PATH_MFMA, S, F * KW, chunks, 1, F * kTileN};
       if (launch_check(M, N, K, l) == SKINNY_OK) return l;
     }
-    for (int Fs : {1}) {  // a single tile per workgroup fits more waves' K
-      for (int chunks = 1; chunks <= kMaxMfmaChunks; chunks *= 2) {
-        const int KW = ceil_div(K, (long)S * kMfmaK * chunks);
-        const skinny_launch l{SKINNY_PATH_MFMA, S, Fs * KW, chunks, 1, Fs * kTileN};
-        if (launch_check(M, N, K, l) == SKINNY_OK) return l;
-      }
+    // a single tile per workgroup leaves more waves for its K range
+    for (int chunks = 1; chunks <= kMaxMfmaChunks; chunks *= 2) {
+      const int KW = ceil_div(K, (long)S * kMfmaK * chunks);
+      const skinny_launch l{SKINNY_PATH_MFMA, S, KW, chunks, 1, kTileN};
+      if (launch_check(M, N, K, l) == SKINNY_OK) return l;
     }
     if (splits) break;
   }
@@ -328,7 +320,6 @@ int skinny_init(int device) {
       hipDeviceSynchronize() != hipSuccess) {
     status = fail(SKINNY_ELAUNCH, "workspace allocation failed on device %d", device);
   } else {
-    st.cus = prop.multiProcessorCount;
     st.ready = true;
   }
   if (hipSetDevice(prev) != hipSuccess && status == SKINNY_OK)
