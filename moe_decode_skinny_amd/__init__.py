@@ -9,7 +9,8 @@ fallback.
 
 Same names as the C ABI:
   skinny_init, skinny_gemm_bf16, skinny_gemm_bf16_launch, skinny_choose,
-  skinny_gemm_unsupported, skinny_launch_unsupported, skinny_rmsnorm_nvfp4,
+  skinny_gemm_unsupported, skinny_launch_unsupported, skinny_gemm_bf16_ring,
+  skinny_gemm_bf16_ring_launch, skinny_ring_choose, skinny_rmsnorm_nvfp4,
   skinny_rmsnorm_bf16, skinny_last_error, skinny_version
 Status codes map to exceptions as on the unpooler page (Unpooler.run /
 Unpooler.unsupported): EINVAL and EUNSUPPORTED raise ValueError, the others
@@ -69,6 +70,10 @@ _sig = {
     "skinny_choose": ([_i, _i, _i, _i, ctypes.POINTER(_CLaunch)], _i),
     "skinny_gemm_unsupported": ([_i, _i, _i, _i], _i),
     "skinny_launch_unsupported": ([_i, _i, _i, ctypes.POINTER(_CLaunch)], _i),
+    "skinny_gemm_bf16_ring": ([_vp, _vp, _vp, _i, _i, _i, _i, _vp], _i),
+    "skinny_gemm_bf16_ring_launch": (
+        [_vp, _vp, _vp, _i, _i, _i, _i, ctypes.POINTER(_CLaunch), _i, _vp], _i),
+    "skinny_ring_choose": ([_i, _i, _i, _i, ctypes.POINTER(_CLaunch), ctypes.POINTER(_i)], _i),
     "skinny_rmsnorm_nvfp4": ([_vp, _vp, _f, _f, _vp, _vp, _vp, _i, _i, _vp], _i),
     "skinny_rmsnorm_bf16": ([_vp, _vp, _f, _f, _vp, _i, _i, _vp], _i),
     "skinny_last_error": ([], ctypes.c_char_p),
@@ -176,6 +181,46 @@ def skinny_gemm_bf16_launch(x, w, y, launch: Launch, stream=None):
     return y
 
 
+def skinny_ring_choose(M: int, N: int, K: int, count: int):
+    """(Launch, workgroups) that skinny_gemm_bf16_ring uses."""
+    out, wg = _CLaunch(), _i(0)
+    _check(_lib.skinny_ring_choose(M, N, K, count, ctypes.byref(out), ctypes.byref(wg)))
+    return Launch(out.path, out.splits, out.waves, out.chunks, out.accs, out.rows), wg.value
+
+
+def _ring_args(xs, ws, ys):
+    if not (len(xs) == len(ws) == len(ys)) or not xs:
+        raise ValueError("xs, ws and ys must be non-empty lists of one length")
+    shapes = [_gemm_args(x, w, y) for x, w, y in zip(xs, ws, ys)]
+    M, N, K = shapes[0][3:]
+    if any(sh[3:] != (M, N, K) for sh in shapes):
+        raise ValueError("every ring item must have the same (M, N, K)")
+    arr = ctypes.c_void_p * len(xs)
+    xa = arr(*[sh[0] for sh in shapes])
+    wa = arr(*[sh[1] for sh in shapes])
+    ya = arr(*[sh[2] for sh in shapes])
+    return xa, wa, ya, len(xs), M, N, K
+
+
+def skinny_gemm_bf16_ring(xs, ws, ys, stream=None):
+    """ys[i] = xs[i] @ ws[i]^T for independent items of one shape, in one
+    launch; returns ys."""
+    xa, wa, ya, count, M, N, K = _ring_args(xs, ws, ys)
+    _check(_lib.skinny_gemm_bf16_ring(xa, wa, ya, count, M, N, K,
+                                      _stream(stream, xs[0].device)))
+    return ys
+
+
+def skinny_gemm_bf16_ring_launch(xs, ws, ys, launch: Launch, workgroups: int = 0,
+                                 stream=None):
+    """The ring at an explicit launch and workgroup count; returns ys."""
+    xa, wa, ya, count, M, N, K = _ring_args(xs, ws, ys)
+    c = Launch(*launch)._c()
+    _check(_lib.skinny_gemm_bf16_ring_launch(xa, wa, ya, count, M, N, K, ctypes.byref(c),
+                                             int(workgroups), _stream(stream, xs[0].device)))
+    return ys
+
+
 def skinny_rmsnorm_nvfp4(r, norm_w, gain_center: float, eps: float, global_scale, a, a_sf,
                          stream=None):
     """NVFP4 expert input of the rows of r into a [M, P/2] u8 and a_sf [M, P/16] u8."""
@@ -217,6 +262,7 @@ def skinny_rmsnorm_bf16(r, norm_w, gain_center: float, eps: float, y, stream=Non
 __all__ = [
     "Launch", "init", "skinny_init", "skinny_gemm_bf16", "skinny_gemm_bf16_launch",
     "skinny_choose", "skinny_gemm_unsupported", "skinny_launch_unsupported",
+    "skinny_gemm_bf16_ring", "skinny_gemm_bf16_ring_launch", "skinny_ring_choose",
     "skinny_rmsnorm_nvfp4", "skinny_rmsnorm_bf16", "skinny_last_error", "skinny_version",
     "LIB_PATH",
 ]

@@ -40,6 +40,15 @@ hipError_t launch_gemm_mfma(const uint16_t *x, const uint16_t *w, uint16_t *y,
 hipError_t launch_gemm_dot2(const uint16_t *x, const uint16_t *w, uint16_t *y,
                             int M, int N, int K, const skinny_launch &l,
                             DeviceState &st, hipStream_t stream);
+// The layer ring: up to kMaxRingItems independent GEMMs of one shape.
+constexpr int kMaxRingItems = 64;
+struct RingItems {
+  const uint16_t *x[kMaxRingItems];
+  const uint16_t *w[kMaxRingItems];
+  uint16_t *y[kMaxRingItems];
+};
+hipError_t launch_gemm_ring(const RingItems &items, int count, int M, int N, int K,
+                            const skinny_launch &l, int workgroups, hipStream_t stream);
 hipError_t launch_split_reduce(const float *partials, uint16_t *y, int M, int N, int S,
                                hipStream_t stream);
 hipError_t launch_rmsnorm(const uint16_t *r, const uint16_t *w, float gain_center,
@@ -56,6 +65,7 @@ constexpr size_t kMaxDynamicLds = 160 * 1024;  // all of a gfx950 CU's LDS
 bool dot2_variant_exists(int rows, int chunks, int mt);
 int dot2_token_tile(int M);  // smallest compiled token count >= M, 0 if none
 int dot2_max_waves();        // waves per DOT2 workgroup (launch bound)
+bool ring_variant_exists(int rows, int chunks, int mt);
 
 }  // namespace skinny
 

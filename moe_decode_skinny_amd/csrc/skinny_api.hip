@@ -233,6 +233,137 @@ static int choose(int M, int N, int K, int splits, skinny_launch *out) {
   return SKINNY_OK;
 }
 
+// Validity of a layer-ring launch: a DOT2 shape with one split whose
+// double-buffered ring kernel is compiled, and 1..count * N / rows
+// workgroups (every workgroup starts with a tile).
+static int ring_check(int count, int M, int N, int K, const skinny_launch &l, int workgroups) {
+  int st = check_problem(M, N, K);
+  if (st) return st;
+  if (count < 1 || count > kMaxRingItems)
+    return fail(SKINNY_EINVAL, "count=%d: needs 1 <= count <= %d", count, kMaxRingItems);
+  if (l.path != SKINNY_PATH_DOT2 || l.splits != 1 || l.accs != 1)
+    return fail(SKINNY_EUNSUPPORTED, "the ring runs DOT2 launches with splits=1 and accs=1");
+  if (l.rows <= 0 || N % l.rows)
+    return fail(SKINNY_EUNSUPPORTED, "N=%d is not a multiple of rows=%d", N, l.rows);
+  if (!ring_variant_exists(l.rows, l.chunks, dot2_token_tile(M)))
+    return fail(SKINNY_EUNSUPPORTED, "no ring kernel with rows=%d chunks=%d tokens=%d", l.rows,
+                l.chunks, dot2_token_tile(M));
+  const long kw = (long)kDot2K * l.chunks;
+  const int need = ceil_div(K, kw);
+  if (l.waves != need || l.waves < 1 || l.waves > dot2_max_waves())
+    return fail(SKINNY_EUNSUPPORTED, "K=%d at kw=%ld needs %d waves (given %d, at most %d)", K,
+                kw, need, l.waves, dot2_max_waves());
+  const long total = (long)count * (N / l.rows);
+  if (workgroups < 1 || workgroups > total)
+    return fail(SKINNY_EUNSUPPORTED, "workgroups=%d: needs 1..%ld (one tile each at least)",
+                workgroups, total);
+  return SKINNY_OK;
+}
+
+// Ring launches measured on MI355X for the shard shapes (60-item rings of
+// distinct weights and activations): {N, K, M_lo, M_hi, launch, workgroups}.
+// More workgroups than output blocks lets two workgroups take alternate
+// items of one block; the count is capped at the ring's tile count.
+struct RingEntry {
+  int N, K, m_lo, m_hi;
+  skinny_launch l;
+  int workgroups;
+};
+static const RingEntry kRingTable[] = {
+    // unpooler shard
+    {1024, 4096, 1, 1, {SKINNY_PATH_DOT2, 1, 2, 4, 1, 2}, 1024},
+    {1024, 4096, 2, 2, {SKINNY_PATH_DOT2, 1, 8, 1, 1, 4}, 512},
+    {1024, 4096, 3, 4, {SKINNY_PATH_DOT2, 1, 8, 1, 1, 8}, 512},
+    {1024, 4096, 5, 8, {SKINNY_PATH_DOT2, 1, 4, 2, 1, 4}, 2048},
+    {1024, 4096, 9, 16, {SKINNY_PATH_DOT2, 1, 8, 1, 1, 4}, 512},
+    // o_proj shard
+    {8192, 1024, 1, 1, {SKINNY_PATH_DOT2, 1, 2, 1, 1, 8}, 512},
+    {8192, 1024, 2, 2, {SKINNY_PATH_DOT2, 1, 2, 1, 1, 4}, 1024},
+    {8192, 1024, 3, 8, {SKINNY_PATH_DOT2, 1, 2, 1, 1, 8}, 1024},
+    {8192, 1024, 9, 16, {SKINNY_PATH_DOT2, 1, 2, 1, 1, 4}, 4096},
+    // pooler shard
+    {512, 8192, 1, 1, {SKINNY_PATH_DOT2, 1, 4, 4, 1, 2}, 1024},
+    {512, 8192, 2, 2, {SKINNY_PATH_DOT2, 1, 8, 2, 1, 4}, 1024},
+    {512, 8192, 3, 4, {SKINNY_PATH_DOT2, 1, 8, 2, 1, 4}, 512},
+    {512, 8192, 5, 8, {SKINNY_PATH_DOT2, 1, 8, 2, 1, 4}, 256},
+    // full pooler
+    {4096, 8192, 1, 1, {SKINNY_PATH_DOT2, 1, 4, 4, 1, 2}, 512},
+    {4096, 8192, 2, 8, {SKINNY_PATH_DOT2, 1, 8, 2, 1, 4}, 256},
+};
+
+// Ring rule for any other shape: 2 rows per workgroup for <= 2 tokens, 4 up
+// to 8, 2 beyond (the register budget of two weight buffers), the most
+// chunks that fit and that K fills, one workgroup per output block.
+static int ring_choose(int M, int N, int K, int count, skinny_launch *out, int *workgroups) {
+  int st = check_problem(M, N, K);
+  if (st) return st;
+  if (count < 1 || count > kMaxRingItems)
+    return fail(SKINNY_EINVAL, "count=%d: needs 1 <= count <= %d", count, kMaxRingItems);
+  skinny_launch l{};
+  int wg = 0;
+  for (const RingEntry &e : kRingTable) {
+    if (e.N != N || e.K != K || M < e.m_lo || M > e.m_hi) continue;
+    const long total = (long)count * (N / e.l.rows);
+    const int w = (int)(e.workgroups < total ? e.workgroups : total);
+    if (ring_check(count, M, N, K, e.l, w) == SKINNY_OK) {
+      l = e.l;
+      wg = w;
+      break;
+    }
+  }
+  if (!l.waves) {
+    const int mt = dot2_token_tile(M);
+    const int prefer = mt <= 2 ? 2 : mt <= 8 ? 4 : 2;
+    const int rows_order[] = {prefer, 4, 2, 8};
+    int c0 = 1;  // no more chunks than K has 512-element units
+    while (c0 < kMaxDot2Chunks && 2L * c0 * kDot2K <= K) c0 *= 2;
+    for (int rows : rows_order) {
+      for (int c = c0; c >= 1 && !l.waves; c /= 2) {
+        const skinny_launch t{SKINNY_PATH_DOT2, 1, ceil_div(K, (long)kDot2K * c), c, 1, rows};
+        if (N % rows == 0 && ring_check(count, M, N, K, t, N / rows) == SKINNY_OK) l = t;
+      }
+      if (l.waves) break;
+    }
+  }
+  if (!l.waves)
+    return fail(SKINNY_EUNSUPPORTED, "no ring launch for M=%d N=%d K=%d (K too long for one "
+                "workgroup)", M, N, K);
+  *out = l;
+  *workgroups = wg ? wg : N / l.rows;
+  return SKINNY_OK;
+}
+
+static int ring_common(const void *const *x, const void *const *W, void *const *y, int count,
+                       int M, int N, int K, const skinny_launch &l, int workgroups,
+                       void *stream) {
+  if (!x || !W || !y) return fail(SKINNY_EINVAL, "null pointer array");
+  RingItems items;
+  const size_t xb = 2ul * M * K, wb = 2ul * N * K, yb = 2ul * M * N;
+  for (int i = 0; i < count; ++i) {
+    if (!x[i] || !W[i] || !y[i]) return fail(SKINNY_EINVAL, "item %d: null pointer", i);
+    if (!aligned(x[i], 16) || !aligned(W[i], 16) || !aligned(y[i], 16))
+      return fail(SKINNY_EINVAL, "item %d: x, W and y must be 16-byte aligned", i);
+    items.x[i] = static_cast<const uint16_t *>(x[i]);
+    items.w[i] = static_cast<const uint16_t *>(W[i]);
+    items.y[i] = static_cast<uint16_t *>(y[i]);
+  }
+  // Items run concurrently: no output may alias any input or another output.
+  for (int i = 0; i < count; ++i)
+    for (int j = 0; j < count; ++j) {
+      if (overlap(y[i], yb, x[j], xb) || overlap(y[i], yb, W[j], wb))
+        return fail(SKINNY_EINVAL, "y of item %d overlaps x or W of item %d (the ring's items "
+                    "are independent)", i, j);
+      if (i != j && overlap(y[i], yb, y[j], yb))
+        return fail(SKINNY_EINVAL, "y of items %d and %d overlap", i, j);
+    }
+  int st = SKINNY_OK;
+  if (!current_state(&st)) return st;
+  hipError_t e = launch_gemm_ring(items, count, M, N, K, l, workgroups,
+                                  static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(SKINNY_ELAUNCH, "launch failed: %s", hipGetErrorString(e));
+  return SKINNY_OK;
+}
+
 static int gemm_common(const void *x, const void *W, void *y, int M, int N, int K,
                        const skinny_launch &l, void *stream) {
   if (!x || !W || !y) return fail(SKINNY_EINVAL, "null pointer");
@@ -356,6 +487,30 @@ int skinny_gemm_bf16_launch(const void *x, const void *W, void *y, int M, int N,
   int st = launch_check(M, N, K, *launch);
   if (st) return st;
   return gemm_common(x, W, y, M, N, K, *launch, stream);
+}
+
+int skinny_ring_choose(int M, int N, int K, int count, skinny_launch *out, int *workgroups) {
+  if (!out || !workgroups) return fail(SKINNY_EINVAL, "null output");
+  return ring_choose(M, N, K, count, out, workgroups);
+}
+
+int skinny_gemm_bf16_ring(const void *const *x, const void *const *W, void *const *y,
+                          int count, int M, int N, int K, void *stream) {
+  skinny_launch l;
+  int workgroups = 0;
+  int st = ring_choose(M, N, K, count, &l, &workgroups);
+  if (st) return st;
+  return ring_common(x, W, y, count, M, N, K, l, workgroups, stream);
+}
+
+int skinny_gemm_bf16_ring_launch(const void *const *x, const void *const *W, void *const *y,
+                                 int count, int M, int N, int K, const skinny_launch *launch,
+                                 int workgroups, void *stream) {
+  if (!launch) return fail(SKINNY_EINVAL, "null launch");
+  if (workgroups == 0 && launch->rows > 0) workgroups = N / launch->rows;  // one per block
+  int st = ring_check(count, M, N, K, *launch, workgroups);
+  if (st) return st;
+  return ring_common(x, W, y, count, M, N, K, *launch, workgroups, stream);
 }
 
 int skinny_rmsnorm_nvfp4(const void *r, const void *norm_w, float gain_center, float eps,

@@ -125,3 +125,95 @@ def test_compute_calls_without_device_fail_cleanly(sk):
     assert lib.skinny_rmsnorm_nvfp4(0x1000, 0x2000, 1.0, 1e-6, 0x3000, 0x4000, 0x5000, 8, 4100,
                                     None) == sk.SKINNY_EINVAL
     assert "P=4100" in sk.skinny_last_error()
+
+
+@pytest.mark.parametrize("M,N,K", [(m, 1024, 4096) for m in (1, 2, 4, 8, 16)]
+                         + [(m, 8192, 1024) for m in (1, 8, 16)]
+                         + [(m, 512, 8192) for m in (1, 8)]
+                         + [(m, 4096, 8192) for m in (1, 8)]
+                         + [(3, 48, 1000), (16, 16, 8), (1, 16, 8)])
+@pytest.mark.parametrize("count", [1, 7, 64])
+def test_ring_chooser_gives_valid_launches(sk, M, N, K, count):
+    launch, wg = sk.skinny_ring_choose(M, N, K, count)
+    assert launch.path == sk.SKINNY_PATH_DOT2 and launch.splits == 1 and launch.accs == 1
+    assert launch.waves == -(-K // (512 * launch.chunks)) <= 8
+    assert N % launch.rows == 0 and 1 <= wg <= count * N // launch.rows
+    # the ring's launch is also a valid single-call launch (same arithmetic)
+    assert sk.skinny_launch_unsupported(M, N, K, launch) is None
+    assert sk.skinny_ring_choose(M, N, K, count) == (launch, wg)
+
+
+def test_ring_unsupported_shapes_and_reasons(sk):
+    with pytest.raises(ValueError, match="count=0"):
+        sk.skinny_ring_choose(1, 1024, 4096, 0)
+    with pytest.raises(ValueError, match="count=65"):
+        sk.skinny_ring_choose(1, 1024, 4096, 65)
+    with pytest.raises(ValueError, match="M=17"):
+        sk.skinny_ring_choose(17, 1024, 4096, 1)
+    # 16 tokens at K = 8192 need 16 waves of one chunk: more than a workgroup
+    with pytest.raises(ValueError, match="no ring launch"):
+        sk.skinny_ring_choose(16, 4096, 8192, 2)
+
+
+def _ring_lib(sk):
+    lib = ctypes.CDLL(sk.LIB_PATH)
+    lib.skinny_gemm_bf16_ring_launch.argtypes = [ctypes.c_void_p] * 3 + [ctypes.c_int] * 4 + [
+        ctypes.POINTER(sk._CLaunch), ctypes.c_int, ctypes.c_void_p]
+    lib.skinny_gemm_bf16_ring.argtypes = [ctypes.c_void_p] * 3 + [ctypes.c_int] * 4 + [
+        ctypes.c_void_p]
+    return lib
+
+
+def _ptrs(*vals):
+    return (ctypes.c_void_p * len(vals))(*vals)
+
+
+def test_ring_launch_reasons_without_device(sk):
+    lib = _ring_lib(sk)
+    M, N, K = 1, 1024, 4096
+    x, w, y = _ptrs(0x100000), _ptrs(0x1000000), _ptrs(0x4000000)
+
+    def call(launch, wg=0, count=1, xs=x, ws=w, ys=y):
+        c = sk.Launch(*launch)._c()
+        return lib.skinny_gemm_bf16_ring_launch(xs, ws, ys, count, M, N, K, ctypes.byref(c), wg,
+                                                None)
+
+    assert call((1, 1, 16, 4, 1, 16)) == sk.SKINNY_EUNSUPPORTED
+    assert "DOT2" in sk.skinny_last_error()
+    assert call((0, 2, 1, 4, 1, 2)) == sk.SKINNY_EUNSUPPORTED
+    assert "splits=1" in sk.skinny_last_error()
+    assert call((0, 1, 3, 4, 1, 2)) == sk.SKINNY_EUNSUPPORTED
+    assert "waves" in sk.skinny_last_error()
+    assert call((0, 1, 2, 4, 1, 2), wg=513) == sk.SKINNY_EUNSUPPORTED
+    assert "workgroups=513" in sk.skinny_last_error()
+    assert call((0, 1, 2, 4, 1, 16)) == sk.SKINNY_EUNSUPPORTED
+    assert "ring kernel" in sk.skinny_last_error()
+    assert call((0, 1, 2, 4, 1, 2), count=65) == sk.SKINNY_EINVAL
+    # a valid launch passes every check and stops at the missing device
+    assert call((0, 1, 2, 4, 1, 2)) in (sk.SKINNY_EDEVICE, sk.SKINNY_ENOTINIT)
+
+
+def test_ring_rejects_aliased_items_without_device(sk):
+    lib = _ring_lib(sk)
+    M, N, K = 2, 64, 256
+    wb, yb = 2 * N * K, 2 * M * N
+    x0, x1 = 0x100000, 0x200000
+    w0, w1 = 0x300000, 0x400000
+    y0, y1 = 0x500000, 0x600000
+
+    def ring(xs, ws, ys):
+        return lib.skinny_gemm_bf16_ring(_ptrs(*xs), _ptrs(*ws), _ptrs(*ys), len(xs), M, N, K,
+                                         None)
+
+    # a chain (x of item 1 = y of item 0) is refused: the items run concurrently
+    assert ring([x0, y0], [w0, w1], [y0, y1]) == sk.SKINNY_EINVAL
+    assert "independent" in sk.skinny_last_error()
+    assert ring([x0, x1], [w0, w1 + wb - 2], [y0, w1 + wb - 16]) == sk.SKINNY_EINVAL
+    assert ring([x0, x1], [w0, w1], [y0, y0 + yb - 16]) == sk.SKINNY_EINVAL
+    assert "items 0 and 1" in sk.skinny_last_error()
+    assert ring([x0, None], [w0, w1], [y0, y1]) == sk.SKINNY_EINVAL
+    assert "item 1" in sk.skinny_last_error()
+    assert ring([x0, x1 + 8], [w0, w1], [y0, y1]) == sk.SKINNY_EINVAL
+    assert "aligned" in sk.skinny_last_error()
+    # one x shared by every item and disjoint outputs are fine
+    assert ring([x0, x0], [w0, w1], [y0, y1]) in (sk.SKINNY_EDEVICE, sk.SKINNY_ENOTINIT)
