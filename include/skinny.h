@@ -118,14 +118,29 @@ int skinny_gemm_unsupported(int M, int N, int K, int splits);
 /* Why (M, N, K) cannot run at `launch`; SKINNY_OK when it can.  Host only. */
 int skinny_launch_unsupported(int M, int N, int K, const skinny_launch *launch);
 
+/* A launch of the layer ring (skinny_gemm_bf16_ring_launch).
+ *   gemm        the per-tile launch shape, splits = 1: DOT2 (rows 2, 4 or 8,
+ *               chunks 1, 2, 4; waves = ceil(K / (512 chunks)) <= 8) or MFMA
+ *               (rows 16, 32, 64; chunks 1..16; accs 1 or 2; waves =
+ *               rows / 16 * ceil(K / (32 chunks)) <= 16, <= 8 at 16 chunks)
+ *   segment     consecutive output blocks of one item a workgroup takes in a
+ *               row, keeping that item's activations in registers; it
+ *               divides N / gemm.rows
+ *   workgroups  persistent workgroups, 1 .. count * N / (rows * segment);
+ *               workgroup b takes segments b, b + workgroups, ... of the
+ *               item-major segment order */
+typedef struct skinny_ring_launch {
+  skinny_launch gemm;
+  int segment;
+  int workgroups;
+} skinny_ring_launch;
+
 /* The layer ring: `count` independent GEMMs y_i = bf16(x_i @ W_i^T) of one
  * shape (M, N, K) in one persistent launch (unpooler page, module
  * description: the weights are loaded before the dependency wait and the
  * activations after it, so that a layer's weight stream overlaps the end of
- * the previous layer).  Each workgroup takes (item, output block) tiles in
- * item order and has the weights of its next tile in flight while it
- * multiplies, reduces and stores the current one; a tile's activations are
- * loaded when the tile starts.
+ * the previous layer).  Each workgroup has the weights of its next tile in
+ * flight while it multiplies, reduces and stores the current one.
  *   x, W, y   HOST arrays of `count` device pointers, read during the call
  *             only; x[i] bf16 [M, K], W[i] bf16 [N, K], y[i] bf16 [M, N], all
  *             16-byte aligned
@@ -133,28 +148,29 @@ int skinny_launch_unsupported(int M, int N, int K, const skinny_launch *launch);
  *   M, N, K   as for skinny_gemm_bf16
  * The items run concurrently: no y[i] may overlap any x[j], W[j] or another
  * y[j] (a chain whose x[i + 1] is y[i] needs one call per item).  Every y[i]
- * is bitwise identical to skinny_gemm_bf16_launch at the ring's launch
- * shape.  Uses no workspace, so ring calls on different streams may overlap.
+ * is bitwise identical to skinny_gemm_bf16_launch at the ring's gemm shape
+ * (when that shape is also a valid single-call launch), whatever the
+ * segment and workgroup count.  Uses no workspace, so ring calls on
+ * different streams may overlap.
  * Errors: SKINNY_EINVAL, SKINNY_EUNSUPPORTED, SKINNY_ENOTINIT, SKINNY_ELAUNCH. */
 int skinny_gemm_bf16_ring(const void *const *x, const void *const *W,
                           void *const *y, int count, int M, int N, int K,
                           void *stream);
 
-/* The ring at an explicit launch: a DOT2 shape with splits = 1 (rows, chunks,
- * waves as for skinny_gemm_bf16_launch) and `workgroups` persistent
- * workgroups, 1 <= workgroups <= count * N / rows (0 = N / rows, one per
- * output block); workgroup b takes tiles b, b + workgroups, ... of the
- * count * N / rows (item, block) tiles in item-major order. */
+/* The ring at an explicit launch (see skinny_ring_launch). */
 int skinny_gemm_bf16_ring_launch(const void *const *x, const void *const *W,
                                  void *const *y, int count, int M, int N,
-                                 int K, const skinny_launch *launch,
-                                 int workgroups, void *stream);
+                                 int K, const skinny_ring_launch *launch,
+                                 void *stream);
 
-/* The ring's chooser: the launch and workgroup count skinny_gemm_bf16_ring
- * uses for (M, N, K, count).  Host only.  SKINNY_OK, or SKINNY_EINVAL /
- * SKINNY_EUNSUPPORTED with the reason in skinny_last_error(). */
-int skinny_ring_choose(int M, int N, int K, int count, skinny_launch *out,
-                       int *workgroups);
+/* The ring's chooser: the launch skinny_gemm_bf16_ring uses for (M, N, K,
+ * count).  Host only.  SKINNY_OK, or SKINNY_EINVAL / SKINNY_EUNSUPPORTED with
+ * the reason in skinny_last_error(). */
+int skinny_ring_choose(int M, int N, int K, int count, skinny_ring_launch *out);
+
+/* Why (M, N, K, count) cannot run at `launch`; SKINNY_OK when it can. */
+int skinny_ring_launch_unsupported(int M, int N, int K, int count,
+                                   const skinny_ring_launch *launch);
 
 /* The NVFP4 expert input (pooler_gather page, module description and
  * compile_norm_quant; nvfp4_compute_output_scale; cvt_e2m1x8_f32;

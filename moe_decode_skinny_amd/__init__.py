@@ -10,8 +10,8 @@ fallback.
 Same names as the C ABI:
   skinny_init, skinny_gemm_bf16, skinny_gemm_bf16_launch, skinny_choose,
   skinny_gemm_unsupported, skinny_launch_unsupported, skinny_gemm_bf16_ring,
-  skinny_gemm_bf16_ring_launch, skinny_ring_choose, skinny_rmsnorm_nvfp4,
-  skinny_rmsnorm_bf16, skinny_last_error, skinny_version
+  skinny_gemm_bf16_ring_launch, skinny_ring_choose, skinny_ring_launch_unsupported,
+  skinny_rmsnorm_nvfp4, skinny_rmsnorm_bf16, skinny_last_error, skinny_version
 Status codes map to exceptions as on the unpooler page (Unpooler.run /
 Unpooler.unsupported): EINVAL and EUNSUPPORTED raise ValueError, the others
 RuntimeError.
@@ -60,6 +60,26 @@ class Launch(NamedTuple):
         return _CLaunch(*self)
 
 
+class _CRingLaunch(ctypes.Structure):
+    _fields_ = [("gemm", _CLaunch), ("segment", ctypes.c_int), ("workgroups", ctypes.c_int)]
+
+
+class RingLaunch(NamedTuple):
+    """skinny_ring_launch: gemm (a Launch with splits = 1), segment, workgroups."""
+    gemm: Launch
+    segment: int
+    workgroups: int
+
+    def _c(self) -> _CRingLaunch:
+        return _CRingLaunch(Launch(*self.gemm)._c(), self.segment, self.workgroups)
+
+    @staticmethod
+    def _from_c(c: _CRingLaunch) -> "RingLaunch":
+        g = c.gemm
+        return RingLaunch(Launch(g.path, g.splits, g.waves, g.chunks, g.accs, g.rows),
+                          c.segment, c.workgroups)
+
+
 _vp = ctypes.c_void_p
 _i = ctypes.c_int
 _f = ctypes.c_float
@@ -72,8 +92,9 @@ _sig = {
     "skinny_launch_unsupported": ([_i, _i, _i, ctypes.POINTER(_CLaunch)], _i),
     "skinny_gemm_bf16_ring": ([_vp, _vp, _vp, _i, _i, _i, _i, _vp], _i),
     "skinny_gemm_bf16_ring_launch": (
-        [_vp, _vp, _vp, _i, _i, _i, _i, ctypes.POINTER(_CLaunch), _i, _vp], _i),
-    "skinny_ring_choose": ([_i, _i, _i, _i, ctypes.POINTER(_CLaunch), ctypes.POINTER(_i)], _i),
+        [_vp, _vp, _vp, _i, _i, _i, _i, ctypes.POINTER(_CRingLaunch), _vp], _i),
+    "skinny_ring_choose": ([_i, _i, _i, _i, ctypes.POINTER(_CRingLaunch)], _i),
+    "skinny_ring_launch_unsupported": ([_i, _i, _i, _i, ctypes.POINTER(_CRingLaunch)], _i),
     "skinny_rmsnorm_nvfp4": ([_vp, _vp, _f, _f, _vp, _vp, _vp, _i, _i, _vp], _i),
     "skinny_rmsnorm_bf16": ([_vp, _vp, _f, _f, _vp, _i, _i, _vp], _i),
     "skinny_last_error": ([], ctypes.c_char_p),
@@ -181,11 +202,18 @@ def skinny_gemm_bf16_launch(x, w, y, launch: Launch, stream=None):
     return y
 
 
-def skinny_ring_choose(M: int, N: int, K: int, count: int):
-    """(Launch, workgroups) that skinny_gemm_bf16_ring uses."""
-    out, wg = _CLaunch(), _i(0)
-    _check(_lib.skinny_ring_choose(M, N, K, count, ctypes.byref(out), ctypes.byref(wg)))
-    return Launch(out.path, out.splits, out.waves, out.chunks, out.accs, out.rows), wg.value
+def skinny_ring_choose(M: int, N: int, K: int, count: int) -> RingLaunch:
+    """The RingLaunch that skinny_gemm_bf16_ring uses."""
+    out = _CRingLaunch()
+    _check(_lib.skinny_ring_choose(M, N, K, count, ctypes.byref(out)))
+    return RingLaunch._from_c(out)
+
+
+def skinny_ring_launch_unsupported(M: int, N: int, K: int, count: int,
+                                   launch: RingLaunch) -> Optional[str]:
+    c = RingLaunch(*launch)._c()
+    st = _lib.skinny_ring_launch_unsupported(M, N, K, count, ctypes.byref(c))
+    return None if st == SKINNY_OK else skinny_last_error()
 
 
 def _ring_args(xs, ws, ys):
@@ -211,13 +239,12 @@ def skinny_gemm_bf16_ring(xs, ws, ys, stream=None):
     return ys
 
 
-def skinny_gemm_bf16_ring_launch(xs, ws, ys, launch: Launch, workgroups: int = 0,
-                                 stream=None):
-    """The ring at an explicit launch and workgroup count; returns ys."""
+def skinny_gemm_bf16_ring_launch(xs, ws, ys, launch: RingLaunch, stream=None):
+    """The ring at an explicit RingLaunch; returns ys."""
     xa, wa, ya, count, M, N, K = _ring_args(xs, ws, ys)
-    c = Launch(*launch)._c()
+    c = RingLaunch(*launch)._c()
     _check(_lib.skinny_gemm_bf16_ring_launch(xa, wa, ya, count, M, N, K, ctypes.byref(c),
-                                             int(workgroups), _stream(stream, xs[0].device)))
+                                             _stream(stream, xs[0].device)))
     return ys
 
 
@@ -260,9 +287,10 @@ def skinny_rmsnorm_bf16(r, norm_w, gain_center: float, eps: float, y, stream=Non
 
 
 __all__ = [
-    "Launch", "init", "skinny_init", "skinny_gemm_bf16", "skinny_gemm_bf16_launch",
+    "Launch", "RingLaunch", "init", "skinny_init", "skinny_gemm_bf16", "skinny_gemm_bf16_launch",
     "skinny_choose", "skinny_gemm_unsupported", "skinny_launch_unsupported",
     "skinny_gemm_bf16_ring", "skinny_gemm_bf16_ring_launch", "skinny_ring_choose",
+    "skinny_ring_launch_unsupported",
     "skinny_rmsnorm_nvfp4", "skinny_rmsnorm_bf16", "skinny_last_error", "skinny_version",
     "LIB_PATH",
 ]

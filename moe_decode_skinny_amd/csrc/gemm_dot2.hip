@@ -26,7 +26,7 @@ __global__ __launch_bounds__(kDot2MaxThreads) void gemm_dot2_kernel(
     uint16_t *__restrict__ y, float *__restrict__ partials, int M, int N, int K,
     int S, int groups, int kw) {
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  const int wave = wave_index();
   const int waves = blockDim.x >> 6;
 
   int group, s;

@@ -43,7 +43,7 @@ __global__ __launch_bounds__(mfma_max_threads(CHUNKS)) void gemm_mfma_kernel(
     uint16_t *__restrict__ y, float *__restrict__ partials, int M, int N, int K,
     int S, int groups, int F, int kw) {
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  const int wave = wave_index();
   const int waves = blockDim.x >> 6;
   const int KW = waves / F;
   const int f = wave / KW, q = wave - f * KW;

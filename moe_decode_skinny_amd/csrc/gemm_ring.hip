@@ -1,20 +1,31 @@
-// The layer-ring launch of the DOT2 GEMM: `count` independent small-M GEMMs
+// The layer-ring launch: `count` independent small-M GEMMs
 // y_i[M, N] = x_i[M, K] @ W_i[N, K]^T of one shape in one persistent launch,
-// each weight matrix streamed while the previous GEMM is finished.
+// each weight matrix streamed while the previous GEMM is finished.  Two
+// kernel families, DOT2 (VALU dot products, lanes along K) and MFMA.
 //
 // The unpooler page's module description loads the weights before the
 // dependency wait and the activations after it, so that one layer's weight
 // stream overlaps the end of the previous kernel.  Within one launch the same
-// ordering becomes a software pipeline per workgroup: the (item, block)
-// tiles are taken in item order, j = blockIdx.x + n * gridDim.x, and while
-// tile j is multiplied, reduced and stored, the weight loads of tile
-// j + gridDim.x are already in flight.  Each tile's activations are loaded
-// only when the tile starts, after the weights of the tile before it.
+// ordering becomes a software pipeline per workgroup: while one tile (item,
+// output block) is multiplied, reduced and stored, the weight loads of the
+// workgroup's next tile are already in flight.  Activations are loaded when a
+// workgroup starts on an item, after the weights of the tile before.
 //
-// Per tile the arithmetic is that of the single-call DOT2 kernel with
-// splits = 1 at the same (rows, chunks, waves): the same lane products, the
-// same wave reduce-scatter and the same wave order through LDS, so every
-// item's y is bitwise identical to skinny_gemm_bf16_launch at that shape.
+// Tile order.  The count * groups tiles (groups = N / rows output blocks per
+// item) are cut into segments of `seg` consecutive blocks of one item, in
+// item-major order; workgroup b takes segments b, b + G, b + 2 G, ... (G
+// workgroups) and the blocks of each in order.  A wave's activations depend
+// only on the item and its K range, so they stay in registers for the whole
+// segment: the activation traffic is that of one tile per segment.
+//
+// Per tile the arithmetic is that of the single-call kernel of the same
+// family with splits = 1 at the same (rows, chunks, waves, accs): the same
+// products in the same order, the same cross-lane and cross-wave sums, so
+// every item's y is bitwise identical to skinny_gemm_bf16_launch at that
+// shape.  The MFMA ring differs from the single-call MFMA kernel only in
+// where its B fragments come from: each wave loads them from global memory
+// (L2) instead of a workgroup copy in LDS, so the LDS capacity does not limit
+// K.
 #include "dot2_device.h"
 
 namespace skinny {
@@ -22,6 +33,23 @@ namespace {
 
 using namespace dot2;
 
+// A workgroup's place in its tile walk and the tile it names.
+struct RingWalk {
+  int groups, seg, spi, segs;  // blocks per item, blocks per segment,
+                               // segments per item, segments in all
+  __device__ int item(int s) const { return s / spi; }
+  __device__ int block(int s, int sub) const { return (s - item(s) * spi) * seg + sub; }
+  // The tile after (s, sub) for this workgroup; false past the last one.
+  __device__ bool advance(int &s, int &sub) const {
+    if (++sub == seg) {
+      sub = 0;
+      s += (int)gridDim.x;
+    }
+    return s < segs;
+  }
+};
+
+// ------------------------------------------------------------------ DOT2 ring
 // Issue the loads of ROWS weight rows of one tile (or of nothing: bytes = 0
 // turns every load into a zero read that touches no memory).
 template <int ROWS, int CHUNKS>
@@ -38,40 +66,45 @@ __device__ __forceinline__ void load_weights(u32x4 (&wv)[ROWS][CHUNKS], const ui
   }
 }
 
-struct RingShape {
-  int count, M, N, K, groups, total, kw;
+struct Dot2Args {
+  int M, N, K;
 };
 
-// One tile: activations of tile j, then the weights of tile j + G into
-// `next`, then the products with `cur`, the reductions and the store.
-// Returns true when tile j + G does not exist.  P selects the LDS buffer.
+// One tile (s, sub): activations if the segment starts here, then the
+// weights of the next tile into `next`, then the products with `cur`, the
+// reductions and the store.  Returns false after the workgroup's last tile.
+// P selects the LDS buffer.
 template <int ROWS, int CHUNKS, int MT, int P>
-__device__ __forceinline__ bool ring_tile(const RingItems &items, const RingShape &sh, int j,
-                                          u32x4 (&cur)[ROWS][CHUNKS],
-                                          u32x4 (&next)[ROWS][CHUNKS],
-                                          float (&red)[2][kDot2MaxThreads / 64][ROWS * MT],
-                                          int lane, int wave, int waves, int k0) {
-  const int item = j / sh.groups;
-  const int f0 = (j - item * sh.groups) * ROWS;
-  const int K = sh.K;
+__device__ __forceinline__ bool dot2_ring_tile(const RingItems &items, const Dot2Args &a,
+                                               const RingWalk &walk, int &s, int &sub,
+                                               u32x4 (&cur)[ROWS][CHUNKS],
+                                               u32x4 (&next)[ROWS][CHUNKS],
+                                               u32x4 (&xv)[MT][CHUNKS],
+                                               float (&red)[2][kDot2MaxThreads / 64][ROWS * MT],
+                                               int lane, int wave, int waves, int k0) {
+  const int K = a.K;
+  const int item = walk.item(s);
+  const int f0 = walk.block(s, sub) * ROWS;
 
-  const __amdgpu_buffer_rsrc_t xres = buffer_rsrc(items.x[item], (unsigned)(sh.M * K * 2));
-  u32x4 xv[MT][CHUNKS];
+  if (sub == 0) {
+    const __amdgpu_buffer_rsrc_t xres = buffer_rsrc(items.x[item], (unsigned)(a.M * K * 2));
 #pragma unroll
-  for (int c = 0; c < CHUNKS; ++c) {
-    const bool in = k0 + c * kDot2K < K;
+    for (int c = 0; c < CHUNKS; ++c) {
+      const bool in = k0 + c * kDot2K < K;
 #pragma unroll
-    for (int t = 0; t < MT; ++t)
-      xv[t][c] = __builtin_amdgcn_raw_buffer_load_b128(
-          xres, in ? (t * K + k0 + c * kDot2K) * 2 : kOutOfRange, 0, 0);
+      for (int t = 0; t < MT; ++t)
+        xv[t][c] = __builtin_amdgcn_raw_buffer_load_b128(
+            xres, in ? (t * K + k0 + c * kDot2K) * 2 : kOutOfRange, 0, 0);
+    }
   }
   __builtin_amdgcn_sched_barrier(0);
-  const int jn = j + (int)gridDim.x;
-  const bool more = jn < sh.total;
+  int ns = s, nsub = sub;
+  const bool more = walk.advance(ns, nsub);
   {
-    const int ni = more ? jn / sh.groups : item;
-    const int nf0 = more ? (jn - ni * sh.groups) * ROWS : 0;
-    load_weights<ROWS, CHUNKS>(next, items.w[ni] + (size_t)nf0 * K,
+    // Past the last tile, name the current one again (with no bytes): the
+    // index arithmetic stays branch-free.
+    const int cs = more ? ns : s, csub = more ? nsub : sub;
+    load_weights<ROWS, CHUNKS>(next, items.w[walk.item(cs)] + (size_t)walk.block(cs, csub) * ROWS * K,
                                more ? (unsigned)(ROWS * K * 2) : 0u, K, k0);
   }
   __builtin_amdgcn_sched_barrier(0);
@@ -105,79 +138,214 @@ __device__ __forceinline__ bool ring_tile(const RingItems &items, const RingShap
     const int r = lane / MT, t = lane % MT;
     float part = red[P][0][lane];
     for (int v2 = 1; v2 < waves; ++v2) part += red[P][v2][lane];
-    if (t < sh.M) items.y[item][(size_t)t * sh.N + f0 + r] = (uint16_t)f32_to_bf16(part);
+    if (t < a.M) items.y[item][(size_t)t * a.N + f0 + r] = (uint16_t)f32_to_bf16(part);
   }
-  return !more;
+  s = ns;
+  sub = nsub;
+  return more;
 }
 
 template <int ROWS, int CHUNKS, int MT>
 __global__ __launch_bounds__(kDot2MaxThreads) void gemm_dot2_ring_kernel(
-    RingItems items, int count, int M, int N, int K, int groups, int kw) {
+    RingItems items, int M, int N, int K, RingWalk walk, int kw) {
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  const int wave = wave_index();
   const int waves = blockDim.x >> 6;
-  const RingShape sh{count, M, N, K, groups, count * groups, kw};
+  const Dot2Args a{M, N, K};
   const int k0 = wave * kw + lane * 8;
   __shared__ float red[2][kDot2MaxThreads / 64][ROWS * MT];
 
-  // gridDim.x <= count * groups, so every workgroup has a first tile.
-  int j = blockIdx.x;
-  u32x4 wa[ROWS][CHUNKS], wb[ROWS][CHUNKS];
-  {
-    const int item = j / groups;
-    const int f0 = (j - item * groups) * ROWS;
-    load_weights<ROWS, CHUNKS>(wa, items.w[item] + (size_t)f0 * K, (unsigned)(ROWS * K * 2),
-                               K, k0);
-  }
+  // gridDim.x <= walk.segs, so every workgroup has a first tile.
+  int s = blockIdx.x, sub = 0;
+  u32x4 wa[ROWS][CHUNKS], wb[ROWS][CHUNKS], xv[MT][CHUNKS];
+  load_weights<ROWS, CHUNKS>(wa, items.w[walk.item(s)] + (size_t)walk.block(s, 0) * ROWS * K,
+                             (unsigned)(ROWS * K * 2), K, k0);
   for (;;) {
-    if (ring_tile<ROWS, CHUNKS, MT, 0>(items, sh, j, wa, wb, red, lane, wave, waves, k0)) break;
-    j += gridDim.x;
-    if (ring_tile<ROWS, CHUNKS, MT, 1>(items, sh, j, wb, wa, red, lane, wave, waves, k0)) break;
-    j += gridDim.x;
+    if (!dot2_ring_tile<ROWS, CHUNKS, MT, 0>(items, a, walk, s, sub, wa, wb, xv, red, lane, wave,
+                                              waves, k0))
+      break;
+    if (!dot2_ring_tile<ROWS, CHUNKS, MT, 1>(items, a, walk, s, sub, wb, wa, xv, red, lane, wave,
+                                              waves, k0))
+      break;
   }
 }
 
-using RingKernel = void (*)(RingItems, int, int, int, int, int, int);
+using Dot2RingKernel = void (*)(RingItems, int, int, int, RingWalk, int);
 
 // Register budget per lane: two weight buffers 8 * ROWS * CHUNKS,
 // activations 4 * MT * CHUNKS, sums ROWS * MT.
-constexpr bool ring_fits(int rows, int chunks, int mt) {
+constexpr bool dot2_ring_fits(int rows, int chunks, int mt) {
   return 8 * rows * chunks + 4 * mt * chunks + rows * mt <= 160;
 }
 
 template <int R, int C, int T>
-constexpr RingKernel ring_variant() {
-  if constexpr (ring_fits(R, C, T)) return gemm_dot2_ring_kernel<R, C, T>;
+constexpr Dot2RingKernel dot2_ring_variant() {
+  if constexpr (dot2_ring_fits(R, C, T)) return gemm_dot2_ring_kernel<R, C, T>;
   else return nullptr;
 }
 
 template <int R, int C>
-RingKernel ring_pick_mt(int mt) {
+Dot2RingKernel dot2_ring_pick_mt(int mt) {
   switch (mt) {
-    case 1: return ring_variant<R, C, 1>();
-    case 2: return ring_variant<R, C, 2>();
-    case 4: return ring_variant<R, C, 4>();
-    case 8: return ring_variant<R, C, 8>();
-    case 16: return ring_variant<R, C, 16>();
+    case 1: return dot2_ring_variant<R, C, 1>();
+    case 2: return dot2_ring_variant<R, C, 2>();
+    case 4: return dot2_ring_variant<R, C, 4>();
+    case 8: return dot2_ring_variant<R, C, 8>();
+    case 16: return dot2_ring_variant<R, C, 16>();
   }
   return nullptr;
 }
 
 template <int R>
-RingKernel ring_pick_chunks(int chunks, int mt) {
+Dot2RingKernel dot2_ring_pick_chunks(int chunks, int mt) {
   switch (chunks) {
-    case 1: return ring_pick_mt<R, 1>(mt);
-    case 2: return ring_pick_mt<R, 2>(mt);
-    case 4: return ring_pick_mt<R, 4>(mt);
+    case 1: return dot2_ring_pick_mt<R, 1>(mt);
+    case 2: return dot2_ring_pick_mt<R, 2>(mt);
+    case 4: return dot2_ring_pick_mt<R, 4>(mt);
   }
   return nullptr;
 }
 
-RingKernel ring_pick(int rows, int chunks, int mt) {
+Dot2RingKernel dot2_ring_pick(int rows, int chunks, int mt) {
   switch (rows) {
-    case 2: return ring_pick_chunks<2>(chunks, mt);
-    case 4: return ring_pick_chunks<4>(chunks, mt);
-    case 8: return ring_pick_chunks<8>(chunks, mt);
+    case 2: return dot2_ring_pick_chunks<2>(chunks, mt);
+    case 4: return dot2_ring_pick_chunks<4>(chunks, mt);
+    case 8: return dot2_ring_pick_chunks<8>(chunks, mt);
+  }
+  return nullptr;
+}
+
+// ------------------------------------------------------------------ MFMA ring
+// A block is F MFMA tiles of 16 features; waves (f, q), q < KW, and wave
+// (f, q) owns K [q kw, (q + 1) kw), kw = 32 CHUNKS, of tile block * F + f.
+// Lane layout of v_mfma_f32_16x16x32_bf16 as in the single-call kernel:
+// A lane l = W[row l % 16][k + 8 (l / 16) ..], B lane l = x[token l % 16][same
+// k], D lane l = features 4 (l / 16) + 0..3 of token l % 16.
+constexpr int mfma_ring_threads(int chunks) { return chunks >= 16 ? 512 : 1024; }
+
+template <int CHUNKS>
+__device__ __forceinline__ void load_tile_weights(u32x4 (&wv)[CHUNKS], const uint16_t *w,
+                                                  unsigned bytes, int K, int k0, int row) {
+  const __amdgpu_buffer_rsrc_t res = buffer_rsrc(w, bytes);
+#pragma unroll
+  for (int i = 0; i < CHUNKS; ++i)
+    wv[i] = __builtin_amdgcn_raw_buffer_load_b128(
+        res, k0 + i * kMfmaK < K ? (row * K + k0 + i * kMfmaK) * 2 : kOutOfRange, 0, kCacheNT);
+}
+
+struct MfmaArgs {
+  int M, N, K, F, KW;
+};
+
+template <int CHUNKS, int ACCS, int P>
+__device__ __forceinline__ bool mfma_ring_tile(const RingItems &items, const MfmaArgs &a,
+                                               const RingWalk &walk, int &s, int &sub,
+                                               u32x4 (&cur)[CHUNKS], u32x4 (&next)[CHUNKS],
+                                               u32x4 (&xv)[CHUNKS], f32x4 (*red)[16][64],
+                                               int lane, int wave, int f, int q, int k0) {
+  const int row = lane & 15, grp = lane >> 4;
+  const int K = a.K;
+  const int item = walk.item(s);
+  const int tile = walk.block(s, sub) * a.F + f;
+
+  // B fragments x[row][k0 + 32 i ..] when the segment starts; rows >= M and
+  // K past the end read zeros.
+  if (sub == 0) {
+    const __amdgpu_buffer_rsrc_t xres = buffer_rsrc(items.x[item], (unsigned)(a.M * K * 2));
+#pragma unroll
+    for (int i = 0; i < CHUNKS; ++i)
+      xv[i] = __builtin_amdgcn_raw_buffer_load_b128(
+          xres, k0 + i * kMfmaK < K ? (row * K + k0 + i * kMfmaK) * 2 : kOutOfRange, 0, 0);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  int ns = s, nsub = sub;
+  const bool more = walk.advance(ns, nsub);
+  {
+    const int cs = more ? ns : s, csub = more ? nsub : sub;  // as in the DOT2 ring
+    load_tile_weights<CHUNKS>(next, items.w[walk.item(cs)] +
+                                        (size_t)(walk.block(cs, csub) * a.F + f) * kTileN * K,
+                              more ? (unsigned)(kTileN * K * 2) : 0u, K, k0, row);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+
+  f32x4 acc[ACCS];
+#pragma unroll
+  for (int c = 0; c < ACCS; ++c) acc[c] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int i = 0; i < CHUNKS; ++i)
+    acc[i % ACCS] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+        __builtin_bit_cast(bf16x8, cur[i]), __builtin_bit_cast(bf16x8, xv[i]), acc[i % ACCS], 0,
+        0, 0);
+  f32x4 part = acc[0];
+#pragma unroll
+  for (int c = 1; c < ACCS; ++c) part += acc[c];
+
+  // Waves q = 0..KW-1 of each tile in order through LDS buffer P (rewritten
+  // two tiles later, after a barrier that follows every read of it).
+  if (a.KW > 1) {
+    red[P][wave][lane] = part;
+    __syncthreads();
+    if (q == 0) {
+      part = red[P][f * a.KW][lane];
+      for (int v = 1; v < a.KW; ++v) part += red[P][f * a.KW + v][lane];
+    }
+  }
+  if (q == 0 && row < a.M) {
+    const int col = tile * kTileN + grp * 4;
+    const unsigned lo = f32_to_bf16(part[0]) | (f32_to_bf16(part[1]) << 16);
+    const unsigned hi = f32_to_bf16(part[2]) | (f32_to_bf16(part[3]) << 16);
+    *reinterpret_cast<uint2 *>(items.y[item] + (size_t)row * a.N + col) = make_uint2(lo, hi);
+  }
+  s = ns;
+  sub = nsub;
+  return more;
+}
+
+template <int CHUNKS, int ACCS>
+__global__ __launch_bounds__(mfma_ring_threads(CHUNKS)) void gemm_mfma_ring_kernel(
+    RingItems items, int M, int N, int K, RingWalk walk, int F, int kw) {
+  const int lane = threadIdx.x & 63;
+  const int wave = wave_index();
+  const int waves = blockDim.x >> 6;
+  const int KW = waves / F;
+  const int f = wave / KW, q = wave - f * KW;
+  const MfmaArgs a{M, N, K, F, KW};
+  const int k0 = q * kw + (lane >> 4) * 8;
+  __shared__ f32x4 red[2][16][64];
+
+  int s = blockIdx.x, sub = 0;  // gridDim.x <= walk.segs
+  u32x4 wa[CHUNKS], wb[CHUNKS], xv[CHUNKS];
+  load_tile_weights<CHUNKS>(wa, items.w[walk.item(s)] + (size_t)(walk.block(s, 0) * F + f) *
+                                                            kTileN * K,
+                            (unsigned)(kTileN * K * 2), K, k0, lane & 15);
+  for (;;) {
+    if (!mfma_ring_tile<CHUNKS, ACCS, 0>(items, a, walk, s, sub, wa, wb, xv, red, lane, wave, f,
+                                          q, k0))
+      break;
+    if (!mfma_ring_tile<CHUNKS, ACCS, 1>(items, a, walk, s, sub, wb, wa, xv, red, lane, wave, f,
+                                          q, k0))
+      break;
+  }
+}
+
+using MfmaRingKernel = void (*)(RingItems, int, int, int, RingWalk, int, int);
+
+template <int C>
+MfmaRingKernel mfma_ring_pick_accs(int accs) {
+  switch (accs) {
+    case 1: return gemm_mfma_ring_kernel<C, 1>;
+    case 2: return gemm_mfma_ring_kernel<C, 2>;
+  }
+  return nullptr;
+}
+
+MfmaRingKernel mfma_ring_pick(int chunks, int accs) {
+  switch (chunks) {
+    case 1: return mfma_ring_pick_accs<1>(accs);
+    case 2: return mfma_ring_pick_accs<2>(accs);
+    case 4: return mfma_ring_pick_accs<4>(accs);
+    case 8: return mfma_ring_pick_accs<8>(accs);
+    case 16: return mfma_ring_pick_accs<16>(accs);
   }
   return nullptr;
 }
@@ -185,15 +353,27 @@ RingKernel ring_pick(int rows, int chunks, int mt) {
 }  // namespace
 
 bool ring_variant_exists(int rows, int chunks, int mt) {
-  return ring_pick(rows, chunks, mt) != nullptr;
+  return dot2_ring_pick(rows, chunks, mt) != nullptr;
 }
 
+bool mfma_ring_variant_exists(int chunks, int accs) {
+  return mfma_ring_pick(chunks, accs) != nullptr;
+}
+
+int mfma_ring_max_waves(int chunks) { return mfma_ring_threads(chunks) / 64; }
+
 hipError_t launch_gemm_ring(const RingItems &items, int count, int M, int N, int K,
-                            const skinny_launch &l, int workgroups, hipStream_t stream) {
-  RingKernel k = ring_pick(l.rows, l.chunks, dot2_token_tile(M));
+                            const skinny_ring_launch &r, hipStream_t stream) {
+  const skinny_launch &l = r.gemm;
   const int groups = N / l.rows;
-  hipLaunchKernelGGL(k, dim3(workgroups), dim3(64 * l.waves), 0, stream, items, count, M, N,
-                     K, groups, kDot2K * l.chunks);
+  const RingWalk walk{groups, r.segment, groups / r.segment, count * (groups / r.segment)};
+  if (l.path == SKINNY_PATH_MFMA) {
+    hipLaunchKernelGGL(mfma_ring_pick(l.chunks, l.accs), dim3(r.workgroups), dim3(64 * l.waves),
+                       0, stream, items, M, N, K, walk, l.rows / kTileN, kMfmaK * l.chunks);
+  } else {
+    hipLaunchKernelGGL(dot2_ring_pick(l.rows, l.chunks, dot2_token_tile(M)), dim3(r.workgroups),
+                       dim3(64 * l.waves), 0, stream, items, M, N, K, walk, kDot2K * l.chunks);
+  }
   return hipGetLastError();
 }
 

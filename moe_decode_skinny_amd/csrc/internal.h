@@ -48,7 +48,7 @@ struct RingItems {
   uint16_t *y[kMaxRingItems];
 };
 hipError_t launch_gemm_ring(const RingItems &items, int count, int M, int N, int K,
-                            const skinny_launch &l, int workgroups, hipStream_t stream);
+                            const skinny_ring_launch &r, hipStream_t stream);
 hipError_t launch_split_reduce(const float *partials, uint16_t *y, int M, int N, int S,
                                hipStream_t stream);
 hipError_t launch_rmsnorm(const uint16_t *r, const uint16_t *w, float gain_center,
@@ -65,7 +65,9 @@ constexpr size_t kMaxDynamicLds = 160 * 1024;  // all of a gfx950 CU's LDS
 bool dot2_variant_exists(int rows, int chunks, int mt);
 int dot2_token_tile(int M);  // smallest compiled token count >= M, 0 if none
 int dot2_max_waves();        // waves per DOT2 workgroup (launch bound)
-bool ring_variant_exists(int rows, int chunks, int mt);
+bool ring_variant_exists(int rows, int chunks, int mt);       // DOT2 ring
+bool mfma_ring_variant_exists(int chunks, int accs);          // MFMA ring
+int mfma_ring_max_waves(int chunks);
 
 }  // namespace skinny
 
@@ -84,6 +86,14 @@ __device__ __forceinline__ unsigned f32_to_bf16(float f) {
   if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;
   u += 0x7fffu + ((u >> 16) & 1u);
   return u >> 16;
+}
+
+// The wave's index in its workgroup as a wave-uniform (scalar) value.  The
+// compiler cannot prove threadIdx.x >> 6 uniform, and a buffer resource
+// derived from a value it takes as divergent is rebuilt lane by lane in a
+// loop around every load.
+__device__ __forceinline__ int wave_index() {
+  return __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
 }
 
 __device__ __forceinline__ float bf16_lo(unsigned u) { return __uint_as_float(u << 16); }

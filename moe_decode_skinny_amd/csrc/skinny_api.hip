@@ -233,109 +233,148 @@ static int choose(int M, int N, int K, int splits, skinny_launch *out) {
   return SKINNY_OK;
 }
 
-// Validity of a layer-ring launch: a DOT2 shape with one split whose
-// double-buffered ring kernel is compiled, and 1..count * N / rows
-// workgroups (every workgroup starts with a tile).
-static int ring_check(int count, int M, int N, int K, const skinny_launch &l, int workgroups) {
+// Validity of a layer-ring launch: splits = 1, a compiled ring kernel of the
+// launch's family (DOT2: rows, chunks, token tile; MFMA: chunks, accs), the
+// waves that cover K in one pass, a segment that divides the blocks of an
+// item, and 1..(segments in all) workgroups (each starts with a segment).
+static int ring_check(int count, int M, int N, int K, const skinny_ring_launch &r) {
+  const skinny_launch &l = r.gemm;
   int st = check_problem(M, N, K);
   if (st) return st;
   if (count < 1 || count > kMaxRingItems)
     return fail(SKINNY_EINVAL, "count=%d: needs 1 <= count <= %d", count, kMaxRingItems);
-  if (l.path != SKINNY_PATH_DOT2 || l.splits != 1 || l.accs != 1)
-    return fail(SKINNY_EUNSUPPORTED, "the ring runs DOT2 launches with splits=1 and accs=1");
-  if (l.rows <= 0 || N % l.rows)
-    return fail(SKINNY_EUNSUPPORTED, "N=%d is not a multiple of rows=%d", N, l.rows);
-  if (!ring_variant_exists(l.rows, l.chunks, dot2_token_tile(M)))
-    return fail(SKINNY_EUNSUPPORTED, "no ring kernel with rows=%d chunks=%d tokens=%d", l.rows,
-                l.chunks, dot2_token_tile(M));
-  const long kw = (long)kDot2K * l.chunks;
-  const int need = ceil_div(K, kw);
-  if (l.waves != need || l.waves < 1 || l.waves > dot2_max_waves())
-    return fail(SKINNY_EUNSUPPORTED, "K=%d at kw=%ld needs %d waves (given %d, at most %d)", K,
-                kw, need, l.waves, dot2_max_waves());
-  const long total = (long)count * (N / l.rows);
-  if (workgroups < 1 || workgroups > total)
-    return fail(SKINNY_EUNSUPPORTED, "workgroups=%d: needs 1..%ld (one tile each at least)",
-                workgroups, total);
+  if (l.splits != 1) return fail(SKINNY_EUNSUPPORTED, "the ring runs launches with splits=1");
+  if (l.path == SKINNY_PATH_MFMA) {
+    if (l.rows != 16 && l.rows != 32 && l.rows != 64)
+      return fail(SKINNY_EUNSUPPORTED, "MFMA rows=%d: needs 16, 32 or 64", l.rows);
+    if (N % l.rows)
+      return fail(SKINNY_EUNSUPPORTED, "N=%d is not a multiple of rows=%d", N, l.rows);
+    if (!mfma_ring_variant_exists(l.chunks, l.accs))
+      return fail(SKINNY_EUNSUPPORTED, "no MFMA ring kernel with chunks=%d accs=%d (chunks 1, "
+                  "2, 4, 8, 16; accs 1, 2)", l.chunks, l.accs);
+    const long kw = (long)kMfmaK * l.chunks;
+    const int need = (l.rows / kTileN) * ceil_div(K, kw);
+    if (l.waves != need || l.waves > mfma_ring_max_waves(l.chunks))
+      return fail(SKINNY_EUNSUPPORTED, "K=%d at kw=%ld and %d tiles needs %d waves (given %d, "
+                  "at most %d)", K, kw, l.rows / kTileN, need, l.waves,
+                  mfma_ring_max_waves(l.chunks));
+  } else if (l.path == SKINNY_PATH_DOT2) {
+    if (l.accs != 1) return fail(SKINNY_EUNSUPPORTED, "DOT2 launch has accs=1");
+    if (l.rows <= 0 || N % l.rows)
+      return fail(SKINNY_EUNSUPPORTED, "N=%d is not a multiple of rows=%d", N, l.rows);
+    if (!ring_variant_exists(l.rows, l.chunks, dot2_token_tile(M)))
+      return fail(SKINNY_EUNSUPPORTED, "no ring kernel with rows=%d chunks=%d tokens=%d",
+                  l.rows, l.chunks, dot2_token_tile(M));
+    const long kw = (long)kDot2K * l.chunks;
+    const int need = ceil_div(K, kw);
+    if (l.waves != need || l.waves < 1 || l.waves > dot2_max_waves())
+      return fail(SKINNY_EUNSUPPORTED, "K=%d at kw=%ld needs %d waves (given %d, at most %d)",
+                  K, kw, need, l.waves, dot2_max_waves());
+  } else {
+    return fail(SKINNY_EUNSUPPORTED, "unknown path %d", l.path);
+  }
+  const int groups = N / l.rows;
+  if (r.segment < 1 || groups % r.segment)
+    return fail(SKINNY_EUNSUPPORTED, "segment=%d must divide the %d blocks of an item",
+                r.segment, groups);
+  const long segs = (long)count * (groups / r.segment);
+  if (r.workgroups < 1 || r.workgroups > segs)
+    return fail(SKINNY_EUNSUPPORTED, "workgroups=%d: needs 1..%ld (one segment each at least)",
+                r.workgroups, segs);
   return SKINNY_OK;
 }
 
 // Ring launches measured on MI355X for the shard shapes (60-item rings of
-// distinct weights and activations): {N, K, M_lo, M_hi, launch, workgroups}.
-// More workgroups than output blocks lets two workgroups take alternate
-// items of one block; the count is capped at the ring's tile count.
+// distinct weights and activations): {N, K, M_lo, M_hi, launch}.  For fewer
+// items the segment is shortened and the workgroup count capped (below).
 struct RingEntry {
   int N, K, m_lo, m_hi;
-  skinny_launch l;
-  int workgroups;
+  skinny_ring_launch r;
 };
+#define DOT2_RING(waves, chunks, rows, seg, wg) \
+  { {SKINNY_PATH_DOT2, 1, waves, chunks, 1, rows}, seg, wg }
+#define MFMA_RING(waves, chunks, accs, rows, seg, wg) \
+  { {SKINNY_PATH_MFMA, 1, waves, chunks, accs, rows}, seg, wg }
 static const RingEntry kRingTable[] = {
     // unpooler shard
-    {1024, 4096, 1, 1, {SKINNY_PATH_DOT2, 1, 2, 4, 1, 2}, 1024},
-    {1024, 4096, 2, 2, {SKINNY_PATH_DOT2, 1, 8, 1, 1, 4}, 512},
-    {1024, 4096, 3, 4, {SKINNY_PATH_DOT2, 1, 8, 1, 1, 8}, 512},
-    {1024, 4096, 5, 8, {SKINNY_PATH_DOT2, 1, 4, 2, 1, 4}, 2048},
-    {1024, 4096, 9, 16, {SKINNY_PATH_DOT2, 1, 8, 1, 1, 4}, 512},
+    {1024, 4096, 1, 1, DOT2_RING(2, 4, 2, 1, 1024)},
+    {1024, 4096, 2, 2, DOT2_RING(8, 1, 8, 2, 2048)},
+    {1024, 4096, 3, 4, DOT2_RING(2, 4, 2, 8, 512)},
+    {1024, 4096, 5, 8, DOT2_RING(4, 2, 4, 4, 512)},
+    {1024, 4096, 9, 16, MFMA_RING(16, 8, 2, 16, 8, 256)},
     // o_proj shard
-    {8192, 1024, 1, 1, {SKINNY_PATH_DOT2, 1, 2, 1, 1, 8}, 512},
-    {8192, 1024, 2, 2, {SKINNY_PATH_DOT2, 1, 2, 1, 1, 4}, 1024},
-    {8192, 1024, 3, 8, {SKINNY_PATH_DOT2, 1, 2, 1, 1, 8}, 1024},
-    {8192, 1024, 9, 16, {SKINNY_PATH_DOT2, 1, 2, 1, 1, 4}, 4096},
+    {8192, 1024, 1, 1, DOT2_RING(1, 4, 4, 8, 1024)},
+    {8192, 1024, 2, 2, DOT2_RING(2, 1, 8, 8, 512)},
+    {8192, 1024, 3, 4, DOT2_RING(2, 1, 4, 8, 1024)},
+    {8192, 1024, 5, 8, DOT2_RING(1, 2, 4, 8, 1024)},
+    {8192, 1024, 9, 16, MFMA_RING(2, 16, 2, 16, 8, 512)},
     // pooler shard
-    {512, 8192, 1, 1, {SKINNY_PATH_DOT2, 1, 4, 4, 1, 2}, 1024},
-    {512, 8192, 2, 2, {SKINNY_PATH_DOT2, 1, 8, 2, 1, 4}, 1024},
-    {512, 8192, 3, 4, {SKINNY_PATH_DOT2, 1, 8, 2, 1, 4}, 512},
-    {512, 8192, 5, 8, {SKINNY_PATH_DOT2, 1, 8, 2, 1, 4}, 256},
+    {512, 8192, 1, 1, DOT2_RING(4, 4, 2, 1, 1024)},
+    {512, 8192, 2, 2, DOT2_RING(4, 4, 2, 4, 2048)},
+    {512, 8192, 3, 4, DOT2_RING(8, 2, 4, 2, 1024)},
+    {512, 8192, 5, 8, DOT2_RING(8, 2, 4, 8, 256)},
     // full pooler
-    {4096, 8192, 1, 1, {SKINNY_PATH_DOT2, 1, 4, 4, 1, 2}, 512},
-    {4096, 8192, 2, 8, {SKINNY_PATH_DOT2, 1, 8, 2, 1, 4}, 256},
+    {4096, 8192, 1, 2, DOT2_RING(4, 4, 2, 8, 256)},
+    {4096, 8192, 3, 8, DOT2_RING(8, 2, 4, 8, 256)},
 };
+#undef DOT2_RING
+#undef MFMA_RING
 
-// Ring rule for any other shape: 2 rows per workgroup for <= 2 tokens, 4 up
-// to 8, 2 beyond (the register budget of two weight buffers), the most
-// chunks that fit and that K fills, one workgroup per output block.
-static int ring_choose(int M, int N, int K, int count, skinny_launch *out, int *workgroups) {
+// Ring rule for any other shape.  Up to 8 tokens DOT2: 2 rows per workgroup
+// for <= 2 tokens, else 4 (the register budget of two weight buffers), the
+// most chunks that fit and that K fills.  Beyond 8 tokens MFMA, one tile per
+// workgroup, the fewest chunks that cover K with the waves a workgroup has;
+// DOT2 if K is too long for that.  One workgroup per output block.
+static int ring_choose(int M, int N, int K, int count, skinny_ring_launch *out) {
   int st = check_problem(M, N, K);
   if (st) return st;
   if (count < 1 || count > kMaxRingItems)
     return fail(SKINNY_EINVAL, "count=%d: needs 1 <= count <= %d", count, kMaxRingItems);
-  skinny_launch l{};
-  int wg = 0;
   for (const RingEntry &e : kRingTable) {
     if (e.N != N || e.K != K || M < e.m_lo || M > e.m_hi) continue;
-    const long total = (long)count * (N / e.l.rows);
-    const int w = (int)(e.workgroups < total ? e.workgroups : total);
-    if (ring_check(count, M, N, K, e.l, w) == SKINNY_OK) {
-      l = e.l;
-      wg = w;
-      break;
+    // Few items: shorter segments (halving keeps a power of two that divides
+    // the blocks) until the ring has the table's workgroup count, if it can.
+    skinny_ring_launch r = e.r;
+    const int groups = N / r.gemm.rows;
+    while (r.segment > 1 && (long)count * (groups / r.segment) < r.workgroups) r.segment /= 2;
+    const long segs = (long)count * (groups / r.segment);
+    if (r.workgroups > segs) r.workgroups = (int)segs;
+    if (ring_check(count, M, N, K, r) == SKINNY_OK) {
+      *out = r;
+      return SKINNY_OK;
     }
   }
-  if (!l.waves) {
-    const int mt = dot2_token_tile(M);
-    const int prefer = mt <= 2 ? 2 : mt <= 8 ? 4 : 2;
-    const int rows_order[] = {prefer, 4, 2, 8};
-    int c0 = 1;  // no more chunks than K has 512-element units
-    while (c0 < kMaxDot2Chunks && 2L * c0 * kDot2K <= K) c0 *= 2;
-    for (int rows : rows_order) {
-      for (int c = c0; c >= 1 && !l.waves; c /= 2) {
-        const skinny_launch t{SKINNY_PATH_DOT2, 1, ceil_div(K, (long)kDot2K * c), c, 1, rows};
-        if (N % rows == 0 && ring_check(count, M, N, K, t, N / rows) == SKINNY_OK) l = t;
+  if (M > 8) {
+    for (int c = 1; c <= kMaxMfmaChunks; c *= 2) {
+      const skinny_ring_launch r{{SKINNY_PATH_MFMA, 1, ceil_div(K, (long)kMfmaK * c), c, 1, kTileN},
+                                 1, N / kTileN};
+      if (ring_check(count, M, N, K, r) == SKINNY_OK) {
+        *out = r;
+        return SKINNY_OK;
       }
-      if (l.waves) break;
     }
   }
-  if (!l.waves)
-    return fail(SKINNY_EUNSUPPORTED, "no ring launch for M=%d N=%d K=%d (K too long for one "
-                "workgroup)", M, N, K);
-  *out = l;
-  *workgroups = wg ? wg : N / l.rows;
-  return SKINNY_OK;
+  const int mt = dot2_token_tile(M);
+  const int rows_order[] = {mt <= 2 ? 2 : 4, 4, 2, 8};
+  int c0 = 1;  // no more chunks than K has 512-element units
+  while (c0 < kMaxDot2Chunks && 2L * c0 * kDot2K <= K) c0 *= 2;
+  for (int rows : rows_order) {
+    if (N % rows) continue;
+    for (int c = c0; c >= 1; c /= 2) {
+      const skinny_ring_launch r{{SKINNY_PATH_DOT2, 1, ceil_div(K, (long)kDot2K * c), c, 1, rows},
+                                 1, N / rows};
+      if (ring_check(count, M, N, K, r) == SKINNY_OK) {
+        *out = r;
+        return SKINNY_OK;
+      }
+    }
+  }
+  return fail(SKINNY_EUNSUPPORTED, "no ring launch for M=%d N=%d K=%d (K too long for one "
+              "workgroup)", M, N, K);
 }
 
 static int ring_common(const void *const *x, const void *const *W, void *const *y, int count,
-                       int M, int N, int K, const skinny_launch &l, int workgroups,
-                       void *stream) {
+                       int M, int N, int K, const skinny_ring_launch &r, void *stream) {
   if (!x || !W || !y) return fail(SKINNY_EINVAL, "null pointer array");
   RingItems items;
   const size_t xb = 2ul * M * K, wb = 2ul * N * K, yb = 2ul * M * N;
@@ -358,8 +397,7 @@ static int ring_common(const void *const *x, const void *const *W, void *const *
     }
   int st = SKINNY_OK;
   if (!current_state(&st)) return st;
-  hipError_t e = launch_gemm_ring(items, count, M, N, K, l, workgroups,
-                                  static_cast<hipStream_t>(stream));
+  hipError_t e = launch_gemm_ring(items, count, M, N, K, r, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return fail(SKINNY_ELAUNCH, "launch failed: %s", hipGetErrorString(e));
   return SKINNY_OK;
 }
@@ -489,28 +527,32 @@ int skinny_gemm_bf16_launch(const void *x, const void *W, void *y, int M, int N,
   return gemm_common(x, W, y, M, N, K, *launch, stream);
 }
 
-int skinny_ring_choose(int M, int N, int K, int count, skinny_launch *out, int *workgroups) {
-  if (!out || !workgroups) return fail(SKINNY_EINVAL, "null output");
-  return ring_choose(M, N, K, count, out, workgroups);
+int skinny_ring_choose(int M, int N, int K, int count, skinny_ring_launch *out) {
+  if (!out) return fail(SKINNY_EINVAL, "null output");
+  return ring_choose(M, N, K, count, out);
+}
+
+int skinny_ring_launch_unsupported(int M, int N, int K, int count,
+                                   const skinny_ring_launch *launch) {
+  if (!launch) return fail(SKINNY_EINVAL, "null launch");
+  return ring_check(count, M, N, K, *launch);
 }
 
 int skinny_gemm_bf16_ring(const void *const *x, const void *const *W, void *const *y,
                           int count, int M, int N, int K, void *stream) {
-  skinny_launch l;
-  int workgroups = 0;
-  int st = ring_choose(M, N, K, count, &l, &workgroups);
+  skinny_ring_launch r;
+  int st = ring_choose(M, N, K, count, &r);
   if (st) return st;
-  return ring_common(x, W, y, count, M, N, K, l, workgroups, stream);
+  return ring_common(x, W, y, count, M, N, K, r, stream);
 }
 
 int skinny_gemm_bf16_ring_launch(const void *const *x, const void *const *W, void *const *y,
-                                 int count, int M, int N, int K, const skinny_launch *launch,
-                                 int workgroups, void *stream) {
+                                 int count, int M, int N, int K,
+                                 const skinny_ring_launch *launch, void *stream) {
   if (!launch) return fail(SKINNY_EINVAL, "null launch");
-  if (workgroups == 0 && launch->rows > 0) workgroups = N / launch->rows;  // one per block
-  int st = ring_check(count, M, N, K, *launch, workgroups);
+  int st = ring_check(count, M, N, K, *launch);
   if (st) return st;
-  return ring_common(x, W, y, count, M, N, K, *launch, workgroups, stream);
+  return ring_common(x, W, y, count, M, N, K, *launch, stream);
 }
 
 int skinny_rmsnorm_nvfp4(const void *r, const void *norm_w, float gain_center, float eps,

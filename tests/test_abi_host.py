@@ -134,13 +134,20 @@ def test_compute_calls_without_device_fail_cleanly(sk):
                          + [(3, 48, 1000), (16, 16, 8), (1, 16, 8)])
 @pytest.mark.parametrize("count", [1, 7, 64])
 def test_ring_chooser_gives_valid_launches(sk, M, N, K, count):
-    launch, wg = sk.skinny_ring_choose(M, N, K, count)
-    assert launch.path == sk.SKINNY_PATH_DOT2 and launch.splits == 1 and launch.accs == 1
-    assert launch.waves == -(-K // (512 * launch.chunks)) <= 8
-    assert N % launch.rows == 0 and 1 <= wg <= count * N // launch.rows
-    # the ring's launch is also a valid single-call launch (same arithmetic)
-    assert sk.skinny_launch_unsupported(M, N, K, launch) is None
-    assert sk.skinny_ring_choose(M, N, K, count) == (launch, wg)
+    r = sk.skinny_ring_choose(M, N, K, count)
+    g = r.gemm
+    assert g.splits == 1
+    if g.path == sk.SKINNY_PATH_DOT2:
+        assert g.accs == 1 and g.waves == -(-K // (512 * g.chunks)) <= 8
+        # the ring's launch is also a valid single-call launch (same arithmetic)
+        assert sk.skinny_launch_unsupported(M, N, K, g) is None
+    else:
+        assert g.waves == g.rows // 16 * -(-K // (32 * g.chunks)) <= 16
+    groups = N // g.rows
+    assert N % g.rows == 0 and groups % r.segment == 0
+    assert 1 <= r.workgroups <= count * groups // r.segment
+    assert sk.skinny_ring_launch_unsupported(M, N, K, count, r) is None
+    assert sk.skinny_ring_choose(M, N, K, count) == r
 
 
 def test_ring_unsupported_shapes_and_reasons(sk):
@@ -158,7 +165,7 @@ def test_ring_unsupported_shapes_and_reasons(sk):
 def _ring_lib(sk):
     lib = ctypes.CDLL(sk.LIB_PATH)
     lib.skinny_gemm_bf16_ring_launch.argtypes = [ctypes.c_void_p] * 3 + [ctypes.c_int] * 4 + [
-        ctypes.POINTER(sk._CLaunch), ctypes.c_int, ctypes.c_void_p]
+        ctypes.POINTER(sk._CRingLaunch), ctypes.c_void_p]
     lib.skinny_gemm_bf16_ring.argtypes = [ctypes.c_void_p] * 3 + [ctypes.c_int] * 4 + [
         ctypes.c_void_p]
     return lib
@@ -173,24 +180,37 @@ def test_ring_launch_reasons_without_device(sk):
     M, N, K = 1, 1024, 4096
     x, w, y = _ptrs(0x100000), _ptrs(0x1000000), _ptrs(0x4000000)
 
-    def call(launch, wg=0, count=1, xs=x, ws=w, ys=y):
-        c = sk.Launch(*launch)._c()
-        return lib.skinny_gemm_bf16_ring_launch(xs, ws, ys, count, M, N, K, ctypes.byref(c), wg,
-                                                None)
+    def call(gemm, seg=1, wg=None, count=1):
+        if wg is None:
+            wg = N // gemm[5] // seg
+        c = sk.RingLaunch(sk.Launch(*gemm), seg, wg)._c()
+        return lib.skinny_gemm_bf16_ring_launch(x, w, y, count, M, N, K, ctypes.byref(c), None)
 
-    assert call((1, 1, 16, 4, 1, 16)) == sk.SKINNY_EUNSUPPORTED
-    assert "DOT2" in sk.skinny_last_error()
+    assert call((1, 1, 16, 4, 1, 16)) == sk.SKINNY_EUNSUPPORTED  # MFMA: K needs 32 waves
+    assert "needs 32 waves" in sk.skinny_last_error()
+    assert call((1, 1, 16, 8, 4, 16)) == sk.SKINNY_EUNSUPPORTED
+    assert "MFMA ring kernel" in sk.skinny_last_error()
+    assert call((1, 1, 16, 8, 1, 48)) == sk.SKINNY_EUNSUPPORTED
+    assert "rows=48" in sk.skinny_last_error()
+    assert call((2, 1, 16, 8, 1, 16)) == sk.SKINNY_EUNSUPPORTED
+    assert "unknown path" in sk.skinny_last_error()
     assert call((0, 2, 1, 4, 1, 2)) == sk.SKINNY_EUNSUPPORTED
     assert "splits=1" in sk.skinny_last_error()
     assert call((0, 1, 3, 4, 1, 2)) == sk.SKINNY_EUNSUPPORTED
     assert "waves" in sk.skinny_last_error()
     assert call((0, 1, 2, 4, 1, 2), wg=513) == sk.SKINNY_EUNSUPPORTED
     assert "workgroups=513" in sk.skinny_last_error()
+    assert call((0, 1, 2, 4, 1, 2), seg=3, wg=1) == sk.SKINNY_EUNSUPPORTED
+    assert "segment=3" in sk.skinny_last_error()
+    assert call((0, 1, 2, 4, 1, 2), seg=4, wg=129) == sk.SKINNY_EUNSUPPORTED
+    assert "workgroups=129" in sk.skinny_last_error()
     assert call((0, 1, 2, 4, 1, 16)) == sk.SKINNY_EUNSUPPORTED
     assert "ring kernel" in sk.skinny_last_error()
     assert call((0, 1, 2, 4, 1, 2), count=65) == sk.SKINNY_EINVAL
-    # a valid launch passes every check and stops at the missing device
+    # valid launches pass every check and stop at the missing device
+    assert call((1, 1, 16, 8, 1, 16)) in (sk.SKINNY_EDEVICE, sk.SKINNY_ENOTINIT)
     assert call((0, 1, 2, 4, 1, 2)) in (sk.SKINNY_EDEVICE, sk.SKINNY_ENOTINIT)
+    assert call((0, 1, 2, 4, 1, 2), seg=512, wg=1) in (sk.SKINNY_EDEVICE, sk.SKINNY_ENOTINIT)
 
 
 def test_ring_rejects_aliased_items_without_device(sk):

@@ -43,7 +43,7 @@ def _items(count, N, K, seed, integer=False, M=16):
     return xs, ws
 
 
-def _ring(sk, xs_bits, ws_bits, M, launch=None, workgroups=0, reps=1):
+def _ring(sk, xs_bits, ws_bits, M, launch=None, reps=1):
     """Run the ring; returns the list of y bit arrays (of the last rep) and
     checks the guard regions around every y."""
     import torch
@@ -61,7 +61,7 @@ def _ring(sk, xs_bits, ws_bits, M, launch=None, workgroups=0, reps=1):
         if launch is None:
             sk.skinny_gemm_bf16_ring(xs, ws, ys)
         else:
-            sk.skinny_gemm_bf16_ring_launch(xs, ws, ys, launch, workgroups)
+            sk.skinny_gemm_bf16_ring_launch(xs, ws, ys, launch)
         torch.cuda.synchronize()
         outs.append([from_dev(y).copy() for y in ys])
     b = from_dev(buf).reshape(count, stride)
@@ -84,15 +84,23 @@ def _single(sk, x_bits, w_bits, M, launch):
 
 
 def _ring_launches(sk, M, N, K):
-    """DOT2 launches with one split that the single-call validator accepts
-    (the ring takes the subset it has kernels for)."""
+    """Ring launch candidates of both families with splits = 1: DOT2 rows
+    2..16 x chunks 1, 2, 4 and MFMA 1, 2, 4 tiles x chunks 1..16 x accs 1, 2
+    (the ring validator decides which it has kernels for)."""
     out = []
     for rows in (2, 4, 8, 16):
         for chunks in (1, 2, 4):
-            l = sk.Launch(0, 1, -(-K // (512 * chunks)), chunks, 1, rows)
-            if N % rows == 0 and sk.skinny_launch_unsupported(M, N, K, l) is None:
-                out.append(l)
-    return out
+            out.append(sk.Launch(0, 1, -(-K // (512 * chunks)), chunks, 1, rows))
+    for rows in (16, 32, 64):
+        for chunks in (1, 2, 4, 8, 16):
+            for accs in (1, 2):
+                out.append(sk.Launch(1, 1, rows // 16 * -(-K // (32 * chunks)), chunks, accs,
+                                     rows))
+    return [l for l in out if N % l.rows == 0]
+
+
+def _single_ok(sk, M, N, K, launch):
+    return sk.skinny_launch_unsupported(M, N, K, launch) is None
 
 
 @pytest.mark.parametrize("M", [1, 2, 3, 8, 9, 16])
@@ -100,40 +108,57 @@ def test_ring_unpooler_parity(gpu_lib, M):
     """Six unpooler-shard items (N=1024, K=4096), each with its own x and W."""
     N, K = 1024, 4096
     xs, ws = _items(6, N, K, seed=100)
-    launch, wg = gpu_lib.skinny_ring_choose(M, N, K, len(ws))
-    _say(f"ring unpooler M={M} {launch} wg={wg}")
+    launch = gpu_lib.skinny_ring_choose(M, N, K, len(ws))
+    _say(f"ring unpooler M={M} {launch}")
     ys = _ring(gpu_lib, xs, ws, M, reps=3)
     for i, (x, w, y) in enumerate(zip(xs, ws, ys)):
         assert_gemm_close(y, oracle.gemm_bf16(x[:M], w, THREADS), f"item {i}")
-        assert np.array_equal(y, _single(gpu_lib, x, w, M, launch)), f"item {i} != single call"
+        if _single_ok(gpu_lib, M, N, K, launch.gemm):
+            assert np.array_equal(y, _single(gpu_lib, x, w, M, launch.gemm)), \
+                f"item {i} != single call"
+
+
+def _walks(groups, count):
+    """(segment, workgroups) pairs: one block per visit and whole items per
+    visit, with one workgroup, three (items interleave across workgroups)
+    and one per segment."""
+    out = []
+    for seg in sorted({1, 2, groups}):
+        if groups % seg:
+            continue
+        segs = count * groups // seg
+        for wg in sorted({1, 3, groups // seg, segs}):
+            if 1 <= wg <= segs:
+                out.append((seg, wg))
+    return out
 
 
 @pytest.mark.parametrize("M,N,K", [(1, 64, 1024), (3, 48, 1000), (7, 128, 2056), (16, 32, 520),
-                                   (4, 16, 8)])
-def test_ring_every_launch_and_grid(gpu_lib, M, N, K):
+                                   (4, 16, 8), (12, 64, 1000)])
+def test_ring_every_launch_and_walk(gpu_lib, M, N, K):
     """Every compiled ring variant the validator accepts on small ragged
-    shapes, with one workgroup per block, one workgroup in all, an odd count
-    that interleaves items, and one workgroup per tile."""
+    shapes, under several tile walks (segment length and workgroup count)."""
     count = 5
     xs, ws = _items(count, N, K, seed=200)
     refs = [oracle.gemm_bf16(x[:M], w, THREADS) for x, w in zip(xs, ws)]
     tried = 0
-    for l in _ring_launches(gpu_lib, M, N, K):
-        groups = N // l.rows
-        for wg in sorted({groups, 1, 3, count * groups}):
-            if wg > count * groups:
-                continue
-            try:
-                ys = _ring(gpu_lib, xs, ws, M, launch=l, workgroups=wg)
-            except ValueError as e:  # no ring kernel for this (rows, chunks, tokens)
-                assert "ring kernel" in str(e), str(e)
+    for g in _ring_launches(gpu_lib, M, N, K):
+        groups = N // g.rows
+        single = _single_ok(gpu_lib, M, N, K, g)
+        singles = [_single(gpu_lib, xs[i], ws[i], M, g) for i in range(count)] if single else None
+        for seg, wg in _walks(groups, count):
+            launch = gpu_lib.RingLaunch(g, seg, wg)
+            reason = gpu_lib.skinny_ring_launch_unsupported(M, N, K, count, launch)
+            if reason is not None:
+                assert "kernel" in reason or "waves" in reason, reason
                 break
             tried += 1
-            _say(f"ring M={M} N={N} K={K} {l} wg={wg}")
+            _say(f"ring M={M} N={N} K={K} {launch}")
+            ys = _ring(gpu_lib, xs, ws, M, launch=launch)
             for i in range(count):
-                assert_gemm_close(ys[i], refs[i], f"{l} wg={wg} item {i}")
-                assert np.array_equal(ys[i], _single(gpu_lib, xs[i], ws[i], M, l)), \
-                    f"{l} wg={wg} item {i} != single call"
+                assert_gemm_close(ys[i], refs[i], f"{launch} item {i}")
+                if single:
+                    assert np.array_equal(ys[i], singles[i]), f"{launch} item {i} != single call"
     assert tried
 
 
@@ -154,8 +179,8 @@ def test_ring_max_count(gpu_lib):
 def test_ring_shard_shapes(gpu_lib, M, N, K, count):
     """The o_proj and pooler shard shapes."""
     xs, ws = _items(count, N, K, seed=400)
-    launch, wg = gpu_lib.skinny_ring_choose(M, N, K, count)
-    _say(f"ring M={M} N={N} K={K} {launch} wg={wg}")
+    launch = gpu_lib.skinny_ring_choose(M, N, K, count)
+    _say(f"ring M={M} N={N} K={K} {launch}")
     ys = _ring(gpu_lib, xs, ws, M)
     for i in range(count):
         assert_gemm_close(ys[i], oracle.gemm_bf16(xs[i][:M], ws[i], THREADS), f"item {i}")
