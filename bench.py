@@ -16,8 +16,11 @@ Output: one JSON line.  `value` is achieved HBM GB/s over the step
 (algorithmic bytes 2NK + 2MK + 2MN per call / step time).  `roofline` is for
 the dominant kernel (the launch with the largest share of the step), with its
 average duration measured here from graph replays of that launch alone over
-the ring.  `cpu_baseline` times the oracle on the host for a bounded sample of
-the same workload.
+the ring.  `ring` reports the same sweep through the layer-ring launch
+(skinny_gemm_bf16_ring: one persistent launch per M over the 60 layers, the
+next layer's weights in flight while one is finished), per item.
+`cpu_baseline` times the oracle on the host for a bounded sample of the same
+workload.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu]
 """
@@ -45,6 +48,7 @@ def log(*a):
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 KERNEL_SOURCES = ["moe_decode_skinny_amd/csrc/gemm_mfma.hip", "moe_decode_skinny_amd/csrc/gemm_dot2.hip",
+                  "moe_decode_skinny_amd/csrc/dot2_device.h",
                   "moe_decode_skinny_amd/csrc/split_reduce.hip", "moe_decode_skinny_amd/csrc/internal.h"]
 
 
@@ -141,6 +145,42 @@ def epilogue_timing(sk, synthetic, dev, stream, reps: int = 50):
             "norm_nvfp4_us_per_call": round(norm_us, 3)}
 
 
+def ring_timing(sk, synthetic, dev, stream, ring, reps: int = 10):
+    """The layer ring (skinny_gemm_bf16_ring): per-item us when the same
+    60-layer unpooler weight ring runs as one 60-item launch per M, each item
+    with its own activations, at the ring chooser's launch."""
+    import torch
+
+    out = {}
+    xb = [synthetic.gemm_inputs(N=16, K=K, seed=900 + i)[0] for i in range(RING)]
+    for M in MS:
+        xs = [synthetic.to_device(b[:M], dev) for b in xb]
+        ys = [torch.empty((M, N), dtype=torch.bfloat16, device=dev) for _ in range(RING)]
+        sk.skinny_gemm_bf16_ring(xs, ring, ys)
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=stream):
+            sk.skinny_gemm_bf16_ring(xs, ring, ys)
+        g.replay()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for _ in range(reps):
+            g.replay()
+        b.record(stream)
+        torch.cuda.synchronize()
+        us = a.elapsed_time(b) * 1e3 / (reps * RING)
+        gbs = algorithmic_bytes(M) / (us * 1e-6) / 1e9
+        r = sk.skinny_ring_choose(M, N, K, RING)
+        out[str(M)] = {"launch": {**dict(r.gemm._asdict()), "segment": r.segment,
+                                  "workgroups": r.workgroups},
+                       "us_per_item": round(us, 3), "GBs": round(gbs, 1),
+                       "pct_peak": round(100 * gbs / PEAK_GBS, 2)}
+        del g
+    return {"workload": f"unpooler shard GEMM M=1,2,4,8,16, N=1024, K=4096: one "
+                        f"{RING}-item skinny_gemm_bf16_ring launch per M over the "
+                        f"{RING}-layer weight ring", "per_m": out}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -231,6 +271,8 @@ def main():
         # The expert-input epilogue (pooler page): full-pooler GEMM at M=8,
         # then RMSNorm -> NVFP4 on its output, both timed per call.
         epi = epilogue_timing(sk, synthetic, dev, stream)
+        # The same weight ring through the layer-ring launch.
+        ring_out = ring_timing(sk, synthetic, dev, stream, ring)
 
     step_bytes = sum(algorithmic_bytes(M) for M in MS)
     value = step_bytes / (ms_step * 1e-3) / 1e9
@@ -266,6 +308,7 @@ def main():
                      "us_per_launch": round(per_kernel[dom], 3)},
         "per_m": detail,
         "epilogue": epi,
+        "ring": ring_out,
         "wall_s": round(wall, 3),
     }
     if not args.no_cpu:

@@ -46,8 +46,11 @@ typedef enum skinny_status {
 
 /* Kernel families of the GEMM. */
 enum {
-  SKINNY_PATH_DOT2 = 0, /* VALU bf16 dot2: lanes run along K, any row count  */
-  SKINNY_PATH_MFMA = 1  /* bf16 MFMA 16x16x32: 16 weight rows x 16 tokens    */
+  SKINNY_PATH_DOT2 = 0,    /* VALU bf16 dot2: lanes run along K, any row count  */
+  SKINNY_PATH_MFMA = 1,    /* bf16 MFMA 16x16x32: 16 weight rows x 16 tokens    */
+  SKINNY_PATH_MFMA_LDS = 2 /* ring only: MFMA with each wave's weights loaded
+                              row by row and re-laid out through LDS; same
+                              operands and results as SKINNY_PATH_MFMA        */
 };
 
 /* A launch shape of the GEMM: the counterpart of the unpooler page's
@@ -123,6 +126,9 @@ int skinny_launch_unsupported(int M, int N, int K, const skinny_launch *launch);
  *               chunks 1, 2, 4; waves = ceil(K / (512 chunks)) <= 8) or MFMA
  *               (rows 16, 32, 64; chunks 1..16; accs 1 or 2; waves =
  *               rows / 16 * ceil(K / (32 chunks)) <= 16, <= 8 at 16 chunks)
+ *               or MFMA_LDS (as MFMA with chunks 2..16, and the staging
+ *               regions, waves x 16 x (64 chunks + 16) bytes, plus 2 KiB per
+ *               wave, within the 160 KiB of LDS)
  *   segment     consecutive output blocks of one item a workgroup takes in a
  *               row, keeping that item's activations in registers; it
  *               divides N / gemm.rows
@@ -149,8 +155,8 @@ typedef struct skinny_ring_launch {
  * The items run concurrently: no y[i] may overlap any x[j], W[j] or another
  * y[j] (a chain whose x[i + 1] is y[i] needs one call per item).  Every y[i]
  * is bitwise identical to skinny_gemm_bf16_launch at the ring's gemm shape
- * (when that shape is also a valid single-call launch), whatever the
- * segment and workgroup count.  Uses no workspace, so ring calls on
+ * (with MFMA for MFMA_LDS; when that shape is also a valid single-call
+ * launch), whatever the segment and workgroup count.  Uses no workspace, so ring calls on
  * different streams may overlap.
  * Errors: SKINNY_EINVAL, SKINNY_EUNSUPPORTED, SKINNY_ENOTINIT, SKINNY_ELAUNCH. */
 int skinny_gemm_bf16_ring(const void *const *x, const void *const *W,

@@ -33,6 +33,7 @@ SKINNY_ELAUNCH = -4
 SKINNY_ENOTINIT = -5
 SKINNY_PATH_DOT2 = 0
 SKINNY_PATH_MFMA = 1
+SKINNY_PATH_MFMA_LDS = 2
 
 if not os.path.exists(LIB_PATH):
     raise ImportError(
@@ -48,7 +49,8 @@ class _CLaunch(ctypes.Structure):
 
 
 class Launch(NamedTuple):
-    """skinny_launch: path (0 DOT2, 1 MFMA), splits, waves, chunks, accs, rows."""
+    """skinny_launch: path (0 DOT2, 1 MFMA, 2 MFMA_LDS: ring only), splits, waves,
+    chunks, accs, rows."""
     path: int
     splits: int
     waves: int

@@ -221,6 +221,13 @@ Dot2RingKernel dot2_ring_pick(int rows, int chunks, int mt) {
 // Lane layout of v_mfma_f32_16x16x32_bf16 as in the single-call kernel:
 // A lane l = W[row l % 16][k + 8 (l / 16) ..], B lane l = x[token l % 16][same
 // k], D lane l = features 4 (l / 16) + 0..3 of token l % 16.
+//
+// Loading A fragments straight from memory makes every load instruction touch
+// 16 rows (64 bytes of each).  The staged form (SKINNY_PATH_MFMA_LDS) loads
+// the wave's 16 x kw weight slice row by row instead (one instruction covers
+// 1 KiB of whole-row pieces), writes it to the wave's own padded LDS region
+// and reads the A fragments back from there.  The MFMA operands, and so the
+// results, are the same.
 constexpr int mfma_ring_threads(int chunks) { return chunks >= 16 ? 512 : 1024; }
 
 template <int CHUNKS>
@@ -233,18 +240,54 @@ __device__ __forceinline__ void load_tile_weights(u32x4 (&wv)[CHUNKS], const uin
         res, k0 + i * kMfmaK < K ? (row * K + k0 + i * kMfmaK) * 2 : kOutOfRange, 0, kCacheNT);
 }
 
-struct MfmaArgs {
-  int M, N, K, F, KW;
+// The staged layout: the wave's slice is 16 rows x 4 CHUNKS pieces of 16
+// bytes; load i, lane l takes piece e = 64 i + l in row-major order.  In LDS
+// a row is 4 CHUNKS + 1 pieces long: the pad piece spreads the 16 rows read
+// by one fragment load over different banks, and the fragment offsets of the
+// chunks stay constants of the instruction (a swizzled layout without the pad
+// measured slower).
+template <int CHUNKS>
+struct Staging {
+  static constexpr int kRow = 4 * CHUNKS + 1;    // LDS row stride in pieces
+  static constexpr int kLog = log2i(4 * CHUNKS);  // pieces per row, log2
+  static constexpr int kPieces = 16 * kRow;      // LDS pieces per wave
+  __device__ static int slot(int r, int p) { return r * kRow + p; }
 };
 
-template <int CHUNKS, int ACCS, int P>
+template <int CHUNKS>
+__device__ __forceinline__ void load_tile_rows(u32x4 (&wv)[CHUNKS], const uint16_t *w,
+                                               unsigned bytes, int K, int kq, int lane) {
+  using St = Staging<CHUNKS>;
+  const __amdgpu_buffer_rsrc_t res = buffer_rsrc(w, bytes);
+#pragma unroll
+  for (int i = 0; i < CHUNKS; ++i) {
+    const int e = i * 64 + lane;
+    const int k = kq + (e & (4 * CHUNKS - 1)) * 8;
+    wv[i] = __builtin_amdgcn_raw_buffer_load_b128(
+        res, k < K ? ((e >> St::kLog) * K + k) * 2 : kOutOfRange, 0, kCacheNT);
+  }
+}
+
+// Orders one wave's LDS writes before its reads of other lanes' data.
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+struct MfmaArgs {
+  int M, N, K, F, KW, waves;
+};
+
+template <int CHUNKS, int ACCS, bool STAGED, int P>
 __device__ __forceinline__ bool mfma_ring_tile(const RingItems &items, const MfmaArgs &a,
                                                const RingWalk &walk, int &s, int &sub,
                                                u32x4 (&cur)[CHUNKS], u32x4 (&next)[CHUNKS],
-                                               u32x4 (&xv)[CHUNKS], f32x4 (*red)[16][64],
-                                               int lane, int wave, int f, int q, int k0) {
+                                               u32x4 (&xv)[CHUNKS], u32x4 *stage, f32x4 *red,
+                                               int lane, int wave, int f, int q, int kq) {
   const int row = lane & 15, grp = lane >> 4;
   const int K = a.K;
+  const int k0 = kq + grp * 8;
   const int item = walk.item(s);
   const int tile = walk.block(s, sub) * a.F + f;
 
@@ -262,11 +305,27 @@ __device__ __forceinline__ bool mfma_ring_tile(const RingItems &items, const Mfm
   const bool more = walk.advance(ns, nsub);
   {
     const int cs = more ? ns : s, csub = more ? nsub : sub;  // as in the DOT2 ring
-    load_tile_weights<CHUNKS>(next, items.w[walk.item(cs)] +
-                                        (size_t)(walk.block(cs, csub) * a.F + f) * kTileN * K,
-                              more ? (unsigned)(kTileN * K * 2) : 0u, K, k0, row);
+    const uint16_t *wn = items.w[walk.item(cs)] +
+                         (size_t)(walk.block(cs, csub) * a.F + f) * kTileN * K;
+    const unsigned bytes = more ? (unsigned)(kTileN * K * 2) : 0u;
+    if constexpr (STAGED)
+      load_tile_rows<CHUNKS>(next, wn, bytes, K, kq, lane);
+    else
+      load_tile_weights<CHUNKS>(next, wn, bytes, K, k0, row);
   }
   __builtin_amdgcn_sched_barrier(0);
+
+  if constexpr (STAGED) {
+    using St = Staging<CHUNKS>;
+#pragma unroll
+    for (int i = 0; i < CHUNKS; ++i) {
+      const int e = i * 64 + lane;
+      stage[St::slot(e >> St::kLog, e & (4 * CHUNKS - 1))] = cur[i];
+    }
+    wave_lds_sync();
+#pragma unroll
+    for (int i = 0; i < CHUNKS; ++i) cur[i] = stage[St::slot(row, 4 * i + grp)];
+  }
 
   f32x4 acc[ACCS];
 #pragma unroll
@@ -283,11 +342,12 @@ __device__ __forceinline__ bool mfma_ring_tile(const RingItems &items, const Mfm
   // Waves q = 0..KW-1 of each tile in order through LDS buffer P (rewritten
   // two tiles later, after a barrier that follows every read of it).
   if (a.KW > 1) {
-    red[P][wave][lane] = part;
+    f32x4 *buf = red + P * a.waves * 64;
+    buf[wave * 64 + lane] = part;
     __syncthreads();
     if (q == 0) {
-      part = red[P][f * a.KW][lane];
-      for (int v = 1; v < a.KW; ++v) part += red[P][f * a.KW + v][lane];
+      part = buf[f * a.KW * 64 + lane];
+      for (int v = 1; v < a.KW; ++v) part += buf[(f * a.KW + v) * 64 + lane];
     }
   }
   if (q == 0 && row < a.M) {
@@ -301,7 +361,9 @@ __device__ __forceinline__ bool mfma_ring_tile(const RingItems &items, const Mfm
   return more;
 }
 
-template <int CHUNKS, int ACCS>
+// Dynamic LDS: the staged form's per-wave regions, then the two reduction
+// buffers of waves x 64 lanes x 16 bytes.
+template <int CHUNKS, int ACCS, bool STAGED>
 __global__ __launch_bounds__(mfma_ring_threads(CHUNKS)) void gemm_mfma_ring_kernel(
     RingItems items, int M, int N, int K, RingWalk walk, int F, int kw) {
   const int lane = threadIdx.x & 63;
@@ -309,45 +371,72 @@ __global__ __launch_bounds__(mfma_ring_threads(CHUNKS)) void gemm_mfma_ring_kern
   const int waves = blockDim.x >> 6;
   const int KW = waves / F;
   const int f = wave / KW, q = wave - f * KW;
-  const MfmaArgs a{M, N, K, F, KW};
-  const int k0 = q * kw + (lane >> 4) * 8;
-  __shared__ f32x4 red[2][16][64];
+  const MfmaArgs a{M, N, K, F, KW, waves};
+  const int kq = q * kw;
+  extern __shared__ __align__(16) u32x4 ring_lds[];
+  constexpr int kStage = STAGED ? Staging<CHUNKS>::kPieces : 0;
+  u32x4 *stage = ring_lds + wave * kStage;
+  f32x4 *red = reinterpret_cast<f32x4 *>(ring_lds + waves * kStage);
 
   int s = blockIdx.x, sub = 0;  // gridDim.x <= walk.segs
   u32x4 wa[CHUNKS], wb[CHUNKS], xv[CHUNKS];
-  load_tile_weights<CHUNKS>(wa, items.w[walk.item(s)] + (size_t)(walk.block(s, 0) * F + f) *
-                                                            kTileN * K,
-                            (unsigned)(kTileN * K * 2), K, k0, lane & 15);
+  {
+    const uint16_t *w0 = items.w[walk.item(s)] + (size_t)(walk.block(s, 0) * F + f) * kTileN * K;
+    if constexpr (STAGED)
+      load_tile_rows<CHUNKS>(wa, w0, (unsigned)(kTileN * K * 2), K, kq, lane);
+    else
+      load_tile_weights<CHUNKS>(wa, w0, (unsigned)(kTileN * K * 2), K, kq + (lane >> 4) * 8,
+                                lane & 15);
+  }
   for (;;) {
-    if (!mfma_ring_tile<CHUNKS, ACCS, 0>(items, a, walk, s, sub, wa, wb, xv, red, lane, wave, f,
-                                          q, k0))
+    if (!mfma_ring_tile<CHUNKS, ACCS, STAGED, 0>(items, a, walk, s, sub, wa, wb, xv, stage, red,
+                                                  lane, wave, f, q, kq))
       break;
-    if (!mfma_ring_tile<CHUNKS, ACCS, 1>(items, a, walk, s, sub, wb, wa, xv, red, lane, wave, f,
-                                          q, k0))
+    if (!mfma_ring_tile<CHUNKS, ACCS, STAGED, 1>(items, a, walk, s, sub, wb, wa, xv, stage, red,
+                                                  lane, wave, f, q, kq))
       break;
   }
 }
 
 using MfmaRingKernel = void (*)(RingItems, int, int, int, RingWalk, int, int);
 
-template <int C>
+template <int C, bool STAGED>
 MfmaRingKernel mfma_ring_pick_accs(int accs) {
   switch (accs) {
-    case 1: return gemm_mfma_ring_kernel<C, 1>;
-    case 2: return gemm_mfma_ring_kernel<C, 2>;
+    case 1: return gemm_mfma_ring_kernel<C, 1, STAGED>;
+    case 2: return gemm_mfma_ring_kernel<C, 2, STAGED>;
   }
   return nullptr;
 }
 
-MfmaRingKernel mfma_ring_pick(int chunks, int accs) {
+MfmaRingKernel mfma_ring_pick(int chunks, int accs, bool staged) {
+  if (staged) {
+    switch (chunks) {
+      case 2: return mfma_ring_pick_accs<2, true>(accs);
+      case 4: return mfma_ring_pick_accs<4, true>(accs);
+      case 8: return mfma_ring_pick_accs<8, true>(accs);
+      case 16: return mfma_ring_pick_accs<16, true>(accs);
+    }
+    return nullptr;
+  }
   switch (chunks) {
-    case 1: return mfma_ring_pick_accs<1>(accs);
-    case 2: return mfma_ring_pick_accs<2>(accs);
-    case 4: return mfma_ring_pick_accs<4>(accs);
-    case 8: return mfma_ring_pick_accs<8>(accs);
-    case 16: return mfma_ring_pick_accs<16>(accs);
+    case 1: return mfma_ring_pick_accs<1, false>(accs);
+    case 2: return mfma_ring_pick_accs<2, false>(accs);
+    case 4: return mfma_ring_pick_accs<4, false>(accs);
+    case 8: return mfma_ring_pick_accs<8, false>(accs);
+    case 16: return mfma_ring_pick_accs<16, false>(accs);
   }
   return nullptr;
+}
+
+size_t stage_pieces(int chunks) {
+  switch (chunks) {
+    case 2: return Staging<2>::kPieces;
+    case 4: return Staging<4>::kPieces;
+    case 8: return Staging<8>::kPieces;
+    case 16: return Staging<16>::kPieces;
+  }
+  return 0;
 }
 
 }  // namespace
@@ -356,20 +445,41 @@ bool ring_variant_exists(int rows, int chunks, int mt) {
   return dot2_ring_pick(rows, chunks, mt) != nullptr;
 }
 
-bool mfma_ring_variant_exists(int chunks, int accs) {
-  return mfma_ring_pick(chunks, accs) != nullptr;
+bool mfma_ring_variant_exists(int chunks, int accs, bool staged) {
+  return mfma_ring_pick(chunks, accs, staged) != nullptr;
 }
 
 int mfma_ring_max_waves(int chunks) { return mfma_ring_threads(chunks) / 64; }
+
+size_t mfma_ring_lds_bytes(const skinny_launch &l) {
+  const size_t stage = l.path == SKINNY_PATH_MFMA_LDS ? stage_pieces(l.chunks) : 0;
+  return (size_t)l.waves * (stage + 2 * 64) * sizeof(u32x4);
+}
+
+hipError_t ring_prepare() {
+  static const int kChunks[] = {1, 2, 4, 8, 16}, kAccs[] = {1, 2};
+  for (int staged = 0; staged < 2; ++staged)
+    for (int c : kChunks)
+      for (int a : kAccs) {
+        MfmaRingKernel k = mfma_ring_pick(c, a, staged != 0);
+        if (!k) continue;
+        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(k),
+                                           hipFuncAttributeMaxDynamicSharedMemorySize,
+                                           (int)kMaxDynamicLds);
+        if (e != hipSuccess) return e;
+      }
+  return hipSuccess;
+}
 
 hipError_t launch_gemm_ring(const RingItems &items, int count, int M, int N, int K,
                             const skinny_ring_launch &r, hipStream_t stream) {
   const skinny_launch &l = r.gemm;
   const int groups = N / l.rows;
   const RingWalk walk{groups, r.segment, groups / r.segment, count * (groups / r.segment)};
-  if (l.path == SKINNY_PATH_MFMA) {
-    hipLaunchKernelGGL(mfma_ring_pick(l.chunks, l.accs), dim3(r.workgroups), dim3(64 * l.waves),
-                       0, stream, items, M, N, K, walk, l.rows / kTileN, kMfmaK * l.chunks);
+  if (l.path == SKINNY_PATH_MFMA || l.path == SKINNY_PATH_MFMA_LDS) {
+    hipLaunchKernelGGL(mfma_ring_pick(l.chunks, l.accs, l.path == SKINNY_PATH_MFMA_LDS),
+                       dim3(r.workgroups), dim3(64 * l.waves), mfma_ring_lds_bytes(l), stream,
+                       items, M, N, K, walk, l.rows / kTileN, kMfmaK * l.chunks);
   } else {
     hipLaunchKernelGGL(dot2_ring_pick(l.rows, l.chunks, dot2_token_tile(M)), dim3(r.workgroups),
                        dim3(64 * l.waves), 0, stream, items, M, N, K, walk, kDot2K * l.chunks);

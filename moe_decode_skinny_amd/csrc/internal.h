@@ -66,8 +66,10 @@ bool dot2_variant_exists(int rows, int chunks, int mt);
 int dot2_token_tile(int M);  // smallest compiled token count >= M, 0 if none
 int dot2_max_waves();        // waves per DOT2 workgroup (launch bound)
 bool ring_variant_exists(int rows, int chunks, int mt);       // DOT2 ring
-bool mfma_ring_variant_exists(int chunks, int accs);          // MFMA ring
+bool mfma_ring_variant_exists(int chunks, int accs, bool staged);  // MFMA ring
 int mfma_ring_max_waves(int chunks);
+size_t mfma_ring_lds_bytes(const skinny_launch &l);  // dynamic LDS of an MFMA ring launch
+hipError_t ring_prepare();  // per-device kernel attributes (skinny_init)
 
 }  // namespace skinny
 

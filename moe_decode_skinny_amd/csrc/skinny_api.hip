@@ -244,20 +244,25 @@ static int ring_check(int count, int M, int N, int K, const skinny_ring_launch &
   if (count < 1 || count > kMaxRingItems)
     return fail(SKINNY_EINVAL, "count=%d: needs 1 <= count <= %d", count, kMaxRingItems);
   if (l.splits != 1) return fail(SKINNY_EUNSUPPORTED, "the ring runs launches with splits=1");
-  if (l.path == SKINNY_PATH_MFMA) {
+  if (l.path == SKINNY_PATH_MFMA || l.path == SKINNY_PATH_MFMA_LDS) {
+    const bool staged = l.path == SKINNY_PATH_MFMA_LDS;
     if (l.rows != 16 && l.rows != 32 && l.rows != 64)
       return fail(SKINNY_EUNSUPPORTED, "MFMA rows=%d: needs 16, 32 or 64", l.rows);
     if (N % l.rows)
       return fail(SKINNY_EUNSUPPORTED, "N=%d is not a multiple of rows=%d", N, l.rows);
-    if (!mfma_ring_variant_exists(l.chunks, l.accs))
-      return fail(SKINNY_EUNSUPPORTED, "no MFMA ring kernel with chunks=%d accs=%d (chunks 1, "
-                  "2, 4, 8, 16; accs 1, 2)", l.chunks, l.accs);
+    if (!mfma_ring_variant_exists(l.chunks, l.accs, staged))
+      return fail(SKINNY_EUNSUPPORTED, "no %s ring kernel with chunks=%d accs=%d (chunks %s; "
+                  "accs 1, 2)", staged ? "MFMA_LDS" : "MFMA", l.chunks, l.accs,
+                  staged ? "2, 4, 8, 16" : "1, 2, 4, 8, 16");
     const long kw = (long)kMfmaK * l.chunks;
     const int need = (l.rows / kTileN) * ceil_div(K, kw);
     if (l.waves != need || l.waves > mfma_ring_max_waves(l.chunks))
       return fail(SKINNY_EUNSUPPORTED, "K=%d at kw=%ld and %d tiles needs %d waves (given %d, "
                   "at most %d)", K, kw, l.rows / kTileN, need, l.waves,
                   mfma_ring_max_waves(l.chunks));
+    if (mfma_ring_lds_bytes(l) > kMaxDynamicLds)
+      return fail(SKINNY_EUNSUPPORTED, "%d waves of %d chunks need %zu bytes of LDS (max %zu)",
+                  l.waves, l.chunks, mfma_ring_lds_bytes(l), kMaxDynamicLds);
   } else if (l.path == SKINNY_PATH_DOT2) {
     if (l.accs != 1) return fail(SKINNY_EUNSUPPORTED, "DOT2 launch has accs=1");
     if (l.rows <= 0 || N % l.rows)
@@ -293,38 +298,37 @@ struct RingEntry {
 };
 #define DOT2_RING(waves, chunks, rows, seg, wg) \
   { {SKINNY_PATH_DOT2, 1, waves, chunks, 1, rows}, seg, wg }
-#define MFMA_RING(waves, chunks, accs, rows, seg, wg) \
-  { {SKINNY_PATH_MFMA, 1, waves, chunks, accs, rows}, seg, wg }
+#define LDS_RING(waves, chunks, accs, rows, seg, wg) \
+  { {SKINNY_PATH_MFMA_LDS, 1, waves, chunks, accs, rows}, seg, wg }
 static const RingEntry kRingTable[] = {
     // unpooler shard
     {1024, 4096, 1, 1, DOT2_RING(2, 4, 2, 1, 1024)},
     {1024, 4096, 2, 2, DOT2_RING(8, 1, 8, 2, 2048)},
-    {1024, 4096, 3, 4, DOT2_RING(2, 4, 2, 8, 512)},
-    {1024, 4096, 5, 8, DOT2_RING(4, 2, 4, 4, 512)},
-    {1024, 4096, 9, 16, MFMA_RING(16, 8, 2, 16, 8, 256)},
+    {1024, 4096, 3, 4, DOT2_RING(4, 2, 4, 4, 2048)},
+    {1024, 4096, 5, 16, LDS_RING(8, 16, 2, 16, 8, 256)},
     // o_proj shard
     {8192, 1024, 1, 1, DOT2_RING(1, 4, 4, 8, 1024)},
     {8192, 1024, 2, 2, DOT2_RING(2, 1, 8, 8, 512)},
     {8192, 1024, 3, 4, DOT2_RING(2, 1, 4, 8, 1024)},
-    {8192, 1024, 5, 8, DOT2_RING(1, 2, 4, 8, 1024)},
-    {8192, 1024, 9, 16, MFMA_RING(2, 16, 2, 16, 8, 512)},
+    {8192, 1024, 5, 16, LDS_RING(4, 16, 2, 32, 16, 256)},
     // pooler shard
     {512, 8192, 1, 1, DOT2_RING(4, 4, 2, 1, 1024)},
     {512, 8192, 2, 2, DOT2_RING(4, 4, 2, 4, 2048)},
     {512, 8192, 3, 4, DOT2_RING(8, 2, 4, 2, 1024)},
-    {512, 8192, 5, 8, DOT2_RING(8, 2, 4, 8, 256)},
+    {512, 8192, 5, 8, DOT2_RING(8, 2, 4, 16, 256)},
     // full pooler
     {4096, 8192, 1, 2, DOT2_RING(4, 4, 2, 8, 256)},
-    {4096, 8192, 3, 8, DOT2_RING(8, 2, 4, 8, 256)},
+    {4096, 8192, 3, 8, DOT2_RING(8, 2, 4, 16, 256)},
 };
 #undef DOT2_RING
-#undef MFMA_RING
+#undef LDS_RING
 
 // Ring rule for any other shape.  Up to 8 tokens DOT2: 2 rows per workgroup
 // for <= 2 tokens, else 4 (the register budget of two weight buffers), the
-// most chunks that fit and that K fills.  Beyond 8 tokens MFMA, one tile per
-// workgroup, the fewest chunks that cover K with the waves a workgroup has;
-// DOT2 if K is too long for that.  One workgroup per output block.
+// most chunks that fit and that K fills.  Beyond 8 tokens MFMA with one tile
+// per workgroup: the staged form with the most chunks that fit, else the
+// direct form with the fewest chunks that cover K with the waves a workgroup
+// has; DOT2 if K is too long for both.  One workgroup per output block.
 static int ring_choose(int M, int N, int K, int count, skinny_ring_launch *out) {
   int st = check_problem(M, N, K);
   if (st) return st;
@@ -345,6 +349,14 @@ static int ring_choose(int M, int N, int K, int count, skinny_ring_launch *out) 
     }
   }
   if (M > 8) {
+    for (int c = kMaxMfmaChunks; c >= 2; c /= 2) {  // staged: the fewest waves that fit
+      const skinny_ring_launch r{
+          {SKINNY_PATH_MFMA_LDS, 1, ceil_div(K, (long)kMfmaK * c), c, 1, kTileN}, 1, N / kTileN};
+      if (ring_check(count, M, N, K, r) == SKINNY_OK) {
+        *out = r;
+        return SKINNY_OK;
+      }
+    }
     for (int c = 1; c <= kMaxMfmaChunks; c *= 2) {
       const skinny_ring_launch r{{SKINNY_PATH_MFMA, 1, ceil_div(K, (long)kMfmaK * c), c, 1, kTileN},
                                  1, N / kTileN};
@@ -485,7 +497,7 @@ int skinny_init(int device) {
   if (hipSetDevice(device) != hipSuccess) return fail(SKINNY_EDEVICE, "cannot select device %d", device);
   int status = SKINNY_OK;
   if (hipMalloc(&st.partials, kWorkspaceFloats * sizeof(float)) != hipSuccess ||
-      mfma_prepare() != hipSuccess ||
+      mfma_prepare() != hipSuccess || ring_prepare() != hipSuccess ||
       hipDeviceSynchronize() != hipSuccess) {
     status = fail(SKINNY_ELAUNCH, "workspace allocation failed on device %d", device);
   } else {

@@ -192,8 +192,13 @@ def test_ring_launch_reasons_without_device(sk):
     assert "MFMA ring kernel" in sk.skinny_last_error()
     assert call((1, 1, 16, 8, 1, 48)) == sk.SKINNY_EUNSUPPORTED
     assert "rows=48" in sk.skinny_last_error()
-    assert call((2, 1, 16, 8, 1, 16)) == sk.SKINNY_EUNSUPPORTED
+    assert call((2, 1, 16, 8, 1, 16)) == sk.SKINNY_EUNSUPPORTED  # staged: LDS too small
+    assert "167936 bytes of LDS" in sk.skinny_last_error()
+    assert call((2, 1, 16, 1, 1, 16)) == sk.SKINNY_EUNSUPPORTED
+    assert "MFMA_LDS ring kernel" in sk.skinny_last_error()
+    assert call((3, 1, 16, 8, 1, 16)) == sk.SKINNY_EUNSUPPORTED
     assert "unknown path" in sk.skinny_last_error()
+    assert call((2, 1, 8, 16, 1, 16)) in (sk.SKINNY_EDEVICE, sk.SKINNY_ENOTINIT)
     assert call((0, 2, 1, 4, 1, 2)) == sk.SKINNY_EUNSUPPORTED
     assert "splits=1" in sk.skinny_last_error()
     assert call((0, 1, 3, 4, 1, 2)) == sk.SKINNY_EUNSUPPORTED

@@ -78,7 +78,7 @@ def _single(sk, x_bits, w_bits, M, launch):
 
     N = w_bits.shape[0]
     y = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
-    sk.skinny_gemm_bf16_launch(to_dev(x_bits[:M]), to_dev(w_bits), y, launch)
+    sk.skinny_gemm_bf16_launch(to_dev(x_bits[:M]), to_dev(w_bits), y, _as_single(sk, launch))
     torch.cuda.synchronize()
     return from_dev(y)
 
@@ -91,16 +91,25 @@ def _ring_launches(sk, M, N, K):
     for rows in (2, 4, 8, 16):
         for chunks in (1, 2, 4):
             out.append(sk.Launch(0, 1, -(-K // (512 * chunks)), chunks, 1, rows))
-    for rows in (16, 32, 64):
-        for chunks in (1, 2, 4, 8, 16):
-            for accs in (1, 2):
-                out.append(sk.Launch(1, 1, rows // 16 * -(-K // (32 * chunks)), chunks, accs,
-                                     rows))
+    for path in (sk.SKINNY_PATH_MFMA, sk.SKINNY_PATH_MFMA_LDS):
+        for rows in (16, 32, 64):
+            for chunks in (1, 2, 4, 8, 16):
+                for accs in (1, 2):
+                    out.append(sk.Launch(path, 1, rows // 16 * -(-K // (32 * chunks)), chunks,
+                                         accs, rows))
     return [l for l in out if N % l.rows == 0]
 
 
+def _as_single(sk, launch):
+    """The single-call launch with the ring launch's arithmetic (the staged
+    MFMA ring computes what the plain MFMA kernel does)."""
+    if launch.path == sk.SKINNY_PATH_MFMA_LDS:
+        return launch._replace(path=sk.SKINNY_PATH_MFMA)
+    return launch
+
+
 def _single_ok(sk, M, N, K, launch):
-    return sk.skinny_launch_unsupported(M, N, K, launch) is None
+    return sk.skinny_launch_unsupported(M, N, K, _as_single(sk, launch)) is None
 
 
 @pytest.mark.parametrize("M", [1, 2, 3, 8, 9, 16])
