@@ -62,6 +62,35 @@ def kernel_source_digest() -> str:
     return h.hexdigest()[:16]
 
 
+RING_SOURCES = ["moe_decode_skinny_amd/csrc/gemm_ring.hip", "moe_decode_skinny_amd/csrc/dot2_device.h",
+                "moe_decode_skinny_amd/csrc/internal.h"]
+
+
+def ring_source_digest() -> str:
+    import hashlib
+
+    h = hashlib.sha256()
+    for rel in RING_SOURCES:
+        with open(os.path.join(HERE, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def ring_traffic(M: int):
+    """HBM bytes per ring item from the committed counter summary, or None if
+    the ring kernels changed since the counters were taken."""
+    path = os.path.join(HERE, "profiles", "hbm_traffic_ring_unpooler.json")
+    try:
+        with open(path) as f:
+            rec = json.load(f)
+    except OSError:
+        return None
+    if rec.get("kernel_source_digest") != ring_source_digest():
+        return None
+    e = rec["per_m"].get(str(M))
+    return None if e is None else e["hbm_bytes_per_item"]
+
+
 def measured_traffic(M: int):
     """HBM bytes per launch of the M=<M> sweep kernel from the committed
     counter summary (FETCH_SIZE + WRITE_SIZE, scaled by the plain-copy
@@ -174,7 +203,8 @@ def ring_timing(sk, synthetic, dev, stream, ring, reps: int = 10):
         out[str(M)] = {"launch": {**dict(r.gemm._asdict()), "segment": r.segment,
                                   "workgroups": r.workgroups},
                        "us_per_item": round(us, 3), "GBs": round(gbs, 1),
-                       "pct_peak": round(100 * gbs / PEAK_GBS, 2)}
+                       "pct_peak": round(100 * gbs / PEAK_GBS, 2),
+                       "hbm_bytes_per_item": ring_traffic(M)}
         del g
     return {"workload": f"unpooler shard GEMM M=1,2,4,8,16, N=1024, K=4096: one "
                         f"{RING}-item skinny_gemm_bf16_ring launch per M over the "
