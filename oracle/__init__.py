@@ -75,6 +75,10 @@ def load_library(path: str):
         ctypes.c_int, ctypes.c_int, _u8p, _u8p, ctypes.c_void_p, ctypes.c_void_p,
         ctypes.c_void_p]
     lib.oracle_rmsnorm_nvfp4.restype = None
+    lib.oracle_mailbox_publish.argtypes = [
+        _u16p, ctypes.c_int, ctypes.c_int, _u16p, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+        ctypes.c_void_p, ctypes.c_void_p]
+    lib.oracle_mailbox_publish.restype = ctypes.c_int
     return lib
 
 
@@ -227,3 +231,28 @@ def rmsnorm_nvfp4(r_bits, w_bits, gain_center: float, eps: float, global_scale: 
     lib.oracle_rmsnorm_nvfp4(r, w, f32(gain_center), f32(eps), f32(global_scale),
                              M, P, a, a_sf, _ptr(yn), _ptr(pre), _ptr(osc))
     return {"a": a, "a_sf": a_sf, "yn": yn, "pre": pre, "os": osc}
+
+
+# ------------------------------------------------------------------- publish
+def mailbox_publish(y_bits, mailbox, rank: int, stage_state=None, ticket=None):
+    """The zero-copy publish of y [M, width] into this rank's slot of
+    mailbox [3, tp, capacity, width] (uint16 bf16 bits, updated in place).
+    With a ticket (int32 [1]) the stage comes from it and stage_state, if
+    given, is not used; otherwise stage_state (int32 [2]) gives the stage and
+    is updated in place.  Returns the stage used, or -1 if it was outside
+    0..2 (nothing written)."""
+    lib = _load()
+    y = np.ascontiguousarray(y_bits, dtype=np.uint16)
+    if mailbox.dtype != np.uint16 or mailbox.ndim != 4 or not mailbox.flags.c_contiguous:
+        raise ValueError("mailbox must be a contiguous uint16 [3, tp, capacity, width] array")
+    stages, tp, capacity, width = mailbox.shape
+    M = y.shape[0]
+    if stages != 3 or y.shape != (M, width) or M > capacity or not 0 <= rank < tp:
+        raise ValueError("shapes do not fit the mailbox")
+    if stage_state is None and ticket is None:
+        raise ValueError("give stage_state or ticket")
+    st = None if stage_state is None else stage_state
+    tk = None if ticket is None else np.ascontiguousarray(ticket, dtype=np.int32)
+    if st is not None and (st.dtype != np.int32 or st.shape != (2,) or not st.flags.c_contiguous):
+        raise ValueError("stage_state must be a contiguous int32 [2] array")
+    return lib.oracle_mailbox_publish(y, M, width, mailbox, tp, rank, capacity, _ptr(st), _ptr(tk))

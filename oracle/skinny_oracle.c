@@ -25,6 +25,11 @@
  *   [oscale]    same page, nvfp4_compute_output_scale: the output scale is the
  *               reciprocal of (decoded scale * reciprocal of global_scale),
  *               and 0 when the decoded scale is 0.
+ *   [publish]   unpooler page, module description (zero-copy epilogue and
+ *               ticket stage) and Unpooler.run; pooler_gather page, module
+ *               description (BF16 edge layers: -0.0 is the mailbox sentinel,
+ *               so publishers store -0.0 as +0.0) and compile_gather (the
+ *               mailbox is BF16 [3, tp, capacity, hidden / tp]).
  *
  * Readings where the pages are silent (each also listed in the design notes):
  *   - block scale: sf = e4m3(global_scale * amax / 6), 6 being the largest
@@ -35,6 +40,12 @@
 #include <math.h>
 #include <stdint.h>
 #include <string.h>
+
+/* Readings for [publish] (the mailbox's body is not printed): the stage
+ * state is int32 [2], [0] the stage a publish writes (the pages' NEXT_STAGE)
+ * and [1] the word a publish sets to it (ACTIVE_STAGE); a ticket holds
+ * stage << 16 and the stage is its upper 16 bits; a stage outside 0..2
+ * publishes nothing. */
 
 /* ---------------------------------------------------------------- bfloat16 */
 
@@ -256,4 +267,27 @@ void oracle_rmsnorm_nvfp4(const uint16_t *r, const uint16_t *w,
       if (osc) osc[(size_t)m * (P / 16) + b] = os;
     }
   }
+}
+
+/* ----------------------------------------------------------------- publish */
+
+/* [publish] The zero-copy epilogue on one GPU: rows 0..M-1 of y [M, width]
+ * into this rank's slot of the mailbox [3][tp][capacity][width] at the
+ * stage, with -0.0 (the sentinel) stored as +0.0; without a ticket the stage
+ * word stage_state[1] is set to the stage, with one (ticket != NULL) the
+ * stage state is not used.  Returns the stage, or -1 (and writes nothing) if
+ * it is outside 0..2. */
+int oracle_mailbox_publish(const uint16_t *y, int M, int width, uint16_t *mailbox, int tp,
+                           int rank, int capacity, int32_t *stage_state,
+                           const int32_t *ticket) {
+  int stage = ticket ? (int)((uint32_t)ticket[0] >> 16) : stage_state[0];
+  if (stage < 0 || stage > 2) return -1;
+  uint16_t *slot = mailbox + ((size_t)stage * tp + rank) * (size_t)capacity * width;
+  for (int t = 0; t < M; ++t)
+    for (int j = 0; j < width; ++j) {
+      uint16_t v = y[(size_t)t * width + j];
+      slot[(size_t)t * width + j] = (v == 0x8000u) ? 0x0000u : v;
+    }
+  if (!ticket) stage_state[1] = stage;
+  return stage;
 }

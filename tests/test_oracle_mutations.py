@@ -16,6 +16,7 @@ import oracle
 from tests import test_oracle_formats as F
 from tests import test_oracle_gemm as G
 from tests import test_oracle_norm as Nm
+from tests import test_oracle_publish as Pb
 
 SRC = os.path.join(os.path.dirname(oracle.__file__), "skinny_oracle.c")
 
@@ -43,6 +44,12 @@ MUTATIONS = [
     ("eps_outside_root", "double inv = 1.0 / sqrt(ss / P + eps);",
      "double inv = 1.0 / (sqrt(ss / P) + eps);"),
     ("gain_center_dropped", "(oracle_bf16_value(w[j]) + gain_center)", "oracle_bf16_value(w[j])"),
+    ("publish_keeps_negative_zero", "(v == 0x8000u) ? 0x0000u : v;", "v;"),
+    ("publish_zeroes_every_sign", "(v == 0x8000u) ? 0x0000u : v;", "v & 0x7FFFu;"),
+    ("publish_rank_stage_swapped", "((size_t)stage * tp + rank)", "((size_t)rank * 3 + stage)"),
+    ("publish_ticket_low_half", "(int)((uint32_t)ticket[0] >> 16)", "(int)((uint32_t)ticket[0] & 0xFFFF)"),
+    ("publish_sets_next_stage", "if (!ticket) stage_state[1] = stage;", "if (!ticket) stage_state[0] = stage;"),
+    ("publish_word_with_ticket", "if (!ticket) stage_state[1] = stage;", "if (stage_state) stage_state[1] = stage;"),
 ]
 
 # The pins (test functions that raise AssertionError on a mismatch).
@@ -69,6 +76,11 @@ BATTERY = [
     Nm.test_global_max_block_hits_the_largest_codes,
     Nm.test_all_zero_block,
     Nm.test_packing_low_nibble_even_column,
+    Pb.test_publish_worked_case,
+    Pb.test_publish_ticket_stage_uses_upper_half_and_stores_no_word,
+    lambda: [Pb.test_publish_outside_stages_writes_nothing(s, t) for s, t in
+             [([3, 7], None), ([-1, 7], None), (None, [3 << 16]), (None, [0x7FFF0000])]],
+    lambda: [Pb.test_publish_properties(k) for k in range(6)],
 ]
 
 
