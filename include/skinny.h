@@ -121,6 +121,43 @@ int skinny_gemm_unsupported(int M, int N, int K, int splits);
 /* Why (M, N, K) cannot run at `launch`; SKINNY_OK when it can.  Host only. */
 int skinny_launch_unsupported(int M, int N, int K, const skinny_launch *launch);
 
+/* The next boundary's mailbox for a zero-copy publish (unpooler page, module
+ * description, zero-copy epilogue and ticket stage; pooler_gather page, module
+ * description and compile_gather).  On one GPU the multicast into the
+ * peers' copies becomes a store into this device buffer.
+ *   data         bf16 [3][tp][capacity][width] on the device, 16-byte aligned:
+ *                three stages of one slot per rank
+ *   stage_state  int32 [2] on the device: [0] the stage a publish writes
+ *                (0..2), [1] set to that stage by the publish; not used with
+ *                a ticket (may then be NULL)
+ *   ticket       NULL, or int32 [1] on the device holding stage << 16: the
+ *                stage is its upper 16 bits and no stage word is written
+ *   tp, rank     ranks sharing the mailbox and this rank's slot, 0 <= rank < tp
+ *   capacity     token rows per slot, >= M
+ *   width        columns per row, == N
+ * The stage is read on the device when the kernel runs; a stage outside 0..2
+ * publishes nothing (y is still stored). */
+typedef struct skinny_mailbox {
+  void *data;
+  int *stage_state;
+  const int *ticket;
+  int tp, rank, capacity, width;
+} skinny_mailbox;
+
+/* The GEMM with its zero-copy publish: y as skinny_gemm_bf16 computes it, and
+ * the same M rows into mailbox->data[stage][rank][0..M) with each bf16 -0.0
+ * stored as +0.0 (-0.0 is the mailbox's "not yet written" sentinel); without a
+ * ticket, stage_state[1] is set to the stage.  The other slots, rows >= M
+ * of this slot, stage_state[0] and the ticket are not written.
+ *   launch   NULL = the chooser's launch; else an explicit launch shape
+ * The mailbox, stage state and ticket must not overlap x, W or y.  Two
+ * publishes into one slot and stage race unless ordered on one stream.
+ * Errors: SKINNY_EINVAL (also: width != N, M > capacity, bad rank),
+ * SKINNY_EUNSUPPORTED, SKINNY_ENOTINIT, SKINNY_ELAUNCH. */
+int skinny_gemm_bf16_publish(const void *x, const void *W, void *y, int M,
+                             int N, int K, const skinny_launch *launch,
+                             const skinny_mailbox *mailbox, void *stream);
+
 /* A launch of the layer ring (skinny_gemm_bf16_ring_launch).
  *   gemm        the per-tile launch shape, splits = 1: DOT2 (rows 2, 4 or 8,
  *               chunks 1, 2, 4; waves = ceil(K / (512 chunks)) <= 8) or MFMA

@@ -9,7 +9,8 @@ fallback.
 
 Same names as the C ABI:
   skinny_init, skinny_gemm_bf16, skinny_gemm_bf16_launch, skinny_choose,
-  skinny_gemm_unsupported, skinny_launch_unsupported, skinny_gemm_bf16_ring,
+  skinny_gemm_unsupported, skinny_launch_unsupported, skinny_gemm_bf16_publish,
+  skinny_gemm_bf16_ring,
   skinny_gemm_bf16_ring_launch, skinny_ring_choose, skinny_ring_launch_unsupported,
   skinny_rmsnorm_nvfp4, skinny_rmsnorm_bf16, skinny_last_error, skinny_version
 Status codes map to exceptions as on the unpooler page (Unpooler.run /
@@ -62,6 +63,12 @@ class Launch(NamedTuple):
         return _CLaunch(*self)
 
 
+class _CMailbox(ctypes.Structure):
+    _fields_ = [("data", ctypes.c_void_p), ("stage_state", ctypes.c_void_p),
+                ("ticket", ctypes.c_void_p), ("tp", ctypes.c_int), ("rank", ctypes.c_int),
+                ("capacity", ctypes.c_int), ("width", ctypes.c_int)]
+
+
 class _CRingLaunch(ctypes.Structure):
     _fields_ = [("gemm", _CLaunch), ("segment", ctypes.c_int), ("workgroups", ctypes.c_int)]
 
@@ -92,6 +99,8 @@ _sig = {
     "skinny_choose": ([_i, _i, _i, _i, ctypes.POINTER(_CLaunch)], _i),
     "skinny_gemm_unsupported": ([_i, _i, _i, _i], _i),
     "skinny_launch_unsupported": ([_i, _i, _i, ctypes.POINTER(_CLaunch)], _i),
+    "skinny_gemm_bf16_publish": (
+        [_vp, _vp, _vp, _i, _i, _i, ctypes.POINTER(_CLaunch), ctypes.POINTER(_CMailbox), _vp], _i),
     "skinny_gemm_bf16_ring": ([_vp, _vp, _vp, _i, _i, _i, _i, _vp], _i),
     "skinny_gemm_bf16_ring_launch": (
         [_vp, _vp, _vp, _i, _i, _i, _i, ctypes.POINTER(_CRingLaunch), _vp], _i),
@@ -204,6 +213,32 @@ def skinny_gemm_bf16_launch(x, w, y, launch: Launch, stream=None):
     return y
 
 
+def skinny_gemm_bf16_publish(x, w, y, mailbox, rank: int, stage_state=None, ticket=None,
+                             launch: Optional[Launch] = None, stream=None):
+    """y = x @ W^T, and y published into mailbox[stage, rank, :M] (bf16
+    [3, tp, capacity, N]) with -0.0 stored as +0.0.  The stage comes from
+    ticket (int32 [1], stage << 16) if given, else from stage_state (int32
+    [2]: [0] the stage, [1] set to it).  Returns y."""
+    import torch
+
+    xp, wp, yp, M, N, K = _gemm_args(x, w, y)
+    dp = _dev_tensor(mailbox, "mailbox", torch.bfloat16)
+    if mailbox.dim() != 4 or mailbox.shape[0] != 3:
+        raise ValueError("mailbox must be [3, tp, capacity, width]")
+    _, tp, capacity, width = mailbox.shape
+    sp = None if stage_state is None else _dev_tensor(stage_state, "stage_state", torch.int32)
+    tk = None if ticket is None else _dev_tensor(ticket, "ticket", torch.int32)
+    if stage_state is not None and stage_state.numel() != 2:
+        raise ValueError("stage_state must be int32 [2]")
+    if ticket is not None and ticket.numel() != 1:
+        raise ValueError("ticket must be int32 [1]")
+    mb = _CMailbox(dp, sp, tk, tp, int(rank), capacity, width)
+    lp = None if launch is None else ctypes.byref(Launch(*launch)._c())
+    _check(_lib.skinny_gemm_bf16_publish(xp, wp, yp, M, N, K, lp, ctypes.byref(mb),
+                                         _stream(stream, x.device)))
+    return y
+
+
 def skinny_ring_choose(M: int, N: int, K: int, count: int) -> RingLaunch:
     """The RingLaunch that skinny_gemm_bf16_ring uses."""
     out = _CRingLaunch()
@@ -291,7 +326,8 @@ def skinny_rmsnorm_bf16(r, norm_w, gain_center: float, eps: float, y, stream=Non
 __all__ = [
     "Launch", "RingLaunch", "init", "skinny_init", "skinny_gemm_bf16", "skinny_gemm_bf16_launch",
     "skinny_choose", "skinny_gemm_unsupported", "skinny_launch_unsupported",
-    "skinny_gemm_bf16_ring", "skinny_gemm_bf16_ring_launch", "skinny_ring_choose",
+    "skinny_gemm_bf16_publish", "skinny_gemm_bf16_ring", "skinny_gemm_bf16_ring_launch",
+    "skinny_ring_choose",
     "skinny_ring_launch_unsupported",
     "skinny_rmsnorm_nvfp4", "skinny_rmsnorm_bf16", "skinny_last_error", "skinny_version",
     "LIB_PATH",

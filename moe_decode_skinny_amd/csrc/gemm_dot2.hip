@@ -24,8 +24,9 @@ template <int ROWS, int CHUNKS, int MT>
 __global__ __launch_bounds__(kDot2MaxThreads) void gemm_dot2_kernel(
     const uint16_t *__restrict__ x, const uint16_t *__restrict__ w,
     uint16_t *__restrict__ y, float *__restrict__ partials, int M, int N, int K,
-    int S, int groups, int kw) {
+    int S, int groups, int kw, Publish pub) {
   const int lane = threadIdx.x & 63;
+  if (S == 1 && blockIdx.x == 0 && threadIdx.x == 0) publish_stage_word(pub);
   const int wave = wave_index();
   const int waves = blockDim.x >> 6;
 
@@ -107,14 +108,16 @@ __global__ __launch_bounds__(kDot2MaxThreads) void gemm_dot2_kernel(
   }
 
   if (!live) return;
-  if (S == 1)
-    y[(size_t)t * N + f0 + r] = (uint16_t)f32_to_bf16(part);
-  else  // FP32 partial of split s: partials[s][token][feature]
+  if (S == 1) {
+    const unsigned b = f32_to_bf16(part);
+    y[(size_t)t * N + f0 + r] = (uint16_t)b;
+    if (uint16_t *slot = publish_slot(pub, N)) slot[(size_t)t * N + f0 + r] = (uint16_t)publish_bits(b);
+  } else  // FP32 partial of split s: partials[s][token][feature]
     partials[((size_t)s * M + t) * N + f0 + r] = part;
 }
 
 using Dot2Kernel = void (*)(const uint16_t *, const uint16_t *, uint16_t *,
-                            float *, int, int, int, int, int, int);
+                            float *, int, int, int, int, int, int, Publish);
 
 // Register budget per lane: weights 4 * ROWS * CHUNKS, activations
 // 4 * MT * CHUNKS, sums ROWS * MT.  Variants above the budget are not built.
@@ -179,15 +182,15 @@ int dot2_max_waves() { return kDot2MaxThreads / 64; }
 
 hipError_t launch_gemm_dot2(const uint16_t *x, const uint16_t *w, uint16_t *y,
                             int M, int N, int K, const skinny_launch &l,
-                            DeviceState &st, hipStream_t stream) {
+                            DeviceState &st, const Publish &pub, hipStream_t stream) {
   Dot2Kernel k = pick(l.rows, l.chunks, dot2_token_tile(M));
   const int groups = N / l.rows;
   dim3 grid(groups * l.splits), block(64 * l.waves);
   hipLaunchKernelGGL(k, grid, block, 0, stream, x, w, y, st.partials, M, N, K, l.splits,
-                     groups, kDot2K * l.chunks);
+                     groups, kDot2K * l.chunks, pub);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || l.splits == 1) return e;
-  return launch_split_reduce(st.partials, y, M, N, l.splits, stream);
+  return launch_split_reduce(st.partials, y, M, N, l.splits, pub, stream);
 }
 
 }  // namespace skinny

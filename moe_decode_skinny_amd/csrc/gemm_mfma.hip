@@ -41,8 +41,9 @@ template <int CHUNKS, int ACCS>
 __global__ __launch_bounds__(mfma_max_threads(CHUNKS)) void gemm_mfma_kernel(
     const uint16_t *__restrict__ x, const uint16_t *__restrict__ w,
     uint16_t *__restrict__ y, float *__restrict__ partials, int M, int N, int K,
-    int S, int groups, int F, int kw) {
+    int S, int groups, int F, int kw, Publish pub) {
   const int lane = threadIdx.x & 63;
+  if (S == 1 && blockIdx.x == 0 && threadIdx.x == 0) publish_stage_word(pub);
   const int wave = wave_index();
   const int waves = blockDim.x >> 6;
   const int KW = waves / F;
@@ -154,6 +155,9 @@ __global__ __launch_bounds__(mfma_max_threads(CHUNKS)) void gemm_mfma_kernel(
     const unsigned lo = f32_to_bf16(part[0]) | (f32_to_bf16(part[1]) << 16);
     const unsigned hi = f32_to_bf16(part[2]) | (f32_to_bf16(part[3]) << 16);
     *reinterpret_cast<uint2 *>(y + (size_t)row * N + col) = make_uint2(lo, hi);
+    if (uint16_t *slot = publish_slot(pub, N))
+      *reinterpret_cast<uint2 *>(slot + (size_t)row * N + col) =
+          make_uint2(publish_pair(lo), publish_pair(hi));
   } else {
     // FP32 partial of split s: partials[s][token][feature]
     *reinterpret_cast<f32x4 *>(partials + ((size_t)s * M + row) * N + col) = part;
@@ -161,7 +165,7 @@ __global__ __launch_bounds__(mfma_max_threads(CHUNKS)) void gemm_mfma_kernel(
 }
 
 using MfmaKernel = void (*)(const uint16_t *, const uint16_t *, uint16_t *,
-                            float *, int, int, int, int, int, int, int);
+                            float *, int, int, int, int, int, int, int, Publish);
 
 template <int C>
 MfmaKernel pick_accs(int accs) {
@@ -213,16 +217,16 @@ size_t mfma_lds_bytes(int M, const skinny_launch &l) {
 
 hipError_t launch_gemm_mfma(const uint16_t *x, const uint16_t *w, uint16_t *y,
                             int M, int N, int K, const skinny_launch &l,
-                            DeviceState &st, hipStream_t stream) {
+                            DeviceState &st, const Publish &pub, hipStream_t stream) {
   MfmaKernel k = pick(l.chunks, l.accs);
   const int F = l.rows / kTileN;
   const int groups = N / l.rows;
   dim3 grid(groups * l.splits), block(64 * l.waves);
   hipLaunchKernelGGL(k, grid, block, mfma_lds_bytes(M, l), stream, x, w, y, st.partials, M, N,
-                     K, l.splits, groups, F, kMfmaK * l.chunks);
+                     K, l.splits, groups, F, kMfmaK * l.chunks, pub);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || l.splits == 1) return e;
-  return launch_split_reduce(st.partials, y, M, N, l.splits, stream);
+  return launch_split_reduce(st.partials, y, M, N, l.splits, pub, stream);
 }
 
 }  // namespace skinny

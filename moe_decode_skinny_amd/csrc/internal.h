@@ -27,6 +27,19 @@ struct DeviceState {
   float *partials = nullptr;  // kWorkspaceFloats
 };
 
+// The zero-copy publish of a GEMM call (unpooler page, module description,
+// zero-copy epilogue): y also goes into this rank's slot of a mailbox
+// [3 stages][tp][capacity][N] at the stage read on the device when the
+// kernel runs, with -0.0 (the mailbox's "not yet written" sentinel) stored
+// as +0.0.  data == nullptr: no publish.
+struct Publish {
+  uint16_t *data = nullptr;
+  const int *stage_src = nullptr;  // stage_state[0], or the ticket word
+  int *stage_word = nullptr;       // stage_state[1]; nullptr with a ticket
+  int shift = 0;                   // 16 with a ticket (stage << 16)
+  int tp = 0, rank = 0, capacity = 0;
+};
+
 // The state of the current HIP device, or nullptr (and a reason) if the
 // device has not been initialised.
 DeviceState *current_state(int *status);
@@ -36,10 +49,10 @@ DeviceState *current_state(int *status);
 // Each returns hipSuccess or the launch error; arguments are already valid.
 hipError_t launch_gemm_mfma(const uint16_t *x, const uint16_t *w, uint16_t *y,
                             int M, int N, int K, const skinny_launch &l,
-                            DeviceState &st, hipStream_t stream);
+                            DeviceState &st, const Publish &pub, hipStream_t stream);
 hipError_t launch_gemm_dot2(const uint16_t *x, const uint16_t *w, uint16_t *y,
                             int M, int N, int K, const skinny_launch &l,
-                            DeviceState &st, hipStream_t stream);
+                            DeviceState &st, const Publish &pub, hipStream_t stream);
 // The layer ring: up to kMaxRingItems independent GEMMs of one shape.
 constexpr int kMaxRingItems = 64;
 struct RingItems {
@@ -50,7 +63,7 @@ struct RingItems {
 hipError_t launch_gemm_ring(const RingItems &items, int count, int M, int N, int K,
                             const skinny_ring_launch &r, hipStream_t stream);
 hipError_t launch_split_reduce(const float *partials, uint16_t *y, int M, int N, int S,
-                               hipStream_t stream);
+                               const Publish &pub, hipStream_t stream);
 hipError_t launch_rmsnorm(const uint16_t *r, const uint16_t *w, float gain_center,
                           float eps, const float *global_scale, uint8_t *a,
                           uint8_t *a_sf, uint16_t *y, int M, int P, bool quant,
@@ -112,6 +125,36 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void *base, 
                                            (int)kBufferFlags);
 }
 __device__ __forceinline__ float bf16_hi(unsigned u) { return __uint_as_float(u & 0xffff0000u); }
+
+// ------------------------------------------------- zero-copy publish helpers
+// The publish stage of this call: the stage word's value, or the upper half
+// of the ticket; anything outside 0..2 (negative values included) means no
+// publish.
+__device__ __forceinline__ unsigned publish_stage(const Publish &p) {
+  return (unsigned)*p.stage_src >> p.shift;
+}
+
+// The slot [capacity][N] this call publishes into, or nullptr.
+__device__ __forceinline__ uint16_t *publish_slot(const Publish &p, int N) {
+  if (!p.data) return nullptr;
+  const unsigned stage = publish_stage(p);
+  if (stage > 2) return nullptr;
+  return p.data + ((size_t)stage * p.tp + p.rank) * (size_t)p.capacity * N;
+}
+
+// Sets the active-stage word (one thread of the writing kernel calls it).
+__device__ __forceinline__ void publish_stage_word(const Publish &p) {
+  if (!p.data || !p.stage_word) return;
+  const unsigned stage = publish_stage(p);
+  if (stage <= 2) *p.stage_word = (int)stage;
+}
+
+// bf16 bits as published: -0.0 (0x8000) becomes +0.0; one value, or two
+// packed in 32 bits.
+__device__ __forceinline__ unsigned publish_bits(unsigned b) { return b == 0x8000u ? 0u : b; }
+__device__ __forceinline__ unsigned publish_pair(unsigned v) {
+  return publish_bits(v & 0xffffu) | (publish_bits(v >> 16) << 16);
+}
 
 }  // namespace skinny
 #endif

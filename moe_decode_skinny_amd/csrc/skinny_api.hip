@@ -415,7 +415,7 @@ static int ring_common(const void *const *x, const void *const *W, void *const *
 }
 
 static int gemm_common(const void *x, const void *W, void *y, int M, int N, int K,
-                       const skinny_launch &l, void *stream) {
+                       const skinny_launch &l, void *stream, const Publish &pub = Publish{}) {
   if (!x || !W || !y) return fail(SKINNY_EINVAL, "null pointer");
   if (!aligned(x, 16) || !aligned(W, 16) || !aligned(y, 16))
     return fail(SKINNY_EINVAL, "x, W and y must be 16-byte aligned");
@@ -429,9 +429,46 @@ static int gemm_common(const void *x, const void *W, void *y, int M, int N, int 
   const uint16_t *wp = static_cast<const uint16_t *>(W);
   uint16_t *yp = static_cast<uint16_t *>(y);
   hipStream_t s = static_cast<hipStream_t>(stream);
-  hipError_t e = l.path == SKINNY_PATH_MFMA ? launch_gemm_mfma(xp, wp, yp, M, N, K, l, *ds, s)
-                                            : launch_gemm_dot2(xp, wp, yp, M, N, K, l, *ds, s);
+  hipError_t e = l.path == SKINNY_PATH_MFMA
+                     ? launch_gemm_mfma(xp, wp, yp, M, N, K, l, *ds, pub, s)
+                     : launch_gemm_dot2(xp, wp, yp, M, N, K, l, *ds, pub, s);
   if (e != hipSuccess) return fail(SKINNY_ELAUNCH, "launch failed: %s", hipGetErrorString(e));
+  return SKINNY_OK;
+}
+
+// The publish target of skinny_gemm_bf16_publish, checked against the call
+// (unpooler page, Unpooler: the mailbox width must equal N, and M is at most
+// the mailbox capacity).
+static int publish_check(const skinny_mailbox *mb, const void *x, const void *W, const void *y,
+                         int M, int N, int K, Publish *out) {
+  if (!mb) return fail(SKINNY_EINVAL, "null mailbox");
+  if (!mb->data) return fail(SKINNY_EINVAL, "null mailbox data");
+  if (!aligned(mb->data, 16)) return fail(SKINNY_EINVAL, "mailbox data must be 16-byte aligned");
+  if (mb->width != N) return fail(SKINNY_EINVAL, "mailbox width %d != N %d", mb->width, N);
+  if (mb->tp < 1 || mb->rank < 0 || mb->rank >= mb->tp)
+    return fail(SKINNY_EINVAL, "rank %d of tp %d", mb->rank, mb->tp);
+  if (mb->capacity < 1 || M > mb->capacity)
+    return fail(SKINNY_EINVAL, "M=%d exceeds the mailbox capacity %d", M, mb->capacity);
+  const int *src = mb->ticket ? mb->ticket : mb->stage_state;
+  if (!src) return fail(SKINNY_EINVAL, "the publish needs a stage state or a ticket");
+  if (!aligned(src, 4) || (mb->stage_state && !aligned(mb->stage_state, 4)))
+    return fail(SKINNY_EINVAL, "stage state and ticket must be 4-byte aligned");
+  const size_t mbytes = 2ul * 3 * (size_t)mb->tp * (size_t)mb->capacity * (size_t)N;
+  const size_t xb = 2ul * M * K, wb = 2ul * N * K, yb = 2ul * M * N;
+  if (overlap(mb->data, mbytes, x, xb) || overlap(mb->data, mbytes, W, wb) ||
+      overlap(mb->data, mbytes, y, yb))
+    return fail(SKINNY_EINVAL, "the mailbox overlaps x, W or y");
+  if (overlap(src, 4, mb->data, mbytes) || overlap(src, 4, y, yb) ||
+      (!mb->ticket && overlap(mb->stage_state, 8, mb->data, mbytes)) ||
+      (!mb->ticket && overlap(mb->stage_state, 8, y, yb)))
+    return fail(SKINNY_EINVAL, "the stage state or ticket overlaps the mailbox or y");
+  out->data = static_cast<uint16_t *>(mb->data);
+  out->stage_src = src;
+  out->stage_word = mb->ticket ? nullptr : mb->stage_state + 1;
+  out->shift = mb->ticket ? 16 : 0;
+  out->tp = mb->tp;
+  out->rank = mb->rank;
+  out->capacity = mb->capacity;
   return SKINNY_OK;
 }
 
@@ -537,6 +574,19 @@ int skinny_gemm_bf16_launch(const void *x, const void *W, void *y, int M, int N,
   int st = launch_check(M, N, K, *launch);
   if (st) return st;
   return gemm_common(x, W, y, M, N, K, *launch, stream);
+}
+
+int skinny_gemm_bf16_publish(const void *x, const void *W, void *y, int M, int N, int K,
+                             const skinny_launch *launch, const skinny_mailbox *mailbox,
+                             void *stream) {
+  skinny_launch l;
+  int st = launch ? launch_check(M, N, K, *launch) : choose(M, N, K, 0, &l);
+  if (st) return st;
+  if (launch) l = *launch;
+  Publish pub;
+  st = publish_check(mailbox, x, W, y, M, N, K, &pub);
+  if (st) return st;
+  return gemm_common(x, W, y, M, N, K, l, stream, pub);
 }
 
 int skinny_ring_choose(int M, int N, int K, int count, skinny_ring_launch *out) {

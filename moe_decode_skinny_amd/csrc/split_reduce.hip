@@ -7,7 +7,7 @@
 // kernel boundary orders it after every partial store of the first: no
 // workgroup ever waits for another.  One thread per four consecutive outputs
 // of a token row: S 16-byte loads (coalesced across the row) and one 8-byte
-// store.
+// store (two with a zero-copy publish, whose stage word thread 0 sets).
 #include "internal.h"
 
 namespace skinny {
@@ -16,8 +16,10 @@ namespace {
 constexpr int kReduceThreads = 256;
 
 __global__ __launch_bounds__(kReduceThreads) void split_reduce_kernel(
-    const float *__restrict__ partials, uint16_t *__restrict__ y, int M, int N, int S) {
+    const float *__restrict__ partials, uint16_t *__restrict__ y, int M, int N, int S,
+    Publish pub) {
   const int i = blockIdx.x * kReduceThreads + threadIdx.x;
+  if (i == 0) publish_stage_word(pub);
   const int quads = M * (N / 4);
   if (i >= quads) return;
   const int t = i / (N / 4), n = (i - t * (N / 4)) * 4;
@@ -29,15 +31,18 @@ __global__ __launch_bounds__(kReduceThreads) void split_reduce_kernel(
   const unsigned lo = f32_to_bf16(sum[0]) | (f32_to_bf16(sum[1]) << 16);
   const unsigned hi = f32_to_bf16(sum[2]) | (f32_to_bf16(sum[3]) << 16);
   *reinterpret_cast<uint2 *>(y + (size_t)t * N + n) = make_uint2(lo, hi);
+  if (uint16_t *slot = publish_slot(pub, N))
+    *reinterpret_cast<uint2 *>(slot + (size_t)t * N + n) =
+        make_uint2(publish_pair(lo), publish_pair(hi));
 }
 
 }  // namespace
 
 hipError_t launch_split_reduce(const float *partials, uint16_t *y, int M, int N, int S,
-                               hipStream_t stream) {
+                               const Publish &pub, hipStream_t stream) {
   const int quads = M * (N / 4);
   dim3 grid((quads + kReduceThreads - 1) / kReduceThreads), block(kReduceThreads);
-  hipLaunchKernelGGL(split_reduce_kernel, grid, block, 0, stream, partials, y, M, N, S);
+  hipLaunchKernelGGL(split_reduce_kernel, grid, block, 0, stream, partials, y, M, N, S, pub);
   return hipGetLastError();
 }
 

@@ -242,3 +242,39 @@ def test_ring_rejects_aliased_items_without_device(sk):
     assert "aligned" in sk.skinny_last_error()
     # one x shared by every item and disjoint outputs are fine
     assert ring([x0, x0], [w0, w1], [y0, y1]) in (sk.SKINNY_EDEVICE, sk.SKINNY_ENOTINIT)
+
+
+def test_publish_reasons_without_device(sk):
+    lib = ctypes.CDLL(sk.LIB_PATH)
+    lib.skinny_gemm_bf16_publish.argtypes = [ctypes.c_void_p] * 3 + [ctypes.c_int] * 3 + [
+        ctypes.POINTER(sk._CLaunch), ctypes.POINTER(sk._CMailbox), ctypes.c_void_p]
+    M, N, K = 4, 64, 256
+    x, w, y = 0x100000, 0x200000, 0x300000
+    data, stage, ticket = 0x400000, 0x500000, 0x500100
+
+    def call(data=data, stage=stage, ticket=None, tp=2, rank=1, capacity=8, width=N, launch=None):
+        mb = sk._CMailbox(data, stage, ticket, tp, rank, capacity, width)
+        lp = None if launch is None else ctypes.byref(sk.Launch(*launch)._c())
+        return lib.skinny_gemm_bf16_publish(x, w, y, M, N, K, lp, ctypes.byref(mb), None)
+
+    def bad(needle, **kw):
+        assert call(**kw) == sk.SKINNY_EINVAL, needle
+        assert needle in sk.skinny_last_error(), sk.skinny_last_error()
+
+    bad("width 32 != N 64", width=32)
+    bad("exceeds the mailbox capacity 3", capacity=3)
+    bad("rank 2 of tp 2", rank=2)
+    bad("rank -1 of tp 2", rank=-1)
+    bad("null mailbox data", data=None)
+    bad("16-byte aligned", data=data + 8)
+    bad("needs a stage state or a ticket", stage=None)
+    bad("4-byte aligned", stage=stage + 2)
+    bad("overlaps x, W or y", data=y - 64)
+    bad("overlaps the mailbox or y", stage=data + 16)
+    assert lib.skinny_gemm_bf16_publish(x, w, y, M, N, K, None, None, None) == sk.SKINNY_EINVAL
+    # an unsupported explicit launch is refused before the mailbox is looked at
+    assert call(launch=(0, 3, 1, 1, 1, 4)) == sk.SKINNY_EUNSUPPORTED
+    # valid: a stage state, or a ticket alone; both stop at the missing device
+    assert call() in (sk.SKINNY_EDEVICE, sk.SKINNY_ENOTINIT)
+    assert call(stage=None, ticket=ticket) in (sk.SKINNY_EDEVICE, sk.SKINNY_ENOTINIT)
+    assert call(launch=(0, 1, 1, 1, 1, 4)) in (sk.SKINNY_EDEVICE, sk.SKINNY_ENOTINIT)
