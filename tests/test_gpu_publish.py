@@ -154,7 +154,7 @@ def test_publish_negative_zero_stored_as_positive_zero(gpu_lib):
     w = np.zeros((N, K), dtype=np.uint16)
     x[:, 0] = oracle.bf16_round(-(2.0 ** -70))
     w[:, 0] = oracle.bf16_round(2.0 ** -70)
-    w[::2, 1] = oracle.bf16_round(1.0)        # even features: -0.0 + x[:, 1] = +0 terms
+    w[::2, 1] = oracle.bf16_round(1.0)        # even features add a -0.0 * 1.0 term
     x[:, 1] = 0x8000                          # -0.0 times 1.0 = -0.0
     ref = oracle.gemm_bf16(x[:M], w, THREADS)
     assert np.all(ref == 0x8000)              # the exact sums round to -0.0
