@@ -107,30 +107,49 @@ def measured_traffic(M: int):
     return None if per_m is None else per_m.get("hbm_bytes_per_launch")
 
 
+def _cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(budget_s: float = 12.0):
     """The oracle (plain C, binary64) on the host cores for a bounded sample of
-    the same sweep: whole steps until the budget is spent."""
-    import numpy as np
-
+    the same sweep: whole steps until the budget is spent, with every host
+    thread it may use (at most 16) and then with one thread."""
     import oracle
     import synthetic
 
     threads = min(16, len(os.sched_getaffinity(0)))
     x, w = synthetic.gemm_inputs(N=N, K=K, seed=0)
     oracle.gemm_bf16(x[:1], w[:16], threads)  # load the library
-    steps, t0 = 0, time.perf_counter()
-    while True:
-        for M in MS:
-            oracle.gemm_bf16(x[:M], w, threads)
-        steps += 1
-        el = time.perf_counter() - t0
-        if el >= budget_s or steps >= 200:
-            break
-    per_step = el / steps
-    gbs = sum(algorithmic_bytes(M) for M in MS) / per_step / 1e9
-    return {"value": round(gbs, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
+    step_bytes = sum(algorithmic_bytes(M) for M in MS)
+
+    def run(nthreads, budget):
+        steps, t0 = 0, time.perf_counter()
+        while True:
+            for M in MS:
+                oracle.gemm_bf16(x[:M], w, nthreads)
+            steps += 1
+            el = time.perf_counter() - t0
+            if el >= budget or steps >= 200:
+                return steps, el
+
+    steps, el = run(threads, budget_s)
+    steps1, el1 = run(1, budget_s / 3)
+    per_step, per_step1 = el / steps, el1 / steps1
+    return {"value": round(step_bytes / per_step / 1e9, 4), "unit": "GB/s", "cores": threads,
+            "kind": "oracle",
             "sample": f"{steps} steps of the M=1,2,4,8,16 sweep on one weight "
-                      f"({el:.1f} s, {per_step * 1e3:.1f} ms/step)"}
+                      f"({el:.1f} s, {per_step * 1e3:.1f} ms/step)",
+            "value_1_thread": round(step_bytes / per_step1 / 1e9, 4),
+            "sample_1_thread": f"{steps1} steps ({el1:.1f} s, {per_step1 * 1e3:.1f} ms/step)",
+            "cpu_model": _cpu_model()}
 
 
 def epilogue_timing(sk, synthetic, dev, stream, reps: int = 50):
