@@ -160,7 +160,8 @@ int skinny_gemm_bf16_publish(const void *x, const void *W, void *y, int M,
 
 /* A launch of the layer ring (skinny_gemm_bf16_ring_launch).
  *   gemm        the per-tile launch shape, splits = 1: DOT2 (rows 2, 4 or 8,
- *               chunks 1, 2, 4; waves = ceil(K / (512 chunks)) <= 8) or MFMA
+ *               chunks 1, 2, 4; waves = ceil(K / (512 chunks)) <= 8, or up to
+ *               16 for the register-light variants) or MFMA
  *               (rows 16, 32, 64; chunks 1..16; accs 1 or 2; waves =
  *               rows / 16 * ceil(K / (32 chunks)) <= 16, <= 8 at 16 chunks)
  *               or MFMA_LDS (as MFMA with chunks 2..16, and the staging

@@ -74,13 +74,13 @@ struct Dot2Args {
 // weights of the next tile into `next`, then the products with `cur`, the
 // reductions and the store.  Returns false after the workgroup's last tile.
 // P selects the LDS buffer.
-template <int ROWS, int CHUNKS, int MT, int P>
+template <int ROWS, int CHUNKS, int MT, int WAVES, int P>
 __device__ __forceinline__ bool dot2_ring_tile(const RingItems &items, const Dot2Args &a,
                                                const RingWalk &walk, int &s, int &sub,
                                                u32x4 (&cur)[ROWS][CHUNKS],
                                                u32x4 (&next)[ROWS][CHUNKS],
                                                u32x4 (&xv)[MT][CHUNKS],
-                                               float (&red)[2][kDot2MaxThreads / 64][ROWS * MT],
+                                               float (&red)[2][WAVES][ROWS * MT],
                                                int lane, int wave, int waves, int k0) {
   const int K = a.K;
   const int item = walk.item(s);
@@ -145,15 +145,17 @@ __device__ __forceinline__ bool dot2_ring_tile(const RingItems &items, const Dot
   return more;
 }
 
-template <int ROWS, int CHUNKS, int MT>
-__global__ __launch_bounds__(kDot2MaxThreads) void gemm_dot2_ring_kernel(
+// THREADS: the launch bound, 512, or 1024 for the variants whose registers
+// fit 16 waves (long K at one chunk per wave).
+template <int ROWS, int CHUNKS, int MT, int THREADS>
+__global__ __launch_bounds__(THREADS) void gemm_dot2_ring_kernel(
     RingItems items, int M, int N, int K, RingWalk walk, int kw) {
   const int lane = threadIdx.x & 63;
   const int wave = wave_index();
   const int waves = blockDim.x >> 6;
   const Dot2Args a{M, N, K};
   const int k0 = wave * kw + lane * 8;
-  __shared__ float red[2][kDot2MaxThreads / 64][ROWS * MT];
+  __shared__ float red[2][THREADS / 64][ROWS * MT];
 
   // gridDim.x <= walk.segs, so every workgroup has a first tile.
   int s = blockIdx.x, sub = 0;
@@ -161,11 +163,11 @@ __global__ __launch_bounds__(kDot2MaxThreads) void gemm_dot2_ring_kernel(
   load_weights<ROWS, CHUNKS>(wa, items.w[walk.item(s)] + (size_t)walk.block(s, 0) * ROWS * K,
                              (unsigned)(ROWS * K * 2), K, k0);
   for (;;) {
-    if (!dot2_ring_tile<ROWS, CHUNKS, MT, 0>(items, a, walk, s, sub, wa, wb, xv, red, lane, wave,
-                                              waves, k0))
+    if (!dot2_ring_tile<ROWS, CHUNKS, MT, THREADS / 64, 0>(items, a, walk, s, sub, wa, wb, xv,
+                                                            red, lane, wave, waves, k0))
       break;
-    if (!dot2_ring_tile<ROWS, CHUNKS, MT, 1>(items, a, walk, s, sub, wb, wa, xv, red, lane, wave,
-                                              waves, k0))
+    if (!dot2_ring_tile<ROWS, CHUNKS, MT, THREADS / 64, 1>(items, a, walk, s, sub, wb, wa, xv,
+                                                            red, lane, wave, waves, k0))
       break;
   }
 }
@@ -173,45 +175,57 @@ __global__ __launch_bounds__(kDot2MaxThreads) void gemm_dot2_ring_kernel(
 using Dot2RingKernel = void (*)(RingItems, int, int, int, RingWalk, int);
 
 // Register budget per lane: two weight buffers 8 * ROWS * CHUNKS,
-// activations 4 * MT * CHUNKS, sums ROWS * MT.
-constexpr bool dot2_ring_fits(int rows, int chunks, int mt) {
-  return 8 * rows * chunks + 4 * mt * chunks + rows * mt <= 160;
+// activations 4 * MT * CHUNKS, sums ROWS * MT: at most 160 for 8 waves, 112
+// for the 16-wave form (128 registers a lane, less the addresses).
+constexpr int dot2_ring_regs(int rows, int chunks, int mt) {
+  return 8 * rows * chunks + 4 * mt * chunks + rows * mt;
 }
 
-template <int R, int C, int T>
+template <int R, int C, int T, int THREADS>
 constexpr Dot2RingKernel dot2_ring_variant() {
-  if constexpr (dot2_ring_fits(R, C, T)) return gemm_dot2_ring_kernel<R, C, T>;
-  else return nullptr;
+  if constexpr (dot2_ring_regs(R, C, T) <= (THREADS > 512 ? 112 : 160))
+    return gemm_dot2_ring_kernel<R, C, T, THREADS>;
+  else
+    return nullptr;
 }
 
-template <int R, int C>
+template <int R, int C, int THREADS>
 Dot2RingKernel dot2_ring_pick_mt(int mt) {
   switch (mt) {
-    case 1: return dot2_ring_variant<R, C, 1>();
-    case 2: return dot2_ring_variant<R, C, 2>();
-    case 4: return dot2_ring_variant<R, C, 4>();
-    case 8: return dot2_ring_variant<R, C, 8>();
-    case 16: return dot2_ring_variant<R, C, 16>();
+    case 1: return dot2_ring_variant<R, C, 1, THREADS>();
+    case 2: return dot2_ring_variant<R, C, 2, THREADS>();
+    case 4: return dot2_ring_variant<R, C, 4, THREADS>();
+    case 8: return dot2_ring_variant<R, C, 8, THREADS>();
+    case 16: return dot2_ring_variant<R, C, 16, THREADS>();
   }
   return nullptr;
 }
 
-template <int R>
+template <int R, int THREADS>
 Dot2RingKernel dot2_ring_pick_chunks(int chunks, int mt) {
   switch (chunks) {
-    case 1: return dot2_ring_pick_mt<R, 1>(mt);
-    case 2: return dot2_ring_pick_mt<R, 2>(mt);
-    case 4: return dot2_ring_pick_mt<R, 4>(mt);
+    case 1: return dot2_ring_pick_mt<R, 1, THREADS>(mt);
+    case 2: return dot2_ring_pick_mt<R, 2, THREADS>(mt);
+    case 4: return dot2_ring_pick_mt<R, 4, THREADS>(mt);
   }
   return nullptr;
 }
 
-Dot2RingKernel dot2_ring_pick(int rows, int chunks, int mt) {
+template <int THREADS>
+Dot2RingKernel dot2_ring_pick_rows(int rows, int chunks, int mt) {
   switch (rows) {
-    case 2: return dot2_ring_pick_chunks<2>(chunks, mt);
-    case 4: return dot2_ring_pick_chunks<4>(chunks, mt);
-    case 8: return dot2_ring_pick_chunks<8>(chunks, mt);
+    case 2: return dot2_ring_pick_chunks<2, THREADS>(chunks, mt);
+    case 4: return dot2_ring_pick_chunks<4, THREADS>(chunks, mt);
+    case 8: return dot2_ring_pick_chunks<8, THREADS>(chunks, mt);
   }
+  return nullptr;
+}
+
+// The variant for a launch of `waves` waves: the 8-wave form up to 8 waves,
+// the 16-wave form beyond.
+Dot2RingKernel dot2_ring_pick(int rows, int chunks, int mt, int waves) {
+  if (waves <= kDot2MaxThreads / 64) return dot2_ring_pick_rows<kDot2MaxThreads>(rows, chunks, mt);
+  if (waves <= 16) return dot2_ring_pick_rows<1024>(rows, chunks, mt);
   return nullptr;
 }
 
@@ -441,8 +455,8 @@ size_t stage_pieces(int chunks) {
 
 }  // namespace
 
-bool ring_variant_exists(int rows, int chunks, int mt) {
-  return dot2_ring_pick(rows, chunks, mt) != nullptr;
+bool ring_variant_exists(int rows, int chunks, int mt, int waves) {
+  return dot2_ring_pick(rows, chunks, mt, waves) != nullptr;
 }
 
 bool mfma_ring_variant_exists(int chunks, int accs, bool staged) {
@@ -481,7 +495,8 @@ hipError_t launch_gemm_ring(const RingItems &items, int count, int M, int N, int
                        dim3(r.workgroups), dim3(64 * l.waves), mfma_ring_lds_bytes(l), stream,
                        items, M, N, K, walk, l.rows / kTileN, kMfmaK * l.chunks);
   } else {
-    hipLaunchKernelGGL(dot2_ring_pick(l.rows, l.chunks, dot2_token_tile(M)), dim3(r.workgroups),
+    hipLaunchKernelGGL(dot2_ring_pick(l.rows, l.chunks, dot2_token_tile(M), l.waves),
+                       dim3(r.workgroups),
                        dim3(64 * l.waves), 0, stream, items, M, N, K, walk, kDot2K * l.chunks);
   }
   return hipGetLastError();

@@ -78,7 +78,7 @@ constexpr size_t kMaxDynamicLds = 160 * 1024;  // all of a gfx950 CU's LDS
 bool dot2_variant_exists(int rows, int chunks, int mt);
 int dot2_token_tile(int M);  // smallest compiled token count >= M, 0 if none
 int dot2_max_waves();        // waves per DOT2 workgroup (launch bound)
-bool ring_variant_exists(int rows, int chunks, int mt);       // DOT2 ring
+bool ring_variant_exists(int rows, int chunks, int mt, int waves);  // DOT2 ring (<= 16 waves)
 bool mfma_ring_variant_exists(int chunks, int accs, bool staged);  // MFMA ring
 int mfma_ring_max_waves(int chunks);
 size_t mfma_ring_lds_bytes(const skinny_launch &l);  // dynamic LDS of an MFMA ring launch

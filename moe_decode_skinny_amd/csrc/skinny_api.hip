@@ -267,14 +267,15 @@ static int ring_check(int count, int M, int N, int K, const skinny_ring_launch &
     if (l.accs != 1) return fail(SKINNY_EUNSUPPORTED, "DOT2 launch has accs=1");
     if (l.rows <= 0 || N % l.rows)
       return fail(SKINNY_EUNSUPPORTED, "N=%d is not a multiple of rows=%d", N, l.rows);
-    if (!ring_variant_exists(l.rows, l.chunks, dot2_token_tile(M)))
-      return fail(SKINNY_EUNSUPPORTED, "no ring kernel with rows=%d chunks=%d tokens=%d",
-                  l.rows, l.chunks, dot2_token_tile(M));
     const long kw = (long)kDot2K * l.chunks;
     const int need = ceil_div(K, kw);
-    if (l.waves != need || l.waves < 1 || l.waves > dot2_max_waves())
-      return fail(SKINNY_EUNSUPPORTED, "K=%d at kw=%ld needs %d waves (given %d, at most %d)",
-                  K, kw, need, l.waves, dot2_max_waves());
+    if (l.waves != need || l.waves < 1 || l.waves > 16)
+      return fail(SKINNY_EUNSUPPORTED, "K=%d at kw=%ld needs %d waves (given %d, at most 16)",
+                  K, kw, need, l.waves);
+    if (!ring_variant_exists(l.rows, l.chunks, dot2_token_tile(M), l.waves))
+      return fail(SKINNY_EUNSUPPORTED, "no ring kernel with rows=%d chunks=%d tokens=%d for %d "
+                  "waves (more than 8 waves: only the register-light variants)", l.rows,
+                  l.chunks, dot2_token_tile(M), l.waves);
   } else {
     return fail(SKINNY_EUNSUPPORTED, "unknown path %d", l.path);
   }
@@ -316,9 +317,11 @@ static const RingEntry kRingTable[] = {
     {512, 8192, 2, 2, DOT2_RING(4, 4, 2, 4, 2048)},
     {512, 8192, 3, 4, DOT2_RING(8, 2, 4, 2, 1024)},
     {512, 8192, 5, 8, DOT2_RING(8, 2, 4, 16, 256)},
+    {512, 8192, 9, 16, DOT2_RING(16, 1, 2, 16, 256)},
     // full pooler
     {4096, 8192, 1, 2, DOT2_RING(4, 4, 2, 8, 256)},
     {4096, 8192, 3, 8, DOT2_RING(8, 2, 4, 16, 256)},
+    {4096, 8192, 9, 16, DOT2_RING(16, 1, 2, 16, 1024)},
 };
 #undef DOT2_RING
 #undef LDS_RING

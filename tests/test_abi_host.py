@@ -157,9 +157,9 @@ def test_ring_unsupported_shapes_and_reasons(sk):
         sk.skinny_ring_choose(1, 1024, 4096, 65)
     with pytest.raises(ValueError, match="M=17"):
         sk.skinny_ring_choose(17, 1024, 4096, 1)
-    # 16 tokens at K = 8192 need 16 waves of one chunk: more than a workgroup
+    # 16 tokens at K = 16384: 32 waves of one chunk, more than a workgroup
     with pytest.raises(ValueError, match="no ring launch"):
-        sk.skinny_ring_choose(16, 4096, 8192, 2)
+        sk.skinny_ring_choose(16, 4096, 16384, 2)
 
 
 def _ring_lib(sk):

@@ -143,7 +143,7 @@ def _walks(groups, count):
 
 
 @pytest.mark.parametrize("M,N,K", [(1, 64, 1024), (3, 48, 1000), (7, 128, 2056), (16, 32, 520),
-                                   (4, 16, 8), (12, 64, 1000)])
+                                   (4, 16, 8), (12, 64, 1000), (16, 32, 8000), (5, 64, 6000)])
 def test_ring_every_launch_and_walk(gpu_lib, M, N, K):
     """Every compiled ring variant the validator accepts on small ragged
     shapes, under several tile walks (segment length and workgroup count)."""
@@ -183,8 +183,9 @@ def test_ring_max_count(gpu_lib):
 
 @pytest.mark.parametrize("M,N,K,count", [(1, 8192, 1024, 4), (8, 8192, 1024, 3),
                                          (16, 8192, 1024, 2), (1, 512, 8192, 4),
-                                         (8, 512, 8192, 4), (1, 4096, 8192, 2),
-                                         (8, 4096, 8192, 2)])
+                                         (8, 512, 8192, 4), (16, 512, 8192, 3),
+                                         (1, 4096, 8192, 2), (8, 4096, 8192, 2),
+                                         (16, 4096, 8192, 2)])
 def test_ring_shard_shapes(gpu_lib, M, N, K, count):
     """The o_proj and pooler shard shapes."""
     xs, ws = _items(count, N, K, seed=400)
