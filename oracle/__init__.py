@@ -27,6 +27,7 @@ _u16p = np.ctypeslib.ndpointer(dtype=np.uint16, flags="C_CONTIGUOUS")
 _u8p = np.ctypeslib.ndpointer(dtype=np.uint8, flags="C_CONTIGUOUS")
 _f64p = np.ctypeslib.ndpointer(dtype=np.float64, flags="C_CONTIGUOUS")
 _i32p = np.ctypeslib.ndpointer(dtype=np.int32, flags="C_CONTIGUOUS")
+_f32p = np.ctypeslib.ndpointer(dtype=np.float32, flags="C_CONTIGUOUS")
 
 
 def _load():
@@ -79,6 +80,11 @@ def load_library(path: str):
         _u16p, ctypes.c_int, ctypes.c_int, _u16p, ctypes.c_int, ctypes.c_int, ctypes.c_int,
         ctypes.c_void_p, ctypes.c_void_p]
     lib.oracle_mailbox_publish.restype = ctypes.c_int
+    lib.oracle_dual_norm.argtypes = [
+        _u16p, _f32p, ctypes.c_void_p, ctypes.c_double, ctypes.c_double, ctypes.c_void_p,
+        ctypes.c_double, _u16p, _u16p, ctypes.c_double, ctypes.c_double, ctypes.c_int,
+        ctypes.c_int, _u16p, ctypes.c_void_p]
+    lib.oracle_dual_norm.restype = None
     return lib
 
 
@@ -256,3 +262,36 @@ def mailbox_publish(y_bits, mailbox, rank: int, stage_state=None, ticket=None):
     if st is not None and (st.dtype != np.int32 or st.shape != (2,) or not st.flags.c_contiguous):
         raise ValueError("stage_state must be a contiguous int32 [2] array")
     return lib.oracle_mailbox_publish(y, M, width, mailbox, tp, rank, capacity, _ptr(st), _ptr(tk))
+
+
+# ----------------------------------------------------------------- dual norm
+def dual_norm(partial_bits, stream, post_w_bits, post_gc: float, post_eps: float, alpha,
+              beta_bits, next_w_bits, pre_gc: float, pre_eps: float):
+    """The single-GPU dual norm after o_proj (a reading: see the C source).
+
+    partial bf16 bits [M, H]; stream float32 [M, H] (a new updated array is
+    returned, the input is not modified); post_w bf16 bits [H] or None;
+    alpha a float (scalar) or bf16 bits [H]; beta, next_w bf16 bits [H].
+    The FP32 scalars are taken as the FP32 numbers the library receives.
+    Returns (out bf16 bits [M, H], updated stream float32 [M, H], h bf16 bits)."""
+    lib = _load()
+    p = np.ascontiguousarray(partial_bits, dtype=np.uint16)
+    M, H = p.shape
+    st = np.array(stream, dtype=np.float32, copy=True, order="C")
+    if st.shape != (M, H):
+        raise ValueError("stream must be [M, H]")
+    pw = None if post_w_bits is None else np.ascontiguousarray(post_w_bits, dtype=np.uint16)
+    if np.isscalar(alpha):
+        al, a_s = None, f32(float(alpha))
+    else:
+        al, a_s = np.ascontiguousarray(alpha, dtype=np.uint16), 0.0
+    be = np.ascontiguousarray(beta_bits, dtype=np.uint16)
+    nw = np.ascontiguousarray(next_w_bits, dtype=np.uint16)
+    for name, v in (("post_w", pw), ("alpha", al), ("beta", be), ("next_w", nw)):
+        if v is not None and v.shape != (H,):
+            raise ValueError(f"{name} must be [H]")
+    out = np.empty((M, H), dtype=np.uint16)
+    h = np.empty((M, H), dtype=np.uint16)
+    lib.oracle_dual_norm(p, st, _ptr(pw), f32(post_gc), f32(post_eps), _ptr(al), a_s, be, nw,
+                         f32(pre_gc), f32(pre_eps), M, H, out, _ptr(h))
+    return out, st, h

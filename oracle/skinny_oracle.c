@@ -30,6 +30,11 @@
  *               description (BF16 edge layers: -0.0 is the mailbox sentinel,
  *               so publishers store -0.0 as +0.0) and compile_gather (the
  *               mailbox is BF16 [3, tp, capacity, hidden / tp]).
+ *   [dual]      page "...specialized_decode.cutedsl.oproj.batt",
+ *               AttentionBoundary: the partial goes through post_attn_norm,
+ *               a gated add into the FP32 residual stream (in place, with
+ *               the connection's alpha and beta) and pre_ffn_norm into the
+ *               BF16 output; the post norm may have no weight.
  *
  * Readings where the pages are silent (each also listed in the design notes):
  *   - block scale: sf = e4m3(global_scale * amax / 6), 6 being the largest
@@ -46,6 +51,15 @@
  * and [1] the word a publish sets to it (ACTIVE_STAGE); a ticket holds
  * stage << 16 and the stage is its upper 16 bits; a stage outside 0..2
  * publishes nothing. */
+
+/* Readings for [dual] (the dual norm's body and constants are not printed;
+ * PARITY UNPINNED by the pages beyond the order of its steps): both norms are
+ * the pooler page's RMSNorm with their own eps and gain center, rounded to
+ * bfloat16 once; a post norm without a weight scales by 1; the gated add is
+ * stream = f32(alpha * stream + beta * h) with h the bfloat16 post-norm
+ * output, alpha a scalar or per channel, beta per channel (bfloat16
+ * parameters), one rounding to binary32 from binary64; the pre norm reads
+ * the updated stream. */
 
 /* ---------------------------------------------------------------- bfloat16 */
 
@@ -290,4 +304,45 @@ int oracle_mailbox_publish(const uint16_t *y, int M, int width, uint16_t *mailbo
     }
   if (!ticket) stage_state[1] = stage;
   return stage;
+}
+
+/* -------------------------------------------------------------- dual norm */
+
+/* [dual] For each row m of partial [M, H] (bf16) and stream [M, H] (binary32,
+ * updated in place):
+ *   h_j      = bf16(p_j / sqrt(mean(p^2) + post_eps) * g_j),
+ *              g_j = post_w_j + post_gc, or 1 without a post weight
+ *   stream_j = f32(a_j * stream_j + beta_j * h_j),  a_j = alpha_j or alpha_scalar
+ *   out_j    = bf16(s_j / sqrt(mean(s^2) + pre_eps) * (next_w_j + pre_gc)),
+ *              s = the updated stream row
+ * h_out (optional) receives h.  Weights, alpha and beta are bf16 [H]. */
+void oracle_dual_norm(const uint16_t *partial, float *stream, const uint16_t *post_w,
+                      double post_gc, double post_eps, const uint16_t *alpha,
+                      double alpha_scalar, const uint16_t *beta, const uint16_t *next_w,
+                      double pre_gc, double pre_eps, int M, int H, uint16_t *out,
+                      uint16_t *h_out) {
+  for (int m = 0; m < M; ++m) {
+    const uint16_t *p = partial + (size_t)m * H;
+    float *st = stream + (size_t)m * H;
+    double ss = 0.0;
+    for (int j = 0; j < H; ++j) {
+      double v = oracle_bf16_value(p[j]);
+      ss += v * v;
+    }
+    double inv = 1.0 / sqrt(ss / H + post_eps);
+    for (int j = 0; j < H; ++j) {
+      double g = post_w ? oracle_bf16_value(post_w[j]) + post_gc : 1.0;
+      uint16_t h = oracle_bf16_round(oracle_bf16_value(p[j]) * inv * g);
+      if (h_out) h_out[(size_t)m * H + j] = h;
+      double a = alpha ? oracle_bf16_value(alpha[j]) : alpha_scalar;
+      double v = a * (double)st[j] + oracle_bf16_value(beta[j]) * oracle_bf16_value(h);
+      st[j] = (float)v;
+    }
+    double ss2 = 0.0;
+    for (int j = 0; j < H; ++j) ss2 += (double)st[j] * (double)st[j];
+    double inv2 = 1.0 / sqrt(ss2 / H + pre_eps);
+    for (int j = 0; j < H; ++j)
+      out[(size_t)m * H + j] = oracle_bf16_round(
+          (double)st[j] * inv2 * (oracle_bf16_value(next_w[j]) + pre_gc));
+  }
 }

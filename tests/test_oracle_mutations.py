@@ -17,6 +17,7 @@ from tests import test_oracle_formats as F
 from tests import test_oracle_gemm as G
 from tests import test_oracle_norm as Nm
 from tests import test_oracle_publish as Pb
+from tests import test_oracle_dual_norm as Dn
 
 SRC = os.path.join(os.path.dirname(oracle.__file__), "skinny_oracle.c")
 
@@ -50,6 +51,17 @@ MUTATIONS = [
     ("publish_ticket_low_half", "(int)((uint32_t)ticket[0] >> 16)", "(int)((uint32_t)ticket[0] & 0xFFFF)"),
     ("publish_sets_next_stage", "if (!ticket) stage_state[1] = stage;", "if (!ticket) stage_state[0] = stage;"),
     ("publish_word_with_ticket", "if (!ticket) stage_state[1] = stage;", "if (stage_state) stage_state[1] = stage;"),
+    ("dual_drops_beta_term", "a * (double)st[j] + oracle_bf16_value(beta[j]) * oracle_bf16_value(h);",
+     "a * (double)st[j];"),
+    ("dual_alpha_on_h", "a * (double)st[j] + oracle_bf16_value(beta[j]) * oracle_bf16_value(h);",
+     "(double)st[j] + oracle_bf16_value(beta[j]) * a * oracle_bf16_value(h);"),
+    ("dual_pre_uses_post_eps", "double inv2 = 1.0 / sqrt(ss2 / H + pre_eps);",
+     "double inv2 = 1.0 / sqrt(ss2 / H + post_eps);"),
+    ("dual_pre_drops_gain_center", "(oracle_bf16_value(next_w[j]) + pre_gc));",
+     "oracle_bf16_value(next_w[j]));"),
+    ("dual_gc_without_weight", "post_w ? oracle_bf16_value(post_w[j]) + post_gc : 1.0;",
+     "post_w ? oracle_bf16_value(post_w[j]) + post_gc : 1.0 + post_gc;"),
+    ("dual_h_not_rounded", "st[j] = (float)v;", "st[j] = (float)(a * (double)st[j] + oracle_bf16_value(beta[j]) * oracle_bf16_value(p[j]) * inv * g);"),
 ]
 
 # The pins (test functions that raise AssertionError on a mismatch).
@@ -81,6 +93,12 @@ BATTERY = [
     lambda: [Pb.test_publish_outside_stages_writes_nothing(s, t) for s, t in
              [([3, 7], None), ([-1, 7], None), (None, [3 << 16]), (None, [0x7FFF0000])]],
     lambda: [Pb.test_publish_properties(k) for k in range(6)],
+    Dn.test_identity_gate_keeps_stream_and_normalises_it,
+    Dn.test_beta_gate_replaces_stream_with_post_norm,
+    Dn.test_post_norm_without_weight_one_hot,
+    lambda: [Dn.test_gated_add_exact_small_numbers(a) for a in (False, True)],
+    Dn.test_pre_norm_reads_the_updated_stream,
+    Dn.test_rows_are_independent,
 ]
 
 
