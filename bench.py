@@ -185,12 +185,22 @@ def epilogue_timing(sk, synthetic, dev, stream, reps: int = 50):
     gemm_us = timed([lambda w=w: sk.skinny_gemm_bf16(x, w, y, 0) for w in ring])
     norm_us = timed([lambda: sk.skinny_rmsnorm_nvfp4(y, nw, 1.0, 1e-6, gs, a, sf)] * 16)
     del ring
+    # The dual norm after the o_proj shard (H = 8192) at M = 8.
+    H = 8192
+    part = torch.randn((M, H), device=dev).to(torch.bfloat16)
+    resid = torch.randn((M, H), device=dev)
+    vecs = [torch.randn(H, device=dev).to(torch.bfloat16) for _ in range(4)]
+    dout = torch.empty((M, H), dtype=torch.bfloat16, device=dev)
+    dual_us = timed([lambda: sk.skinny_dual_norm(part, resid, vecs[0], 1.0, 1e-6, vecs[1],
+                                                 vecs[2], vecs[3], 1.0, 1e-6, dout)] * 16)
     gbytes = algorithmic_bytes(M, N2, K2)
     return {"workload": "full pooler GEMM M=8 N=4096 K=8192 -> RMSNorm -> NVFP4 [8, 4096]",
             "gemm_us_per_call": round(gemm_us, 3),
             "gemm_GBs": round(gbytes / (gemm_us * 1e-6) / 1e9, 1),
             "gemm_launch": dict(sk.skinny_choose(M, N2, K2, 0)._asdict()),
-            "norm_nvfp4_us_per_call": round(norm_us, 3)}
+            "norm_nvfp4_us_per_call": round(norm_us, 3),
+            "dual_norm_us_per_call": round(dual_us, 3),
+            "dual_norm_workload": "M=8, H=8192 (o_proj output), post weight, per-channel alpha"}
 
 
 def ring_timing(sk, synthetic, dev, stream, ring, reps: int = 10):

@@ -243,6 +243,31 @@ int skinny_rmsnorm_nvfp4(const void *r, const void *norm_w, float gain_center,
 int skinny_rmsnorm_bf16(const void *r, const void *norm_w, float gain_center,
                         float eps, void *y, int M, int P, void *stream);
 
+/* The single-GPU dual norm after o_proj (oproj.batt page, AttentionBoundary:
+ * post_attn_norm, gated add into the FP32 residual stream in place,
+ * pre_ffn_norm into a BF16 output; the multi-GPU all-reduce before it is the
+ * identity on one GPU).  The pages print neither the kernel nor its
+ * constants; this computes the reading
+ *   h_j        = bf16( p_j / sqrt(mean(p^2) + post_eps) * g_j ),
+ *                g_j = post_w_j + post_gain_center, or 1 if post_w is NULL
+ *   residual_j = f32( a_j * residual_j + beta_j * h_j ),
+ *                a_j = alpha_j, or alpha_scalar if alpha is NULL
+ *   out_j      = bf16( s_j / sqrt(mean(s^2) + pre_eps) * (next_w_j + pre_gain_center) )
+ * per row, s being the updated residual row (binary64 arithmetic, one
+ * rounding per narrowing).
+ *   partial      bf16 [M, H]
+ *   residual     float [M, H], read and written in place
+ *   post_w       bf16 [H] or NULL; alpha bf16 [H] or NULL; beta, next_w bf16 [H]
+ *   out          bf16 [M, H]
+ *   M >= 1 rows; H > 0, H % 16 == 0; every array 16-byte aligned
+ * partial, residual and out must not overlap, nor a weight the residual or
+ * out.  Errors: SKINNY_EINVAL, SKINNY_ENOTINIT, SKINNY_ELAUNCH. */
+int skinny_dual_norm(const void *partial, float *residual, const void *post_w,
+                     float post_gain_center, float post_eps, const void *alpha,
+                     float alpha_scalar, const void *beta, const void *next_w,
+                     float pre_gain_center, float pre_eps, void *out, int M, int H,
+                     void *stream);
+
 /* The reason for the last non-OK status on this thread ("" if none). */
 const char *skinny_last_error(void);
 

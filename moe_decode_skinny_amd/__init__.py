@@ -12,7 +12,8 @@ Same names as the C ABI:
   skinny_gemm_unsupported, skinny_launch_unsupported, skinny_gemm_bf16_publish,
   skinny_gemm_bf16_ring,
   skinny_gemm_bf16_ring_launch, skinny_ring_choose, skinny_ring_launch_unsupported,
-  skinny_rmsnorm_nvfp4, skinny_rmsnorm_bf16, skinny_last_error, skinny_version
+  skinny_rmsnorm_nvfp4, skinny_rmsnorm_bf16, skinny_dual_norm, skinny_last_error,
+  skinny_version
 Status codes map to exceptions as on the unpooler page (Unpooler.run /
 Unpooler.unsupported): EINVAL and EUNSUPPORTED raise ValueError, the others
 RuntimeError.
@@ -38,7 +39,7 @@ SKINNY_PATH_MFMA_LDS = 2
 
 if not os.path.exists(LIB_PATH):
     raise ImportError(
-        f"{LIB_PATH} is not built; run `python -m moe_decode_skinny_amd.build` "
+        f"{LIB_PATH} is not built; run `python moe_decode_skinny_amd/build.py` "
         "(there is no CPU fallback)")
 
 _lib = ctypes.CDLL(LIB_PATH)
@@ -108,6 +109,7 @@ _sig = {
     "skinny_ring_launch_unsupported": ([_i, _i, _i, _i, ctypes.POINTER(_CRingLaunch)], _i),
     "skinny_rmsnorm_nvfp4": ([_vp, _vp, _f, _f, _vp, _vp, _vp, _i, _i, _vp], _i),
     "skinny_rmsnorm_bf16": ([_vp, _vp, _f, _f, _vp, _i, _i, _vp], _i),
+    "skinny_dual_norm": ([_vp, _vp, _vp, _f, _f, _vp, _f, _vp, _vp, _f, _f, _vp, _i, _i, _vp], _i),
     "skinny_last_error": ([], ctypes.c_char_p),
     "skinny_version": ([], _i),
 }
@@ -323,12 +325,49 @@ def skinny_rmsnorm_bf16(r, norm_w, gain_center: float, eps: float, y, stream=Non
     return y
 
 
+def skinny_dual_norm(partial, residual, post_w, post_gain_center: float, post_eps: float,
+                     alpha, beta, next_w, pre_gain_center: float, pre_eps: float, out,
+                     stream=None):
+    """The dual norm after o_proj: post norm of partial [M, H] (bf16), gated add
+    into residual [M, H] (float32, in place), pre norm into out [M, H] (bf16).
+    post_w: bf16 [H] or None; alpha: a float or bf16 [H]; beta, next_w: bf16
+    [H].  Returns out."""
+    import torch
+
+    pp = _dev_tensor(partial, "partial", torch.bfloat16)
+    rp = _dev_tensor(residual, "residual", torch.float32)
+    op = _dev_tensor(out, "out", torch.bfloat16)
+    if partial.dim() != 2 or tuple(residual.shape) != tuple(partial.shape) or \
+            tuple(out.shape) != tuple(partial.shape):
+        raise ValueError("partial, residual and out must all be [M, H]")
+    M, H = partial.shape
+    vecs = {}
+    for name, t in (("post_w", post_w), ("beta", beta), ("next_w", next_w)):
+        if t is None and name == "post_w":
+            vecs[name] = None
+            continue
+        vecs[name] = _dev_tensor(t, name, torch.bfloat16)
+        if tuple(t.shape) != (H,):
+            raise ValueError(f"{name} must be [H]")
+    if isinstance(alpha, torch.Tensor):
+        ap, a_s = _dev_tensor(alpha, "alpha", torch.bfloat16), 0.0
+        if tuple(alpha.shape) != (H,):
+            raise ValueError("alpha must be a float or [H]")
+    else:
+        ap, a_s = None, float(alpha)
+    _check(_lib.skinny_dual_norm(pp, rp, vecs["post_w"], float(post_gain_center),
+                                 float(post_eps), ap, a_s, vecs["beta"], vecs["next_w"],
+                                 float(pre_gain_center), float(pre_eps), op, M, H,
+                                 _stream(stream, partial.device)))
+    return out
+
+
 __all__ = [
     "Launch", "RingLaunch", "init", "skinny_init", "skinny_gemm_bf16", "skinny_gemm_bf16_launch",
     "skinny_choose", "skinny_gemm_unsupported", "skinny_launch_unsupported",
     "skinny_gemm_bf16_publish", "skinny_gemm_bf16_ring", "skinny_gemm_bf16_ring_launch",
     "skinny_ring_choose",
     "skinny_ring_launch_unsupported",
-    "skinny_rmsnorm_nvfp4", "skinny_rmsnorm_bf16", "skinny_last_error", "skinny_version",
+    "skinny_rmsnorm_nvfp4", "skinny_rmsnorm_bf16", "skinny_dual_norm", "skinny_last_error", "skinny_version",
     "LIB_PATH",
 ]

@@ -64,6 +64,11 @@ hipError_t launch_gemm_ring(const RingItems &items, int count, int M, int N, int
                             const skinny_ring_launch &r, hipStream_t stream);
 hipError_t launch_split_reduce(const float *partials, uint16_t *y, int M, int N, int S,
                                const Publish &pub, hipStream_t stream);
+hipError_t launch_dual_norm(const uint16_t *partial, float *residual, const uint16_t *post_w,
+                            float post_gc, float post_eps, const uint16_t *alpha,
+                            float alpha_scalar, const uint16_t *beta, const uint16_t *next_w,
+                            float pre_gc, float pre_eps, uint16_t *out, int M, int H,
+                            hipStream_t stream);
 hipError_t launch_rmsnorm(const uint16_t *r, const uint16_t *w, float gain_center,
                           float eps, const float *global_scale, uint8_t *a,
                           uint8_t *a_sf, uint16_t *y, int M, int P, bool quant,

@@ -24,28 +24,12 @@
 // Readings (the norm/quant kernel body is not printed): the block scale is
 // e4m3(global_scale * amax / 6); the output scale is global_scale / dec(sf);
 // a negative value that rounds to zero keeps its sign.
-#include "internal.h"
+#include "norm_device.h"
 
 namespace skinny {
 namespace {
 
-constexpr int kNormThreads = 256;
-
-// binary64 -> bfloat16 bits, round to nearest even (finite inputs; overflow
-// gives infinity).
-__device__ __forceinline__ unsigned f64_to_bf16(double v) {
-  const unsigned long long u = (unsigned long long)__double_as_longlong(v);
-  const unsigned sign = (unsigned)(u >> 48) & 0x8000u;
-  const double a = fabs(v);
-  if (a < 0x1p-126) {                       // bfloat16 subnormals: step 2^-133
-    return sign | (unsigned)rint(a * 0x1p133);  // 128 -> smallest normal
-  }
-  unsigned long long b = u & 0x7fffffffffffffffull;
-  b += 0xfffffffffffull + ((b >> 45) & 1ull);   // keep 7 of 52 mantissa bits
-  const int exp = (int)(b >> 52) - 1023 + 127;
-  if (exp >= 255) return sign | 0x7f80u;
-  return sign | ((unsigned)exp << 7) | (unsigned)((b >> 45) & 0x7full);
-}
+using namespace norm;
 
 // |v| -> e4m3fn code, round to nearest even, saturating at 448 (0x7E).
 __device__ __forceinline__ unsigned e4m3_rn_satfinite(double v) {
@@ -76,17 +60,6 @@ __device__ __forceinline__ unsigned e2m1_rn_satfinite(double v) {
   return (signbit(v) ? 8u : 0u) | idx;
 }
 
-__device__ __forceinline__ void load16(const uint16_t *p, double (&v)[16]) {
-  const u32x4 a = *reinterpret_cast<const u32x4 *>(p);
-  const u32x4 b = *reinterpret_cast<const u32x4 *>(p + 8);
-  const unsigned u[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    v[2 * i] = (double)bf16_lo(u[i]);
-    v[2 * i + 1] = (double)bf16_hi(u[i]);
-  }
-}
-
 template <bool QUANT>
 __global__ __launch_bounds__(kNormThreads) void rmsnorm_kernel(
     const uint16_t *__restrict__ r, const uint16_t *__restrict__ w, float gain_center,
@@ -111,14 +84,8 @@ __global__ __launch_bounds__(kNormThreads) void rmsnorm_kernel(
 #pragma unroll
     for (int j = 0; j < 16; ++j) ss += v[j] * v[j];
   }
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) ss += __shfl_xor(ss, off);
   __shared__ double wave_ss[kNormThreads / 64];
-  if ((tid & 63) == 0) wave_ss[tid >> 6] = ss;
-  __syncthreads();
-  double total = wave_ss[0];
-#pragma unroll
-  for (int i = 1; i < kNormThreads / 64; ++i) total += wave_ss[i];
+  const double total = block_sum(ss, wave_ss);
   const double inv = 1.0 / sqrt(total / (double)P + (double)eps);
   const double gc = (double)gain_center;
   const double gs = QUANT ? (double)*global_scale : 0.0;

@@ -513,7 +513,7 @@ using namespace skinny;
 
 extern "C" {
 
-int skinny_version(void) { return 100; }
+int skinny_version(void) { return 101; }
 
 const char *skinny_last_error(void) { return g_error; }
 
@@ -625,6 +625,38 @@ int skinny_rmsnorm_nvfp4(const void *r, const void *norm_w, float gain_center, f
                          void *stream) {
   return norm_common(r, norm_w, gain_center, eps, global_scale, a, a_sf, nullptr, M, P,
                      true, stream);
+}
+
+int skinny_dual_norm(const void *partial, float *residual, const void *post_w,
+                     float post_gain_center, float post_eps, const void *alpha,
+                     float alpha_scalar, const void *beta, const void *next_w,
+                     float pre_gain_center, float pre_eps, void *out, int M, int H,
+                     void *stream) {
+  if (M < 1 || M > 65535) return fail(SKINNY_EINVAL, "M=%d: needs 1 <= M <= 65535", M);
+  if (H <= 0 || H % 16) return fail(SKINNY_EINVAL, "H=%d: needs H > 0 and H %% 16 == 0", H);
+  if (!partial || !residual || !beta || !next_w || !out)
+    return fail(SKINNY_EINVAL, "null pointer");
+  const void *ptrs[] = {partial, residual, post_w, alpha, beta, next_w, out};
+  for (const void *q : ptrs)
+    if (q && !aligned(q, 16)) return fail(SKINNY_EINVAL, "every array must be 16-byte aligned");
+  const size_t pb = 2ul * M * H, rb = 4ul * M * H, ob = 2ul * M * H, vb = 2ul * H;
+  if (overlap(out, ob, partial, pb) || overlap(out, ob, residual, rb) ||
+      overlap(residual, rb, partial, pb))
+    return fail(SKINNY_EINVAL, "partial, residual and out must not overlap");
+  const void *params[] = {post_w, alpha, beta, next_w};
+  for (const void *q : params)
+    if (q && (overlap(q, vb, residual, rb) || overlap(q, vb, out, ob)))
+      return fail(SKINNY_EINVAL, "a weight overlaps the residual or out");
+  int st = SKINNY_OK;
+  if (!current_state(&st)) return st;
+  hipError_t e = launch_dual_norm(
+      static_cast<const uint16_t *>(partial), residual, static_cast<const uint16_t *>(post_w),
+      post_gain_center, post_eps, static_cast<const uint16_t *>(alpha), alpha_scalar,
+      static_cast<const uint16_t *>(beta), static_cast<const uint16_t *>(next_w),
+      pre_gain_center, pre_eps, static_cast<uint16_t *>(out), M, H,
+      static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(SKINNY_ELAUNCH, "launch failed: %s", hipGetErrorString(e));
+  return SKINNY_OK;
 }
 
 int skinny_rmsnorm_bf16(const void *r, const void *norm_w, float gain_center, float eps,

@@ -278,3 +278,31 @@ def test_publish_reasons_without_device(sk):
     assert call() in (sk.SKINNY_EDEVICE, sk.SKINNY_ENOTINIT)
     assert call(stage=None, ticket=ticket) in (sk.SKINNY_EDEVICE, sk.SKINNY_ENOTINIT)
     assert call(launch=(0, 1, 1, 1, 1, 4)) in (sk.SKINNY_EDEVICE, sk.SKINNY_ENOTINIT)
+
+
+def test_dual_norm_reasons_without_device(sk):
+    lib = ctypes.CDLL(sk.LIB_PATH)
+    f = ctypes.c_float
+    lib.skinny_dual_norm.argtypes = [ctypes.c_void_p] * 3 + [f, f, ctypes.c_void_p, f] + [
+        ctypes.c_void_p] * 2 + [f, f, ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
+    M, H = 4, 256
+    p, r, pw, al, be, nw, o = 0x100000, 0x200000, 0x300000, 0x310000, 0x320000, 0x330000, 0x400000
+
+    def call(p=p, r=r, pw=pw, al=al, be=be, nw=nw, o=o, M=M, H=H):
+        return lib.skinny_dual_norm(p, r, pw, 1.0, 1e-6, al, 1.0, be, nw, 1.0, 1e-6, o, M, H,
+                                    None)
+
+    def bad(needle, **kw):
+        assert call(**kw) == sk.SKINNY_EINVAL, needle
+        assert needle in sk.skinny_last_error(), sk.skinny_last_error()
+
+    bad("H=100", H=100)
+    bad("M=0", M=0)
+    bad("null pointer", be=None)
+    bad("null pointer", r=None)
+    bad("16-byte aligned", pw=pw + 2)
+    bad("must not overlap", o=r + 16)
+    bad("must not overlap", r=p + 64)
+    bad("overlaps the residual or out", nw=r + 32)
+    assert call() in (sk.SKINNY_EDEVICE, sk.SKINNY_ENOTINIT)
+    assert call(pw=None, al=None) in (sk.SKINNY_EDEVICE, sk.SKINNY_ENOTINIT)
