@@ -19,6 +19,7 @@ average duration measured here from graph replays of that launch alone over
 the ring.  `ring` reports the same sweep through the layer-ring launch
 (skinny_gemm_bf16_ring: one persistent launch per M over the 60 layers, the
 next layer's weights in flight while one is finished), per item.
+`oproj` reports the o_proj shard (N=8192, K=1024) the same two ways.
 `cpu_baseline` times the oracle on the host for a bounded sample of the same
 workload.
 
@@ -240,6 +241,47 @@ def ring_timing(sk, synthetic, dev, stream, ring, reps: int = 10):
                         f"{RING}-layer weight ring", "per_m": out}
 
 
+def oproj_timing(sk, synthetic, dev, stream, reps: int = 10):
+    """The o_proj shard (N=8192, K=1024, 16 MiB of weights) on its own
+    60-layer ring: us per single call (graph of 60 calls) and per ring item
+    (one 60-item launch), M = 1..16."""
+    import torch
+
+    N2, K2 = 8192, 1024
+    ring = synthetic.device_weight_ring(RING, N2, K2, dev, base_seed=7000)
+
+    def timed(fn, per):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=stream):
+            fn()
+        g.replay()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            g.replay()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e3 / (reps * per)
+
+    out = {}
+    for M in MS:
+        xs = [synthetic.to_device(synthetic.gemm_inputs(N=16, K=K2, seed=950 + i)[0][:M], dev)
+              for i in range(RING)]
+        ys = [torch.empty((M, N2), dtype=torch.bfloat16, device=dev) for _ in range(RING)]
+        single = timed(lambda: [sk.skinny_gemm_bf16(x, w, y, 0) for x, w, y in zip(xs, ring, ys)],
+                       RING)
+        item = timed(lambda: sk.skinny_gemm_bf16_ring(xs, ring, ys), RING)
+        b = algorithmic_bytes(M, N2, K2)
+        out[str(M)] = {"us_per_call": round(single, 3),
+                       "pct_peak_call": round(100 * b / (single * 1e-6) / 1e9 / PEAK_GBS, 2),
+                       "ring_us_per_item": round(item, 3),
+                       "pct_peak_ring": round(100 * b / (item * 1e-6) / 1e9 / PEAK_GBS, 2)}
+    del ring
+    return {"workload": f"o_proj shard GEMM M=1,2,4,8,16, N=8192, K=1024, {RING}-layer weight "
+                        "ring: single calls and one ring launch per M", "per_m": out}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -332,6 +374,8 @@ def main():
         epi = epilogue_timing(sk, synthetic, dev, stream)
         # The same weight ring through the layer-ring launch.
         ring_out = ring_timing(sk, synthetic, dev, stream, ring)
+        # The other shard the target names.
+        oproj_out = oproj_timing(sk, synthetic, dev, stream)
 
     step_bytes = sum(algorithmic_bytes(M) for M in MS)
     value = step_bytes / (ms_step * 1e-3) / 1e9
@@ -368,6 +412,7 @@ def main():
         "per_m": detail,
         "epilogue": epi,
         "ring": ring_out,
+        "oproj": oproj_out,
         "wall_s": round(wall, 3),
     }
     if not args.no_cpu:

@@ -12,19 +12,23 @@
 //   out_j    = bf16( s_j / sqrt(mean(s^2) + pre_eps) * (next_w_j + pre_gain_center) )
 // with s the updated stream row.
 //
-// gfx950 design as for the pooler norm: one 256-thread workgroup per row,
-// thread t owns the 16-column blocks t, t + 256, ...; binary64 arithmetic
+// gfx950 design as for the pooler norm: one workgroup per row (512 threads:
+// one 16-column block a thread at H = 8192), thread t owning the blocks t,
+// t + 512, ...; every load of a thread's first block is issued before the
+// first reduction, so the kernel waits on memory once; binary64 arithmetic
 // (the products a * stream and beta * h are exact in binary64, their sum is
 // rounded once there and then once to binary32; every bfloat16 is one
 // round-to-nearest-even from binary64); both sums of squares in a fixed
-// order.  A thread re-reads the stream values it wrote itself for the
-// second norm.
+// order.  Past the first block a thread reloads, and for the second norm
+// re-reads the stream values it stored itself.
 #include "norm_device.h"
 
 namespace skinny {
 namespace {
 
 using namespace norm;
+
+constexpr int kDualThreads = 512;  // one 16-column block a thread at H = 8192
 
 __device__ __forceinline__ void load16_f32(const float *p, double (&v)[16]) {
 #pragma unroll
@@ -35,7 +39,69 @@ __device__ __forceinline__ void load16_f32(const float *p, double (&v)[16]) {
   }
 }
 
-__global__ __launch_bounds__(kNormThreads) void dual_norm_kernel(
+// Everything one 16-column block needs, as loaded (bf16 as doubles).
+struct Block {
+  double p[16], g[16], a[16], b[16], s[16], w[16];
+};
+
+__device__ __forceinline__ void load_block(Block &k, int blk, const uint16_t *prow,
+                                           const float *srow, const uint16_t *post_w,
+                                           float post_gc, const uint16_t *alpha,
+                                           float alpha_scalar, const uint16_t *beta,
+                                           const uint16_t *next_w) {
+  load16(prow + blk * 16, k.p);
+  load16_f32(srow + blk * 16, k.s);
+  if (post_w) {
+    load16(post_w + blk * 16, k.g);
+#pragma unroll
+    for (int j = 0; j < 16; ++j) k.g[j] += (double)post_gc;
+  } else {
+#pragma unroll
+    for (int j = 0; j < 16; ++j) k.g[j] = 1.0;
+  }
+  if (alpha) {
+    load16(alpha + blk * 16, k.a);
+  } else {
+#pragma unroll
+    for (int j = 0; j < 16; ++j) k.a[j] = (double)alpha_scalar;
+  }
+  load16(beta + blk * 16, k.b);
+  load16(next_w + blk * 16, k.w);
+}
+
+// Post norm and gated add of one block: the new residual values (stored and
+// returned in s) and their sum of squares.
+__device__ __forceinline__ double gate_block(Block &k, double inv, float *dst) {
+  double ss2 = 0.0;
+  f32x4 o[4];
+#pragma unroll
+  for (int j = 0; j < 16; ++j) {
+    const double h = (double)__uint_as_float(f64_to_bf16(k.p[j] * inv * k.g[j]) << 16);
+    const float v = (float)(k.a[j] * k.s[j] + k.b[j] * h);
+    o[j / 4][j % 4] = v;
+    k.s[j] = (double)v;
+    ss2 += (double)v * (double)v;
+  }
+#pragma unroll
+  for (int q = 0; q < 4; ++q) *reinterpret_cast<f32x4 *>(dst + 4 * q) = o[q];
+  return ss2;
+}
+
+__device__ __forceinline__ void out_block(const double (&s)[16], const double (&w)[16],
+                                          double inv2, float pre_gc, uint16_t *dst) {
+  unsigned yb[16];
+#pragma unroll
+  for (int j = 0; j < 16; ++j) yb[j] = f64_to_bf16(s[j] * inv2 * (w[j] + (double)pre_gc));
+  u32x4 o0, o1;
+  o0.x = yb[0] | (yb[1] << 16);   o0.y = yb[2] | (yb[3] << 16);
+  o0.z = yb[4] | (yb[5] << 16);   o0.w = yb[6] | (yb[7] << 16);
+  o1.x = yb[8] | (yb[9] << 16);   o1.y = yb[10] | (yb[11] << 16);
+  o1.z = yb[12] | (yb[13] << 16); o1.w = yb[14] | (yb[15] << 16);
+  reinterpret_cast<u32x4 *>(dst)[0] = o0;
+  reinterpret_cast<u32x4 *>(dst)[1] = o1;
+}
+
+__global__ __launch_bounds__(kDualThreads) void dual_norm_kernel(
     const uint16_t *__restrict__ partial, float *__restrict__ residual,
     const uint16_t *__restrict__ post_w, float post_gc, float post_eps,
     const uint16_t *__restrict__ alpha, float alpha_scalar, const uint16_t *__restrict__ beta,
@@ -47,66 +113,45 @@ __global__ __launch_bounds__(kNormThreads) void dual_norm_kernel(
   const uint16_t *prow = partial + (size_t)row * H;
   float *srow = residual + (size_t)row * H;
   uint16_t *orow = out + (size_t)row * H;
-  __shared__ double slots_post[kNormThreads / 64], slots_pre[kNormThreads / 64];
+  __shared__ double slots_post[kDualThreads / 64], slots_pre[kDualThreads / 64];
+
+  // The thread's first block: every load issued before the first reduction
+  // (one memory latency for the whole kernel up to H = 16 * kDualThreads).
+  const bool have = tid < blocks;
+  Block first;
+  if (have)
+    load_block(first, tid, prow, srow, post_w, post_gc, alpha, alpha_scalar, beta, next_w);
 
   double ss = 0.0;
-  for (int blk = tid; blk < blocks; blk += kNormThreads) {
+  if (have) {
+#pragma unroll
+    for (int j = 0; j < 16; ++j) ss += first.p[j] * first.p[j];
+  }
+  for (int blk = tid + kDualThreads; blk < blocks; blk += kDualThreads) {
     double v[16];
     load16(prow + blk * 16, v);
 #pragma unroll
     for (int j = 0; j < 16; ++j) ss += v[j] * v[j];
   }
-  const double inv = 1.0 / sqrt(block_sum(ss, slots_post) / (double)H + (double)post_eps);
+  const double inv =
+      1.0 / sqrt(block_sum<kDualThreads>(ss, slots_post) / (double)H + (double)post_eps);
 
-  // Post norm and gated add; the new stream's sum of squares on the way.
   double ss2 = 0.0;
-  for (int blk = tid; blk < blocks; blk += kNormThreads) {
-    double p[16], g[16], a[16], b[16], s[16];
-    load16(prow + blk * 16, p);
-    if (post_w) {
-      load16(post_w + blk * 16, g);
-#pragma unroll
-      for (int j = 0; j < 16; ++j) g[j] += (double)post_gc;
-    } else {
-#pragma unroll
-      for (int j = 0; j < 16; ++j) g[j] = 1.0;
-    }
-    if (alpha) {
-      load16(alpha + blk * 16, a);
-    } else {
-#pragma unroll
-      for (int j = 0; j < 16; ++j) a[j] = (double)alpha_scalar;
-    }
-    load16(beta + blk * 16, b);
-    load16_f32(srow + blk * 16, s);
-    f32x4 o[4];
-#pragma unroll
-    for (int j = 0; j < 16; ++j) {
-      const double h = (double)__uint_as_float(f64_to_bf16(p[j] * inv * g[j]) << 16);
-      const float v = (float)(a[j] * s[j] + b[j] * h);
-      o[j / 4][j % 4] = v;
-      ss2 += (double)v * (double)v;
-    }
-#pragma unroll
-    for (int q = 0; q < 4; ++q) *reinterpret_cast<f32x4 *>(srow + blk * 16 + 4 * q) = o[q];
+  if (have) ss2 += gate_block(first, inv, srow + tid * 16);
+  for (int blk = tid + kDualThreads; blk < blocks; blk += kDualThreads) {
+    Block k;
+    load_block(k, blk, prow, srow, post_w, post_gc, alpha, alpha_scalar, beta, next_w);
+    ss2 += gate_block(k, inv, srow + blk * 16);
   }
-  const double inv2 = 1.0 / sqrt(block_sum(ss2, slots_pre) / (double)H + (double)pre_eps);
+  const double inv2 =
+      1.0 / sqrt(block_sum<kDualThreads>(ss2, slots_pre) / (double)H + (double)pre_eps);
 
-  for (int blk = tid; blk < blocks; blk += kNormThreads) {
+  if (have) out_block(first.s, first.w, inv2, pre_gc, orow + tid * 16);
+  for (int blk = tid + kDualThreads; blk < blocks; blk += kDualThreads) {
     double s[16], w[16];
     load16_f32(srow + blk * 16, s);  // this thread's own stores above
     load16(next_w + blk * 16, w);
-    unsigned yb[16];
-#pragma unroll
-    for (int j = 0; j < 16; ++j) yb[j] = f64_to_bf16(s[j] * inv2 * (w[j] + (double)pre_gc));
-    u32x4 o0, o1;
-    o0.x = yb[0] | (yb[1] << 16);   o0.y = yb[2] | (yb[3] << 16);
-    o0.z = yb[4] | (yb[5] << 16);   o0.w = yb[6] | (yb[7] << 16);
-    o1.x = yb[8] | (yb[9] << 16);   o1.y = yb[10] | (yb[11] << 16);
-    o1.z = yb[12] | (yb[13] << 16); o1.w = yb[14] | (yb[15] << 16);
-    u32x4 *dst = reinterpret_cast<u32x4 *>(orow + blk * 16);
-    dst[0] = o0;
-    dst[1] = o1;
+    out_block(s, w, inv2, pre_gc, orow + blk * 16);
   }
 }
 
@@ -117,7 +162,7 @@ hipError_t launch_dual_norm(const uint16_t *partial, float *residual, const uint
                             float alpha_scalar, const uint16_t *beta, const uint16_t *next_w,
                             float pre_gc, float pre_eps, uint16_t *out, int M, int H,
                             hipStream_t stream) {
-  hipLaunchKernelGGL(dual_norm_kernel, dim3(M), dim3(kNormThreads), 0, stream, partial,
+  hipLaunchKernelGGL(dual_norm_kernel, dim3(M), dim3(kDualThreads), 0, stream, partial,
                      residual, post_w, post_gc, post_eps, alpha, alpha_scalar, beta, next_w,
                      pre_gc, pre_eps, out, H);
   return hipGetLastError();

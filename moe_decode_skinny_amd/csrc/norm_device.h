@@ -40,7 +40,8 @@ __device__ __forceinline__ void load16(const uint16_t *p, double (&v)[16]) {
 
 // Sum over the workgroup in a fixed order: a lane butterfly inside each wave,
 // then the wave sums in wave order (every thread gets the total).  `slots`
-// is LDS of kNormThreads / 64 doubles used only by this call.
+// is LDS of THREADS / 64 doubles used only by this call.
+template <int THREADS = kNormThreads>
 __device__ __forceinline__ double block_sum(double v, double *slots) {
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off);
@@ -48,7 +49,7 @@ __device__ __forceinline__ double block_sum(double v, double *slots) {
   __syncthreads();
   double total = slots[0];
 #pragma unroll
-  for (int i = 1; i < kNormThreads / 64; ++i) total += slots[i];
+  for (int i = 1; i < THREADS / 64; ++i) total += slots[i];
   return total;
 }
 

@@ -70,11 +70,13 @@ __global__ __launch_bounds__(kNormThreads) void rmsnorm_kernel(
   const int blocks = P / 16;
   const uint16_t *rrow = r + (size_t)row * P;
 
-  // Sum of squares in a fixed order; the first block stays in registers.
-  double first[16];
+  // Sum of squares in a fixed order; the first block and its weights are
+  // loaded before the reduction and stay in registers.
+  double first[16], gfirst[16];
   double ss = 0.0;
   if (tid < blocks) {
     load16(rrow + tid * 16, first);
+    load16(w + tid * 16, gfirst);
 #pragma unroll
     for (int j = 0; j < 16; ++j) ss += first[j] * first[j];
   }
@@ -94,11 +96,14 @@ __global__ __launch_bounds__(kNormThreads) void rmsnorm_kernel(
     double v[16], g[16];
     if (blk == tid) {
 #pragma unroll
-      for (int j = 0; j < 16; ++j) v[j] = first[j];
+      for (int j = 0; j < 16; ++j) {
+        v[j] = first[j];
+        g[j] = gfirst[j];
+      }
     } else {
       load16(rrow + blk * 16, v);
+      load16(w + blk * 16, g);
     }
-    load16(w + blk * 16, g);
     unsigned yb[16];
     double amax = 0.0;
 #pragma unroll
