@@ -50,7 +50,7 @@ def log(*a):
 HERE = os.path.dirname(os.path.abspath(__file__))
 KERNEL_SOURCES = ["moe_decode_skinny_amd/csrc/gemm_mfma.hip", "moe_decode_skinny_amd/csrc/gemm_dot2.hip",
                   "moe_decode_skinny_amd/csrc/dot2_device.h",
-                  "moe_decode_skinny_amd/csrc/split_reduce.hip", "moe_decode_skinny_amd/csrc/internal.h"]
+                  "moe_decode_skinny_amd/csrc/split_reduce.hip", "moe_decode_skinny_amd/csrc/device.h"]
 
 
 def kernel_source_digest() -> str:
@@ -64,7 +64,7 @@ def kernel_source_digest() -> str:
 
 
 RING_SOURCES = ["moe_decode_skinny_amd/csrc/gemm_ring.hip", "moe_decode_skinny_amd/csrc/dot2_device.h",
-                "moe_decode_skinny_amd/csrc/internal.h"]
+                "moe_decode_skinny_amd/csrc/device.h"]
 
 
 def ring_source_digest() -> str:

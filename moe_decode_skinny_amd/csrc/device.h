@@ -1,0 +1,121 @@
+// What the kernels depend on, shared by the libskinny translation units: the
+// limits, the structs passed to kernels by value and the device helpers.
+// Not installed.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "skinny.h"
+
+namespace skinny {
+
+// ---------------------------------------------------------------- limits
+constexpr int kMaxM = 16;          // tokens (unpooler page: 1 <= M <= 16)
+constexpr int kTileN = 16;         // features per MFMA tile (grid N / 16)
+constexpr int kMfmaK = 32;         // K per v_mfma_f32_16x16x32_bf16
+constexpr int kDot2K = 512;        // K per DOT2 chunk: 64 lanes x 8 bf16
+constexpr int kMaxMfmaChunks = 16;
+constexpr int kMaxDot2Chunks = 4;
+constexpr int kMaxSplits = 16;
+// Split-K workspace owned by the library (per device, from skinny_init):
+// FP32 partials [split][token][feature], S * M * N floats at most.
+constexpr size_t kWorkspaceFloats = size_t(2) << 20;  // 8 MiB
+
+constexpr size_t kMaxDynamicLds = 160 * 1024;  // all of a gfx950 CU's LDS
+
+// The zero-copy publish of a GEMM call (unpooler page, module description,
+// zero-copy epilogue): y also goes into this rank's slot of a mailbox
+// [3 stages][tp][capacity][N] at the stage read on the device when the
+// kernel runs, with -0.0 (the mailbox's "not yet written" sentinel) stored
+// as +0.0.  data == nullptr: no publish.
+struct Publish {
+  uint16_t *data = nullptr;
+  const int *stage_src = nullptr;  // stage_state[0], or the ticket word
+  int *stage_word = nullptr;       // stage_state[1]; nullptr with a ticket
+  int shift = 0;                   // 16 with a ticket (stage << 16)
+  int tp = 0, rank = 0, capacity = 0;
+};
+
+// The layer ring: up to kMaxRingItems independent GEMMs of one shape.
+constexpr int kMaxRingItems = 64;
+struct RingItems {
+  const uint16_t *x[kMaxRingItems];
+  const uint16_t *w[kMaxRingItems];
+  uint16_t *y[kMaxRingItems];
+};
+}  // namespace skinny
+
+// ------------------------------------------------------------ device helpers
+#if defined(__HIPCC__)
+namespace skinny {
+
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// FP32 -> bfloat16 bits, round to nearest even; NaN stays a quiet NaN.
+__device__ __forceinline__ unsigned f32_to_bf16(float f) {
+  unsigned u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+
+// The wave's index in its workgroup as a wave-uniform (scalar) value.  The
+// compiler cannot prove threadIdx.x >> 6 uniform, and a buffer resource
+// derived from a value it takes as divergent is rebuilt lane by lane in a
+// loop around every load.
+__device__ __forceinline__ int wave_index() {
+  return __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+}
+
+__device__ __forceinline__ float bf16_lo(unsigned u) { return __uint_as_float(u << 16); }
+
+// Raw buffer resource over [base, base + bytes): loads at offsets >= bytes
+// return zeros instead of touching memory, which gives token padding and
+// ragged-K tails without branches.  bytes must be < 2^31.
+constexpr unsigned kBufferFlags = 0x00020000u;  // gfx9 dword3: 32-bit data format
+constexpr int kOutOfRange = 0x7FFFF000;         // an offset past any resource used here
+constexpr int kCacheNT = 2;                     // nontemporal (streaming) load policy
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void *base, unsigned bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes,
+                                           (int)kBufferFlags);
+}
+__device__ __forceinline__ float bf16_hi(unsigned u) { return __uint_as_float(u & 0xffff0000u); }
+
+// ------------------------------------------------- zero-copy publish helpers
+// The publish stage of this call: the stage word's value, or the upper half
+// of the ticket; anything outside 0..2 (negative values included) means no
+// publish.
+__device__ __forceinline__ unsigned publish_stage(const Publish &p) {
+  return (unsigned)*p.stage_src >> p.shift;
+}
+
+// The slot [capacity][N] this call publishes into, or nullptr.
+__device__ __forceinline__ uint16_t *publish_slot(const Publish &p, int N) {
+  if (!p.data) return nullptr;
+  const unsigned stage = publish_stage(p);
+  if (stage > 2) return nullptr;
+  return p.data + ((size_t)stage * p.tp + p.rank) * (size_t)p.capacity * N;
+}
+
+// Sets the active-stage word (one thread of the writing kernel calls it).
+__device__ __forceinline__ void publish_stage_word(const Publish &p) {
+  if (!p.data || !p.stage_word) return;
+  const unsigned stage = publish_stage(p);
+  if (stage <= 2) *p.stage_word = (int)stage;
+}
+
+// bf16 bits as published: -0.0 (0x8000) becomes +0.0; one value, or two
+// packed in 32 bits.
+__device__ __forceinline__ unsigned publish_bits(unsigned b) { return b == 0x8000u ? 0u : b; }
+__device__ __forceinline__ unsigned publish_pair(unsigned v) {
+  return publish_bits(v & 0xffffu) | (publish_bits(v >> 16) << 16);
+}
+
+}  // namespace skinny
+#endif

@@ -3,7 +3,7 @@
 // single-call and the ring kernels only.
 #pragma once
 
-#include "internal.h"
+#include "device.h"
 
 namespace skinny {
 namespace dot2 {

@@ -22,6 +22,7 @@
 // order.  Past the first block a thread reloads, and for the second norm
 // re-reads the stream values it stored itself.
 #include "norm_device.h"
+#include "internal.h"
 
 namespace skinny {
 namespace {

@@ -14,6 +14,7 @@
 //   0..waves-1 in order through LDS, and with S > 1 an FP32 partial per split
 //   that split_reduce.hip sums s = 0..S-1 in order.
 #include "dot2_device.h"
+#include "internal.h"
 
 namespace skinny {
 namespace {

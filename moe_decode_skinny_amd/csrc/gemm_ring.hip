@@ -27,6 +27,7 @@
 // (L2) instead of a workgroup copy in LDS, so the LDS capacity does not limit
 // K.
 #include "dot2_device.h"
+#include "internal.h"
 
 namespace skinny {
 namespace {

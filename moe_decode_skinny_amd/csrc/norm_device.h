@@ -3,7 +3,7 @@
 // the fixed-order workgroup sum.
 #pragma once
 
-#include "internal.h"
+#include "device.h"
 
 namespace skinny {
 namespace norm {

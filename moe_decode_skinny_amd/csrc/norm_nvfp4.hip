@@ -25,6 +25,7 @@
 // e4m3(global_scale * amax / 6); the output scale is global_scale / dec(sf);
 // a negative value that rounds to zero keeps its sign.
 #include "norm_device.h"
+#include "internal.h"
 
 namespace skinny {
 namespace {
