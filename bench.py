@@ -64,7 +64,7 @@ def kernel_source_digest() -> str:
 
 
 RING_SOURCES = ["moe_decode_skinny_amd/csrc/gemm_ring.hip", "moe_decode_skinny_amd/csrc/dot2_device.h",
-                "moe_decode_skinny_amd/csrc/device.h"]
+                "moe_decode_skinny_amd/csrc/blocks_device.h", "moe_decode_skinny_amd/csrc/device.h"]
 
 
 def ring_source_digest() -> str:
@@ -245,10 +245,26 @@ def oproj_timing(sk, synthetic, dev, stream, reps: int = 10):
     """The o_proj shard (N=8192, K=1024, 16 MiB of weights) on its own
     60-layer ring: us per single call (graph of 60 calls) and per ring item
     (one 60-item launch), M = 1..16."""
+    out = shard_timing(sk, synthetic, dev, stream, 8192, 1024, MS, 7000, 950, reps)
+    return {"workload": f"o_proj shard GEMM M=1,2,4,8,16, N=8192, K=1024, {RING}-layer weight "
+                        "ring: single calls and one ring launch per M", "per_m": out}
+
+
+def pooler_timing(sk, synthetic, dev, stream, reps: int = 5):
+    """The pooler shard (N=512, K=8192) and the single-GPU full pooler
+    (N=4096, K=8192, 64 MiB of weights), each on its own 60-layer ring, at
+    M = 1, 8, 16: us per single call and per ring item."""
+    shard = shard_timing(sk, synthetic, dev, stream, 512, 8192, (1, 8, 16), 7100, 960, reps)
+    full = shard_timing(sk, synthetic, dev, stream, 4096, 8192, (1, 8, 16), 7200, 970, reps)
+    return {"workload": f"pooler shard N=512, K=8192 and full pooler N=4096, K=8192 at "
+                        f"M=1,8,16, {RING}-layer weight rings: single calls and one ring "
+                        "launch per M", "shard": shard, "full": full}
+
+
+def shard_timing(sk, synthetic, dev, stream, N2, K2, ms, wseed, xseed, reps):
     import torch
 
-    N2, K2 = 8192, 1024
-    ring = synthetic.device_weight_ring(RING, N2, K2, dev, base_seed=7000)
+    ring = synthetic.device_weight_ring(RING, N2, K2, dev, base_seed=wseed)
 
     def timed(fn, per):
         g = torch.cuda.CUDAGraph()
@@ -265,8 +281,8 @@ def oproj_timing(sk, synthetic, dev, stream, reps: int = 10):
         return e0.elapsed_time(e1) * 1e3 / (reps * per)
 
     out = {}
-    for M in MS:
-        xs = [synthetic.to_device(synthetic.gemm_inputs(N=16, K=K2, seed=950 + i)[0][:M], dev)
+    for M in ms:
+        xs = [synthetic.to_device(synthetic.gemm_inputs(N=16, K=K2, seed=xseed + i)[0][:M], dev)
               for i in range(RING)]
         ys = [torch.empty((M, N2), dtype=torch.bfloat16, device=dev) for _ in range(RING)]
         single = timed(lambda: [sk.skinny_gemm_bf16(x, w, y, 0) for x, w, y in zip(xs, ring, ys)],
@@ -277,9 +293,10 @@ def oproj_timing(sk, synthetic, dev, stream, reps: int = 10):
                        "pct_peak_call": round(100 * b / (single * 1e-6) / 1e9 / PEAK_GBS, 2),
                        "ring_us_per_item": round(item, 3),
                        "pct_peak_ring": round(100 * b / (item * 1e-6) / 1e9 / PEAK_GBS, 2)}
+        del xs, ys
     del ring
-    return {"workload": f"o_proj shard GEMM M=1,2,4,8,16, N=8192, K=1024, {RING}-layer weight "
-                        "ring: single calls and one ring launch per M", "per_m": out}
+    torch.cuda.empty_cache()
+    return out
 
 
 def main():
@@ -376,6 +393,8 @@ def main():
         ring_out = ring_timing(sk, synthetic, dev, stream, ring)
         # The other shard the target names.
         oproj_out = oproj_timing(sk, synthetic, dev, stream)
+        # The pooler shapes (K = 8192).
+        pooler_out = pooler_timing(sk, synthetic, dev, stream)
 
     step_bytes = sum(algorithmic_bytes(M) for M in MS)
     value = step_bytes / (ms_step * 1e-3) / 1e9
@@ -413,6 +432,7 @@ def main():
         "epilogue": epi,
         "ring": ring_out,
         "oproj": oproj_out,
+        "pooler": pooler_out,
         "wall_s": round(wall, 3),
     }
     if not args.no_cpu:

@@ -48,9 +48,11 @@ typedef enum skinny_status {
 enum {
   SKINNY_PATH_DOT2 = 0,    /* VALU bf16 dot2: lanes run along K, any row count  */
   SKINNY_PATH_MFMA = 1,    /* bf16 MFMA 16x16x32: 16 weight rows x 16 tokens    */
-  SKINNY_PATH_MFMA_LDS = 2 /* ring only: MFMA with each wave's weights loaded
+  SKINNY_PATH_MFMA_LDS = 2,/* ring only: MFMA with each wave's weights loaded
                               row by row and re-laid out through LDS; same
                               operands and results as SKINNY_PATH_MFMA        */
+  SKINNY_PATH_MFMA_4X4 = 3 /* bf16 MFMA 4x4x4 in 16 blocks: lanes run along K
+                              as in DOT2, 4 weight rows x 4 tokens a block    */
 };
 
 /* A launch shape of the GEMM: the counterpart of the unpooler page's
@@ -66,16 +68,21 @@ enum {
  *   DOT2: a workgroup owns `rows` output features; each wave owns
  *         kw = 512 * chunks consecutive K (64 lanes x 8 bf16 per chunk);
  *         waves = ceil(K / (splits * kw)).
- * In both, wave partials are summed in LDS in wave order; with splits > 1
+ *   MFMA_4X4: a workgroup owns rows = 4 or 8 output features; each wave owns
+ *         kw = 128 * chunks consecutive K (16 blocks x 8 bf16 per chunk,
+ *         chunks 1, 2, 4, 8) and all tokens in sets of 4;
+ *         waves = ceil(K / (splits * kw)) <= 16.
+ * In all three, wave partials are summed in LDS in wave order; with splits > 1
  * each workgroup writes an FP32 partial and a second kernel on the same
  * stream sums splits 0..S-1 in order. */
 typedef struct skinny_launch {
-  int path;   /* SKINNY_PATH_MFMA or SKINNY_PATH_DOT2                       */
+  int path;   /* SKINNY_PATH_MFMA, SKINNY_PATH_DOT2 or SKINNY_PATH_MFMA_4X4 */
   int splits; /* S in {1, 2, 4, 8, 16}: workgroups along K per output block   */
   int waves;  /* waves per workgroup (see above)                             */
-  int chunks; /* K chunks per wave (MFMA 1, 2, 4, 8, 16; DOT2 1, 2, 4)        */
-  int accs;   /* MFMA: accumulators per wave, 1, 2 or 4; DOT2: 1             */
-  int rows;   /* output features per workgroup: MFMA 16, 32, 64; DOT2 2..16  */
+  int chunks; /* K chunks per wave: MFMA 1..16, DOT2 1, 2, 4, MFMA_4X4 1..8  */
+  int accs;   /* MFMA: accumulators per wave, 1, 2 or 4; others: 1           */
+  int rows;   /* features per workgroup: MFMA 16, 32, 64; DOT2 2..16;
+                 MFMA_4X4 4, 8                                                */
 } skinny_launch;
 
 /* Prepare `device` (a HIP ordinal) for the compute calls: checks that it is a

@@ -36,6 +36,7 @@ SKINNY_ENOTINIT = -5
 SKINNY_PATH_DOT2 = 0
 SKINNY_PATH_MFMA = 1
 SKINNY_PATH_MFMA_LDS = 2
+SKINNY_PATH_MFMA_4X4 = 3
 
 if not os.path.exists(LIB_PATH):
     raise ImportError(

@@ -1,6 +1,7 @@
-// Device helpers of the DOT2 (VALU) GEMM kernels: the eight-product bf16
-// dot and the cross-lane reduce-scatter of a wave.  Included by the
-// single-call and the ring kernels only.
+// Device helpers of the GEMM kernels whose lanes run along K (the DOT2
+// (VALU) path and the 16-block MFMA path): the eight-product bf16 dot and
+// the cross-lane reduce-scatters of a wave.  Included by the single-call and
+// the ring kernels only.
 #pragma once
 
 #include "device.h"
@@ -92,6 +93,43 @@ __device__ __forceinline__ void wave_reduce_scatter(float *v, int lane) {
   dpp_step<c3, 0x141, 4>(v, lane);  // row_half_mirror: l ^ 7
   dpp_step<c4, 0x1B, 2>(v, lane);   // quad_perm [3, 2, 1, 0]: l ^ 3
   dpp_step<c5, 0xB1, 1>(v, lane);   // quad_perm [1, 0, 3, 2]: l ^ 1
+}
+
+// l ^ 4 inside each 8-lane half row: DPP row_half_mirror (l ^ 7) followed
+// by quad_perm [3, 2, 1, 0] (l ^ 3).
+__device__ __forceinline__ float dpp_xor4(float x) { return dpp<0x1B>(dpp<0x141>(x)); }
+
+template <int C>
+__device__ __forceinline__ void xor4_step(float *v, int lane) {
+  const bool hi = (lane & 4) != 0;
+  if constexpr (C >= 2) {
+#pragma unroll
+    for (int j = 0; j < C / 2; ++j) {
+      const float keep = hi ? v[j + C / 2] : v[j];
+      const float give = hi ? v[j] : v[j + C / 2];
+      v[j] = keep + dpp_xor4(give);
+    }
+  } else {
+    v[0] = v[0] + dpp_xor4(v[0]);
+  }
+}
+
+// Reduce-scatter of R values per lane (R a power of two, <= 32) over the 16
+// lanes that share bits 1..0 of their index (the 16 blocks of a
+// v_mfma_f32_4x4x4_16b_bf16 result; bits 1..0 index a block's column).
+// Steps pair lane l with l ^ 32, l ^ 16 (permlane swaps), l ^ 8 (DPP
+// row_ror:8) and l ^ 4, halving the values while more than one is left, as
+// in wave_reduce_scatter; afterwards a lane holds the full 16-lane sums of
+// value index lane >> (6 - log2 R) for R <= 16, and of indices
+// 2 (lane >> 2) and 2 (lane >> 2) + 1 in v[0], v[1] for R = 32.
+template <int R>
+__device__ __forceinline__ void block_reduce_scatter(float *v, int lane) {
+  static_assert(R >= 1 && R <= 32 && (R & (R - 1)) == 0, "R must be a power of two <= 32");
+  constexpr int c0 = R, c1 = halve(c0), c2 = halve(c1), c3 = halve(c2);
+  swap_step<c0, 32>(v);
+  swap_step<c1, 16>(v);
+  dpp_step<c2, 0x128, 8>(v, lane);  // row_ror:8: l ^ 8 inside a 16-lane row
+  xor4_step<c3>(v, lane);
 }
 
 }  // namespace dot2

@@ -1,7 +1,8 @@
 // The layer-ring launch: `count` independent small-M GEMMs
 // y_i[M, N] = x_i[M, K] @ W_i[N, K]^T of one shape in one persistent launch,
-// each weight matrix streamed while the previous GEMM is finished.  Two
-// kernel families, DOT2 (VALU dot products, lanes along K) and MFMA.
+// each weight matrix streamed while the previous GEMM is finished.  Three
+// kernel families: DOT2 (VALU dot products, lanes along K), MFMA 16x16x32
+// and the 16-block MFMA 4x4x4 (lanes along K, products on the matrix cores).
 //
 // The unpooler page's module description loads the weights before the
 // dependency wait and the activations after it, so that one layer's weight
@@ -26,6 +27,7 @@
 // where its B fragments come from: each wave loads them from global memory
 // (L2) instead of a workgroup copy in LDS, so the LDS capacity does not limit
 // K.
+#include "blocks_device.h"
 #include "dot2_device.h"
 #include "internal.h"
 
@@ -227,6 +229,145 @@ Dot2RingKernel dot2_ring_pick_rows(int rows, int chunks, int mt) {
 Dot2RingKernel dot2_ring_pick(int rows, int chunks, int mt, int waves) {
   if (waves <= kDot2MaxThreads / 64) return dot2_ring_pick_rows<kDot2MaxThreads>(rows, chunks, mt);
   if (waves <= 16) return dot2_ring_pick_rows<1024>(rows, chunks, mt);
+  return nullptr;
+}
+
+// --------------------------------------------------------- 16-block MFMA ring
+// Per tile the arithmetic of the single-call kernel (blocks_device.h) at
+// splits = 1: wave w owns K [w kw, (w + 1) kw), kw = 128 CHUNKS, of the
+// tile's 4 R4 rows; the pipeline is the DOT2 ring's.
+template <int R4, int CHUNKS, int Q, int WAVES, int P>
+__device__ __forceinline__ bool blocks_ring_tile(const RingItems &items, const Dot2Args &a,
+                                                 const RingWalk &walk, int &s, int &sub,
+                                                 u32x4 (&cur)[R4][CHUNKS],
+                                                 u32x4 (&next)[R4][CHUNKS],
+                                                 u32x4 (&xv)[Q][CHUNKS],
+                                                 float (&red)[2][WAVES][blocks::kOutputs<R4, Q>],
+                                                 int lane, int wave, int waves, int k0) {
+  constexpr int ROWS = 4 * R4;
+  const int K = a.K;
+  const int item = walk.item(s);
+  const int f0 = walk.block(s, sub) * ROWS;
+
+  if (sub == 0) {
+    // The activation offsets are recomputed here (a few adds once per
+    // segment) rather than held in registers across the tile loop.
+    int kx = k0;
+    asm volatile("" : "+v"(kx));
+    blocks::load_sets<Q, CHUNKS, 0>(xv, buffer_rsrc(items.x[item], (unsigned)(a.M * K * 2)), K,
+                                    kx, lane & 3);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  int ns = s, nsub = sub;
+  const bool more = walk.advance(ns, nsub);
+  {
+    const int cs = more ? ns : s, csub = more ? nsub : sub;
+    blocks::load_sets<R4, CHUNKS, kCacheNT>(
+        next,
+        buffer_rsrc(items.w[walk.item(cs)] + (size_t)walk.block(cs, csub) * ROWS * K,
+                    more ? (unsigned)(ROWS * K * 2) : 0u),
+        K, k0, lane & 3);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+
+  f32x4 acc[Q][R4];
+  blocks::products<R4, CHUNKS, Q>(cur, xv, acc);
+  // Buffer P: as in the DOT2 ring.
+  blocks::reduce_to_lds<R4, Q>(acc, red[P][wave], lane);
+  __syncthreads();
+  if (wave == 0) {
+    constexpr int kOut = blocks::kOutputs<R4, Q>;
+#pragma unroll
+    for (int o0 = 0; o0 < kOut; o0 += 64) {
+      const int o = o0 + lane;
+      if (o < kOut) {
+        float part = red[P][0][o];
+        for (int v2 = 1; v2 < waves; ++v2) part += red[P][v2][o];
+        const int t = blocks::output_token(o, R4), r = blocks::output_row(o, R4);
+        if (t < a.M) items.y[item][(size_t)t * a.N + f0 + r] = (uint16_t)f32_to_bf16(part);
+      }
+    }
+  }
+  s = ns;
+  sub = nsub;
+  return more;
+}
+
+template <int R4, int CHUNKS, int Q, int THREADS>
+__global__ __launch_bounds__(THREADS) void gemm_blocks_ring_kernel(
+    RingItems items, int M, int N, int K, RingWalk walk, int kw) {
+  constexpr int ROWS = 4 * R4;
+  const int lane = threadIdx.x & 63;
+  const int wave = wave_index();
+  const int waves = blockDim.x >> 6;
+  const Dot2Args a{M, N, K};
+  const int k0 = wave * kw + (lane >> 2) * 8;
+  __shared__ float red[2][THREADS / 64][blocks::kOutputs<R4, Q>];
+
+  // gridDim.x <= walk.segs, so every workgroup has a first tile.
+  int s = blockIdx.x, sub = 0;
+  u32x4 wa[R4][CHUNKS], wb[R4][CHUNKS], xv[Q][CHUNKS];
+  blocks::load_sets<R4, CHUNKS, kCacheNT>(
+      wa, buffer_rsrc(items.w[walk.item(s)] + (size_t)walk.block(s, 0) * ROWS * K,
+                      (unsigned)(ROWS * K * 2)),
+      K, k0, lane & 3);
+  for (;;) {
+    if (!blocks_ring_tile<R4, CHUNKS, Q, THREADS / 64, 0>(items, a, walk, s, sub, wa, wb, xv,
+                                                          red, lane, wave, waves, k0))
+      break;
+    if (!blocks_ring_tile<R4, CHUNKS, Q, THREADS / 64, 1>(items, a, walk, s, sub, wb, wa, xv,
+                                                          red, lane, wave, waves, k0))
+      break;
+  }
+}
+
+// Register budget per lane: two weight buffers 8 * R4 * CHUNKS, activations
+// 4 * Q * CHUNKS, sums 4 * Q * R4; the DOT2 ring's limits.
+constexpr int blocks_ring_regs(int r4, int chunks, int q) {
+  return 8 * r4 * chunks + 4 * q * chunks + 4 * q * r4;
+}
+
+template <int R4, int C, int Q, int THREADS>
+constexpr Dot2RingKernel blocks_ring_variant() {
+  if constexpr (blocks_ring_regs(R4, C, Q) <= (THREADS > 512 ? 112 : 160))
+    return gemm_blocks_ring_kernel<R4, C, Q, THREADS>;
+  else
+    return nullptr;
+}
+
+template <int R4, int C, int THREADS>
+Dot2RingKernel blocks_ring_pick_q(int q) {
+  switch (q) {
+    case 1: return blocks_ring_variant<R4, C, 1, THREADS>();
+    case 2: return blocks_ring_variant<R4, C, 2, THREADS>();
+    case 4: return blocks_ring_variant<R4, C, 4, THREADS>();
+  }
+  return nullptr;
+}
+
+template <int R4, int THREADS>
+Dot2RingKernel blocks_ring_pick_chunks(int chunks, int q) {
+  switch (chunks) {
+    case 1: return blocks_ring_pick_q<R4, 1, THREADS>(q);
+    case 2: return blocks_ring_pick_q<R4, 2, THREADS>(q);
+    case 4: return blocks_ring_pick_q<R4, 4, THREADS>(q);
+    case 8: return blocks_ring_pick_q<R4, 8, THREADS>(q);
+  }
+  return nullptr;
+}
+
+template <int THREADS>
+Dot2RingKernel blocks_ring_pick_rows(int rows, int chunks, int q) {
+  switch (rows) {
+    case 4: return blocks_ring_pick_chunks<1, THREADS>(chunks, q);
+    case 8: return blocks_ring_pick_chunks<2, THREADS>(chunks, q);
+  }
+  return nullptr;
+}
+
+Dot2RingKernel blocks_ring_pick(int rows, int chunks, int q, int waves) {
+  if (waves >= 1 && waves <= 8) return blocks_ring_pick_rows<512>(rows, chunks, q);
+  if (waves <= 16) return blocks_ring_pick_rows<1024>(rows, chunks, q);
   return nullptr;
 }
 
@@ -460,6 +601,10 @@ bool ring_variant_exists(int rows, int chunks, int mt, int waves) {
   return dot2_ring_pick(rows, chunks, mt, waves) != nullptr;
 }
 
+bool blocks_ring_variant_exists(int rows, int chunks, int q, int waves) {
+  return blocks_ring_pick(rows, chunks, q, waves) != nullptr;
+}
+
 bool mfma_ring_variant_exists(int chunks, int accs, bool staged) {
   return mfma_ring_pick(chunks, accs, staged) != nullptr;
 }
@@ -495,6 +640,10 @@ hipError_t launch_gemm_ring(const RingItems &items, int count, int M, int N, int
     hipLaunchKernelGGL(mfma_ring_pick(l.chunks, l.accs, l.path == SKINNY_PATH_MFMA_LDS),
                        dim3(r.workgroups), dim3(64 * l.waves), mfma_ring_lds_bytes(l), stream,
                        items, M, N, K, walk, l.rows / kTileN, kMfmaK * l.chunks);
+  } else if (l.path == SKINNY_PATH_MFMA_4X4) {
+    hipLaunchKernelGGL(blocks_ring_pick(l.rows, l.chunks, blocks_token_sets(M), l.waves),
+                       dim3(r.workgroups), dim3(64 * l.waves), 0, stream, items, M, N, K, walk,
+                       kBlockK * l.chunks);
   } else {
     hipLaunchKernelGGL(dot2_ring_pick(l.rows, l.chunks, dot2_token_tile(M), l.waves),
                        dim3(r.workgroups),

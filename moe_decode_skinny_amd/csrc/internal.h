@@ -26,6 +26,9 @@ hipError_t launch_gemm_mfma(const uint16_t *x, const uint16_t *w, uint16_t *y,
 hipError_t launch_gemm_dot2(const uint16_t *x, const uint16_t *w, uint16_t *y,
                             int M, int N, int K, const skinny_launch &l,
                             DeviceState &st, const Publish &pub, hipStream_t stream);
+hipError_t launch_gemm_blocks(const uint16_t *x, const uint16_t *w, uint16_t *y,
+                              int M, int N, int K, const skinny_launch &l,
+                              DeviceState &st, const Publish &pub, hipStream_t stream);
 hipError_t launch_gemm_ring(const RingItems &items, int count, int M, int N, int K,
                             const skinny_ring_launch &r, hipStream_t stream);
 hipError_t launch_split_reduce(const float *partials, uint16_t *y, int M, int N, int S,
@@ -48,7 +51,10 @@ hipError_t mfma_prepare();  // per-device kernel attributes (skinny_init)
 bool dot2_variant_exists(int rows, int chunks, int mt);
 int dot2_token_tile(int M);  // smallest compiled token count >= M, 0 if none
 int dot2_max_waves();        // waves per DOT2 workgroup (launch bound)
+int blocks_token_sets(int M);  // 4-token sets of the 16-block MFMA path (1, 2, 4), 0 if none
+bool blocks_variant_exists(int rows, int chunks, int q, int waves);
 bool ring_variant_exists(int rows, int chunks, int mt, int waves);  // DOT2 ring (<= 16 waves)
+bool blocks_ring_variant_exists(int rows, int chunks, int q, int waves);  // MFMA 4x4 ring
 bool mfma_ring_variant_exists(int chunks, int accs, bool staged);  // MFMA ring
 int mfma_ring_max_waves(int chunks);
 size_t mfma_ring_lds_bytes(const skinny_launch &l);  // dynamic LDS of an MFMA ring launch

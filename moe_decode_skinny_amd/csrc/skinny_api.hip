@@ -127,6 +127,27 @@ static int launch_check(int M, int N, int K, const skinny_launch &l) {
                   dot2_max_waves());
     return SKINNY_OK;
   }
+  if (l.path == SKINNY_PATH_MFMA_4X4) {
+    const int q = blocks_token_sets(M);
+    if (q == 0) return fail(SKINNY_EUNSUPPORTED, "MFMA 4x4 path takes M <= 16, got %d", M);
+    if (l.accs != 1) return fail(SKINNY_EUNSUPPORTED, "MFMA 4x4 launch has accs=1");
+    if (l.rows != 4 && l.rows != 8)
+      return fail(SKINNY_EUNSUPPORTED, "MFMA 4x4 rows=%d: needs 4 or 8", l.rows);
+    if (N % l.rows)
+      return fail(SKINNY_EUNSUPPORTED, "N=%d is not a multiple of rows=%d", N, l.rows);
+    const long kw = (long)kBlockK * l.chunks;
+    const int need = ceil_div(K, (long)l.splits * kw);
+    if (l.waves != need)
+      return fail(SKINNY_EUNSUPPORTED, "K=%d does not split into %d x %d waves x %ld "
+                  "(needs %d waves)", K, l.splits, l.waves, kw, need);
+    if (l.waves < 1 || l.waves > kBlocksMaxWaves)
+      return fail(SKINNY_EUNSUPPORTED, "%d waves per workgroup (MFMA 4x4: 1..%d)", l.waves,
+                  kBlocksMaxWaves);
+    if (!blocks_variant_exists(l.rows, l.chunks, q, l.waves))
+      return fail(SKINNY_EUNSUPPORTED, "no MFMA 4x4 kernel with rows=%d chunks=%d tokens=%d "
+                  "at %d waves", l.rows, l.chunks, 4 * q, l.waves);
+    return SKINNY_OK;
+  }
   return fail(SKINNY_EUNSUPPORTED, "unknown path %d", l.path);
 }
 
@@ -276,6 +297,18 @@ static int ring_check(int count, int M, int N, int K, const skinny_ring_launch &
       return fail(SKINNY_EUNSUPPORTED, "no ring kernel with rows=%d chunks=%d tokens=%d for %d "
                   "waves (more than 8 waves: only the register-light variants)", l.rows,
                   l.chunks, dot2_token_tile(M), l.waves);
+  } else if (l.path == SKINNY_PATH_MFMA_4X4) {
+    if (l.accs != 1) return fail(SKINNY_EUNSUPPORTED, "MFMA 4x4 launch has accs=1");
+    if (l.rows != 4 && l.rows != 8)
+      return fail(SKINNY_EUNSUPPORTED, "MFMA 4x4 rows=%d: needs 4 or 8", l.rows);
+    const long kw = (long)kBlockK * l.chunks;
+    const int need = ceil_div(K, kw);
+    if (l.waves != need || l.waves < 1 || l.waves > 16)
+      return fail(SKINNY_EUNSUPPORTED, "K=%d at kw=%ld needs %d waves (given %d, at most 16)",
+                  K, kw, need, l.waves);
+    if (!blocks_ring_variant_exists(l.rows, l.chunks, blocks_token_sets(M), l.waves))
+      return fail(SKINNY_EUNSUPPORTED, "no MFMA 4x4 ring kernel with rows=%d chunks=%d "
+                  "tokens=%d for %d waves", l.rows, l.chunks, 4 * blocks_token_sets(M), l.waves);
   } else {
     return fail(SKINNY_EUNSUPPORTED, "unknown path %d", l.path);
   }
@@ -301,37 +334,44 @@ struct RingEntry {
   { {SKINNY_PATH_DOT2, 1, waves, chunks, 1, rows}, seg, wg }
 #define LDS_RING(waves, chunks, accs, rows, seg, wg) \
   { {SKINNY_PATH_MFMA_LDS, 1, waves, chunks, accs, rows}, seg, wg }
+#define MFMA4X4_RING(waves, chunks, rows, seg, wg) \
+  { {SKINNY_PATH_MFMA_4X4, 1, waves, chunks, 1, rows}, seg, wg }
 static const RingEntry kRingTable[] = {
     // unpooler shard
     {1024, 4096, 1, 1, DOT2_RING(2, 4, 2, 1, 1024)},
     {1024, 4096, 2, 2, DOT2_RING(8, 1, 8, 2, 2048)},
-    {1024, 4096, 3, 4, DOT2_RING(4, 2, 4, 4, 2048)},
-    {1024, 4096, 5, 16, LDS_RING(8, 16, 2, 16, 8, 256)},
+    {1024, 4096, 3, 4, DOT2_RING(4, 2, 4, 4, 1024)},
+    {1024, 4096, 5, 8, MFMA4X4_RING(8, 4, 8, 32, 240)},
+    {1024, 4096, 9, 16, LDS_RING(8, 16, 2, 16, 8, 256)},
     // o_proj shard
-    {8192, 1024, 1, 1, DOT2_RING(1, 4, 4, 8, 1024)},
+    {8192, 1024, 1, 1, MFMA4X4_RING(2, 4, 4, 8, 1024)},
     {8192, 1024, 2, 2, DOT2_RING(2, 1, 8, 8, 512)},
-    {8192, 1024, 3, 4, DOT2_RING(2, 1, 4, 8, 1024)},
-    {8192, 1024, 5, 16, LDS_RING(4, 16, 2, 32, 16, 256)},
+    {8192, 1024, 3, 4, MFMA4X4_RING(2, 4, 8, 8, 512)},
+    {8192, 1024, 5, 8, LDS_RING(4, 16, 2, 32, 2, 256)},
+    {8192, 1024, 9, 16, LDS_RING(4, 16, 2, 32, 16, 256)},
     // pooler shard
     {512, 8192, 1, 1, DOT2_RING(4, 4, 2, 1, 1024)},
-    {512, 8192, 2, 2, DOT2_RING(4, 4, 2, 4, 2048)},
-    {512, 8192, 3, 4, DOT2_RING(8, 2, 4, 2, 1024)},
-    {512, 8192, 5, 8, DOT2_RING(8, 2, 4, 16, 256)},
-    {512, 8192, 9, 16, DOT2_RING(16, 1, 2, 16, 256)},
+    {512, 8192, 2, 2, DOT2_RING(16, 1, 2, 4, 512)},
+    {512, 8192, 3, 4, MFMA4X4_RING(16, 4, 4, 32, 240)},
+    {512, 8192, 5, 8, MFMA4X4_RING(8, 8, 4, 32, 240)},
+    {512, 8192, 9, 16, MFMA4X4_RING(16, 4, 4, 32, 240)},
     // full pooler
     {4096, 8192, 1, 2, DOT2_RING(4, 4, 2, 8, 256)},
     {4096, 8192, 3, 8, DOT2_RING(8, 2, 4, 16, 256)},
-    {4096, 8192, 9, 16, DOT2_RING(16, 1, 2, 16, 1024)},
+    {4096, 8192, 9, 16, MFMA4X4_RING(16, 4, 4, 64, 960)},
 };
 #undef DOT2_RING
 #undef LDS_RING
+#undef MFMA4X4_RING
 
 // Ring rule for any other shape.  Up to 8 tokens DOT2: 2 rows per workgroup
 // for <= 2 tokens, else 4 (the register budget of two weight buffers), the
-// most chunks that fit and that K fills.  Beyond 8 tokens MFMA with one tile
-// per workgroup: the staged form with the most chunks that fit, else the
-// direct form with the fewest chunks that cover K with the waves a workgroup
-// has; DOT2 if K is too long for both.  One workgroup per output block.
+// most chunks that fit and that K fills, one workgroup per output block.
+// Beyond 8 tokens MFMA with one tile per workgroup: the staged form with the
+// most chunks that fit; else (long K) the 16-block MFMA with 4 rows and the
+// most chunks that fit, in segments of up to 32 blocks on at most 256
+// workgroups; else the direct MFMA form with the fewest chunks that cover K
+// with the waves a workgroup has; DOT2 if K is too long for all of them.
 static int ring_choose(int M, int N, int K, int count, skinny_ring_launch *out) {
   int st = check_problem(M, N, K);
   if (st) return st;
@@ -355,6 +395,18 @@ static int ring_choose(int M, int N, int K, int count, skinny_ring_launch *out) 
     for (int c = kMaxMfmaChunks; c >= 2; c /= 2) {  // staged: the fewest waves that fit
       const skinny_ring_launch r{
           {SKINNY_PATH_MFMA_LDS, 1, ceil_div(K, (long)kMfmaK * c), c, 1, kTileN}, 1, N / kTileN};
+      if (ring_check(count, M, N, K, r) == SKINNY_OK) {
+        *out = r;
+        return SKINNY_OK;
+      }
+    }
+    const int groups = N / 4;
+    int seg = 32;
+    while (groups % seg) seg /= 2;
+    const long segs = (long)count * (groups / seg);
+    for (int c = 4; c >= 1; c /= 2) {
+      const skinny_ring_launch r{{SKINNY_PATH_MFMA_4X4, 1, ceil_div(K, (long)kBlockK * c), c, 1, 4},
+                                 seg, (int)(segs < 256 ? segs : 256)};
       if (ring_check(count, M, N, K, r) == SKINNY_OK) {
         *out = r;
         return SKINNY_OK;
@@ -432,9 +484,13 @@ static int gemm_common(const void *x, const void *W, void *y, int M, int N, int 
   const uint16_t *wp = static_cast<const uint16_t *>(W);
   uint16_t *yp = static_cast<uint16_t *>(y);
   hipStream_t s = static_cast<hipStream_t>(stream);
-  hipError_t e = l.path == SKINNY_PATH_MFMA
-                     ? launch_gemm_mfma(xp, wp, yp, M, N, K, l, *ds, pub, s)
-                     : launch_gemm_dot2(xp, wp, yp, M, N, K, l, *ds, pub, s);
+  hipError_t e;
+  if (l.path == SKINNY_PATH_MFMA)
+    e = launch_gemm_mfma(xp, wp, yp, M, N, K, l, *ds, pub, s);
+  else if (l.path == SKINNY_PATH_MFMA_4X4)
+    e = launch_gemm_blocks(xp, wp, yp, M, N, K, l, *ds, pub, s);
+  else
+    e = launch_gemm_dot2(xp, wp, yp, M, N, K, l, *ds, pub, s);
   if (e != hipSuccess) return fail(SKINNY_ELAUNCH, "launch failed: %s", hipGetErrorString(e));
   return SKINNY_OK;
 }

@@ -107,6 +107,28 @@ def test_launch_unsupported_reasons(sk):
     assert sk.skinny_launch_unsupported(16, 1024, 4096, L(1, 4, 8, 4, 2, 16)) is None
 
 
+def test_mfma_4x4_launch_reasons(sk):
+    """The 16-block MFMA path: rows 4 or 8, accs 1, waves = ceil(K / (S * 128
+    chunks)) <= 16, and only the register-budgeted variants."""
+    L, P = sk.Launch, sk.SKINNY_PATH_MFMA_4X4
+    assert sk.skinny_launch_unsupported(16, 1024, 4096, L(P, 1, 8, 4, 1, 4)) is None
+    assert sk.skinny_launch_unsupported(16, 1024, 4096, L(P, 2, 4, 4, 1, 8)) is None
+    assert sk.skinny_launch_unsupported(1, 512, 8192, L(P, 1, 16, 4, 1, 4)) is None
+    assert "rows=2" in sk.skinny_launch_unsupported(16, 1024, 4096, L(P, 1, 8, 4, 1, 2))
+    assert "rows=16" in sk.skinny_launch_unsupported(16, 1024, 4096, L(P, 1, 8, 4, 1, 16))
+    assert "accs" in sk.skinny_launch_unsupported(16, 1024, 4096, L(P, 1, 8, 4, 2, 4))
+    assert "needs 8 waves" in sk.skinny_launch_unsupported(16, 1024, 4096, L(P, 1, 4, 4, 1, 4))
+    assert "MFMA 4x4: 1..16" in sk.skinny_launch_unsupported(16, 1024, 4096,
+                                                            L(P, 1, 32, 1, 1, 4))
+    # 8 rows x 8 chunks x 16 tokens needs 224 registers a lane: not built
+    assert "no MFMA 4x4 kernel" in sk.skinny_launch_unsupported(16, 1024, 4096,
+                                                                L(P, 1, 4, 8, 1, 8))
+    # the same at 1024 threads (112 registers): 4 rows x 4 chunks x 16 tokens is 96
+    assert sk.skinny_launch_unsupported(16, 512, 8192, L(P, 1, 16, 4, 1, 4)) is None
+    assert "no MFMA 4x4 kernel" in sk.skinny_launch_unsupported(16, 512, 8192,
+                                                                L(P, 1, 16, 4, 1, 8))
+
+
 def test_compute_calls_without_device_fail_cleanly(sk):
     # Pointer checks come before any device access: null pointers are EINVAL.
     lib = ctypes.CDLL(sk.LIB_PATH)
@@ -129,16 +151,20 @@ def test_compute_calls_without_device_fail_cleanly(sk):
 
 @pytest.mark.parametrize("M,N,K", [(m, 1024, 4096) for m in (1, 2, 4, 8, 16)]
                          + [(m, 8192, 1024) for m in (1, 8, 16)]
-                         + [(m, 512, 8192) for m in (1, 8)]
-                         + [(m, 4096, 8192) for m in (1, 8)]
-                         + [(3, 48, 1000), (16, 16, 8), (1, 16, 8)])
+                         + [(m, 512, 8192) for m in (1, 8, 16)]
+                         + [(m, 4096, 8192) for m in (1, 8, 16)]
+                         + [(3, 48, 1000), (16, 16, 8), (1, 16, 8), (16, 1024, 6000)])
 @pytest.mark.parametrize("count", [1, 7, 64])
 def test_ring_chooser_gives_valid_launches(sk, M, N, K, count):
     r = sk.skinny_ring_choose(M, N, K, count)
     g = r.gemm
     assert g.splits == 1
     if g.path == sk.SKINNY_PATH_DOT2:
-        assert g.accs == 1 and g.waves == -(-K // (512 * g.chunks)) <= 8
+        assert g.accs == 1 and g.waves == -(-K // (512 * g.chunks)) <= 16
+        if g.waves <= 8:  # the single-call DOT2 kernel has up to 8 waves
+            assert sk.skinny_launch_unsupported(M, N, K, g) is None
+    elif g.path == sk.SKINNY_PATH_MFMA_4X4:
+        assert g.accs == 1 and g.rows in (4, 8) and g.waves == -(-K // (128 * g.chunks)) <= 16
         # the ring's launch is also a valid single-call launch (same arithmetic)
         assert sk.skinny_launch_unsupported(M, N, K, g) is None
     else:
@@ -196,8 +222,17 @@ def test_ring_launch_reasons_without_device(sk):
     assert "167936 bytes of LDS" in sk.skinny_last_error()
     assert call((2, 1, 16, 1, 1, 16)) == sk.SKINNY_EUNSUPPORTED
     assert "MFMA_LDS ring kernel" in sk.skinny_last_error()
-    assert call((3, 1, 16, 8, 1, 16)) == sk.SKINNY_EUNSUPPORTED
+    assert call((4, 1, 16, 8, 1, 16)) == sk.SKINNY_EUNSUPPORTED
     assert "unknown path" in sk.skinny_last_error()
+    assert call((3, 1, 16, 8, 1, 16)) == sk.SKINNY_EUNSUPPORTED  # MFMA 4x4: rows 4 or 8
+    assert "MFMA 4x4 rows=16" in sk.skinny_last_error()
+    assert call((3, 1, 8, 8, 1, 4)) == sk.SKINNY_EUNSUPPORTED  # K=4096 at 8 chunks: 4 waves
+    assert "needs 4 waves" in sk.skinny_last_error()
+    assert call((3, 1, 4, 8, 2, 4)) == sk.SKINNY_EUNSUPPORTED
+    assert "accs=1" in sk.skinny_last_error()
+    assert call((3, 1, 4, 8, 1, 8)) == sk.SKINNY_EUNSUPPORTED  # 8 rows x 8 chunks: too many registers
+    assert "MFMA 4x4 ring kernel" in sk.skinny_last_error()
+    assert call((3, 1, 8, 4, 1, 4)) in (sk.SKINNY_EDEVICE, sk.SKINNY_ENOTINIT)
     assert call((2, 1, 8, 16, 1, 16)) in (sk.SKINNY_EDEVICE, sk.SKINNY_ENOTINIT)
     assert call((0, 2, 1, 4, 1, 2)) == sk.SKINNY_EUNSUPPORTED
     assert "splits=1" in sk.skinny_last_error()

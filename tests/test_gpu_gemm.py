@@ -116,13 +116,16 @@ def test_pooler_weight_ring_layers(gpu_lib):
 
 def _all_launches(sk, M, N, K):
     out = []
-    for path in (sk.SKINNY_PATH_MFMA, sk.SKINNY_PATH_DOT2):
+    rows_of = {sk.SKINNY_PATH_MFMA: (16, 32, 64), sk.SKINNY_PATH_DOT2: (2, 4, 8, 16),
+               sk.SKINNY_PATH_MFMA_4X4: (4, 8)}
+    k_of = {sk.SKINNY_PATH_MFMA: 32, sk.SKINNY_PATH_DOT2: 512, sk.SKINNY_PATH_MFMA_4X4: 128}
+    for path in rows_of:
         for splits in (1, 2, 4, 8, 16):
             for chunks in (1, 2, 4, 8, 16):
                 for accs in (1, 2, 4):
                     mfma = path == sk.SKINNY_PATH_MFMA
-                    for rows in ((16, 32, 64) if mfma else (2, 4, 8, 16)):
-                        kw = (32 if mfma else 512) * chunks
+                    for rows in rows_of[path]:
+                        kw = k_of[path] * chunks
                         waves = (rows // 16 if mfma else 1) * -(-K // (splits * kw))
                         l = sk.Launch(path, splits, waves, chunks, accs, rows)
                         if sk.skinny_launch_unsupported(M, N, K, l) is None:
@@ -197,7 +200,7 @@ def test_graph_capture_replay(gpu_lib):
                 assert_gemm_close(from_dev(y), expect, "graph replay with new x")
 
 
-@pytest.mark.parametrize("path", ["mfma", "mfma4", "dot2"])
+@pytest.mark.parametrize("path", ["mfma", "mfma_f4", "mfma_4x4", "dot2"])
 @pytest.mark.parametrize("splits", [2, 4, 8, 16])
 def test_split_k_handoff_alternating_inputs(gpu_lib, path, splits):
     """Back-to-back split calls on alternating weights share the partials
@@ -211,8 +214,10 @@ def test_split_k_handoff_alternating_inputs(gpu_lib, path, splits):
     refs = [oracle.gemm_bf16(xa[:M], wa, THREADS), oracle.gemm_bf16(xa[:M], wb, THREADS)]
     if path == "mfma":
         launch = gpu_lib.Launch(1, splits, -(-K // (splits * 32 * 4)), 4, 2, 16)
-    elif path == "mfma4":
+    elif path == "mfma_f4":
         launch = gpu_lib.Launch(1, splits, 4 * -(-K // (splits * 32 * 4)), 4, 2, 64)
+    elif path == "mfma_4x4":
+        launch = gpu_lib.Launch(3, splits, -(-K // (splits * 128 * 4)), 4, 1, 8)
     else:
         launch = gpu_lib.Launch(0, splits, -(-K // (splits * 512)), 1, 1, 4)
     if gpu_lib.skinny_launch_unsupported(M, N, K, launch) is not None:

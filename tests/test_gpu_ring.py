@@ -84,13 +84,18 @@ def _single(sk, x_bits, w_bits, M, launch):
 
 
 def _ring_launches(sk, M, N, K):
-    """Ring launch candidates of both families with splits = 1: DOT2 rows
-    2..16 x chunks 1, 2, 4 and MFMA 1, 2, 4 tiles x chunks 1..16 x accs 1, 2
-    (the ring validator decides which it has kernels for)."""
+    """Ring launch candidates of every family with splits = 1: DOT2 rows
+    2..16 x chunks 1, 2, 4, MFMA 4x4 rows 4, 8 x chunks 1..8 and MFMA 1, 2, 4
+    tiles x chunks 1..16 x accs 1, 2 (the ring validator decides which it has
+    kernels for)."""
     out = []
     for rows in (2, 4, 8, 16):
         for chunks in (1, 2, 4):
             out.append(sk.Launch(0, 1, -(-K // (512 * chunks)), chunks, 1, rows))
+    for rows in (4, 8):
+        for chunks in (1, 2, 4, 8):
+            out.append(sk.Launch(sk.SKINNY_PATH_MFMA_4X4, 1, -(-K // (128 * chunks)), chunks, 1,
+                                 rows))
     for path in (sk.SKINNY_PATH_MFMA, sk.SKINNY_PATH_MFMA_LDS):
         for rows in (16, 32, 64):
             for chunks in (1, 2, 4, 8, 16):
