@@ -49,7 +49,8 @@ def log(*a):
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 KERNEL_SOURCES = ["moe_decode_skinny_amd/csrc/gemm_mfma.hip", "moe_decode_skinny_amd/csrc/gemm_dot2.hip",
-                  "moe_decode_skinny_amd/csrc/dot2_device.h",
+                  "moe_decode_skinny_amd/csrc/gemm_blocks.hip", "moe_decode_skinny_amd/csrc/gemm_ring.hip",
+                  "moe_decode_skinny_amd/csrc/dot2_device.h", "moe_decode_skinny_amd/csrc/blocks_device.h",
                   "moe_decode_skinny_amd/csrc/split_reduce.hip", "moe_decode_skinny_amd/csrc/device.h"]
 
 
@@ -92,10 +93,11 @@ def ring_traffic(M: int):
     return None if e is None else e["hbm_bytes_per_item"]
 
 
-def measured_traffic(M: int):
+def measured_traffic(M: int, sk=None):
     """HBM bytes per launch of the M=<M> sweep kernel from the committed
     counter summary (FETCH_SIZE + WRITE_SIZE, scaled by the plain-copy
-    reference), or None when the kernels changed since it was taken."""
+    reference), or None when the kernels, or the launch and walk the chooser
+    picks, changed since it was taken."""
     path = os.path.join(HERE, "profiles", "hbm_traffic_unpooler_sweep.json")
     try:
         with open(path) as f:
@@ -105,7 +107,17 @@ def measured_traffic(M: int):
     if rec.get("kernel_source_digest") != kernel_source_digest():
         return None
     per_m = rec.get("per_m", {}).get(str(M))
-    return None if per_m is None else per_m.get("hbm_bytes_per_launch")
+    if per_m is None:
+        return None
+    if sk is not None and per_m.get("walk") != walk_record(sk, M, N, K):
+        return None
+    return per_m.get("hbm_bytes_per_launch")
+
+
+def walk_record(sk, M: int, n: int, k: int) -> dict:
+    """The launch and walk skinny_gemm_bf16 runs (segment 0: the plain kernel)."""
+    w = sk.skinny_choose_walk(M, n, k, 0)
+    return {**dict(w.gemm._asdict()), "segment": w.segment, "workgroups": w.workgroups}
 
 
 def _cpu_model() -> str:
@@ -289,7 +301,7 @@ def shard_timing(sk, synthetic, dev, stream, N2, K2, ms, wseed, xseed, reps):
                        RING)
         item = timed(lambda: sk.skinny_gemm_bf16_ring(xs, ring, ys), RING)
         b = algorithmic_bytes(M, N2, K2)
-        out[str(M)] = {"us_per_call": round(single, 3),
+        out[str(M)] = {"walk": walk_record(sk, M, N2, K2), "us_per_call": round(single, 3),
                        "pct_peak_call": round(100 * b / (single * 1e-6) / 1e9 / PEAK_GBS, 2),
                        "ring_us_per_item": round(item, 3),
                        "pct_peak_ring": round(100 * b / (item * 1e-6) / 1e9 / PEAK_GBS, 2)}
@@ -401,6 +413,7 @@ def main():
     dom = max(MS, key=lambda M: per_kernel[M])
     ach = algorithmic_bytes(dom) / (per_kernel[dom] * 1e-6) / 1e9
     detail = {str(M): {"launch": dict(launches[M]._asdict()),
+                       "walk": walk_record(sk, M, N, K),
                        "us_per_call": round(per_kernel[M], 3),
                        "GBs": round(algorithmic_bytes(M) / (per_kernel[M] * 1e-6) / 1e9, 1),
                        "pct_peak": round(100 * algorithmic_bytes(M) / (per_kernel[M] * 1e-6)
@@ -424,8 +437,8 @@ def main():
                    "global_batch": list(MS), "parallelism": "single GPU shard"},
         "roofline": {"bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_GBS,
                      "unit": "GB/s", "frac": round(ach / PEAK_GBS, 4),
-                     "traffic": measured_traffic(dom),
-                     "kernel": f"M={dom} {dict(launches[dom]._asdict())}",
+                     "traffic": measured_traffic(dom, sk),
+                     "kernel": f"M={dom} {walk_record(sk, dom, N, K)}",
                      "bytes_per_launch": algorithmic_bytes(dom),
                      "us_per_launch": round(per_kernel[dom], 3)},
         "per_m": detail,

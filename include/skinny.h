@@ -105,6 +105,10 @@ int skinny_init(int device);
  * (M, N, K, launch) on one device.  A launch with S > 1 enqueues two kernels
  * and uses the device's workspace: two such calls must not run concurrently
  * on different streams of one device (calls on one stream are ordered).
+ * For some measured shapes the chosen launch runs as a persistent walk over
+ * the output blocks (the layer-ring kernel with one item, see
+ * skinny_choose_walk); the result is still bitwise that of
+ * skinny_gemm_bf16_launch at the launch skinny_choose returns.
  * Errors: SKINNY_EINVAL, SKINNY_EUNSUPPORTED, SKINNY_ENOTINIT, SKINNY_ELAUNCH. */
 int skinny_gemm_bf16(const void *x, const void *W, void *y, int M, int N,
                      int K, int splits, void *stream);
@@ -222,6 +226,17 @@ int skinny_ring_choose(int M, int N, int K, int count, skinny_ring_launch *out);
 /* Why (M, N, K, count) cannot run at `launch`; SKINNY_OK when it can. */
 int skinny_ring_launch_unsupported(int M, int N, int K, int count,
                                    const skinny_ring_launch *launch);
+
+/* How skinny_gemm_bf16 runs (M, N, K, splits), for profiling and tests: on
+ * SKINNY_OK, out->segment == 0 means the plain kernel at out->gemm (the
+ * launch skinny_choose returns); otherwise the call is exactly
+ * skinny_gemm_bf16_ring_launch with one item at *out (out->gemm then has the
+ * same arithmetic as skinny_choose's launch; SKINNY_PATH_MFMA_LDS stands for
+ * SKINNY_PATH_MFMA with the ring's staged weight loads).  The unpooler
+ * page's module description orders a kernel's weight loads ahead of its
+ * activations; the walk keeps one block's weights in flight while the
+ * previous block is finished.  Pure host function; errors as skinny_choose. */
+int skinny_choose_walk(int M, int N, int K, int splits, skinny_ring_launch *out);
 
 /* The NVFP4 expert input (pooler_gather page, module description and
  * compile_norm_quant; nvfp4_compute_output_scale; cvt_e2m1x8_f32;

@@ -107,6 +107,7 @@ _sig = {
     "skinny_gemm_bf16_ring_launch": (
         [_vp, _vp, _vp, _i, _i, _i, _i, ctypes.POINTER(_CRingLaunch), _vp], _i),
     "skinny_ring_choose": ([_i, _i, _i, _i, ctypes.POINTER(_CRingLaunch)], _i),
+    "skinny_choose_walk": ([_i, _i, _i, _i, ctypes.POINTER(_CRingLaunch)], _i),
     "skinny_ring_launch_unsupported": ([_i, _i, _i, _i, ctypes.POINTER(_CRingLaunch)], _i),
     "skinny_rmsnorm_nvfp4": ([_vp, _vp, _f, _f, _vp, _vp, _vp, _i, _i, _vp], _i),
     "skinny_rmsnorm_bf16": ([_vp, _vp, _f, _f, _vp, _i, _i, _vp], _i),
@@ -246,6 +247,14 @@ def skinny_ring_choose(M: int, N: int, K: int, count: int) -> RingLaunch:
     """The RingLaunch that skinny_gemm_bf16_ring uses."""
     out = _CRingLaunch()
     _check(_lib.skinny_ring_choose(M, N, K, count, ctypes.byref(out)))
+    return RingLaunch._from_c(out)
+
+
+def skinny_choose_walk(M: int, N: int, K: int, splits: int = 0) -> RingLaunch:
+    """How skinny_gemm_bf16 runs: segment 0 = the plain kernel at .gemm,
+    else the one-item ring launch it is."""
+    out = _CRingLaunch()
+    _check(_lib.skinny_choose_walk(M, N, K, splits, ctypes.byref(out)))
     return RingLaunch._from_c(out)
 
 

@@ -151,25 +151,37 @@ static int launch_check(int M, int N, int K, const skinny_launch &l) {
   return fail(SKINNY_EUNSUPPORTED, "unknown path %d", l.path);
 }
 
+// How the chooser runs a launch: the plain kernel (one output block per
+// workgroup), or the persistent walk of the layer-ring kernel over this one
+// GEMM (each workgroup takes `segment` consecutive output blocks, the next
+// block's weights in flight while the current one is finished, the
+// activations loaded once per segment).  The walk does not change the
+// result: a ring item is bitwise the single call at its launch.
+struct Walk {
+  int segment = 0;       // 0: the plain kernel
+  int workgroups = 0;
+  bool staged = false;   // MFMA launches: the ring's staged (LDS) weight path
+};
+
 // Launch shapes measured best on MI355X for the pages' shard shapes (sweeps
-// of every valid launch, weights cycling through a ring larger than the
-// Infinity Cache): {N, K, M_lo, M_hi, launch}.
+// of every valid launch and walk, weights cycling through a ring larger than
+// the Infinity Cache): {N, K, M_lo, M_hi, launch, walk}.
 struct TableEntry {
   int N, K, m_lo, m_hi;
   skinny_launch l;
+  Walk walk;
 };
 static const TableEntry kTable[] = {
     // unpooler shard
     {1024, 4096, 1, 1, {SKINNY_PATH_DOT2, 1, 2, 4, 1, 2}},
-    {1024, 4096, 2, 2, {SKINNY_PATH_DOT2, 1, 4, 2, 1, 2}},
-    {1024, 4096, 3, 8, {SKINNY_PATH_DOT2, 1, 4, 2, 1, 4}},
+    {1024, 4096, 2, 2, {SKINNY_PATH_DOT2, 1, 2, 4, 1, 2}, {2, 256}},
+    {1024, 4096, 3, 4, {SKINNY_PATH_DOT2, 1, 4, 2, 1, 2}, {2, 256}},
+    {1024, 4096, 5, 8, {SKINNY_PATH_DOT2, 1, 4, 2, 1, 4}},
     {1024, 4096, 9, 16, {SKINNY_PATH_DOT2, 1, 8, 1, 1, 4}},
     // o_proj shard
     {8192, 1024, 1, 1, {SKINNY_PATH_DOT2, 1, 1, 2, 1, 2}},
-    {8192, 1024, 2, 2, {SKINNY_PATH_DOT2, 1, 1, 2, 1, 4}},
-    {8192, 1024, 3, 4, {SKINNY_PATH_DOT2, 1, 1, 2, 1, 2}},
-    {8192, 1024, 5, 8, {SKINNY_PATH_DOT2, 1, 2, 1, 1, 4}},
-    {8192, 1024, 9, 16, {SKINNY_PATH_MFMA, 1, 16, 4, 1, 32}},
+    {8192, 1024, 2, 4, {SKINNY_PATH_DOT2, 1, 1, 2, 1, 4}, {2, 1024}},
+    {8192, 1024, 5, 16, {SKINNY_PATH_MFMA, 1, 2, 16, 2, 16}, {2, 256, true}},
     // pooler shard
     {512, 8192, 1, 4, {SKINNY_PATH_DOT2, 1, 4, 4, 1, 2}},
     {512, 8192, 5, 8, {SKINNY_PATH_DOT2, 1, 8, 2, 1, 2}},
@@ -177,8 +189,8 @@ static const TableEntry kTable[] = {
     // full pooler
     {4096, 8192, 1, 1, {SKINNY_PATH_DOT2, 1, 8, 2, 1, 2}},
     {4096, 8192, 2, 4, {SKINNY_PATH_DOT2, 1, 8, 2, 1, 8}},
-    {4096, 8192, 5, 8, {SKINNY_PATH_DOT2, 1, 8, 2, 1, 4}},
-    {4096, 8192, 9, 16, {SKINNY_PATH_MFMA, 8, 16, 4, 2, 32}},
+    {4096, 8192, 5, 8, {SKINNY_PATH_DOT2, 1, 8, 2, 1, 4}, {4, 256}},
+    {4096, 8192, 9, 16, {SKINNY_PATH_MFMA_4X4, 1, 16, 4, 1, 4}, {4, 256}},
 };
 
 // The general rule the table follows (used for any other shape, or when an
@@ -230,18 +242,31 @@ static skinny_launch rule(int M, int N, int K, int splits) {
   return skinny_launch{};
 }
 
+static int ring_check(int count, int M, int N, int K, const skinny_ring_launch &r);
+
+// The persistent walk of a chosen launch as a one-item ring launch.
+static skinny_ring_launch walk_launch(const skinny_launch &l, const Walk &w) {
+  skinny_ring_launch r{l, w.segment, w.workgroups};
+  if (w.staged) r.gemm.path = SKINNY_PATH_MFMA_LDS;
+  return r;
+}
+
 // The chooser: a pure function of (M, N, K, splits): the measured table for
-// the shard shapes, the rule above otherwise.
-static int choose(int M, int N, int K, int splits, skinny_launch *out) {
+// the shard shapes, the rule above otherwise; *walk (if asked for) says how
+// the launch runs (table entries only, and only if the walk is valid).
+static int choose(int M, int N, int K, int splits, skinny_launch *out, Walk *walk = nullptr) {
   int st = check_problem(M, N, K);
   if (st) return st;
   if (splits != 0 && (splits < 1 || splits > kMaxSplits || (splits & (splits - 1))))
     return fail(SKINNY_EINVAL, "splits=%d: needs 0 (auto), 1, 2, 4, 8 or 16", splits);
   skinny_launch l{};
+  Walk w{};
   for (const TableEntry &e : kTable)
     if (e.N == N && e.K == K && M >= e.m_lo && M <= e.m_hi &&
         (splits == 0 || splits == e.l.splits) && launch_check(M, N, K, e.l) == SKINNY_OK) {
       l = e.l;
+      if (e.walk.segment && ring_check(1, M, N, K, walk_launch(e.l, e.walk)) == SKINNY_OK)
+        w = e.walk;
       break;
     }
   if (!l.waves) l = rule(M, N, K, splits);
@@ -251,6 +276,7 @@ static int choose(int M, int N, int K, int splits, skinny_launch *out) {
   st = launch_check(M, N, K, l);
   if (st) return st;
   *out = l;
+  if (walk) *walk = w;
   return SKINNY_OK;
 }
 
@@ -469,15 +495,20 @@ static int ring_common(const void *const *x, const void *const *W, void *const *
   return SKINNY_OK;
 }
 
-static int gemm_common(const void *x, const void *W, void *y, int M, int N, int K,
-                       const skinny_launch &l, void *stream, const Publish &pub = Publish{}) {
+static int gemm_pointers(const void *x, const void *W, const void *y, int M, int N, int K) {
   if (!x || !W || !y) return fail(SKINNY_EINVAL, "null pointer");
   if (!aligned(x, 16) || !aligned(W, 16) || !aligned(y, 16))
     return fail(SKINNY_EINVAL, "x, W and y must be 16-byte aligned");
   const size_t xb = 2ul * M * K, wb = 2ul * N * K, yb = 2ul * M * N;
   if (overlap(y, yb, x, xb) || overlap(y, yb, W, wb))
     return fail(SKINNY_EINVAL, "y overlaps x or W");
-  int st = SKINNY_OK;
+  return SKINNY_OK;
+}
+
+static int gemm_common(const void *x, const void *W, void *y, int M, int N, int K,
+                       const skinny_launch &l, void *stream, const Publish &pub = Publish{}) {
+  int st = gemm_pointers(x, W, y, M, N, K);
+  if (st) return st;
   DeviceState *ds = current_state(&st);
   if (!ds) return st;
   const uint16_t *xp = static_cast<const uint16_t *>(x);
@@ -569,7 +600,7 @@ using namespace skinny;
 
 extern "C" {
 
-int skinny_version(void) { return 101; }
+int skinny_version(void) { return 102; }
 
 const char *skinny_last_error(void) { return g_error; }
 
@@ -609,6 +640,16 @@ int skinny_choose(int M, int N, int K, int splits, skinny_launch *out) {
   return choose(M, N, K, splits, out);
 }
 
+int skinny_choose_walk(int M, int N, int K, int splits, skinny_ring_launch *out) {
+  if (!out) return fail(SKINNY_EINVAL, "null output");
+  skinny_launch l;
+  Walk w;
+  int st = choose(M, N, K, splits, &l, &w);
+  if (st) return st;
+  *out = w.segment ? walk_launch(l, w) : skinny_ring_launch{l, 0, 0};
+  return SKINNY_OK;
+}
+
 int skinny_gemm_unsupported(int M, int N, int K, int splits) {
   skinny_launch l;
   return choose(M, N, K, splits, &l);
@@ -622,9 +663,15 @@ int skinny_launch_unsupported(int M, int N, int K, const skinny_launch *launch) 
 int skinny_gemm_bf16(const void *x, const void *W, void *y, int M, int N, int K,
                      int splits, void *stream) {
   skinny_launch l;
-  int st = choose(M, N, K, splits, &l);
+  Walk w;
+  int st = choose(M, N, K, splits, &l, &w);
   if (st) return st;
-  return gemm_common(x, W, y, M, N, K, l, stream);
+  if (!w.segment) return gemm_common(x, W, y, M, N, K, l, stream);
+  st = gemm_pointers(x, W, y, M, N, K);
+  if (st) return st;
+  const void *xs[1] = {x}, *ws[1] = {W};
+  void *ys[1] = {y};
+  return ring_common(xs, ws, ys, 1, M, N, K, walk_launch(l, w), stream);
 }
 
 int skinny_gemm_bf16_launch(const void *x, const void *W, void *y, int M, int N, int K,

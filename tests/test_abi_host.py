@@ -69,9 +69,11 @@ def test_chooser_gives_valid_launches(sk, M, N, K, splits):
     if splits:
         assert launch.splits == splits
     # waves = F * ceil(K / (splits * kw)): kw = 32 * chunks and F = rows / 16
-    # tiles (MFMA), or kw = 512 * chunks and F = 1 (DOT2)
+    # tiles (MFMA), or kw = 512 * chunks (DOT2) or 128 * chunks (MFMA 4x4)
+    # and F = 1
     mfma = launch.path == sk.SKINNY_PATH_MFMA
-    kw = (32 if mfma else 512) * launch.chunks
+    kw = {sk.SKINNY_PATH_MFMA: 32, sk.SKINNY_PATH_DOT2: 512,
+          sk.SKINNY_PATH_MFMA_4X4: 128}[launch.path] * launch.chunks
     F = launch.rows // 16 if mfma else 1
     assert launch.waves == F * -(-K // (launch.splits * kw))
     # pure: the same arguments give the same launch
@@ -105,6 +107,36 @@ def test_launch_unsupported_reasons(sk):
     assert "multiple" in sk.skinny_launch_unsupported(1, 1040, 4096, L(0, 1, 8, 1, 1, 32))
     assert sk.skinny_launch_unsupported(1, 1024, 4096, L(0, 1, 8, 1, 1, 4)) is None
     assert sk.skinny_launch_unsupported(16, 1024, 4096, L(1, 4, 8, 4, 2, 16)) is None
+
+
+@pytest.mark.parametrize("N,K", [(1024, 4096), (8192, 1024), (512, 8192), (4096, 8192), (48, 1000)])
+@pytest.mark.parametrize("M", range(1, 17))
+def test_chooser_walk(sk, M, N, K):
+    """skinny_choose_walk describes what skinny_gemm_bf16 runs: the plain
+    kernel at skinny_choose's launch, or a valid one-item ring launch with the
+    same arithmetic (the staged MFMA ring standing for the MFMA launch)."""
+    launch = sk.skinny_choose(M, N, K, 0)
+    walk = sk.skinny_choose_walk(M, N, K, 0)
+    if walk.segment == 0:
+        assert walk.gemm == launch and walk.workgroups == 0
+    else:
+        g = walk.gemm
+        if g.path == sk.SKINNY_PATH_MFMA_LDS:
+            g = g._replace(path=sk.SKINNY_PATH_MFMA)
+        assert g == launch
+        assert sk.skinny_ring_launch_unsupported(M, N, K, 1, walk) is None
+    assert sk.skinny_choose_walk(M, N, K, 0) == walk
+
+
+def test_chooser_walks_the_measured_shapes(sk):
+    """The shapes whose single calls measured faster as a persistent walk."""
+    for M, N, K in [(2, 1024, 4096), (4, 1024, 4096), (3, 8192, 1024), (8, 8192, 1024),
+                    (16, 8192, 1024), (8, 4096, 8192), (16, 4096, 8192)]:
+        assert sk.skinny_choose_walk(M, N, K, 0).segment > 0, (M, N, K)
+    for M, N, K in [(1, 1024, 4096), (16, 1024, 4096), (1, 8192, 1024), (48, 96, 1000)][:3]:
+        assert sk.skinny_choose_walk(M, N, K, 0).segment == 0, (M, N, K)
+    with pytest.raises(ValueError, match="M=17"):
+        sk.skinny_choose_walk(17, 1024, 4096, 0)
 
 
 def test_mfma_4x4_launch_reasons(sk):

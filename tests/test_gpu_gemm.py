@@ -234,3 +234,19 @@ def test_split_k_handoff_alternating_inputs(gpu_lib, path, splits):
         assert_gemm_close(first[j], refs[j], f"alternating {path} S={splits} weight {j}")
     for i, y in enumerate(ys):
         assert np.array_equal(from_dev(y), first[i % 2]), f"call {i} differs"
+
+
+@pytest.mark.parametrize("N,K", [(1024, 4096), (8192, 1024), (512, 8192), (4096, 8192)])
+def test_chooser_walk_is_bitwise_the_plain_launch(gpu_lib, N, K):
+    """skinny_gemm_bf16 runs some shapes as a persistent walk (the ring kernel
+    with one item): bit for bit the plain kernel at skinny_choose's launch,
+    within tolerance of the oracle, and no write outside y."""
+    x, w = synthetic.gemm_inputs(N=N, K=K, seed=31)
+    ref16 = oracle.gemm_bf16(x[:16], w, THREADS)  # rows are independent
+    for M in (1, 2, 3, 4, 5, 8, 9, 16):
+        walk = gpu_lib.skinny_choose_walk(M, N, K, 0)
+        launch = gpu_lib.skinny_choose(M, N, K, 0)
+        _say(f"chooser N={N} K={K} M={M} walk={walk}")
+        y = _run(gpu_lib, x, w, M)
+        assert np.array_equal(y, _run(gpu_lib, x, w, M, launch=launch)), f"M={M} {walk}"
+        assert_gemm_close(y, ref16[:M], f"M={M} {walk}")
