@@ -67,7 +67,8 @@ enum {
  *         each keeping `accs` FP32 accumulators.
  *   DOT2: a workgroup owns `rows` output features; each wave owns
  *         kw = 512 * chunks consecutive K (64 lanes x 8 bf16 per chunk);
- *         waves = ceil(K / (splits * kw)).
+ *         waves = ceil(K / (splits * kw)) <= 16 (more than 8 only for the
+ *         register-light variants).
  *   MFMA_4X4: a workgroup owns rows = 4 or 8 output features; each wave owns
  *         kw = 128 * chunks consecutive K (16 blocks x 8 bf16 per chunk,
  *         chunks 1, 2, 4, 8) and all tokens in sets of 4;

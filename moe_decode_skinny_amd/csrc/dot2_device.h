@@ -9,7 +9,7 @@
 namespace skinny {
 namespace dot2 {
 
-constexpr int kDot2MaxThreads = 512;  // launch bound of the DOT2 kernels
+constexpr int kDot2MaxThreads = 512;  // launch bound of the DOT2 kernels' 8-wave form
 
 // Eight bf16 products accumulated in FP32 by four v_dot2_f32_bf16.  The
 // operands are split with vector shuffles of a whole-vector bit cast (a bit

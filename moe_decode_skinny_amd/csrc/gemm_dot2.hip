@@ -21,8 +21,10 @@ namespace {
 
 using namespace dot2;
 
-template <int ROWS, int CHUNKS, int MT>
-__global__ __launch_bounds__(kDot2MaxThreads) void gemm_dot2_kernel(
+// THREADS: the launch bound, 512, or 1024 for the register-light variants
+// that run 16 waves (long K at one chunk per wave).
+template <int ROWS, int CHUNKS, int MT, int THREADS>
+__global__ __launch_bounds__(THREADS) void gemm_dot2_kernel(
     const uint16_t *__restrict__ x, const uint16_t *__restrict__ w,
     uint16_t *__restrict__ y, float *__restrict__ partials, int M, int N, int K,
     int S, int groups, int kw, Publish pub) {
@@ -96,7 +98,7 @@ __global__ __launch_bounds__(kDot2MaxThreads) void gemm_dot2_kernel(
 
   // Waves in order through LDS; lane i < ROWS * MT then owns (row i / MT,
   // token i % MT).
-  __shared__ float red[kDot2MaxThreads / 64][kOut];
+  __shared__ float red[THREADS / 64][kOut];
   if ((lane & ((1 << kShift) - 1)) == 0) red[wave][lane >> kShift] = v[0];
   __syncthreads();
   if (wave != 0) return;
@@ -121,46 +123,57 @@ using Dot2Kernel = void (*)(const uint16_t *, const uint16_t *, uint16_t *,
                             float *, int, int, int, int, int, int, Publish);
 
 // Register budget per lane: weights 4 * ROWS * CHUNKS, activations
-// 4 * MT * CHUNKS, sums ROWS * MT.  Variants above the budget are not built.
-constexpr bool fits(int rows, int chunks, int mt) {
-  return 4 * rows * chunks + 4 * mt * chunks + rows * mt <= 160;
+// 4 * MT * CHUNKS, sums ROWS * MT: at most 160 for 8 waves, 112 for the
+// 16-wave form (128 registers a lane, less the addresses).  Variants above
+// the budget are not built.
+constexpr bool fits(int rows, int chunks, int mt, int threads) {
+  return 4 * rows * chunks + 4 * mt * chunks + rows * mt <= (threads > 512 ? 112 : 160);
 }
 
-template <int R, int C, int T>
+template <int R, int C, int T, int THREADS>
 constexpr Dot2Kernel variant() {
-  if constexpr (fits(R, C, T)) return gemm_dot2_kernel<R, C, T>;
+  if constexpr (fits(R, C, T, THREADS)) return gemm_dot2_kernel<R, C, T, THREADS>;
   else return nullptr;
 }
 
-template <int R, int C>
+template <int R, int C, int THREADS>
 Dot2Kernel pick_mt(int mt) {
   switch (mt) {
-    case 1: return variant<R, C, 1>();
-    case 2: return variant<R, C, 2>();
-    case 4: return variant<R, C, 4>();
-    case 8: return variant<R, C, 8>();
-    case 16: return variant<R, C, 16>();
+    case 1: return variant<R, C, 1, THREADS>();
+    case 2: return variant<R, C, 2, THREADS>();
+    case 4: return variant<R, C, 4, THREADS>();
+    case 8: return variant<R, C, 8, THREADS>();
+    case 16: return variant<R, C, 16, THREADS>();
   }
   return nullptr;
 }
 
-template <int R>
+template <int R, int THREADS>
 Dot2Kernel pick_chunks(int chunks, int mt) {
   switch (chunks) {
-    case 1: return pick_mt<R, 1>(mt);
-    case 2: return pick_mt<R, 2>(mt);
-    case 4: return pick_mt<R, 4>(mt);
+    case 1: return pick_mt<R, 1, THREADS>(mt);
+    case 2: return pick_mt<R, 2, THREADS>(mt);
+    case 4: return pick_mt<R, 4, THREADS>(mt);
   }
   return nullptr;
 }
 
-Dot2Kernel pick(int rows, int chunks, int mt) {
+template <int THREADS>
+Dot2Kernel pick_rows(int rows, int chunks, int mt) {
   switch (rows) {
-    case 2: return pick_chunks<2>(chunks, mt);
-    case 4: return pick_chunks<4>(chunks, mt);
-    case 8: return pick_chunks<8>(chunks, mt);
-    case 16: return pick_chunks<16>(chunks, mt);
+    case 2: return pick_chunks<2, THREADS>(chunks, mt);
+    case 4: return pick_chunks<4, THREADS>(chunks, mt);
+    case 8: return pick_chunks<8, THREADS>(chunks, mt);
+    case 16: return pick_chunks<16, THREADS>(chunks, mt);
   }
+  return nullptr;
+}
+
+// The variant for a launch of `waves` waves: the 8-wave form up to 8 waves,
+// the 16-wave form beyond.
+Dot2Kernel pick(int rows, int chunks, int mt, int waves) {
+  if (waves >= 1 && waves <= kDot2MaxThreads / 64) return pick_rows<kDot2MaxThreads>(rows, chunks, mt);
+  if (waves > kDot2MaxThreads / 64 && waves <= 16) return pick_rows<1024>(rows, chunks, mt);
   return nullptr;
 }
 
@@ -175,16 +188,16 @@ int dot2_token_tile(int M) {
   return 0;
 }
 
-bool dot2_variant_exists(int rows, int chunks, int mt) {
-  return pick(rows, chunks, mt) != nullptr;
+bool dot2_variant_exists(int rows, int chunks, int mt, int waves) {
+  return pick(rows, chunks, mt, waves) != nullptr;
 }
 
-int dot2_max_waves() { return kDot2MaxThreads / 64; }
+int dot2_max_waves() { return 16; }
 
 hipError_t launch_gemm_dot2(const uint16_t *x, const uint16_t *w, uint16_t *y,
                             int M, int N, int K, const skinny_launch &l,
                             DeviceState &st, const Publish &pub, hipStream_t stream) {
-  Dot2Kernel k = pick(l.rows, l.chunks, dot2_token_tile(M));
+  Dot2Kernel k = pick(l.rows, l.chunks, dot2_token_tile(M), l.waves);
   const int groups = N / l.rows;
   dim3 grid(groups * l.splits), block(64 * l.waves);
   hipLaunchKernelGGL(k, grid, block, 0, stream, x, w, y, st.partials, M, N, K, l.splits,

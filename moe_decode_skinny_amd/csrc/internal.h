@@ -48,9 +48,9 @@ bool mfma_variant_exists(int chunks, int accs);
 int mfma_max_waves(int chunks);  // waves per MFMA workgroup (launch bound)
 size_t mfma_lds_bytes(int M, const skinny_launch &l);  // dynamic LDS of a launch
 hipError_t mfma_prepare();  // per-device kernel attributes (skinny_init)
-bool dot2_variant_exists(int rows, int chunks, int mt);
+bool dot2_variant_exists(int rows, int chunks, int mt, int waves);
 int dot2_token_tile(int M);  // smallest compiled token count >= M, 0 if none
-int dot2_max_waves();        // waves per DOT2 workgroup (launch bound)
+int dot2_max_waves();        // waves per DOT2 workgroup (the 16-wave form's bound)
 int blocks_token_sets(int M);  // 4-token sets of the 16-block MFMA path (1, 2, 4), 0 if none
 bool blocks_variant_exists(int rows, int chunks, int q, int waves);
 bool ring_variant_exists(int rows, int chunks, int mt, int waves);  // DOT2 ring (<= 16 waves)

@@ -114,9 +114,6 @@ static int launch_check(int M, int N, int K, const skinny_launch &l) {
     if (l.accs != 1) return fail(SKINNY_EUNSUPPORTED, "DOT2 launch has accs=1");
     if (l.rows <= 0 || N % l.rows)
       return fail(SKINNY_EUNSUPPORTED, "N=%d is not a multiple of rows=%d", N, l.rows);
-    if (!dot2_variant_exists(l.rows, l.chunks, mt))
-      return fail(SKINNY_EUNSUPPORTED, "no DOT2 kernel with rows=%d chunks=%d tokens=%d",
-                  l.rows, l.chunks, mt);
     const long kw = (long)kDot2K * l.chunks;
     const int need = ceil_div(K, (long)l.splits * kw);
     if (l.waves != need)
@@ -125,6 +122,10 @@ static int launch_check(int M, int N, int K, const skinny_launch &l) {
     if (l.waves < 1 || l.waves > dot2_max_waves())
       return fail(SKINNY_EUNSUPPORTED, "%d waves per workgroup (DOT2: 1..%d)", l.waves,
                   dot2_max_waves());
+    if (!dot2_variant_exists(l.rows, l.chunks, mt, l.waves))
+      return fail(SKINNY_EUNSUPPORTED, "no DOT2 kernel with rows=%d chunks=%d tokens=%d at %d "
+                  "waves (more than 8 waves: only the register-light variants)", l.rows,
+                  l.chunks, mt, l.waves);
     return SKINNY_OK;
   }
   if (l.path == SKINNY_PATH_MFMA_4X4) {
@@ -185,7 +186,7 @@ static const TableEntry kTable[] = {
     // pooler shard
     {512, 8192, 1, 4, {SKINNY_PATH_DOT2, 1, 4, 4, 1, 2}},
     {512, 8192, 5, 8, {SKINNY_PATH_DOT2, 1, 8, 2, 1, 2}},
-    {512, 8192, 9, 16, {SKINNY_PATH_DOT2, 2, 8, 1, 1, 4}},
+    {512, 8192, 9, 16, {SKINNY_PATH_DOT2, 1, 16, 1, 1, 2}},
     // full pooler
     {4096, 8192, 1, 1, {SKINNY_PATH_DOT2, 1, 8, 2, 1, 2}},
     {4096, 8192, 2, 4, {SKINNY_PATH_DOT2, 1, 8, 2, 1, 8}},

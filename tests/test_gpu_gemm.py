@@ -133,7 +133,8 @@ def _all_launches(sk, M, N, K):
     return out
 
 
-@pytest.mark.parametrize("M,N,K", [(1, 64, 1024), (3, 48, 1000), (7, 128, 2048), (16, 32, 520)])
+@pytest.mark.parametrize("M,N,K", [(1, 64, 1024), (3, 48, 1000), (7, 128, 2048), (16, 32, 520),
+                                   (16, 32, 8000)])
 def test_every_launch_shape(gpu_lib, M, N, K):
     """Every compiled variant the validator accepts, on a small ragged case
     (N with tiles % 8 != 0, K not a multiple of the chunk)."""
