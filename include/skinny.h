@@ -178,17 +178,27 @@ int skinny_gemm_bf16_publish(const void *x, const void *W, void *y, int M,
  *               rows / 16 * ceil(K / (32 chunks)) <= 16, <= 8 at 16 chunks)
  *               or MFMA_LDS (as MFMA with chunks 2..16, and the staging
  *               regions, waves x 16 x (64 chunks + 16) bytes, plus 2 KiB per
- *               wave, within the 160 KiB of LDS)
+ *               wave, within the 160 KiB of LDS) or MFMA_4X4 (rows 4 or 8,
+ *               chunks 1..8, waves = ceil(K / (128 chunks)) <= 16)
  *   segment     consecutive output blocks of one item a workgroup takes in a
  *               row, keeping that item's activations in registers; it
  *               divides N / gemm.rows
  *   workgroups  persistent workgroups, 1 .. count * N / (rows * segment);
- *               workgroup b takes segments b, b + workgroups, ... of the
- *               item-major segment order */
+ *               workgroup b takes segment slots b, b + workgroups, ...
+ *   order       how slots map to segments: SKINNY_RING_ITEM_MAJOR (slot t is
+ *               segment t of the item-major order) or SKINNY_RING_XCD_LOCAL
+ *               (when workgroups is a multiple of 8, slot t of the first
+ *               8 (count / 8) items belongs to an item congruent to t mod 8,
+ *               so all segments of such an item run on one of the eight XCDs
+ *               and its activations reach one L2; the other items, and any
+ *               workgroup count that is not a multiple of 8, item-major).
+ *               The order never changes a result. */
+enum { SKINNY_RING_ITEM_MAJOR = 0, SKINNY_RING_XCD_LOCAL = 1 };
 typedef struct skinny_ring_launch {
   skinny_launch gemm;
   int segment;
   int workgroups;
+  int order;
 } skinny_ring_launch;
 
 /* The layer ring: `count` independent GEMMs y_i = bf16(x_i @ W_i^T) of one

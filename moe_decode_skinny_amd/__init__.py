@@ -37,6 +37,8 @@ SKINNY_PATH_DOT2 = 0
 SKINNY_PATH_MFMA = 1
 SKINNY_PATH_MFMA_LDS = 2
 SKINNY_PATH_MFMA_4X4 = 3
+SKINNY_RING_ITEM_MAJOR = 0
+SKINNY_RING_XCD_LOCAL = 1
 
 if not os.path.exists(LIB_PATH):
     raise ImportError(
@@ -72,23 +74,26 @@ class _CMailbox(ctypes.Structure):
 
 
 class _CRingLaunch(ctypes.Structure):
-    _fields_ = [("gemm", _CLaunch), ("segment", ctypes.c_int), ("workgroups", ctypes.c_int)]
+    _fields_ = [("gemm", _CLaunch), ("segment", ctypes.c_int), ("workgroups", ctypes.c_int),
+                ("order", ctypes.c_int)]
 
 
 class RingLaunch(NamedTuple):
-    """skinny_ring_launch: gemm (a Launch with splits = 1), segment, workgroups."""
+    """skinny_ring_launch: gemm (a Launch with splits = 1), segment, workgroups,
+    order (SKINNY_RING_ITEM_MAJOR or SKINNY_RING_XCD_LOCAL)."""
     gemm: Launch
     segment: int
     workgroups: int
+    order: int = 0
 
     def _c(self) -> _CRingLaunch:
-        return _CRingLaunch(Launch(*self.gemm)._c(), self.segment, self.workgroups)
+        return _CRingLaunch(Launch(*self.gemm)._c(), self.segment, self.workgroups, self.order)
 
     @staticmethod
     def _from_c(c: _CRingLaunch) -> "RingLaunch":
         g = c.gemm
         return RingLaunch(Launch(g.path, g.splits, g.waves, g.chunks, g.accs, g.rows),
-                          c.segment, c.workgroups)
+                          c.segment, c.workgroups, c.order)
 
 
 _vp = ctypes.c_void_p

@@ -13,11 +13,17 @@
 // workgroup starts on an item, after the weights of the tile before.
 //
 // Tile order.  The count * groups tiles (groups = N / rows output blocks per
-// item) are cut into segments of `seg` consecutive blocks of one item, in
-// item-major order; workgroup b takes segments b, b + G, b + 2 G, ... (G
-// workgroups) and the blocks of each in order.  A wave's activations depend
-// only on the item and its K range, so they stay in registers for the whole
-// segment: the activation traffic is that of one tile per segment.
+// item) are cut into segments of `seg` consecutive blocks of one item;
+// workgroup b takes segment slots b, b + G, b + 2 G, ... (G workgroups) and
+// the blocks of each segment in order.  A wave's activations depend only on
+// the item and its K range, so they stay in registers for the whole segment:
+// the activation traffic is that of one tile per segment.  Slots map to
+// segments item-major, or (the XCD-local order) so that, when G is a
+// multiple of 8, every segment of one item runs on one XCD (workgroups are dealt to the eight XCDs round-robin, so slot t
+// runs on XCD t mod 8): slot t < local belongs to item (t mod 8) + 8 q, where
+// q = (t div 8) div spi, for the first 8 (count div 8) items; the remaining
+// items follow in item-major order.  Each item's activations then reach one
+// XCD's L2 instead of all eight.  Any slot order computes the same tiles.
 //
 // Per tile the arithmetic is that of the single-call kernel of the same
 // family with splits = 1 at the same (rows, chunks, waves, accs): the same
@@ -40,8 +46,29 @@ using namespace dot2;
 struct RingWalk {
   int groups, seg, spi, segs;  // blocks per item, blocks per segment,
                                // segments per item, segments in all
-  __device__ int item(int s) const { return s / spi; }
-  __device__ int block(int s, int sub) const { return (s - item(s) * spi) * seg + sub; }
+  int local;                   // slots dealt XCD by XCD (0: item-major only)
+  // Item and segment-in-item of slot s.
+  __device__ void place(int s, int &item, int &j) const {
+    if (s < local) {
+      const int r = s >> 3, q = r / spi;
+      item = (s & 7) + 8 * q;
+      j = r - q * spi;
+    } else {
+      const int t = s - local, q = t / spi;
+      item = local / spi + q;
+      j = t - q * spi;
+    }
+  }
+  __device__ int item(int s) const {
+    int i, j;
+    place(s, i, j);
+    return i;
+  }
+  __device__ int block(int s, int sub) const {
+    int i, j;
+    place(s, i, j);
+    return j * seg + sub;
+  }
   // The tile after (s, sub) for this workgroup; false past the last one.
   __device__ bool advance(int &s, int &sub) const {
     if (++sub == seg) {
@@ -635,7 +662,11 @@ hipError_t launch_gemm_ring(const RingItems &items, int count, int M, int N, int
                             const skinny_ring_launch &r, hipStream_t stream) {
   const skinny_launch &l = r.gemm;
   const int groups = N / l.rows;
-  const RingWalk walk{groups, r.segment, groups / r.segment, count * (groups / r.segment)};
+  const int spi = groups / r.segment;
+  // XCD-local slots only when the workgroups divide evenly over the 8 XCDs.
+  const int local =
+      r.order == SKINNY_RING_XCD_LOCAL && r.workgroups % 8 == 0 ? (count / 8) * 8 * spi : 0;
+  const RingWalk walk{groups, r.segment, spi, count * spi, local};
   if (l.path == SKINNY_PATH_MFMA || l.path == SKINNY_PATH_MFMA_LDS) {
     hipLaunchKernelGGL(mfma_ring_pick(l.chunks, l.accs, l.path == SKINNY_PATH_MFMA_LDS),
                        dim3(r.workgroups), dim3(64 * l.waves), mfma_ring_lds_bytes(l), stream,

@@ -247,7 +247,7 @@ static int ring_check(int count, int M, int N, int K, const skinny_ring_launch &
 
 // The persistent walk of a chosen launch as a one-item ring launch.
 static skinny_ring_launch walk_launch(const skinny_launch &l, const Walk &w) {
-  skinny_ring_launch r{l, w.segment, w.workgroups};
+  skinny_ring_launch r{l, w.segment, w.workgroups, SKINNY_RING_ITEM_MAJOR};
   if (w.staged) r.gemm.path = SKINNY_PATH_MFMA_LDS;
   return r;
 }
@@ -339,6 +339,9 @@ static int ring_check(int count, int M, int N, int K, const skinny_ring_launch &
   } else {
     return fail(SKINNY_EUNSUPPORTED, "unknown path %d", l.path);
   }
+  if (r.order != SKINNY_RING_ITEM_MAJOR && r.order != SKINNY_RING_XCD_LOCAL)
+    return fail(SKINNY_EUNSUPPORTED, "order=%d: needs SKINNY_RING_ITEM_MAJOR (0) or "
+                "SKINNY_RING_XCD_LOCAL (1)", r.order);
   const int groups = N / l.rows;
   if (r.segment < 1 || groups % r.segment)
     return fail(SKINNY_EUNSUPPORTED, "segment=%d must divide the %d blocks of an item",
@@ -357,36 +360,42 @@ struct RingEntry {
   int N, K, m_lo, m_hi;
   skinny_ring_launch r;
 };
-#define DOT2_RING(waves, chunks, rows, seg, wg) \
-  { {SKINNY_PATH_DOT2, 1, waves, chunks, 1, rows}, seg, wg }
-#define LDS_RING(waves, chunks, accs, rows, seg, wg) \
-  { {SKINNY_PATH_MFMA_LDS, 1, waves, chunks, accs, rows}, seg, wg }
-#define MFMA4X4_RING(waves, chunks, rows, seg, wg) \
-  { {SKINNY_PATH_MFMA_4X4, 1, waves, chunks, 1, rows}, seg, wg }
+// order: I = item-major, X = XCD-local (SKINNY_RING_*).
+#define I SKINNY_RING_ITEM_MAJOR
+#define X SKINNY_RING_XCD_LOCAL
+#define DOT2_RING(waves, chunks, rows, seg, wg, order) \
+  { {SKINNY_PATH_DOT2, 1, waves, chunks, 1, rows}, seg, wg, order }
+#define LDS_RING(waves, chunks, accs, rows, seg, wg, order) \
+  { {SKINNY_PATH_MFMA_LDS, 1, waves, chunks, accs, rows}, seg, wg, order }
+#define MFMA4X4_RING(waves, chunks, rows, seg, wg, order) \
+  { {SKINNY_PATH_MFMA_4X4, 1, waves, chunks, 1, rows}, seg, wg, order }
 static const RingEntry kRingTable[] = {
     // unpooler shard
-    {1024, 4096, 1, 1, DOT2_RING(2, 4, 2, 1, 1024)},
-    {1024, 4096, 2, 2, DOT2_RING(8, 1, 8, 2, 2048)},
-    {1024, 4096, 3, 4, DOT2_RING(4, 2, 4, 4, 1024)},
-    {1024, 4096, 5, 8, MFMA4X4_RING(8, 4, 8, 32, 240)},
-    {1024, 4096, 9, 16, LDS_RING(8, 16, 2, 16, 8, 256)},
+    {1024, 4096, 1, 1, DOT2_RING(2, 4, 2, 1, 1024, I)},
+    {1024, 4096, 2, 2, DOT2_RING(8, 1, 8, 2, 2048, I)},
+    {1024, 4096, 3, 4, DOT2_RING(4, 2, 4, 4, 1024, I)},
+    {1024, 4096, 5, 8, MFMA4X4_RING(8, 4, 8, 32, 240, X)},
+    {1024, 4096, 9, 16, LDS_RING(8, 16, 2, 16, 8, 240, X)},
     // o_proj shard
-    {8192, 1024, 1, 1, MFMA4X4_RING(2, 4, 4, 8, 1024)},
-    {8192, 1024, 2, 2, DOT2_RING(2, 1, 8, 8, 512)},
-    {8192, 1024, 3, 4, MFMA4X4_RING(2, 4, 8, 8, 512)},
-    {8192, 1024, 5, 8, LDS_RING(4, 16, 2, 32, 2, 256)},
-    {8192, 1024, 9, 16, LDS_RING(4, 16, 2, 32, 16, 256)},
+    {8192, 1024, 1, 1, MFMA4X4_RING(2, 4, 4, 8, 1024, I)},
+    {8192, 1024, 2, 2, DOT2_RING(2, 1, 8, 8, 512, I)},
+    {8192, 1024, 3, 4, MFMA4X4_RING(2, 4, 8, 8, 512, I)},
+    {8192, 1024, 5, 8, LDS_RING(4, 16, 2, 32, 2, 256, I)},
+    {8192, 1024, 9, 16, LDS_RING(2, 16, 2, 16, 8, 256, X)},
     // pooler shard
-    {512, 8192, 1, 1, DOT2_RING(4, 4, 2, 1, 1024)},
-    {512, 8192, 2, 2, DOT2_RING(16, 1, 2, 4, 512)},
-    {512, 8192, 3, 4, MFMA4X4_RING(16, 4, 4, 32, 240)},
-    {512, 8192, 5, 8, MFMA4X4_RING(8, 8, 4, 32, 240)},
-    {512, 8192, 9, 16, MFMA4X4_RING(16, 4, 4, 32, 240)},
+    {512, 8192, 1, 1, DOT2_RING(4, 4, 2, 1, 2048, I)},
+    {512, 8192, 2, 2, DOT2_RING(16, 1, 2, 4, 512, I)},
+    {512, 8192, 3, 4, MFMA4X4_RING(16, 4, 4, 32, 240, I)},
+    {512, 8192, 5, 8, MFMA4X4_RING(8, 8, 4, 32, 240, X)},
+    {512, 8192, 9, 16, MFMA4X4_RING(16, 4, 4, 32, 240, X)},
     // full pooler
-    {4096, 8192, 1, 2, DOT2_RING(4, 4, 2, 8, 256)},
-    {4096, 8192, 3, 8, DOT2_RING(8, 2, 4, 16, 256)},
-    {4096, 8192, 9, 16, MFMA4X4_RING(16, 4, 4, 64, 960)},
+    {4096, 8192, 1, 2, DOT2_RING(4, 4, 2, 8, 256, I)},
+    {4096, 8192, 3, 4, DOT2_RING(8, 2, 4, 16, 256, I)},
+    {4096, 8192, 5, 8, MFMA4X4_RING(16, 4, 4, 128, 480, X)},
+    {4096, 8192, 9, 16, MFMA4X4_RING(16, 4, 4, 128, 480, X)},
 };
+#undef I
+#undef X
 #undef DOT2_RING
 #undef LDS_RING
 #undef MFMA4X4_RING
@@ -433,7 +442,7 @@ static int ring_choose(int M, int N, int K, int count, skinny_ring_launch *out) 
     const long segs = (long)count * (groups / seg);
     for (int c = 4; c >= 1; c /= 2) {
       const skinny_ring_launch r{{SKINNY_PATH_MFMA_4X4, 1, ceil_div(K, (long)kBlockK * c), c, 1, 4},
-                                 seg, (int)(segs < 256 ? segs : 256)};
+                                 seg, (int)(segs < 256 ? segs : 256), SKINNY_RING_XCD_LOCAL};
       if (ring_check(count, M, N, K, r) == SKINNY_OK) {
         *out = r;
         return SKINNY_OK;
@@ -601,7 +610,7 @@ using namespace skinny;
 
 extern "C" {
 
-int skinny_version(void) { return 102; }
+int skinny_version(void) { return 103; }
 
 const char *skinny_last_error(void) { return g_error; }
 
@@ -647,7 +656,7 @@ int skinny_choose_walk(int M, int N, int K, int splits, skinny_ring_launch *out)
   Walk w;
   int st = choose(M, N, K, splits, &l, &w);
   if (st) return st;
-  *out = w.segment ? walk_launch(l, w) : skinny_ring_launch{l, 0, 0};
+  *out = w.segment ? walk_launch(l, w) : skinny_ring_launch{l, 0, 0, SKINNY_RING_ITEM_MAJOR};
   return SKINNY_OK;
 }
 

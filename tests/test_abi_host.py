@@ -268,6 +268,13 @@ def test_ring_launch_reasons_without_device(sk):
     assert call((2, 1, 8, 16, 1, 16)) in (sk.SKINNY_EDEVICE, sk.SKINNY_ENOTINIT)
     assert call((0, 2, 1, 4, 1, 2)) == sk.SKINNY_EUNSUPPORTED
     assert "splits=1" in sk.skinny_last_error()
+    c = sk.RingLaunch(sk.Launch(0, 1, 2, 4, 1, 2), 1, 512, 2)._c()
+    assert lib.skinny_gemm_bf16_ring_launch(x, w, y, 1, M, N, K, ctypes.byref(c), None) == \
+        sk.SKINNY_EUNSUPPORTED
+    assert "order=2" in sk.skinny_last_error()
+    c = sk.RingLaunch(sk.Launch(0, 1, 2, 4, 1, 2), 1, 512, sk.SKINNY_RING_XCD_LOCAL)._c()
+    assert lib.skinny_gemm_bf16_ring_launch(x, w, y, 1, M, N, K, ctypes.byref(c), None) in (
+        sk.SKINNY_EDEVICE, sk.SKINNY_ENOTINIT)
     assert call((0, 1, 3, 4, 1, 2)) == sk.SKINNY_EUNSUPPORTED
     assert "waves" in sk.skinny_last_error()
     assert call((0, 1, 2, 4, 1, 2), wg=513) == sk.SKINNY_EUNSUPPORTED

@@ -176,6 +176,33 @@ def test_ring_every_launch_and_walk(gpu_lib, M, N, K):
     assert tried
 
 
+@pytest.mark.parametrize("path", ["dot2", "mfma_4x4", "mfma_lds"])
+def test_ring_xcd_local_walk(gpu_lib, path):
+    """19 items: in the XCD-local order with a workgroup count divisible by 8
+    the first 16 items' segments are dealt XCD by XCD and the last 3 follow
+    item-major; with other counts, and in the item-major order, all slots are
+    item-major.  Every item must be bitwise the single call at the same
+    launch under every walk and order."""
+    M, N, K, count = 12, 128, 1032, 19
+    g = {"dot2": gpu_lib.Launch(0, 1, 3, 1, 1, 4),
+         "mfma_4x4": gpu_lib.Launch(3, 1, 5, 2, 1, 8),
+         "mfma_lds": gpu_lib.Launch(2, 1, 9, 4, 1, 16)}[path]
+    xs, ws = _items(count, N, K, seed=250)
+    singles = [_single(gpu_lib, xs[i], ws[i], M, g) for i in range(count)]
+    for i in (0, count - 1):
+        assert_gemm_close(singles[i], oracle.gemm_bf16(xs[i][:M], ws[i], THREADS), f"item {i}")
+    groups = N // g.rows
+    for seg in (1, 2, groups):
+        for wg in (8, 16, 24, 12, 7):
+            for order in (gpu_lib.SKINNY_RING_XCD_LOCAL, gpu_lib.SKINNY_RING_ITEM_MAJOR):
+                launch = gpu_lib.RingLaunch(g, seg, min(wg, count * groups // seg), order)
+                assert gpu_lib.skinny_ring_launch_unsupported(M, N, K, count, launch) is None
+                _say(f"xcd walk {path} {launch}")
+                ys = _ring(gpu_lib, xs, ws, M, launch=launch)
+                for i in range(count):
+                    assert np.array_equal(ys[i], singles[i]), f"{launch} item {i}"
+
+
 def test_ring_max_count(gpu_lib):
     """64 items (the most one call takes) on a small ragged shape."""
     M, N, K = 4, 64, 1032
