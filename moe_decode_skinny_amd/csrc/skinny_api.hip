@@ -373,24 +373,24 @@ static const RingEntry kRingTable[] = {
     // unpooler shard
     {1024, 4096, 1, 1, DOT2_RING(2, 4, 2, 1, 1024, I)},
     {1024, 4096, 2, 2, DOT2_RING(8, 1, 8, 2, 2048, I)},
-    {1024, 4096, 3, 4, DOT2_RING(4, 2, 4, 4, 1024, I)},
+    {1024, 4096, 3, 4, DOT2_RING(8, 1, 4, 4, 2048, X)},
     {1024, 4096, 5, 8, MFMA4X4_RING(8, 4, 8, 32, 240, X)},
-    {1024, 4096, 9, 16, LDS_RING(8, 16, 2, 16, 8, 240, X)},
+    {1024, 4096, 9, 16, LDS_RING(8, 16, 1, 16, 16, 240, X)},
     // o_proj shard
     {8192, 1024, 1, 1, MFMA4X4_RING(2, 4, 4, 8, 1024, I)},
-    {8192, 1024, 2, 2, DOT2_RING(2, 1, 8, 8, 512, I)},
-    {8192, 1024, 3, 4, MFMA4X4_RING(2, 4, 8, 8, 512, I)},
-    {8192, 1024, 5, 8, LDS_RING(4, 16, 2, 32, 2, 256, I)},
+    {8192, 1024, 2, 2, DOT2_RING(1, 2, 8, 1, 512, X)},
+    {8192, 1024, 3, 4, DOT2_RING(1, 2, 4, 1, 1024, X)},
+    {8192, 1024, 5, 8, LDS_RING(4, 16, 1, 32, 1, 256, X)},
     {8192, 1024, 9, 16, LDS_RING(2, 16, 2, 16, 8, 256, X)},
     // pooler shard
     {512, 8192, 1, 1, DOT2_RING(4, 4, 2, 1, 2048, I)},
-    {512, 8192, 2, 2, DOT2_RING(16, 1, 2, 4, 512, I)},
-    {512, 8192, 3, 4, MFMA4X4_RING(16, 4, 4, 32, 240, I)},
+    {512, 8192, 2, 2, DOT2_RING(4, 4, 2, 4, 2048, X)},
+    {512, 8192, 3, 4, DOT2_RING(4, 4, 2, 4, 1024, X)},
     {512, 8192, 5, 8, MFMA4X4_RING(8, 8, 4, 32, 240, X)},
     {512, 8192, 9, 16, MFMA4X4_RING(16, 4, 4, 32, 240, X)},
     // full pooler
     {4096, 8192, 1, 2, DOT2_RING(4, 4, 2, 8, 256, I)},
-    {4096, 8192, 3, 4, DOT2_RING(8, 2, 4, 16, 256, I)},
+    {4096, 8192, 3, 4, DOT2_RING(16, 1, 4, 4, 240, X)},
     {4096, 8192, 5, 8, MFMA4X4_RING(16, 4, 4, 128, 480, X)},
     {4096, 8192, 9, 16, MFMA4X4_RING(16, 4, 4, 128, 480, X)},
 };
