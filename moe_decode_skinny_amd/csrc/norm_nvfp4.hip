@@ -7,9 +7,16 @@
 // nvfp4_compute_output_scale (the reciprocal of dec(sf) / global_scale, zero
 // when dec(sf) is zero).
 //
-// gfx950 design: one workgroup of 256 threads per row; thread t owns whole
-// 16-column blocks (t, t + 256, ...), so a block's amax, scale and codes stay
-// in one thread and its 8 code bytes leave as one 8-byte store.
+// gfx950 design: a row is spread over C = ceil(P / 1024) workgroups of 256
+// threads.  Every workgroup of the row computes the row's sum of squares
+// itself (thread t sums the 16-column blocks t, t + 256, ... in column
+// order; the row is re-read from L2), so all of them reach the same bits
+// without talking to each other; then workgroup c quantises blocks
+// 64 c .. 64 c + 63 with four threads a block (four columns each: the block
+// amax is a max over the quad, the scale is computed by all four alike, and
+// each thread stores its four codes as two bytes).  Spreading a block's
+// binary64 encoding over four threads and a row over C compute units cut the
+// kernel's serial chain; the codes are the same.
 // Arithmetic is binary64 (gfx950 has full-rate FP64 vector units and the
 // kernel is latency-bound, so this costs nothing measurable): the sum of
 // squares, the reciprocal root, the product r * inv * (w + gain_center), the
@@ -61,79 +68,71 @@ __device__ __forceinline__ unsigned e2m1_rn_satfinite(double v) {
   return (signbit(v) ? 8u : 0u) | idx;
 }
 
+constexpr int kQuantBlocks = kNormThreads / 4;  // 16-column blocks a workgroup quantises
+
 template <bool QUANT>
 __global__ __launch_bounds__(kNormThreads) void rmsnorm_kernel(
     const uint16_t *__restrict__ r, const uint16_t *__restrict__ w, float gain_center,
     float eps, const float *__restrict__ global_scale, uint8_t *__restrict__ a,
-    uint8_t *__restrict__ a_sf, uint16_t *__restrict__ y, int P) {
-  const int row = blockIdx.x;
+    uint8_t *__restrict__ a_sf, uint16_t *__restrict__ y, int P, int parts) {
+  const int row = blockIdx.x / parts, part = blockIdx.x - row * parts;
   const int tid = threadIdx.x;
   const int blocks = P / 16;
   const uint16_t *rrow = r + (size_t)row * P;
-
-  // Sum of squares in a fixed order; the first block and its weights are
-  // loaded before the reduction and stay in registers.
-  double first[16], gfirst[16];
-  double ss = 0.0;
-  if (tid < blocks) {
-    load16(rrow + tid * 16, first);
-    load16(w + tid * 16, gfirst);
-#pragma unroll
-    for (int j = 0; j < 16; ++j) ss += first[j] * first[j];
+  // This thread's quarter (columns 4 q .. 4 q + 3) of block blk; its loads
+  // are issued first, ahead of the reduction.
+  const int blk = part * kQuantBlocks + (tid >> 2);
+  const int q = tid & 3;
+  const bool mine = blk < blocks;  // the four threads of a block agree
+  uint2 rq = make_uint2(0, 0), wq = make_uint2(0, 0);
+  if (mine) {
+    rq = *reinterpret_cast<const uint2 *>(rrow + blk * 16 + 4 * q);
+    wq = *reinterpret_cast<const uint2 *>(w + blk * 16 + 4 * q);
   }
-  for (int blk = tid + kNormThreads; blk < blocks; blk += kNormThreads) {
+
+  // Sum of squares of the whole row in a fixed order.
+  double ss = 0.0;
+  for (int b = tid; b < blocks; b += kNormThreads) {
     double v[16];
-    load16(rrow + blk * 16, v);
+    load16(rrow + b * 16, v);
 #pragma unroll
     for (int j = 0; j < 16; ++j) ss += v[j] * v[j];
   }
   __shared__ double wave_ss[kNormThreads / 64];
   const double total = block_sum(ss, wave_ss);
+  if (!mine) return;
   const double inv = 1.0 / sqrt(total / (double)P + (double)eps);
   const double gc = (double)gain_center;
-  const double gs = QUANT ? (double)*global_scale : 0.0;
 
-  for (int blk = tid; blk < blocks; blk += kNormThreads) {
-    double v[16], g[16];
-    if (blk == tid) {
+  const unsigned ru[2] = {rq.x, rq.y}, wu[2] = {wq.x, wq.y};
+  unsigned yb[4];
+  double amax = 0.0;
 #pragma unroll
-      for (int j = 0; j < 16; ++j) {
-        v[j] = first[j];
-        g[j] = gfirst[j];
-      }
-    } else {
-      load16(rrow + blk * 16, v);
-      load16(w + blk * 16, g);
-    }
-    unsigned yb[16];
-    double amax = 0.0;
+  for (int j = 0; j < 4; ++j) {
+    const unsigned rb = (ru[j / 2] >> (16 * (j % 2))) & 0xffffu;
+    const unsigned wb = (wu[j / 2] >> (16 * (j % 2))) & 0xffffu;
+    yb[j] = f64_to_bf16((double)__uint_as_float(rb << 16) * inv *
+                        ((double)__uint_as_float(wb << 16) + gc));
+    amax = fmax(amax, fabs((double)__uint_as_float(yb[j] << 16)));
+  }
+  if constexpr (QUANT) {
+    amax = fmax(amax, __shfl_xor(amax, 1));  // the block's amax over its quad
+    amax = fmax(amax, __shfl_xor(amax, 2));
+    const double gs = (double)*global_scale;
+    const unsigned sf = e4m3_rn_satfinite(gs * amax / 6.0);
+    const double dec = e4m3_value(sf);
+    const double os = dec == 0.0 ? 0.0 : gs / dec;
+    unsigned codes = 0;
 #pragma unroll
-    for (int j = 0; j < 16; ++j) {
-      yb[j] = f64_to_bf16(v[j] * inv * (g[j] + gc));
-      amax = fmax(amax, fabs((double)__uint_as_float(yb[j] << 16)));
-    }
-    if constexpr (QUANT) {
-      const unsigned sf = e4m3_rn_satfinite(gs * amax / 6.0);
-      const double dec = e4m3_value(sf);
-      const double os = dec == 0.0 ? 0.0 : gs / dec;
-      unsigned lo = 0, hi = 0;
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        lo |= e2m1_rn_satfinite((double)__uint_as_float(yb[j] << 16) * os) << (4 * j);
-        hi |= e2m1_rn_satfinite((double)__uint_as_float(yb[j + 8] << 16) * os) << (4 * j);
-      }
-      *reinterpret_cast<uint2 *>(a + (size_t)row * (P / 2) + blk * 8) = make_uint2(lo, hi);
-      a_sf[(size_t)row * blocks + blk] = (uint8_t)sf;
-    } else {
-      u32x4 o0, o1;
-      o0.x = yb[0] | (yb[1] << 16);   o0.y = yb[2] | (yb[3] << 16);
-      o0.z = yb[4] | (yb[5] << 16);   o0.w = yb[6] | (yb[7] << 16);
-      o1.x = yb[8] | (yb[9] << 16);   o1.y = yb[10] | (yb[11] << 16);
-      o1.z = yb[12] | (yb[13] << 16); o1.w = yb[14] | (yb[15] << 16);
-      u32x4 *dst = reinterpret_cast<u32x4 *>(y + (size_t)row * P + blk * 16);
-      dst[0] = o0;
-      dst[1] = o1;
-    }
+    for (int j = 0; j < 4; ++j)
+      codes |= e2m1_rn_satfinite((double)__uint_as_float(yb[j] << 16) * os) << (4 * j);
+    // Column 4 q + j is nibble j of this thread's two bytes (even column low).
+    *reinterpret_cast<uint16_t *>(a + (size_t)row * (P / 2) + blk * 8 + 2 * q) =
+        (uint16_t)codes;
+    if (q == 0) a_sf[(size_t)row * blocks + blk] = (uint8_t)sf;
+  } else {
+    *reinterpret_cast<uint2 *>(y + (size_t)row * P + blk * 16 + 4 * q) =
+        make_uint2(yb[0] | (yb[1] << 16), yb[2] | (yb[3] << 16));
   }
 }
 
@@ -143,13 +142,14 @@ hipError_t launch_rmsnorm(const uint16_t *r, const uint16_t *w, float gain_cente
                           float eps, const float *global_scale, uint8_t *a,
                           uint8_t *a_sf, uint16_t *y, int M, int P, bool quant,
                           hipStream_t stream) {
-  dim3 grid(M), block(kNormThreads);
+  const int parts = (P / 16 + kQuantBlocks - 1) / kQuantBlocks;
+  dim3 grid(parts * M), block(kNormThreads);
   if (quant)
     hipLaunchKernelGGL(rmsnorm_kernel<true>, grid, block, 0, stream, r, w, gain_center,
-                       eps, global_scale, a, a_sf, y, P);
+                       eps, global_scale, a, a_sf, y, P, parts);
   else
     hipLaunchKernelGGL(rmsnorm_kernel<false>, grid, block, 0, stream, r, w, gain_center,
-                       eps, global_scale, a, a_sf, y, P);
+                       eps, global_scale, a, a_sf, y, P, parts);
   return hipGetLastError();
 }
 

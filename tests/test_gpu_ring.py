@@ -238,29 +238,35 @@ def test_ring_exact_integer_inputs_bit_exact(gpu_lib, M):
         assert np.array_equal(ys[i], oracle.gemm_bf16(xs[i][:M], ws[i], THREADS)), f"item {i}"
 
 
-def test_ring_sixty_layer_weight_ring(gpu_lib):
-    """A 60-layer weight ring of unpooler-shard weights (480 MiB, more than
-    the caches hold) as one 60-item call with one x shared by every item;
-    sampled oracle positions on every layer, full check on two."""
+@pytest.mark.parametrize("M,N,K", [(8, 1024, 4096), (16, 1024, 4096), (16, 8192, 1024),
+                                   (16, 512, 8192), (8, 4096, 8192), (16, 4096, 8192)])
+def test_ring_sixty_layer_weight_ring(gpu_lib, M, N, K):
+    """A 60-layer weight ring of shard weights (more than the caches hold) as
+    one 60-item call at the ring chooser's launch (the bench's launches:
+    XCD-local slots), each item with its own x; sampled oracle positions on
+    every layer, full check on two."""
     import torch
 
-    N, K, M = 1024, 4096, 8
-    _say("ring over 60 device layers")
     ring = synthetic.device_weight_ring(60, N, K, "cuda")
-    x_bits, _ = synthetic.gemm_inputs(N=16, K=K, seed=600)
-    x = to_dev(x_bits[:M])
+    _say(f"ring over 60 device layers M={M} N={N} K={K} {gpu_lib.skinny_ring_choose(M, N, K, 60)}")
+    xs_bits = [synthetic.gemm_inputs(N=16, K=K, seed=600 + i)[0][:M] for i in range(60)]
+    xs = [to_dev(x) for x in xs_bits]
     ys = [torch.empty((M, N), dtype=torch.bfloat16, device="cuda") for _ in ring]
-    gpu_lib.skinny_gemm_bf16_ring([x] * 60, ring, ys)
+    gpu_lib.skinny_gemm_bf16_ring(xs, ring, ys)
     torch.cuda.synchronize()
     rng = np.random.default_rng(601)
     rows = rng.integers(0, M, 64)
     cols = rng.integers(0, N, 64)
+    tile = gpu_lib.skinny_ring_choose(M, N, K, 60).gemm
     for layer in range(60):
+        x_bits = xs_bits[layer]
         w_bits = from_dev(ring[layer])
         y = from_dev(ys[layer])
         if layer in (0, 59):
-            assert_gemm_close(y, oracle.gemm_bf16(x_bits[:M], w_bits, THREADS), f"layer {layer}")
-        ref, exact = oracle.gemm_bf16_sampled(x_bits[:M], w_bits, rows, cols)
+            assert_gemm_close(y, oracle.gemm_bf16(x_bits, w_bits, THREADS), f"layer {layer}")
+        if layer in (0, 31, 59) and _single_ok(gpu_lib, M, N, K, tile):
+            assert np.array_equal(y, _single(gpu_lib, x_bits, w_bits, M, tile)), f"layer {layer}"
+        ref, exact = oracle.gemm_bf16_sampled(x_bits, w_bits, rows, cols)
         r = oracle.bf16_value(ref)
         g = oracle.bf16_value(y[rows, cols])
         scale = np.sqrt(np.mean(exact ** 2))  # rms of y estimated from the samples
