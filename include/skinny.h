@@ -88,7 +88,8 @@ typedef struct skinny_launch {
 
 /* Prepare `device` (a HIP ordinal) for the compute calls: checks that it is a
  * gfx950 GPU, allocates the library's split-K workspace on it (8 MiB of FP32
- * partials, enough for S * M * N <= 2^21) and sets the kernels' LDS limits.
+ * partials, enough for S * M * N <= 2^21) and the dual norm's buffer (512 KiB
+ * of per-slice sums) and sets the kernels' LDS limits.
  * Call it before any graph capture.  Idempotent.  Returns SKINNY_OK,
  * SKINNY_EDEVICE or SKINNY_ELAUNCH (allocation failure). */
 int skinny_init(int device);
@@ -294,7 +295,11 @@ int skinny_rmsnorm_bf16(const void *r, const void *norm_w, float gain_center,
  *   out          bf16 [M, H]
  *   M >= 1 rows; H > 0, H % 16 == 0; every array 16-byte aligned
  * partial, residual and out must not overlap, nor a weight the residual or
- * out.  Errors: SKINNY_EINVAL, SKINNY_ENOTINIT, SKINNY_ELAUNCH. */
+ * out.  Rows of H >= 2048 run as two kernels that pass per-slice sums
+ * through the device's dual-norm buffer (from skinny_init): two such calls
+ * must not run concurrently on different streams of one device (calls on
+ * one stream are ordered).  Errors: SKINNY_EINVAL, SKINNY_ENOTINIT,
+ * SKINNY_ELAUNCH. */
 int skinny_dual_norm(const void *partial, float *residual, const void *post_w,
                      float post_gain_center, float post_eps, const void *alpha,
                      float alpha_scalar, const void *beta, const void *next_w,

@@ -27,6 +27,11 @@ constexpr size_t kWorkspaceFloats = size_t(2) << 20;  // 8 MiB
 
 constexpr size_t kMaxDynamicLds = 160 * 1024;  // all of a gfx950 CU's LDS
 
+// The dual norm's per-slice sums of squares (binary64), M * slices of them,
+// in a buffer of its own (per device, from skinny_init).
+constexpr size_t kNormPartials = 65536;
+constexpr int kDualSlice = 1024;  // columns per workgroup of the two-kernel dual norm
+
 // The zero-copy publish of a GEMM call (unpooler page, module description,
 // zero-copy epilogue): y also goes into this rank's slot of a mailbox
 // [3 stages][tp][capacity][N] at the stage read on the device when the

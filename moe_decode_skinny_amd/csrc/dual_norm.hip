@@ -156,13 +156,130 @@ __global__ __launch_bounds__(kDualThreads) void dual_norm_kernel(
   }
 }
 
+// ------------------------------------------------------------- two kernels
+// Rows of at least 2 kDualSlice columns are spread over S = ceil(H /
+// kDualSlice) workgroups of 256 threads (thread t: columns 4t .. 4t + 3 of
+// its slice); one workgroup per row must pull every byte of the row through
+// one CU, whose cache-miss concurrency then bounds the call.  The first
+// kernel: every workgroup of a row computes the post-norm sum of squares over
+// the whole partial row itself (16-column blocks t, t + 256, ... per thread,
+// then the fixed-order workgroup sum: the same bits in all of them), then
+// the gated add of its slice, stores the new residual values and the slice's
+// sum of their squares into slice_ss[row * S + slice]; the second kernel sums
+// a row's S slice sums in slice order and writes its slice of out.  The
+// kernel boundary orders the two; arithmetic as in the one-kernel form.
+constexpr int kSplitThreads = 256;
+
+__device__ __forceinline__ void load4(const uint16_t *p, double (&v)[4]) {
+  const uint2 u = *reinterpret_cast<const uint2 *>(p);
+  v[0] = (double)bf16_lo(u.x);
+  v[1] = (double)bf16_hi(u.x);
+  v[2] = (double)bf16_lo(u.y);
+  v[3] = (double)bf16_hi(u.y);
+}
+
+__global__ __launch_bounds__(kSplitThreads) void dual_gate_kernel(
+    const uint16_t *__restrict__ partial, float *__restrict__ residual,
+    const uint16_t *__restrict__ post_w, float post_gc, float post_eps,
+    const uint16_t *__restrict__ alpha, float alpha_scalar, const uint16_t *__restrict__ beta,
+    double *__restrict__ slice_ss, int H, int slices) {
+  const int row = blockIdx.x / slices, sl = blockIdx.x - row * slices;
+  const int tid = threadIdx.x;
+  const int c0 = sl * kDualSlice + 4 * tid;
+  const bool mine = c0 < H;  // H % 16 == 0: all four columns or none
+  const uint16_t *prow = partial + (size_t)row * H;
+  float *srow = residual + (size_t)row * H;
+
+  // The thread's own columns first (in flight during the reduction).
+  double p[4], g[4], a[4], b[4], s[4];
+  if (mine) {
+    load4(prow + c0, p);
+    const f32x4 sv = *reinterpret_cast<const f32x4 *>(srow + c0);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) s[j] = (double)sv[j];
+    if (post_w) {
+      load4(post_w + c0, g);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) g[j] += (double)post_gc;
+    } else {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) g[j] = 1.0;
+    }
+    if (alpha) {
+      load4(alpha + c0, a);
+    } else {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) a[j] = (double)alpha_scalar;
+    }
+    load4(beta + c0, b);
+  }
+
+  double ss = 0.0;
+  for (int blk = tid; blk < H / 16; blk += kSplitThreads) {
+    double v[16];
+    load16(prow + blk * 16, v);
+#pragma unroll
+    for (int j = 0; j < 16; ++j) ss += v[j] * v[j];
+  }
+  __shared__ double slots[kSplitThreads / 64], slots2[kSplitThreads / 64];
+  const double inv =
+      1.0 / sqrt(block_sum<kSplitThreads>(ss, slots) / (double)H + (double)post_eps);
+
+  double ss2 = 0.0;
+  if (mine) {
+    f32x4 o;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const double h = (double)__uint_as_float(f64_to_bf16(p[j] * inv * g[j]) << 16);
+      const float v = (float)(a[j] * s[j] + b[j] * h);
+      o[j] = v;
+      ss2 += (double)v * (double)v;
+    }
+    *reinterpret_cast<f32x4 *>(srow + c0) = o;
+  }
+  const double slice_total = block_sum<kSplitThreads>(ss2, slots2);
+  if (tid == 0) slice_ss[(size_t)row * slices + sl] = slice_total;
+}
+
+__global__ __launch_bounds__(kSplitThreads) void dual_out_kernel(
+    const float *__restrict__ residual, const uint16_t *__restrict__ next_w, float pre_gc,
+    float pre_eps, const double *__restrict__ slice_ss, uint16_t *__restrict__ out, int H,
+    int slices) {
+  const int row = blockIdx.x / slices, sl = blockIdx.x - row * slices;
+  const int c0 = sl * kDualSlice + 4 * threadIdx.x;
+  if (c0 >= H) return;
+  const double *ps = slice_ss + (size_t)row * slices;
+  double ss2 = ps[0];
+  for (int i = 1; i < slices; ++i) ss2 += ps[i];
+  const double inv2 = 1.0 / sqrt(ss2 / (double)H + (double)pre_eps);
+  const f32x4 sv = *reinterpret_cast<const f32x4 *>(residual + (size_t)row * H + c0);
+  double w[4];
+  load4(next_w + c0, w);
+  unsigned yb[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) yb[j] = f64_to_bf16((double)sv[j] * inv2 * (w[j] + (double)pre_gc));
+  *reinterpret_cast<uint2 *>(out + (size_t)row * H + c0) =
+      make_uint2(yb[0] | (yb[1] << 16), yb[2] | (yb[3] << 16));
+}
+
 }  // namespace
 
 hipError_t launch_dual_norm(const uint16_t *partial, float *residual, const uint16_t *post_w,
                             float post_gc, float post_eps, const uint16_t *alpha,
                             float alpha_scalar, const uint16_t *beta, const uint16_t *next_w,
                             float pre_gc, float pre_eps, uint16_t *out, int M, int H,
-                            hipStream_t stream) {
+                            DeviceState &st, hipStream_t stream) {
+  const int slices = (H + kDualSlice - 1) / kDualSlice;
+  if (H >= 2 * kDualSlice && (size_t)M * slices <= kNormPartials) {
+    hipLaunchKernelGGL(dual_gate_kernel, dim3(M * slices), dim3(kSplitThreads), 0, stream,
+                       partial, residual, post_w, post_gc, post_eps, alpha, alpha_scalar, beta,
+                       st.norm_partials, H, slices);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(dual_out_kernel, dim3(M * slices), dim3(kSplitThreads), 0, stream,
+                       residual, next_w, pre_gc, pre_eps, st.norm_partials, out, H, slices);
+    return hipGetLastError();
+  }
   hipLaunchKernelGGL(dual_norm_kernel, dim3(M), dim3(kDualThreads), 0, stream, partial,
                      residual, post_w, post_gc, post_eps, alpha, alpha_scalar, beta, next_w,
                      pre_gc, pre_eps, out, H);

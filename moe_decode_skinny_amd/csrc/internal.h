@@ -10,7 +10,8 @@ namespace skinny {
 
 struct DeviceState {
   bool ready = false;
-  float *partials = nullptr;  // kWorkspaceFloats
+  float *partials = nullptr;         // kWorkspaceFloats
+  double *norm_partials = nullptr;   // kNormPartials
 };
 
 // The state of the current HIP device, or nullptr (and a reason) if the
@@ -37,7 +38,7 @@ hipError_t launch_dual_norm(const uint16_t *partial, float *residual, const uint
                             float post_gc, float post_eps, const uint16_t *alpha,
                             float alpha_scalar, const uint16_t *beta, const uint16_t *next_w,
                             float pre_gc, float pre_eps, uint16_t *out, int M, int H,
-                            hipStream_t stream);
+                            DeviceState &st, hipStream_t stream);
 hipError_t launch_rmsnorm(const uint16_t *r, const uint16_t *w, float gain_center,
                           float eps, const float *global_scale, uint8_t *a,
                           uint8_t *a_sf, uint16_t *y, int M, int P, bool quant,

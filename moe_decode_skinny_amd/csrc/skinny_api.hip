@@ -634,6 +634,7 @@ int skinny_init(int device) {
   if (hipSetDevice(device) != hipSuccess) return fail(SKINNY_EDEVICE, "cannot select device %d", device);
   int status = SKINNY_OK;
   if (hipMalloc(&st.partials, kWorkspaceFloats * sizeof(float)) != hipSuccess ||
+      hipMalloc(&st.norm_partials, kNormPartials * sizeof(double)) != hipSuccess ||
       mfma_prepare() != hipSuccess || ring_prepare() != hipSuccess ||
       hipDeviceSynchronize() != hipSuccess) {
     status = fail(SKINNY_ELAUNCH, "workspace allocation failed on device %d", device);
@@ -761,12 +762,13 @@ int skinny_dual_norm(const void *partial, float *residual, const void *post_w,
     if (q && (overlap(q, vb, residual, rb) || overlap(q, vb, out, ob)))
       return fail(SKINNY_EINVAL, "a weight overlaps the residual or out");
   int st = SKINNY_OK;
-  if (!current_state(&st)) return st;
+  DeviceState *ds = current_state(&st);
+  if (!ds) return st;
   hipError_t e = launch_dual_norm(
       static_cast<const uint16_t *>(partial), residual, static_cast<const uint16_t *>(post_w),
       post_gain_center, post_eps, static_cast<const uint16_t *>(alpha), alpha_scalar,
       static_cast<const uint16_t *>(beta), static_cast<const uint16_t *>(next_w),
-      pre_gain_center, pre_eps, static_cast<uint16_t *>(out), M, H,
+      pre_gain_center, pre_eps, static_cast<uint16_t *>(out), M, H, *ds,
       static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return fail(SKINNY_ELAUNCH, "launch failed: %s", hipGetErrorString(e));
   return SKINNY_OK;
