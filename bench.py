@@ -19,8 +19,10 @@ average duration measured here from graph replays of that launch alone over
 the ring.  `ring` reports the same sweep through the layer-ring launch
 (skinny_gemm_bf16_ring: one persistent launch per M over the 60 layers, the
 next layer's weights in flight while one is finished), per item.
-`oproj` reports the o_proj shard (N=8192, K=1024) the same two ways.
-`cpu_baseline` times the oracle on the host for a bounded sample of the same
+`oproj` reports the o_proj shard (N=8192, K=1024) the same two ways, and
+`pooler` the pooler shard (N=512) and the full pooler (N=4096) at K=8192.
+`epilogue` times the expert-input chain (full-pooler GEMM, RMSNorm -> NVFP4)
+and the dual norm.  `cpu_baseline` times the oracle on the host for a bounded sample of the same
 workload.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu]
