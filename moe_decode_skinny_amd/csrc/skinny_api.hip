@@ -638,6 +638,9 @@ int skinny_init(int device) {
       mfma_prepare() != hipSuccess || ring_prepare() != hipSuccess ||
       hipDeviceSynchronize() != hipSuccess) {
     status = fail(SKINNY_ELAUNCH, "workspace allocation failed on device %d", device);
+    // leave the device as it was: a later skinny_init may try again
+    if (st.partials && hipFree(st.partials) == hipSuccess) st.partials = nullptr;
+    if (st.norm_partials && hipFree(st.norm_partials) == hipSuccess) st.norm_partials = nullptr;
   } else {
     st.ready = true;
   }
