@@ -198,8 +198,9 @@ static const TableEntry kTable[] = {
 // explicit split count is asked for):
 //   DOT2 (lanes along K; activation traffic M / rows of the weight traffic;
 //   no split-K) for M <= 8, and for M <= 16 on narrow shards (< 256 MFMA
-//   tiles); 2 rows per workgroup for M <= 2, else 4; 4 chunks per wave for
-//   <= 4 tokens when K allows, else 2 (1 at 16 tokens).
+//   tiles); 2 rows per workgroup for M <= 2, else 4, and 2 rows when that
+//   lets one split cover K (the 16-wave form); 4 chunks per wave for <= 4
+//   tokens when K allows, else 2 (1 at 16 tokens).
 //   MFMA otherwise: 2 tiles per workgroup on wide shards (>= 256 tiles), the
 //   split count that gives each workgroup about 32 KiB of weights (64 KiB
 //   past 16 MiB of weights), and the fewest chunks per wave that keep a
@@ -212,9 +213,11 @@ static skinny_launch rule(int M, int N, int K, int splits) {
     const int mt = dot2_token_tile(M);
     const int chunks = mt >= 16 ? 1 : (mt <= 4 && units >= 8) ? 4 : (units >= 2 ? 2 : 1);
     for (int S = splits ? splits : 1; S <= kMaxSplits; S *= 2) {
-      for (int c = chunks; c >= 1; c /= 2) {
-        const skinny_launch l{SKINNY_PATH_DOT2, S, ceil_div(K, (long)S * kDot2K * c), c, 1, rows};
-        if (launch_check(M, N, K, l) == SKINNY_OK) return l;
+      for (int r : {rows, 2}) {
+        for (int c = chunks; c >= 1; c /= 2) {
+          const skinny_launch l{SKINNY_PATH_DOT2, S, ceil_div(K, (long)S * kDot2K * c), c, 1, r};
+          if (launch_check(M, N, K, l) == SKINNY_OK) return l;
+        }
       }
       if (splits) break;
     }

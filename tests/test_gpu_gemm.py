@@ -251,3 +251,37 @@ def test_chooser_walk_is_bitwise_the_plain_launch(gpu_lib, N, K):
         y = _run(gpu_lib, x, w, M)
         assert np.array_equal(y, _run(gpu_lib, x, w, M, launch=launch)), f"M={M} {walk}"
         assert_gemm_close(y, ref16[:M], f"M={M} {walk}")
+
+
+def test_random_shapes_through_the_choosers(gpu_lib):
+    """Seeded random shapes (N a multiple of 16 up to 2048, K a multiple of 8
+    up to 9000, M 1..16) through skinny_gemm_bf16 (the chooser's launch and
+    walk) and skinny_gemm_bf16_ring (the ring chooser, 1..12 items), against
+    the oracle; the plain kernel at skinny_choose's launch bit for bit."""
+    import torch
+
+    rng = np.random.default_rng(77)
+    for case in range(24):
+        M = int(rng.integers(1, 17))
+        N = 16 * int(rng.integers(1, 129))
+        K = 8 * int(rng.integers(1, 1126))
+        count = int(rng.integers(1, 13))
+        walk = gpu_lib.skinny_choose_walk(M, N, K, 0)
+        ring = gpu_lib.skinny_ring_choose(M, N, K, count)
+        _say(f"random case {case}: M={M} N={N} K={K} walk={walk} ring(count={count})={ring}")
+        x, w = synthetic.gemm_inputs(N=N, K=K, seed=1000 + case)
+        ref = oracle.gemm_bf16(x[:M], w, THREADS)
+        y = _run(gpu_lib, x, w, M)
+        assert_gemm_close(y, ref, f"case {case}")
+        assert np.array_equal(y, _run(gpu_lib, x, w, M, launch=walk.gemm if walk.segment == 0
+                                      else gpu_lib.skinny_choose(M, N, K, 0))), f"case {case}"
+        xs = [to_dev(synthetic.gemm_inputs(N=16, K=K, seed=2000 + case * 16 + i)[0][:M])
+              for i in range(count)]
+        ws = [to_dev(w)] + [to_dev(synthetic.gemm_inputs(N=N, K=K, seed=3000 + case * 16 + i)[1])
+                            for i in range(1, count)]
+        ys = [torch.empty((M, N), dtype=torch.bfloat16, device="cuda") for _ in range(count)]
+        gpu_lib.skinny_gemm_bf16_ring(xs, ws, ys)
+        torch.cuda.synchronize()
+        for i in (0, count - 1):
+            ref_i = oracle.gemm_bf16(from_dev(xs[i]), from_dev(ws[i]), THREADS)
+            assert_gemm_close(from_dev(ys[i]), ref_i, f"case {case} ring item {i}")
