@@ -213,7 +213,8 @@ def test_ring_max_count(gpu_lib):
         assert_gemm_close(ys[i], oracle.gemm_bf16(xs[i][:M], ws[i], THREADS), f"item {i}")
 
 
-@pytest.mark.parametrize("M,N,K,count", [(1, 8192, 1024, 4), (8, 8192, 1024, 3),
+@pytest.mark.parametrize("M,N,K,count", [(4, 65536, 64, 3), (16, 49152, 520, 2),
+                                         (1, 8192, 1024, 4), (8, 8192, 1024, 3),
                                          (16, 8192, 1024, 2), (1, 512, 8192, 4),
                                          (8, 512, 8192, 4), (16, 512, 8192, 3),
                                          (1, 4096, 8192, 2), (8, 4096, 8192, 2),
