@@ -9,8 +9,12 @@ module only marshals numpy arrays into it.  Every bfloat16 array is handled as
 its ``uint16`` bit pattern.
 
 Parity pins: every function here is checked by ``tests/test_oracle_*.py``
-against brute force, closed forms, library routines and the format
-definitions.  Nothing here is "parity unpinned".
+against brute force, closed forms, library routines, worked cases and the
+format definitions, and ``tests/test_oracle_mutations.py`` checks that
+planted mistakes fail those pins.  One function is parity unpinned by the
+pages beyond the order of its steps: ``dual_norm`` (the dual norm's formula
+and constants are not printed; its pins check the stated reading, given with
+its C source).
 """
 from __future__ import annotations
 
