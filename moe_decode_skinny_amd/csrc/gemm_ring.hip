@@ -349,14 +349,16 @@ __global__ __launch_bounds__(THREADS) void gemm_blocks_ring_kernel(
 }
 
 // Register budget per lane: two weight buffers 8 * R4 * CHUNKS, activations
-// 4 * Q * CHUNKS, sums 4 * Q * R4; the DOT2 ring's limits.
+// 4 * Q * CHUNKS, sums 4 * Q * R4: at most 112 for 16 waves (128 registers a
+// lane), 224 for 8 waves (256 a lane; the largest forms compile to 230-238
+// registers without spilling).
 constexpr int blocks_ring_regs(int r4, int chunks, int q) {
   return 8 * r4 * chunks + 4 * q * chunks + 4 * q * r4;
 }
 
 template <int R4, int C, int Q, int THREADS>
 constexpr Dot2RingKernel blocks_ring_variant() {
-  if constexpr (blocks_ring_regs(R4, C, Q) <= (THREADS > 512 ? 112 : 160))
+  if constexpr (blocks_ring_regs(R4, C, Q) <= (THREADS > 512 ? 112 : 224))
     return gemm_blocks_ring_kernel<R4, C, Q, THREADS>;
   else
     return nullptr;

@@ -262,7 +262,10 @@ def test_ring_launch_reasons_without_device(sk):
     assert "needs 4 waves" in sk.skinny_last_error()
     assert call((3, 1, 4, 8, 2, 4)) == sk.SKINNY_EUNSUPPORTED
     assert "accs=1" in sk.skinny_last_error()
-    assert call((3, 1, 4, 8, 1, 8)) == sk.SKINNY_EUNSUPPORTED  # 8 rows x 8 chunks: too many registers
+    # 8 rows x 8 chunks x 16 tokens: 288 registers a lane, more than any form has
+    c = sk.RingLaunch(sk.Launch(3, 1, 4, 8, 1, 8), 1, 128)._c()
+    assert lib.skinny_gemm_bf16_ring_launch(x, w, y, 1, 16, N, K, ctypes.byref(c), None) == \
+        sk.SKINNY_EUNSUPPORTED
     assert "MFMA 4x4 ring kernel" in sk.skinny_last_error()
     assert call((3, 1, 8, 4, 1, 4)) in (sk.SKINNY_EDEVICE, sk.SKINNY_ENOTINIT)
     assert call((2, 1, 8, 16, 1, 16)) in (sk.SKINNY_EDEVICE, sk.SKINNY_ENOTINIT)
