@@ -174,22 +174,22 @@ struct TableEntry {
 };
 static const TableEntry kTable[] = {
     // unpooler shard
-    {1024, 4096, 1, 1, {SKINNY_PATH_DOT2, 1, 2, 4, 1, 2}},
+    {1024, 4096, 1, 1, {SKINNY_PATH_DOT2, 1, 2, 4, 1, 2}, {}},
     {1024, 4096, 2, 2, {SKINNY_PATH_DOT2, 1, 2, 4, 1, 2}, {2, 256}},
     {1024, 4096, 3, 4, {SKINNY_PATH_DOT2, 1, 4, 2, 1, 2}, {2, 256}},
-    {1024, 4096, 5, 8, {SKINNY_PATH_DOT2, 1, 4, 2, 1, 4}},
-    {1024, 4096, 9, 16, {SKINNY_PATH_DOT2, 1, 8, 1, 1, 4}},
+    {1024, 4096, 5, 8, {SKINNY_PATH_DOT2, 1, 4, 2, 1, 4}, {}},
+    {1024, 4096, 9, 16, {SKINNY_PATH_DOT2, 1, 8, 1, 1, 4}, {}},
     // o_proj shard
-    {8192, 1024, 1, 1, {SKINNY_PATH_DOT2, 1, 1, 2, 1, 2}},
+    {8192, 1024, 1, 1, {SKINNY_PATH_DOT2, 1, 1, 2, 1, 2}, {}},
     {8192, 1024, 2, 4, {SKINNY_PATH_DOT2, 1, 1, 2, 1, 4}, {2, 1024}},
     {8192, 1024, 5, 16, {SKINNY_PATH_MFMA, 1, 2, 16, 2, 16}, {2, 256, true}},
     // pooler shard
-    {512, 8192, 1, 4, {SKINNY_PATH_DOT2, 1, 4, 4, 1, 2}},
-    {512, 8192, 5, 8, {SKINNY_PATH_DOT2, 1, 8, 2, 1, 2}},
-    {512, 8192, 9, 16, {SKINNY_PATH_DOT2, 1, 16, 1, 1, 2}},
+    {512, 8192, 1, 4, {SKINNY_PATH_DOT2, 1, 4, 4, 1, 2}, {}},
+    {512, 8192, 5, 8, {SKINNY_PATH_DOT2, 1, 8, 2, 1, 2}, {}},
+    {512, 8192, 9, 16, {SKINNY_PATH_DOT2, 1, 16, 1, 1, 2}, {}},
     // full pooler
-    {4096, 8192, 1, 1, {SKINNY_PATH_DOT2, 1, 8, 2, 1, 2}},
-    {4096, 8192, 2, 4, {SKINNY_PATH_DOT2, 1, 8, 2, 1, 8}},
+    {4096, 8192, 1, 1, {SKINNY_PATH_DOT2, 1, 8, 2, 1, 2}, {}},
+    {4096, 8192, 2, 4, {SKINNY_PATH_DOT2, 1, 8, 2, 1, 8}, {}},
     {4096, 8192, 5, 8, {SKINNY_PATH_DOT2, 1, 8, 2, 1, 4}, {4, 256}},
     {4096, 8192, 9, 16, {SKINNY_PATH_MFMA_4X4, 1, 16, 4, 1, 4}, {4, 256}},
 };
@@ -433,7 +433,8 @@ static int ring_choose(int M, int N, int K, int count, skinny_ring_launch *out) 
   if (M > 8) {
     for (int c = kMaxMfmaChunks; c >= 2; c /= 2) {  // staged: the fewest waves that fit
       const skinny_ring_launch r{
-          {SKINNY_PATH_MFMA_LDS, 1, ceil_div(K, (long)kMfmaK * c), c, 1, kTileN}, 1, N / kTileN};
+          {SKINNY_PATH_MFMA_LDS, 1, ceil_div(K, (long)kMfmaK * c), c, 1, kTileN}, 1, N / kTileN,
+          SKINNY_RING_ITEM_MAJOR};
       if (ring_check(count, M, N, K, r) == SKINNY_OK) {
         *out = r;
         return SKINNY_OK;
@@ -453,7 +454,7 @@ static int ring_choose(int M, int N, int K, int count, skinny_ring_launch *out) 
     }
     for (int c = 1; c <= kMaxMfmaChunks; c *= 2) {
       const skinny_ring_launch r{{SKINNY_PATH_MFMA, 1, ceil_div(K, (long)kMfmaK * c), c, 1, kTileN},
-                                 1, N / kTileN};
+                                 1, N / kTileN, SKINNY_RING_ITEM_MAJOR};
       if (ring_check(count, M, N, K, r) == SKINNY_OK) {
         *out = r;
         return SKINNY_OK;
@@ -468,7 +469,7 @@ static int ring_choose(int M, int N, int K, int count, skinny_ring_launch *out) 
     if (N % rows) continue;
     for (int c = c0; c >= 1; c /= 2) {
       const skinny_ring_launch r{{SKINNY_PATH_DOT2, 1, ceil_div(K, (long)kDot2K * c), c, 1, rows},
-                                 1, N / rows};
+                                 1, N / rows, SKINNY_RING_ITEM_MAJOR};
       if (ring_check(count, M, N, K, r) == SKINNY_OK) {
         *out = r;
         return SKINNY_OK;
