@@ -8,8 +8,9 @@ distinct layers (60 layers = 480 MiB, twice the 256 MiB Infinity Cache, so no
 call finds its weights in a cache).  Inputs are seeded synthetic tensors
 already resident in HBM: x ~ N(0, 1), W ~ N(0, 1/K).
 
-Steps run as HIP-graph replays (the decode loop records its calls once and
-replays them: the calls allocate nothing and never synchronize).  Timing uses
+Steps run as HIP-graph replays (the decode loop records one pass over the
+layer ring, 12 steps = 60 calls, as one graph and replays it: the calls
+allocate nothing and never synchronize).  Timing uses
 HIP events on the stream the kernels run on.
 
 Output: one JSON line.  `value` is achieved HBM GB/s over the step
@@ -352,30 +353,40 @@ def main():
     launches = {M: sk.skinny_choose(M, N, K, 0) for M in MS}
     stream = torch.cuda.Stream(dev)
 
-    # One graph per group of five ring layers: step i replays graph i % 12,
-    # which runs the sweep M = 1..16 on layers 5 (i % 12) .. + 4.
+    # The decode loop records one pass over the layer ring as one graph: step
+    # i runs the sweep M = 1..16 on layers 5 (i % 12) .. + 4, and a graph
+    # holds the 12 steps of a ring pass (60 calls); K steps replay it K // 12
+    # times, then a graph of the first K % 12 steps.
     groups = RING // len(MS)
-    graphs = []
+
+    def record(n_steps):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=stream):
+            for gi in range(n_steps):
+                for j, M in enumerate(MS):
+                    sk.skinny_gemm_bf16(xs[M], ring[gi * len(MS) + j], ys[M], 0)
+        return g
+
     with torch.cuda.stream(stream):
         for M in MS:  # eager warm-up of every launch
             sk.skinny_gemm_bf16(xs[M], ring[0], ys[M], 0)
         torch.cuda.synchronize()
-        for gi in range(groups):
-            g = torch.cuda.CUDAGraph()
-            with torch.cuda.graph(g, stream=stream):
-                for j, M in enumerate(MS):
-                    sk.skinny_gemm_bf16(xs[M], ring[gi * len(MS) + j], ys[M], 0)
-            graphs.append(g)
+        full = record(groups)
+        tails = {r: record(r) for r in {args.steps % groups, args.warmup % groups} if r}
         torch.cuda.synchronize()
 
-        for i in range(args.warmup):
-            graphs[i % groups].replay()
+        def run_steps(n):
+            for _ in range(n // groups):
+                full.replay()
+            if n % groups:
+                tails[n % groups].replay()
+
+        run_steps(args.warmup)
         torch.cuda.synchronize()
         start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         t0 = time.perf_counter()
         start.record(stream)
-        for i in range(args.steps):
-            graphs[i % groups].replay()
+        run_steps(args.steps)
         end.record(stream)
         torch.cuda.synchronize()
         wall = time.perf_counter() - t0
