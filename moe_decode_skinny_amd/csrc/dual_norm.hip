@@ -170,8 +170,7 @@ __global__ __launch_bounds__(kDualThreads) void dual_norm_kernel(
 // kernel boundary orders the two; arithmetic as in the one-kernel form.
 constexpr int kSplitThreads = 256;
 
-__device__ __forceinline__ void load4(const uint16_t *p, double (&v)[4]) {
-  const uint2 u = *reinterpret_cast<const uint2 *>(p);
+__device__ __forceinline__ void unpack4(uint2 u, double (&v)[4]) {
   v[0] = (double)bf16_lo(u.x);
   v[1] = (double)bf16_hi(u.x);
   v[2] = (double)bf16_lo(u.y);
@@ -190,15 +189,30 @@ __global__ __launch_bounds__(kSplitThreads) void dual_gate_kernel(
   const uint16_t *prow = partial + (size_t)row * H;
   float *srow = residual + (size_t)row * H;
 
-  // The thread's own columns first (in flight during the reduction).
-  double p[4], g[4], a[4], b[4], s[4];
+  // The thread's own columns first, as raw bits, all in flight during the
+  // reduction (an absent post weight or alpha reads beta's bits, unused).
+  uint2 pr = make_uint2(0, 0), gr = pr, ar = pr, br = pr;
+  f32x4 sv = {0.f, 0.f, 0.f, 0.f};
   if (mine) {
-    load4(prow + c0, p);
-    const f32x4 sv = *reinterpret_cast<const f32x4 *>(srow + c0);
-#pragma unroll
-    for (int j = 0; j < 4; ++j) s[j] = (double)sv[j];
+    pr = *reinterpret_cast<const uint2 *>(prow + c0);
+    sv = *reinterpret_cast<const f32x4 *>(srow + c0);
+    gr = *reinterpret_cast<const uint2 *>((post_w ? post_w : beta) + c0);
+    ar = *reinterpret_cast<const uint2 *>((alpha ? alpha : beta) + c0);
+    br = *reinterpret_cast<const uint2 *>(beta + c0);
+  }
+
+  const double ss = sum_squares<kSplitThreads>(prow, H / 16, tid);
+  __shared__ double slots[kSplitThreads / 64], slots2[kSplitThreads / 64];
+  const double inv =
+      1.0 / sqrt(block_sum<kSplitThreads>(ss, slots) / (double)H + (double)post_eps);
+
+  double ss2 = 0.0;
+  if (mine) {
+    double p[4], g[4], a[4], b[4], s[4];
+    unpack4(pr, p);
+    unpack4(br, b);
     if (post_w) {
-      load4(post_w + c0, g);
+      unpack4(gr, g);
 #pragma unroll
       for (int j = 0; j < 4; ++j) g[j] += (double)post_gc;
     } else {
@@ -206,27 +220,13 @@ __global__ __launch_bounds__(kSplitThreads) void dual_gate_kernel(
       for (int j = 0; j < 4; ++j) g[j] = 1.0;
     }
     if (alpha) {
-      load4(alpha + c0, a);
+      unpack4(ar, a);
     } else {
 #pragma unroll
       for (int j = 0; j < 4; ++j) a[j] = (double)alpha_scalar;
     }
-    load4(beta + c0, b);
-  }
-
-  double ss = 0.0;
-  for (int blk = tid; blk < H / 16; blk += kSplitThreads) {
-    double v[16];
-    load16(prow + blk * 16, v);
 #pragma unroll
-    for (int j = 0; j < 16; ++j) ss += v[j] * v[j];
-  }
-  __shared__ double slots[kSplitThreads / 64], slots2[kSplitThreads / 64];
-  const double inv =
-      1.0 / sqrt(block_sum<kSplitThreads>(ss, slots) / (double)H + (double)post_eps);
-
-  double ss2 = 0.0;
-  if (mine) {
+    for (int j = 0; j < 4; ++j) s[j] = (double)sv[j];
     f32x4 o;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
@@ -248,13 +248,23 @@ __global__ __launch_bounds__(kSplitThreads) void dual_out_kernel(
   const int row = blockIdx.x / slices, sl = blockIdx.x - row * slices;
   const int c0 = sl * kDualSlice + 4 * threadIdx.x;
   if (c0 >= H) return;
-  const double *ps = slice_ss + (size_t)row * slices;
-  double ss2 = ps[0];
-  for (int i = 1; i < slices; ++i) ss2 += ps[i];
-  const double inv2 = 1.0 / sqrt(ss2 / (double)H + (double)pre_eps);
+  // The thread's columns first, then the row's slice sums eight at a time
+  // (loads in flight together), summed in slice order.
   const f32x4 sv = *reinterpret_cast<const f32x4 *>(residual + (size_t)row * H + c0);
+  const uint2 wr = *reinterpret_cast<const uint2 *>(next_w + c0);
+  const double *ps = slice_ss + (size_t)row * slices;
+  double ss2 = 0.0;
+  for (int i0 = 0; i0 < slices; i0 += 8) {
+    double part[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) part[i] = i0 + i < slices ? ps[i0 + i] : 0.0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      if (i0 + i < slices) ss2 = i0 + i == 0 ? part[0] : ss2 + part[i];
+  }
+  const double inv2 = 1.0 / sqrt(ss2 / (double)H + (double)pre_eps);
   double w[4];
-  load4(next_w + c0, w);
+  unpack4(wr, w);
   unsigned yb[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j) yb[j] = f64_to_bf16((double)sv[j] * inv2 * (w[j] + (double)pre_gc));

@@ -38,6 +38,31 @@ __device__ __forceinline__ void load16(const uint16_t *p, double (&v)[16]) {
   }
 }
 
+// This thread's part of a row's sum of squares: the 16-column blocks t,
+// t + THREADS, ... of `row` in column order, two blocks' loads in flight at
+// a time (the order of the sum is that of the blocks either way).
+template <int THREADS>
+__device__ __forceinline__ double sum_squares(const uint16_t *row, int blocks, int t) {
+  double ss = 0.0;
+  int b = t;
+  for (; b + THREADS < blocks; b += 2 * THREADS) {
+    double v[16], u[16];
+    load16(row + b * 16, v);
+    load16(row + (b + THREADS) * 16, u);
+#pragma unroll
+    for (int j = 0; j < 16; ++j) ss += v[j] * v[j];
+#pragma unroll
+    for (int j = 0; j < 16; ++j) ss += u[j] * u[j];
+  }
+  if (b < blocks) {
+    double v[16];
+    load16(row + b * 16, v);
+#pragma unroll
+    for (int j = 0; j < 16; ++j) ss += v[j] * v[j];
+  }
+  return ss;
+}
+
 // Sum over the workgroup in a fixed order: a lane butterfly inside each wave,
 // then the wave sums in wave order (every thread gets the total).  `slots`
 // is LDS of THREADS / 64 doubles used only by this call.

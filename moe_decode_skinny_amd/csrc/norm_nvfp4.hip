@@ -89,15 +89,12 @@ __global__ __launch_bounds__(kNormThreads) void rmsnorm_kernel(
     rq = *reinterpret_cast<const uint2 *>(rrow + blk * 16 + 4 * q);
     wq = *reinterpret_cast<const uint2 *>(w + blk * 16 + 4 * q);
   }
+  // The global scale too: read after the barrier it would cost one more
+  // memory round trip at the end of the chain.
+  const float gsf = QUANT ? *global_scale : 0.f;
 
   // Sum of squares of the whole row in a fixed order.
-  double ss = 0.0;
-  for (int b = tid; b < blocks; b += kNormThreads) {
-    double v[16];
-    load16(rrow + b * 16, v);
-#pragma unroll
-    for (int j = 0; j < 16; ++j) ss += v[j] * v[j];
-  }
+  const double ss = sum_squares<kNormThreads>(rrow, blocks, tid);
   __shared__ double wave_ss[kNormThreads / 64];
   const double total = block_sum(ss, wave_ss);
   if (!mine) return;
@@ -118,7 +115,7 @@ __global__ __launch_bounds__(kNormThreads) void rmsnorm_kernel(
   if constexpr (QUANT) {
     amax = fmax(amax, __shfl_xor(amax, 1));  // the block's amax over its quad
     amax = fmax(amax, __shfl_xor(amax, 2));
-    const double gs = (double)*global_scale;
+    const double gs = (double)gsf;
     const unsigned sf = e4m3_rn_satfinite(gs * amax / 6.0);
     const double dec = e4m3_value(sf);
     const double os = dec == 0.0 ? 0.0 : gs / dec;
