@@ -100,8 +100,11 @@ int skinny_init(int device);
  *   W       bf16 [N, K], 16-byte aligned
  *   y       bf16 [M, N], 16-byte aligned; only these M rows are written
  *   M       1..16 tokens
- *   N       output features, N > 0, N % 16 == 0
- *   K       reduction length, K > 0, K % 8 == 0 (16-byte rows)
+ *   N       output features, N > 0, N % 16 == 0, N <= 2^24
+ *   K       reduction length, K > 0, K % 8 == 0 (16-byte rows); the longest
+ *           K with a launch is 16 splits x 16 waves x the widest DOT2 wave
+ *           slice: 524288 for M <= 4, 262144 for M <= 8, 131072 for M <= 16
+ *           (longer K: SKINNY_EUNSUPPORTED)
  *   splits  0 = let the chooser pick; otherwise S in {1, 2, 4, 8, 16}
  * x, W and y must not overlap.  The result is bitwise identical for the same
  * (M, N, K, launch) on one device.  A launch with S > 1 enqueues two kernels

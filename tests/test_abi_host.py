@@ -84,7 +84,10 @@ def test_chooser_gives_valid_launches(sk, M, N, K, splits):
     "M,N,K,splits,needle",
     [(0, 1024, 4096, 0, "M=0"), (17, 1024, 4096, 0, "M=17"), (1, 1000, 4096, 0, "N=1000"),
      (1, 0, 4096, 0, "N=0"), (1, 1024, 4095, 0, "K=4095"), (1, 1024, 0, 0, "K=0"),
-     (1, 1024, 4096, 3, "splits=3"), (1, 1024, 4096, 32, "splits=32")],
+     (1, 1024, 4096, 3, "splits=3"), (1, 1024, 4096, 32, "splits=32"),
+     (1, 16, (1 << 25) + 8, 0, "at most"), (1, (1 << 24) + 16, 8, 0, "at most"),
+     (4, 16, 524288 + 8, 0, "K too long"), (8, 16, 262144 + 8, 0, "K too long"),
+     (16, 16, 131072 + 8, 0, "K too long")],
 )
 def test_unsupported_reasons(sk, M, N, K, splits, needle):
     reason = sk.skinny_gemm_unsupported(M, N, K, splits)

@@ -171,6 +171,18 @@ def test_edge_shapes(gpu_lib, M, N, K):
     assert_gemm_close(_run(gpu_lib, x, w, M), oracle.gemm_bf16(x[:M], w, THREADS), "edge")
 
 
+@pytest.mark.parametrize("M,N,K", [(4, 16, 524288), (8, 16, 262144), (16, 32, 131072),
+                                   (2, 1 << 24, 8)])
+def test_size_limits(gpu_lib, M, N, K):
+    """The longest K the chooser supports at 4, 8 and 16 tokens (16 splits of
+    16 waves, the 16-partial reduction) and the widest N (2^24 features, 8M
+    workgroups)."""
+    assert gpu_lib.skinny_gemm_unsupported(M, N, K) is None
+    x, w = synthetic.gemm_inputs(N=N, K=K, seed=8)
+    _say(f"limit M={M} N={N} K={K} {gpu_lib.skinny_choose(M, N, K, 0)}")
+    assert_gemm_close(_run(gpu_lib, x, w, M), oracle.gemm_bf16(x[:M], w, THREADS), "limit")
+
+
 def test_graph_capture_replay(gpu_lib):
     """The GEMM recorded in a HIP graph (allocates nothing, no host sync),
     replayed with new inputs and eager work between replays."""
@@ -220,8 +232,9 @@ def test_split_k_handoff_alternating_inputs(gpu_lib, path, splits):
     refs = [oracle.gemm_bf16(xa[:M], wa, THREADS), oracle.gemm_bf16(xa[:M], wb, THREADS)]
     if path == "mfma":
         launch = gpu_lib.Launch(1, splits, -(-K // (splits * 32 * 4)), 4, 2, 16)
-    elif path == "mfma_f4":
-        launch = gpu_lib.Launch(1, splits, 4 * -(-K // (splits * 32 * 4)), 4, 2, 64)
+    elif path == "mfma_f4":  # 4 tiles a workgroup: the fewest chunks within 16 waves
+        chunks = next(c for c in (1, 2, 4, 8, 16) if 4 * -(-K // (splits * 32 * c)) <= 16)
+        launch = gpu_lib.Launch(1, splits, 4 * -(-K // (splits * 32 * chunks)), chunks, 2, 64)
     elif path == "mfma_4x4":
         launch = gpu_lib.Launch(3, splits, -(-K // (splits * 128 * 4)), 4, 1, 8)
     else:
