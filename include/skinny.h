@@ -51,8 +51,9 @@ enum {
   SKINNY_PATH_MFMA_LDS = 2,/* ring only: MFMA with each wave's weights loaded
                               row by row and re-laid out through LDS; same
                               operands and results as SKINNY_PATH_MFMA        */
-  SKINNY_PATH_MFMA_4X4 = 3 /* bf16 MFMA 4x4x4 in 16 blocks: lanes run along K
-                              as in DOT2, 4 weight rows x 4 tokens a block    */
+  SKINNY_PATH_MFMA_4X4 = 3 /* bf16 MFMA 4x4x4 in 16 blocks: lanes load along K
+                              as in DOT2, then a transpose in each 4-lane
+                              group gives 4 weight rows x 4 tokens a block    */
 };
 
 /* A launch shape of the GEMM: the counterpart of the unpooler page's
@@ -71,8 +72,8 @@ enum {
  *         register-light variants).
  *   MFMA_4X4: a workgroup owns rows = 4 or 8 output features; each wave owns
  *         kw = 128 * chunks consecutive K (16 blocks x 8 bf16 per chunk,
- *         chunks 1, 2, 4, 8) and all tokens in sets of 4;
- *         waves = ceil(K / (splits * kw)) <= 16.
+ *         chunks 4 or 8: whole groups of 512 K, loaded as 1 KiB row pieces)
+ *         and all tokens in sets of 4; waves = ceil(K / (splits * kw)) <= 16.
  * In all three, wave partials are summed in LDS in wave order; with splits > 1
  * each workgroup writes an FP32 partial and a second kernel on the same
  * stream sums splits 0..S-1 in order. */
@@ -80,7 +81,7 @@ typedef struct skinny_launch {
   int path;   /* SKINNY_PATH_MFMA, SKINNY_PATH_DOT2 or SKINNY_PATH_MFMA_4X4 */
   int splits; /* S in {1, 2, 4, 8, 16}: workgroups along K per output block   */
   int waves;  /* waves per workgroup (see above)                             */
-  int chunks; /* K chunks per wave: MFMA 1..16, DOT2 1, 2, 4, MFMA_4X4 1..8  */
+  int chunks; /* K chunks per wave: MFMA 1..16, DOT2 1, 2, 4, MFMA_4X4 4, 8  */
   int accs;   /* MFMA: accumulators per wave, 1, 2 or 4; others: 1           */
   int rows;   /* features per workgroup: MFMA 16, 32, 64; DOT2 2..16;
                  MFMA_4X4 4, 8                                                */
@@ -183,7 +184,7 @@ int skinny_gemm_bf16_publish(const void *x, const void *W, void *y, int M,
  *               or MFMA_LDS (as MFMA with chunks 2..16, and the staging
  *               regions, waves x 16 x (64 chunks + 16) bytes, plus 2 KiB per
  *               wave, within the 160 KiB of LDS) or MFMA_4X4 (rows 4 or 8,
- *               chunks 1..8, waves = ceil(K / (128 chunks)) <= 16)
+ *               chunks 4 or 8, waves = ceil(K / (128 chunks)) <= 16)
  *   segment     consecutive output blocks of one item a workgroup takes in a
  *               row, keeping that item's activations in registers; it
  *               divides N / gemm.rows

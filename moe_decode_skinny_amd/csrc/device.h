@@ -17,6 +17,7 @@ constexpr int kTileN = 16;         // features per MFMA tile (grid N / 16)
 constexpr int kMfmaK = 32;         // K per v_mfma_f32_16x16x32_bf16
 constexpr int kDot2K = 512;        // K per DOT2 chunk: 64 lanes x 8 bf16
 constexpr int kBlockK = 128;       // K per 16-block MFMA chunk: 16 blocks x 8 bf16
+constexpr int kGroupK = 4 * kBlockK;  // K per 16-block load group (4 chunks, 1 KiB a row)
 constexpr int kBlocksMaxWaves = 16;
 constexpr int kMaxMfmaChunks = 16;
 constexpr int kMaxDot2Chunks = 4;

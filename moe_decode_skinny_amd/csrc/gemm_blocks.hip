@@ -3,8 +3,10 @@
 // path, the products go to the matrix cores (v_mfma_f32_4x4x4_16b_bf16; the
 // lane layout and the order of the sums are in blocks_device.h).
 //   wave w of workgroup (group, s) owns K range (s * waves + w) * kw,
-//   kw = 128 * CHUNKS, of the workgroup's 4 * R4 weight rows, and all M
-//   tokens in Q sets of 4; weights are loaded first, then activations.
+//   kw = 128 * CHUNKS (CHUNKS 4 or 8: whole 512-K load groups), of the
+//   workgroup's 4 * R4 weight rows, and all M tokens in Q sets of 4; weights
+//   are loaded first, then activations, then both are transposed into the
+//   MFMA layout inside each 4-lane group.
 // Reduction in an order fixed by the launch shape (module description): the
 // 16 blocks across lanes, waves 0..waves-1 in order through LDS, and with
 // S > 1 an FP32 partial per split that split_reduce.hip sums s = 0..S-1 in
@@ -12,8 +14,9 @@
 //
 // Against DOT2 this replaces 4 VALU instructions per (row, token, 8 K) and a
 // 64-lane reduce-scatter with one MFMA per (row set, token set, 4 K x 16
-// blocks) and a 16-lane one, but every load instruction touches 4 rows (or
-// tokens) with 64 bytes each per 16 lanes instead of 256 contiguous bytes.
+// blocks), a 16-lane reduce-scatter and 4 DPP moves and selects per loaded
+// 4 bytes
+// (the transpose); the loads are the same 1 KiB row pieces as DOT2's.
 #include "blocks_device.h"
 #include "internal.h"
 
@@ -44,14 +47,16 @@ __global__ __launch_bounds__(THREADS) void gemm_blocks_kernel(
     s = b % S;
   }
   const int f0 = group * ROWS;
-  const int k0 = (s * waves + wave) * kw + (lane >> 2) * 8;
+  const int k0 = (s * waves + wave) * kw + lane * 8;
 
   u32x4 wv[R4][CHUNKS], xv[Q][CHUNKS];
   load_sets<R4, CHUNKS, kCacheNT>(wv, buffer_rsrc(w + (size_t)f0 * K, (unsigned)(ROWS * K * 2)),
-                                  K, k0, lane & 3);
+                                  K, k0);
   __builtin_amdgcn_sched_barrier(0);
-  load_sets<Q, CHUNKS, 0>(xv, buffer_rsrc(x, (unsigned)(M * K * 2)), K, k0, lane & 3);
+  load_sets<Q, CHUNKS, 0>(xv, buffer_rsrc(x, (unsigned)(M * K * 2)), K, k0);
   __builtin_amdgcn_sched_barrier(0);
+  transpose_sets<R4, CHUNKS>(wv, lane);
+  transpose_sets<Q, CHUNKS>(xv, lane);
   f32x4 acc[Q][R4];
   products<R4, CHUNKS, Q>(wv, xv, acc);
 
@@ -107,8 +112,6 @@ BlocksKernel pick_q(int q) {
 template <int R4, int T>
 BlocksKernel pick_chunks(int chunks, int q) {
   switch (chunks) {
-    case 1: return pick_q<R4, 1, T>(q);
-    case 2: return pick_q<R4, 2, T>(q);
     case 4: return pick_q<R4, 4, T>(q);
     case 8: return pick_q<R4, 8, T>(q);
   }

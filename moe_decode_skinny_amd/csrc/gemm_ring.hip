@@ -282,7 +282,7 @@ __device__ __forceinline__ bool blocks_ring_tile(const RingItems &items, const D
     int kx = k0;
     asm volatile("" : "+v"(kx));
     blocks::load_sets<Q, CHUNKS, 0>(xv, buffer_rsrc(items.x[item], (unsigned)(a.M * K * 2)), K,
-                                    kx, lane & 3);
+                                    kx);
   }
   __builtin_amdgcn_sched_barrier(0);
   int ns = s, nsub = sub;
@@ -293,10 +293,13 @@ __device__ __forceinline__ bool blocks_ring_tile(const RingItems &items, const D
         next,
         buffer_rsrc(items.w[walk.item(cs)] + (size_t)walk.block(cs, csub) * ROWS * K,
                     more ? (unsigned)(ROWS * K * 2) : 0u),
-        K, k0, lane & 3);
+        K, k0);
   }
   __builtin_amdgcn_sched_barrier(0);
 
+  // Into the MFMA layout: the segment's activations once, this tile's weights.
+  if (sub == 0) blocks::transpose_sets<Q, CHUNKS>(xv, lane);
+  blocks::transpose_sets<R4, CHUNKS>(cur, lane);
   f32x4 acc[Q][R4];
   blocks::products<R4, CHUNKS, Q>(cur, xv, acc);
   // Buffer P: as in the DOT2 ring.
@@ -328,7 +331,7 @@ __global__ __launch_bounds__(THREADS) void gemm_blocks_ring_kernel(
   const int wave = wave_index();
   const int waves = blockDim.x >> 6;
   const Dot2Args a{M, N, K};
-  const int k0 = wave * kw + (lane >> 2) * 8;
+  const int k0 = wave * kw + lane * 8;
   __shared__ float red[2][THREADS / 64][blocks::kOutputs<R4, Q>];
 
   // gridDim.x <= walk.segs, so every workgroup has a first tile.
@@ -337,7 +340,7 @@ __global__ __launch_bounds__(THREADS) void gemm_blocks_ring_kernel(
   blocks::load_sets<R4, CHUNKS, kCacheNT>(
       wa, buffer_rsrc(items.w[walk.item(s)] + (size_t)walk.block(s, 0) * ROWS * K,
                       (unsigned)(ROWS * K * 2)),
-      K, k0, lane & 3);
+      K, k0);
   for (;;) {
     if (!blocks_ring_tile<R4, CHUNKS, Q, THREADS / 64, 0>(items, a, walk, s, sub, wa, wb, xv,
                                                           red, lane, wave, waves, k0))
@@ -377,8 +380,6 @@ Dot2RingKernel blocks_ring_pick_q(int q) {
 template <int R4, int THREADS>
 Dot2RingKernel blocks_ring_pick_chunks(int chunks, int q) {
   switch (chunks) {
-    case 1: return blocks_ring_pick_q<R4, 1, THREADS>(q);
-    case 2: return blocks_ring_pick_q<R4, 2, THREADS>(q);
     case 4: return blocks_ring_pick_q<R4, 4, THREADS>(q);
     case 8: return blocks_ring_pick_q<R4, 8, THREADS>(q);
   }

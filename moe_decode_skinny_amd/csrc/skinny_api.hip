@@ -134,6 +134,9 @@ static int launch_check(int M, int N, int K, const skinny_launch &l) {
     if (l.accs != 1) return fail(SKINNY_EUNSUPPORTED, "MFMA 4x4 launch has accs=1");
     if (l.rows != 4 && l.rows != 8)
       return fail(SKINNY_EUNSUPPORTED, "MFMA 4x4 rows=%d: needs 4 or 8", l.rows);
+    if (l.chunks != 4 && l.chunks != 8)
+      return fail(SKINNY_EUNSUPPORTED, "MFMA 4x4 chunks=%d: needs 4 or 8 (whole 512-K load "
+                  "groups)", l.chunks);
     if (N % l.rows)
       return fail(SKINNY_EUNSUPPORTED, "N=%d is not a multiple of rows=%d", N, l.rows);
     const long kw = (long)kBlockK * l.chunks;
@@ -178,7 +181,7 @@ static const TableEntry kTable[] = {
     {1024, 4096, 2, 2, {SKINNY_PATH_DOT2, 1, 2, 4, 1, 2}, {2, 256}},
     {1024, 4096, 3, 4, {SKINNY_PATH_DOT2, 1, 4, 2, 1, 2}, {2, 256}},
     {1024, 4096, 5, 8, {SKINNY_PATH_DOT2, 1, 4, 2, 1, 4}, {}},
-    {1024, 4096, 9, 16, {SKINNY_PATH_DOT2, 1, 8, 1, 1, 4}, {}},
+    {1024, 4096, 9, 16, {SKINNY_PATH_MFMA_4X4, 1, 8, 4, 1, 4}, {}},
     // o_proj shard
     {8192, 1024, 1, 1, {SKINNY_PATH_DOT2, 1, 1, 2, 1, 2}, {}},
     {8192, 1024, 2, 4, {SKINNY_PATH_DOT2, 1, 1, 2, 1, 4}, {2, 1024}},
@@ -196,6 +199,9 @@ static const TableEntry kTable[] = {
 
 // The general rule the table follows (used for any other shape, or when an
 // explicit split count is asked for):
+//   the 16-block MFMA for 9..16 tokens when one split of at most 16 waves
+//   covers K = 4096..8192 and N gives every compute unit a 4-row block
+//   (N / 4 >= 256): 4 rows, 4 chunks per wave;
 //   DOT2 (lanes along K; activation traffic M / rows of the weight traffic;
 //   no split-K) for M <= 8, and for M <= 16 on narrow shards (< 256 MFMA
 //   tiles); 2 rows per workgroup for M <= 2, else 4, and 2 rows when that
@@ -208,6 +214,10 @@ static const TableEntry kTable[] = {
 static skinny_launch rule(int M, int N, int K, int splits) {
   const long tiles = N / kTileN;
   const long units = ceil_div(K, kDot2K);
+  if (M > 8 && splits <= 1 && N / 4 >= 256 && K >= 4096 && K <= 16 * kGroupK) {
+    const skinny_launch l{SKINNY_PATH_MFMA_4X4, 1, ceil_div(K, (long)kGroupK), 4, 1, 4};
+    if (launch_check(M, N, K, l) == SKINNY_OK) return l;
+  }
   if (M <= 8 || tiles < 256) {
     const int rows = M <= 2 ? 2 : 4;
     const int mt = dot2_token_tile(M);
@@ -331,6 +341,9 @@ static int ring_check(int count, int M, int N, int K, const skinny_ring_launch &
     if (l.accs != 1) return fail(SKINNY_EUNSUPPORTED, "MFMA 4x4 launch has accs=1");
     if (l.rows != 4 && l.rows != 8)
       return fail(SKINNY_EUNSUPPORTED, "MFMA 4x4 rows=%d: needs 4 or 8", l.rows);
+    if (l.chunks != 4 && l.chunks != 8)
+      return fail(SKINNY_EUNSUPPORTED, "MFMA 4x4 chunks=%d: needs 4 or 8 (whole 512-K load "
+                  "groups)", l.chunks);
     const long kw = (long)kBlockK * l.chunks;
     const int need = ceil_div(K, kw);
     if (l.waves != need || l.waves < 1 || l.waves > 16)
@@ -377,7 +390,7 @@ static const RingEntry kRingTable[] = {
     {1024, 4096, 1, 1, DOT2_RING(2, 4, 2, 1, 1024, I)},
     {1024, 4096, 2, 2, DOT2_RING(8, 1, 8, 2, 2048, I)},
     {1024, 4096, 3, 4, DOT2_RING(8, 1, 4, 4, 2048, X)},
-    {1024, 4096, 5, 8, MFMA4X4_RING(8, 4, 8, 32, 240, X)},
+    {1024, 4096, 5, 8, MFMA4X4_RING(8, 4, 8, 16, 240, X)},
     {1024, 4096, 9, 16, LDS_RING(8, 16, 1, 16, 16, 240, X)},
     // o_proj shard
     {8192, 1024, 1, 1, MFMA4X4_RING(2, 4, 4, 8, 1024, I)},
@@ -389,7 +402,7 @@ static const RingEntry kRingTable[] = {
     {512, 8192, 1, 1, DOT2_RING(4, 4, 2, 1, 2048, I)},
     {512, 8192, 2, 2, DOT2_RING(4, 4, 2, 4, 2048, X)},
     {512, 8192, 3, 4, DOT2_RING(4, 4, 2, 4, 1024, X)},
-    {512, 8192, 5, 8, MFMA4X4_RING(8, 8, 4, 32, 240, X)},
+    {512, 8192, 5, 8, MFMA4X4_RING(16, 4, 4, 32, 240, X)},
     {512, 8192, 9, 16, MFMA4X4_RING(16, 4, 4, 32, 240, X)},
     // full pooler
     {4096, 8192, 1, 2, DOT2_RING(4, 4, 2, 8, 256, I)},
@@ -444,7 +457,7 @@ static int ring_choose(int M, int N, int K, int count, skinny_ring_launch *out) 
     int seg = 32;
     while (groups % seg) seg /= 2;
     const long segs = (long)count * (groups / seg);
-    for (int c = 4; c >= 1; c /= 2) {
+    for (int c = 4; c <= 8; c *= 2) {
       const skinny_ring_launch r{{SKINNY_PATH_MFMA_4X4, 1, ceil_div(K, (long)kBlockK * c), c, 1, 4},
                                  seg, (int)(segs < 256 ? segs : 256), SKINNY_RING_XCD_LOCAL};
       if (ring_check(count, M, N, K, r) == SKINNY_OK) {

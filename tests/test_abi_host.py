@@ -143,8 +143,9 @@ def test_chooser_walks_the_measured_shapes(sk):
 
 
 def test_mfma_4x4_launch_reasons(sk):
-    """The 16-block MFMA path: rows 4 or 8, accs 1, waves = ceil(K / (S * 128
-    chunks)) <= 16, and only the register-budgeted variants."""
+    """The 16-block MFMA path: rows 4 or 8, accs 1, chunks 4 or 8 (whole
+    512-K load groups), waves = ceil(K / (S * 128 chunks)) <= 16, and only the
+    register-budgeted variants."""
     L, P = sk.Launch, sk.SKINNY_PATH_MFMA_4X4
     assert sk.skinny_launch_unsupported(16, 1024, 4096, L(P, 1, 8, 4, 1, 4)) is None
     assert sk.skinny_launch_unsupported(16, 1024, 4096, L(P, 2, 4, 4, 1, 8)) is None
@@ -153,8 +154,11 @@ def test_mfma_4x4_launch_reasons(sk):
     assert "rows=16" in sk.skinny_launch_unsupported(16, 1024, 4096, L(P, 1, 8, 4, 1, 16))
     assert "accs" in sk.skinny_launch_unsupported(16, 1024, 4096, L(P, 1, 8, 4, 2, 4))
     assert "needs 8 waves" in sk.skinny_launch_unsupported(16, 1024, 4096, L(P, 1, 4, 4, 1, 4))
-    assert "MFMA 4x4: 1..16" in sk.skinny_launch_unsupported(16, 1024, 4096,
-                                                            L(P, 1, 32, 1, 1, 4))
+    assert "MFMA 4x4: 1..16" in sk.skinny_launch_unsupported(16, 1024, 16384,
+                                                            L(P, 1, 32, 4, 1, 4))
+    for chunks in (1, 2, 16):
+        assert "needs 4 or 8" in sk.skinny_launch_unsupported(
+            16, 1024, 4096, L(P, 1, 4096 // (128 * chunks), chunks, 1, 4))
     # 8 rows x 8 chunks x 16 tokens needs 224 registers a lane: not built
     assert "no MFMA 4x4 kernel" in sk.skinny_launch_unsupported(16, 1024, 4096,
                                                                 L(P, 1, 4, 8, 1, 8))

@@ -85,7 +85,7 @@ def _single(sk, x_bits, w_bits, M, launch):
 
 def _ring_launches(sk, M, N, K):
     """Ring launch candidates of every family with splits = 1: DOT2 rows
-    2..16 x chunks 1, 2, 4, MFMA 4x4 rows 4, 8 x chunks 1..8 and MFMA 1, 2, 4
+    2..16 x chunks 1, 2, 4, MFMA 4x4 rows 4, 8 x chunks 4, 8 and MFMA 1, 2, 4
     tiles x chunks 1..16 x accs 1, 2 (the ring validator decides which it has
     kernels for)."""
     out = []
@@ -93,7 +93,7 @@ def _ring_launches(sk, M, N, K):
         for chunks in (1, 2, 4):
             out.append(sk.Launch(0, 1, -(-K // (512 * chunks)), chunks, 1, rows))
     for rows in (4, 8):
-        for chunks in (1, 2, 4, 8):
+        for chunks in (4, 8):
             out.append(sk.Launch(sk.SKINNY_PATH_MFMA_4X4, 1, -(-K // (128 * chunks)), chunks, 1,
                                  rows))
     for path in (sk.SKINNY_PATH_MFMA, sk.SKINNY_PATH_MFMA_LDS):
@@ -185,7 +185,7 @@ def test_ring_xcd_local_walk(gpu_lib, path):
     launch under every walk and order."""
     M, N, K, count = 12, 128, 1032, 19
     g = {"dot2": gpu_lib.Launch(0, 1, 3, 1, 1, 4),
-         "mfma_4x4": gpu_lib.Launch(3, 1, 5, 2, 1, 8),
+         "mfma_4x4": gpu_lib.Launch(3, 1, 3, 4, 1, 8),
          "mfma_lds": gpu_lib.Launch(2, 1, 9, 4, 1, 16)}[path]
     xs, ws = _items(count, N, K, seed=250)
     singles = [_single(gpu_lib, xs[i], ws[i], M, g) for i in range(count)]
