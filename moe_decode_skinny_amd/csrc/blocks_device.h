@@ -12,10 +12,9 @@
 //   taking 16 bytes at K offset k_w + 8 l, so every load instruction is 1 KiB
 //   of one row and each 4-lane group reads 64 contiguous bytes;
 //   a transpose inside every 4-lane group (two exchange steps, DPP quad
-//   permutations and selects) then
-//   leaves lane 4b + j with row j at the K offsets k_w + 32 b + 8 s of its
-//   four registers s = 0..3, the layout the MFMA needs (all four lanes of a
-//   block at the same K);
+//   permutations and selects) then leaves lane 4b + j with row j at the K
+//   offsets k_w + 32 b + 8 s of its four registers s = 0..3, the layout the
+//   MFMA needs (all four lanes of a block at the same K);
 //   chunk c = 4 g + s of a set is register s of group g, and the two halves
 //   of a register feed two MFMAs.
 // (Loading each block's four rows directly puts four rows, so four cache

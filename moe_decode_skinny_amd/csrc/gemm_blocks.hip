@@ -15,8 +15,7 @@
 // Against DOT2 this replaces 4 VALU instructions per (row, token, 8 K) and a
 // 64-lane reduce-scatter with one MFMA per (row set, token set, 4 K x 16
 // blocks), a 16-lane reduce-scatter and 4 DPP moves and selects per loaded
-// 4 bytes
-// (the transpose); the loads are the same 1 KiB row pieces as DOT2's.
+// 4 bytes (the transpose); the loads are the same 1 KiB row pieces as DOT2's.
 #include "blocks_device.h"
 #include "internal.h"
 
