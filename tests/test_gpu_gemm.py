@@ -161,11 +161,14 @@ def test_exact_integer_inputs_bit_exact(gpu_lib, M):
 
 @pytest.mark.parametrize("M,N,K", [(1, 16, 8), (16, 16, 8), (2, 16, 32), (5, 80, 8), (16, 16, 4104),
                                    (1, 16, 65536), (16, 32, 65536), (4, 65536, 64),
-                                   (16, 49152, 520)])
+                                   (16, 49152, 520), (12, 2048, 4096), (9, 1024, 8192),
+                                   (16, 1040, 6000)])
 def test_edge_shapes(gpu_lib, M, N, K):
     """Single rows and tiles, K of one 16-byte piece, long K (split-K with 16
-    waves per split), very wide N (16384 workgroups) and a wide 16-token
-    MFMA call."""
+    waves per split), very wide N (16384 workgroups), a wide 16-token MFMA
+    call, and shapes outside the table that the chooser's rule gives to the
+    16-block MFMA (9-16 tokens, N / 4 >= 256, K 4096..8192, a ragged last
+    load group)."""
     x, w = synthetic.gemm_inputs(N=N, K=K, seed=7)
     _say(f"edge M={M} N={N} K={K}")
     assert_gemm_close(_run(gpu_lib, x, w, M), oracle.gemm_bf16(x[:M], w, THREADS), "edge")
