@@ -4,7 +4,7 @@
 The pages fix only the order of the steps, the dtypes (BF16 partial and
 output, FP32 stream updated in place) and the parameters (optional post
 weight, alpha as a tensor or a float, beta, next weight).  The formula of the
-gated add and the rounding points are a reading of them (stated in the oracle
+gated add and the rounding points are a reading of the pages (stated in the oracle
 source): these pins check the oracle against closed forms of that reading,
 so a slip in it (a dropped term, swapped constants, the wrong stream fed to
 the second norm) fails; whether the reading is the pages' own stays unpinned.
