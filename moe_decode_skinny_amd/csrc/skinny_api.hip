@@ -192,8 +192,9 @@ static const TableEntry kTable[] = {
     {512, 8192, 9, 16, {SKINNY_PATH_DOT2, 1, 16, 1, 1, 2}, {}},
     // full pooler
     {4096, 8192, 1, 1, {SKINNY_PATH_DOT2, 1, 8, 2, 1, 2}, {}},
-    {4096, 8192, 2, 4, {SKINNY_PATH_DOT2, 1, 8, 2, 1, 8}, {}},
-    {4096, 8192, 5, 8, {SKINNY_PATH_DOT2, 1, 8, 2, 1, 4}, {4, 256}},
+    {4096, 8192, 2, 2, {SKINNY_PATH_DOT2, 1, 8, 2, 1, 8}, {}},
+    {4096, 8192, 3, 4, {SKINNY_PATH_MFMA_4X4, 1, 16, 4, 1, 8}, {}},
+    {4096, 8192, 5, 8, {SKINNY_PATH_MFMA_4X4, 1, 8, 8, 1, 4}, {4, 256}},
     {4096, 8192, 9, 16, {SKINNY_PATH_MFMA_4X4, 1, 16, 4, 1, 4}, {4, 256}},
 };
 
