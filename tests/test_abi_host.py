@@ -142,6 +142,21 @@ def test_chooser_walks_the_measured_shapes(sk):
         sk.skinny_choose_walk(17, 1024, 4096, 0)
 
 
+def test_rule_takes_the_16_block_path_for_many_tokens_on_long_k(sk):
+    """The chooser's rule outside the table: the 16-block MFMA (4 rows, 4
+    chunks, one split) for 9..16 tokens when N / 4 >= 256 and 4096 <= K <=
+    8192; DOT2 or the 16x16 MFMA otherwise (fewer tokens, narrow N, short or
+    very long K, or an explicit split count)."""
+    P3 = sk.SKINNY_PATH_MFMA_4X4
+    for M, N, K in [(9, 1024, 4096), (12, 2048, 4096), (16, 1040, 6000), (16, 2048, 8192)]:
+        l = sk.skinny_choose(M, N, K, 0)
+        assert (l.path, l.splits, l.chunks, l.rows) == (P3, 1, 4, 4), (M, N, K, l)
+        assert l.waves == -(-K // 512)
+    for M, N, K, splits in [(8, 2048, 4096, 0), (12, 1008, 4096, 0), (12, 2048, 2048, 0),
+                            (12, 2048, 8200, 0), (12, 2048, 4096, 2)]:
+        assert sk.skinny_choose(M, N, K, splits).path != P3, (M, N, K, splits)
+
+
 def test_mfma_4x4_launch_reasons(sk):
     """The 16-block MFMA path: rows 4 or 8, accs 1, chunks 4 or 8 (whole
     512-K load groups), waves = ceil(K / (S * 128 chunks)) <= 16, and only the
