@@ -628,7 +628,7 @@ using namespace skinny;
 
 extern "C" {
 
-int skinny_version(void) { return 103; }
+int skinny_version(void) { return 104; }
 
 const char *skinny_last_error(void) { return g_error; }
 
