@@ -142,6 +142,24 @@ def test_chooser_walks_the_measured_shapes(sk):
         sk.skinny_choose_walk(17, 1024, 4096, 0)
 
 
+def test_off_table_staged_walks(sk):
+    """Off the table, 9..16 tokens with K <= 4096 on N >= 2048 run the MFMA
+    launch of 16 rows x 16 chunks as the staged walk: one segment a
+    workgroup, at most 256 workgroups; fewer tokens, narrow N, long K, an
+    explicit split count and the 16-block rule's shapes do not."""
+    for M, N, K, seg, wgs in [(16, 8192, 2048, 2, 256), (12, 4096, 1024, 1, 256),
+                              (9, 2048, 1000, 1, 128), (16, 16384, 1024, 4, 256),
+                              (16, 8192, 3072, 2, 256), (16, 8192, 4096, 2, 256),
+                              (12, 4096, 4096, 1, 256)]:
+        w = sk.skinny_choose_walk(M, N, K, 0)
+        l = sk.skinny_choose(M, N, K, 0)
+        assert (w.gemm.path, w.segment, w.workgroups) == (sk.SKINNY_PATH_MFMA_LDS, seg, wgs)
+        assert (l.path, l.splits, l.chunks, l.rows, l.waves) == (1, 1, 16, 16, -(-K // 512))
+    for M, N, K, splits in [(8, 8192, 2048, 0), (16, 1024, 2048, 0), (16, 8192, 8192, 0),
+                            (16, 8192, 2048, 2), (16, 2048, 4096, 0)]:
+        assert sk.skinny_choose_walk(M, N, K, splits).segment == 0, (M, N, K, splits)
+
+
 def test_rule_takes_the_16_block_path_for_many_tokens_on_long_k(sk):
     """The chooser's rule outside the table: the 16-block MFMA (4 rows, 4
     chunks, one split) for 9..16 tokens when N / 4 >= 256 and 4096 <= K <=
