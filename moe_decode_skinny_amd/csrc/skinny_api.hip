@@ -294,6 +294,21 @@ static skinny_ring_launch walk_launch(const skinny_launch &l, const Walk &w) {
 // The chooser: a pure function of (M, N, K, splits): the measured table for
 // the shard shapes, the rule above otherwise; *walk (if asked for) says how
 // the launch runs (table entries only, and only if the walk is valid).
+// A 16-block launch of the rule on 512 or more output blocks runs as a walk
+// of one segment per workgroup, the segment as long as keeps 256 or more
+// workgroups (the activations loaded once per segment instead of once per
+// block). Measured against the plain launch: 8-46% faster on
+// N = 2048..8192, K = 4096..8192.
+static void blocks_walk(int M, int N, int K, const skinny_launch &l, Walk *w) {
+  if (l.path != SKINNY_PATH_MFMA_4X4 || l.splits != 1) return;
+  const int groups = N / l.rows;
+  int seg = 1;
+  while (groups / (2 * seg) >= 256 && groups % (2 * seg) == 0) seg *= 2;
+  if (seg == 1) return;
+  const Walk walk{seg, groups / seg, false};
+  if (ring_check(1, M, N, K, walk_launch(l, walk)) == SKINNY_OK) *w = walk;
+}
+
 static int choose(int M, int N, int K, int splits, skinny_launch *out, Walk *walk = nullptr) {
   int st = check_problem(M, N, K);
   if (st) return st;
@@ -309,7 +324,10 @@ static int choose(int M, int N, int K, int splits, skinny_launch *out, Walk *wal
         w = e.walk;
       break;
     }
-  if (!l.waves && !staged_walk(M, N, K, splits, &l, &w)) l = rule(M, N, K, splits);
+  if (!l.waves && !staged_walk(M, N, K, splits, &l, &w)) {
+    l = rule(M, N, K, splits);
+    blocks_walk(M, N, K, l, &w);
+  }
   if (!l.waves)
     return fail(SKINNY_EUNSUPPORTED, "no launch for M=%d N=%d K=%d splits=%d (K too long "
                 "for the requested splits)", M, N, K, splits);

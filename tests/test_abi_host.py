@@ -157,7 +157,23 @@ def test_off_table_staged_walks(sk):
         assert (l.path, l.splits, l.chunks, l.rows, l.waves) == (1, 1, 16, 16, -(-K // 512))
     for M, N, K, splits in [(8, 8192, 2048, 0), (16, 1024, 2048, 0), (16, 8192, 8192, 0),
                             (16, 8192, 2048, 2), (16, 2048, 4096, 0)]:
-        assert sk.skinny_choose_walk(M, N, K, splits).segment == 0, (M, N, K, splits)
+        w = sk.skinny_choose_walk(M, N, K, splits)
+        assert w.segment == 0 or w.gemm.path != sk.SKINNY_PATH_MFMA_LDS, (M, N, K, splits)
+
+
+def test_off_table_16_block_walks(sk):
+    """The rule's 16-block launches on 512 or more output blocks run as walks
+    of one segment per workgroup, the segment as long as keeps 256 or more
+    workgroups; fewer blocks run the plain kernel."""
+    P3 = sk.SKINNY_PATH_MFMA_4X4
+    for M, N, K, seg, wgs in [(16, 2048, 8192, 2, 256), (12, 8192, 8192, 8, 256),
+                              (9, 2048, 4096, 2, 256), (16, 2064, 4096, 2, 258)]:
+        w = sk.skinny_choose_walk(M, N, K, 0)
+        assert (w.gemm.path, w.segment, w.workgroups) == (P3, seg, wgs), (M, N, K, w)
+        assert tuple(w.gemm) == tuple(sk.skinny_choose(M, N, K, 0))
+    for M, N, K in [(16, 1040, 6000), (16, 1024, 8192), (12, 2032, 4096)]:
+        w = sk.skinny_choose_walk(M, N, K, 0)
+        assert w.gemm.path == P3 and w.segment == 0, (M, N, K, w)
 
 
 def test_rule_takes_the_16_block_path_for_many_tokens_on_long_k(sk):
