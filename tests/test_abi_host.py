@@ -264,6 +264,24 @@ def test_ring_chooser_gives_valid_launches(sk, M, N, K, count):
     assert sk.skinny_ring_choose(M, N, K, count) == r
 
 
+def test_ring_rule_off_the_table(sk):
+    """The ring chooser off the table: 5..16 tokens take the staged MFMA ring
+    in 32-block segments over 240 workgroups (K <= 4096) or the 16-block ring
+    over 256; 1..4 tokens the DOT2 ring with 4 rows, 2 chunks, 4-block
+    segments over 1024 workgroups; all in XCD-local order; few items shorten
+    the segment first, then the workgroup count."""
+    X = sk.SKINNY_RING_XCD_LOCAL
+    cases = [((16, 2048, 4096, 60), (2, 16, 16, 32, 240)), ((8, 8192, 2048, 60), (2, 16, 16, 32, 240)),
+             ((16, 2048, 8192, 60), (3, 4, 4, 32, 256)), ((2, 4096, 2048, 60), (0, 2, 4, 4, 1024)),
+             ((4, 2048, 8192, 60), (0, 2, 4, 4, 1024)), ((16, 2048, 4096, 3), (2, 16, 16, 1, 240)),
+             ((1, 1024, 8192, 3), (0, 2, 4, 1, 768))]
+    for (M, N, K, count), (path, chunks, rows, seg, wgs) in cases:
+        r = sk.skinny_ring_choose(M, N, K, count)
+        got = (r.gemm.path, r.gemm.chunks, r.gemm.rows, r.segment, r.workgroups)
+        assert got == (path, chunks, rows, seg, wgs) and r.order == X, (M, N, K, count, r)
+        assert sk.skinny_ring_launch_unsupported(M, N, K, count, r) is None
+
+
 def test_ring_unsupported_shapes_and_reasons(sk):
     with pytest.raises(ValueError, match="count=0"):
         sk.skinny_ring_choose(1, 1024, 4096, 0)
