@@ -263,7 +263,8 @@ static int ring_check(int count, int M, int N, int K, const skinny_ring_launch &
 // from N = 4096 up; below that the 16-block rule is faster): the MFMA launch
 // of 16 rows and 16 chunks a wave, run as the staged walk (weights through
 // LDS, so every load is one row's contiguous bytes), one segment per
-// workgroup, at most 256 workgroups. Measured against the rule's direct MFMA
+// workgroup, the segment as long as keeps 256 or more workgroups (all the
+// blocks' workgroups below 512 blocks). Measured against the rule's direct MFMA
 // launch: 11-35% faster on N = 2048..16384, K = 1024..3072; against the
 // 16-block launch at K = 4096: 12% faster on N = 4096 and 8192, 22% slower
 // on N = 2048.
@@ -273,7 +274,7 @@ static bool staged_walk(int M, int N, int K, int splits, skinny_launch *out, Wal
   const skinny_launch l{SKINNY_PATH_MFMA, 1, ceil_div(K, (long)kMfmaK * 16), 16, 1, kTileN};
   const int groups = N / kTileN;
   int seg = 1;
-  while (groups / seg > 256 && groups % (2 * seg) == 0) seg *= 2;
+  while (groups / (2 * seg) >= 256 && groups % (2 * seg) == 0) seg *= 2;
   const Walk walk{seg, groups / seg, true};
   if (launch_check(M, N, K, l) != SKINNY_OK) return false;
   skinny_ring_launch r{l, walk.segment, walk.workgroups, SKINNY_RING_ITEM_MAJOR};
@@ -291,9 +292,6 @@ static skinny_ring_launch walk_launch(const skinny_launch &l, const Walk &w) {
   return r;
 }
 
-// The chooser: a pure function of (M, N, K, splits): the measured table for
-// the shard shapes, the rule above otherwise; *walk (if asked for) says how
-// the launch runs (table entries only, and only if the walk is valid).
 // A 16-block launch of the rule on 512 or more output blocks runs as a walk
 // of one segment per workgroup, the segment as long as keeps 256 or more
 // workgroups (the activations loaded once per segment instead of once per
@@ -309,6 +307,10 @@ static void blocks_walk(int M, int N, int K, const skinny_launch &l, Walk *w) {
   if (ring_check(1, M, N, K, walk_launch(l, walk)) == SKINNY_OK) *w = walk;
 }
 
+// The chooser: a pure function of (M, N, K, splits): the measured table for
+// the shard shapes, the staged walk or the rule above otherwise; *walk (if
+// asked for) says how the launch runs (a table entry's walk, the staged walk,
+// or the rule's 16-block walk, each only if valid; else the plain kernel).
 static int choose(int M, int N, int K, int splits, skinny_launch *out, Walk *walk = nullptr) {
   int st = check_problem(M, N, K);
   if (st) return st;
