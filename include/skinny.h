@@ -95,6 +95,10 @@ typedef struct skinny_launch {
  * SKINNY_EDEVICE or SKINNY_ELAUNCH (allocation failure). */
 int skinny_init(int device);
 
+/* Every call below runs on the calling thread's current HIP device (as set by
+ * hipSetDevice), which must have been prepared by skinny_init; every pointer
+ * it takes must be memory of that device, and the stream a stream of it. */
+
 /* y[M, N] = bf16( x[M, K] @ W[N, K]^T ), FP32 accumulation (unpooler page,
  * module description and Unpooler.run).
  *   x       bf16 [M, K], 16-byte aligned

@@ -148,6 +148,9 @@ def _stream(stream, device) -> Optional[int]:
 
     if stream is None:
         stream = torch.cuda.current_stream(device)
+    sdev = getattr(stream, "device", None)
+    if sdev is not None and torch.device(sdev) != torch.device(device):
+        raise ValueError(f"stream is on {sdev} but the arguments are on {device}")
     return getattr(stream, "cuda_stream", stream)
 
 
@@ -163,6 +166,29 @@ def _dev_tensor(t, name, dtype):
     if not t.is_contiguous():
         raise ValueError(f"{name} must be contiguous")
     return t.data_ptr()
+
+
+def _common_device(*named):
+    """The one device of the (name, tensor) pairs given (None entries skipped);
+    ValueError if they are on different devices.  The library runs on the
+    current HIP device, so every call is made with this device current."""
+    dev = None
+    for name, t in named:
+        if t is None:
+            continue
+        if dev is None:
+            dev, first = t.device, name
+        elif t.device != dev:
+            raise ValueError(f"{name} is on {t.device} but {first} is on {dev}: "
+                             "all arguments must be on one device")
+    return dev
+
+
+def _on(device):
+    """Context that makes `device` the current device for a library call."""
+    import torch
+
+    return torch.cuda.device(device)
 
 
 def skinny_init(device: int = 0) -> None:
@@ -203,13 +229,15 @@ def _gemm_args(x, w, y):
     N = w.shape[0]
     if w.shape[1] != K or tuple(y.shape) != (M, N):
         raise ValueError(f"shapes x{tuple(x.shape)} W{tuple(w.shape)} y{tuple(y.shape)}")
+    _common_device(("x", x), ("W", w), ("y", y))
     return xp, wp, yp, M, N, K
 
 
 def skinny_gemm_bf16(x, w, y, splits: int = 0, stream=None):
     """y[M, N] = x[M, K] @ W[N, K]^T into the caller's y; returns y."""
     xp, wp, yp, M, N, K = _gemm_args(x, w, y)
-    _check(_lib.skinny_gemm_bf16(xp, wp, yp, M, N, K, splits, _stream(stream, x.device)))
+    with _on(x.device):
+        _check(_lib.skinny_gemm_bf16(xp, wp, yp, M, N, K, splits, _stream(stream, x.device)))
     return y
 
 
@@ -217,8 +245,9 @@ def skinny_gemm_bf16_launch(x, w, y, launch: Launch, stream=None):
     """The GEMM at an explicit launch shape; returns y."""
     xp, wp, yp, M, N, K = _gemm_args(x, w, y)
     c = Launch(*launch)._c()
-    _check(_lib.skinny_gemm_bf16_launch(xp, wp, yp, M, N, K, ctypes.byref(c),
-                                        _stream(stream, x.device)))
+    with _on(x.device):
+        _check(_lib.skinny_gemm_bf16_launch(xp, wp, yp, M, N, K, ctypes.byref(c),
+                                            _stream(stream, x.device)))
     return y
 
 
@@ -241,10 +270,13 @@ def skinny_gemm_bf16_publish(x, w, y, mailbox, rank: int, stage_state=None, tick
         raise ValueError("stage_state must be int32 [2]")
     if ticket is not None and ticket.numel() != 1:
         raise ValueError("ticket must be int32 [1]")
+    _common_device(("x", x), ("mailbox", mailbox), ("stage_state", stage_state),
+                   ("ticket", ticket))
     mb = _CMailbox(dp, sp, tk, tp, int(rank), capacity, width)
     lp = None if launch is None else ctypes.byref(Launch(*launch)._c())
-    _check(_lib.skinny_gemm_bf16_publish(xp, wp, yp, M, N, K, lp, ctypes.byref(mb),
-                                         _stream(stream, x.device)))
+    with _on(x.device):
+        _check(_lib.skinny_gemm_bf16_publish(xp, wp, yp, M, N, K, lp, ctypes.byref(mb),
+                                             _stream(stream, x.device)))
     return y
 
 
@@ -274,6 +306,7 @@ def _ring_args(xs, ws, ys):
     if not (len(xs) == len(ws) == len(ys)) or not xs:
         raise ValueError("xs, ws and ys must be non-empty lists of one length")
     shapes = [_gemm_args(x, w, y) for x, w, y in zip(xs, ws, ys)]
+    _common_device(*[(f"xs[{i}]", x) for i, x in enumerate(xs)])
     M, N, K = shapes[0][3:]
     if any(sh[3:] != (M, N, K) for sh in shapes):
         raise ValueError("every ring item must have the same (M, N, K)")
@@ -288,8 +321,9 @@ def skinny_gemm_bf16_ring(xs, ws, ys, stream=None):
     """ys[i] = xs[i] @ ws[i]^T for independent items of one shape, in one
     launch; returns ys."""
     xa, wa, ya, count, M, N, K = _ring_args(xs, ws, ys)
-    _check(_lib.skinny_gemm_bf16_ring(xa, wa, ya, count, M, N, K,
-                                      _stream(stream, xs[0].device)))
+    with _on(xs[0].device):
+        _check(_lib.skinny_gemm_bf16_ring(xa, wa, ya, count, M, N, K,
+                                          _stream(stream, xs[0].device)))
     return ys
 
 
@@ -297,8 +331,9 @@ def skinny_gemm_bf16_ring_launch(xs, ws, ys, launch: RingLaunch, stream=None):
     """The ring at an explicit RingLaunch; returns ys."""
     xa, wa, ya, count, M, N, K = _ring_args(xs, ws, ys)
     c = RingLaunch(*launch)._c()
-    _check(_lib.skinny_gemm_bf16_ring_launch(xa, wa, ya, count, M, N, K, ctypes.byref(c),
-                                             _stream(stream, xs[0].device)))
+    with _on(xs[0].device):
+        _check(_lib.skinny_gemm_bf16_ring_launch(xa, wa, ya, count, M, N, K, ctypes.byref(c),
+                                                 _stream(stream, xs[0].device)))
     return ys
 
 
@@ -318,8 +353,11 @@ def skinny_rmsnorm_nvfp4(r, norm_w, gain_center: float, eps: float, global_scale
     if (tuple(norm_w.shape) != (P,) or global_scale.numel() != 1
             or tuple(a.shape) != (M, P // 2) or tuple(a_sf.shape) != (M, P // 16)):
         raise ValueError("norm_w [P], global_scale [1], a [M, P/2], a_sf [M, P/16]")
-    _check(_lib.skinny_rmsnorm_nvfp4(rp, wp, float(gain_center), float(eps), gp, ap, sp,
-                                     M, P, _stream(stream, r.device)))
+    _common_device(("r", r), ("norm_w", norm_w), ("global_scale", global_scale), ("a", a),
+                   ("a_sf", a_sf))
+    with _on(r.device):
+        _check(_lib.skinny_rmsnorm_nvfp4(rp, wp, float(gain_center), float(eps), gp, ap, sp,
+                                         M, P, _stream(stream, r.device)))
     return a, a_sf
 
 
@@ -335,8 +373,10 @@ def skinny_rmsnorm_bf16(r, norm_w, gain_center: float, eps: float, y, stream=Non
     M, P = r.shape
     if tuple(norm_w.shape) != (P,):
         raise ValueError("norm_w must be [P]")
-    _check(_lib.skinny_rmsnorm_bf16(rp, wp, float(gain_center), float(eps), yp, M, P,
-                                    _stream(stream, r.device)))
+    _common_device(("r", r), ("norm_w", norm_w), ("y", y))
+    with _on(r.device):
+        _check(_lib.skinny_rmsnorm_bf16(rp, wp, float(gain_center), float(eps), yp, M, P,
+                                        _stream(stream, r.device)))
     return y
 
 
@@ -370,10 +410,14 @@ def skinny_dual_norm(partial, residual, post_w, post_gain_center: float, post_ep
             raise ValueError("alpha must be a float or [H]")
     else:
         ap, a_s = None, float(alpha)
-    _check(_lib.skinny_dual_norm(pp, rp, vecs["post_w"], float(post_gain_center),
-                                 float(post_eps), ap, a_s, vecs["beta"], vecs["next_w"],
-                                 float(pre_gain_center), float(pre_eps), op, M, H,
-                                 _stream(stream, partial.device)))
+    _common_device(("partial", partial), ("residual", residual), ("out", out),
+                   ("post_w", post_w), ("beta", beta), ("next_w", next_w),
+                   ("alpha", alpha if isinstance(alpha, torch.Tensor) else None))
+    with _on(partial.device):
+        _check(_lib.skinny_dual_norm(pp, rp, vecs["post_w"], float(post_gain_center),
+                                     float(post_eps), ap, a_s, vecs["beta"], vecs["next_w"],
+                                     float(pre_gain_center), float(pre_eps), op, M, H,
+                                     _stream(stream, partial.device)))
     return out
 
 

@@ -457,3 +457,21 @@ def test_dual_norm_reasons_without_device(sk):
     bad("overlaps the residual or out", nw=r + 32)
     assert call() in (sk.SKINNY_EDEVICE, sk.SKINNY_ENOTINIT)
     assert call(pw=None, al=None) in (sk.SKINNY_EDEVICE, sk.SKINNY_ENOTINIT)
+
+
+def test_binding_keeps_every_argument_on_one_device(sk):
+    """The library computes on the current HIP device; the binding refuses
+    arguments spread over several devices, and a stream of another device."""
+    import torch
+
+    class OnDevice:
+        def __init__(self, d):
+            self.device = torch.device(d)
+
+    same = sk._common_device(("x", OnDevice("cuda:0")), ("W", OnDevice("cuda:0")),
+                             ("ticket", None))
+    assert same == torch.device("cuda:0")
+    with pytest.raises(ValueError, match="one device"):
+        sk._common_device(("x", OnDevice("cuda:0")), ("W", OnDevice("cuda:1")))
+    with pytest.raises(ValueError, match="stream is on"):
+        sk._stream(OnDevice("cuda:1"), torch.device("cuda:0"))
