@@ -4,12 +4,16 @@
 // argument structs, device helpers) is in device.h.  Not installed.
 #pragma once
 
+#include <atomic>
+
 #include "device.h"
 
 namespace skinny {
 
 struct DeviceState {
-  bool ready = false;
+  // Set (release) by skinny_init once the buffers below exist; compute calls
+  // on other threads read it (acquire) without taking the init lock.
+  std::atomic<bool> ready{false};
   float *partials = nullptr;         // kWorkspaceFloats
   double *norm_partials = nullptr;   // kNormPartials
 };

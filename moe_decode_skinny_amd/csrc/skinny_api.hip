@@ -65,7 +65,7 @@ DeviceState *current_state(int *status) {
     *status = fail(SKINNY_EDEVICE, "no current HIP device");
     return nullptr;
   }
-  if (!g_state[dev].ready) {
+  if (!g_state[dev].ready.load(std::memory_order_acquire)) {
     *status = fail(SKINNY_ENOTINIT, "skinny_init(%d) has not been called", dev);
     return nullptr;
   }
@@ -682,7 +682,7 @@ int skinny_init(int device) {
   if (device < 0 || device >= count || device >= kMaxDevices)
     return fail(SKINNY_EDEVICE, "device %d out of range (0..%d)", device, count - 1);
   DeviceState &st = g_state[device];
-  if (st.ready) return SKINNY_OK;
+  if (st.ready.load(std::memory_order_acquire)) return SKINNY_OK;
   hipDeviceProp_t prop;
   if (hipGetDeviceProperties(&prop, device) != hipSuccess)
     return fail(SKINNY_EDEVICE, "cannot query device %d", device);
@@ -702,7 +702,7 @@ int skinny_init(int device) {
     if (st.partials && hipFree(st.partials) == hipSuccess) st.partials = nullptr;
     if (st.norm_partials && hipFree(st.norm_partials) == hipSuccess) st.norm_partials = nullptr;
   } else {
-    st.ready = true;
+    st.ready.store(true, std::memory_order_release);
   }
   if (hipSetDevice(prev) != hipSuccess && status == SKINNY_OK)
     status = fail(SKINNY_EDEVICE, "cannot restore device %d", prev);
