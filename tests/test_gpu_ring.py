@@ -272,6 +272,14 @@ def test_ring_sixty_layer_weight_ring(gpu_lib, M, N, K):
         g = oracle.bf16_value(y[rows, cols])
         scale = np.sqrt(np.mean(exact ** 2))  # rms of y estimated from the samples
         assert np.all(np.abs(g - r) <= 2.0 ** -7 * np.abs(r) + 2.0 ** -10 * scale), f"layer {layer}"
+    # the same launch again: every item bitwise as before
+    first = [from_dev(y) for y in ys]
+    for y in ys:
+        y.fill_(0)
+    gpu_lib.skinny_gemm_bf16_ring(xs, ring, ys)
+    torch.cuda.synchronize()
+    for layer in range(60):
+        assert np.array_equal(from_dev(ys[layer]), first[layer]), f"layer {layer} not reproducible"
 
 
 def test_ring_graph_capture_replay(gpu_lib):
