@@ -23,7 +23,11 @@ next layer's weights in flight while one is finished), per item.
 `oproj` reports the o_proj shard (N=8192, K=1024) the same two ways, and
 `pooler` the pooler shard (N=512) and the full pooler (N=4096) at K=8192.
 `epilogue` times the expert-input chain (full-pooler GEMM, RMSNorm -> NVFP4)
-and the dual norm.  `cpu_baseline` times the oracle on the host for a bounded sample of the same
+and the dual norm.  `ceiling` times, the same way, what one launch reaches by
+itself on this device: an empty kernel, and the library's stream reference
+reading each 8 MiB weight once (skinny_ceiling_stream); its
+`dominant_call_fraction` is that stream's time over the dominant call's.
+`cpu_baseline` times the oracle on the host for a bounded sample of the same
 workload.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu]
@@ -256,6 +260,44 @@ def ring_timing(sk, synthetic, dev, stream, ring, reps: int = 10):
                         f"{RING}-layer weight ring", "per_m": out}
 
 
+def ceiling_timing(sk, dev, stream, ring, reps: int = 10):
+    """What one launch on this device reaches by itself, measured as the calls
+    are (graphs of 60 launches over the same 60-layer weight ring): an empty
+    kernel, and the library's stream reference reading each 8 MiB weight
+    matrix once (best of 1, 2, 4, 8 loads per lane)."""
+    import torch
+
+    def timed(fn):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=stream):
+            fn()
+        g.replay()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            g.replay()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e3 / (reps * RING)
+
+    empty = timed(lambda: [sk.skinny_ceiling_empty(dev) for _ in range(RING)])
+    nbytes = ring[0].numel() * ring[0].element_size()
+    by_l = {}
+    for L in (1, 2, 4, 8):
+        sinks = [torch.zeros(nbytes // (8192 * L), dtype=torch.int32, device=dev) for _ in ring]
+        by_l[L] = timed(lambda: [sk.skinny_ceiling_stream(w, s, L) for w, s in zip(ring, sinks)])
+    L = min(by_l, key=by_l.get)
+    us = by_l[L]
+    return {"workload": f"one launch per weight of the {RING}-layer unpooler ring "
+                        f"({nbytes} bytes each)",
+            "empty_launch_us": round(empty, 3), "stream_us": round(us, 3),
+            "stream_GBs": round(nbytes / (us * 1e-6) / 1e9, 1),
+            "stream_pct_peak": round(100 * nbytes / (us * 1e-6) / 1e9 / PEAK_GBS, 2),
+            "stream_loads_per_lane": L, "stream_workgroups": nbytes // (8192 * L),
+            "stream_us_by_loads_per_lane": {str(k): round(v, 3) for k, v in by_l.items()}}
+
+
 def oproj_timing(sk, synthetic, dev, stream, reps: int = 10):
     """The o_proj shard (N=8192, K=1024, 16 MiB of weights) on its own
     60-layer ring: us per single call (graph of 60 calls) and per ring item
@@ -420,6 +462,8 @@ def main():
         oproj_out = oproj_timing(sk, synthetic, dev, stream)
         # The pooler shapes (K = 8192).
         pooler_out = pooler_timing(sk, synthetic, dev, stream)
+        # What a single launch reaches by itself on this device.
+        ceiling = ceiling_timing(sk, dev, stream, ring)
 
     step_bytes = sum(algorithmic_bytes(M) for M in MS)
     value = step_bytes / (ms_step * 1e-3) / 1e9
@@ -455,6 +499,8 @@ def main():
                      "bytes_per_launch": algorithmic_bytes(dom),
                      "us_per_launch": round(per_kernel[dom], 3)},
         "per_m": detail,
+        "ceiling": {**ceiling,
+                    "dominant_call_fraction": round(ceiling["stream_us"] / per_kernel[dom], 4)},
         "epilogue": epi,
         "ring": ring_out,
         "oproj": oproj_out,

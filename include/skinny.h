@@ -315,6 +315,28 @@ int skinny_dual_norm(const void *partial, float *residual, const void *post_w,
                      void *stream);
 
 /* The reason for the last non-OK status on this thread ("" if none). */
+/* Measurement references (not steps of the method).  The weight stream is
+ * the decode GEMM's dominant cost (unpooler page, module description); these
+ * two calls measure, on the caller's device and stream, what one launch costs
+ * by itself and how fast one launch can stream a buffer the way the GEMM
+ * kernels stream weights, so that a GEMM call's time can be set against the
+ * ceiling a single launch reaches.
+ *
+ * skinny_ceiling_empty: launches one empty 64-thread workgroup.
+ * skinny_ceiling_stream: reads the `bytes` bytes at src (16-byte aligned,
+ *   a positive multiple of 8192 * loads_per_lane, below 2^31) once, with
+ *   bytes / (8192 * loads_per_lane) workgroups of 512 threads; thread t of
+ *   workgroup b issues loads_per_lane (1, 2, 4 or 8) 16-byte loads, load i at
+ *   byte b * 8192 * loads_per_lane + 8192 * i + 16 t, all before the first
+ *   use.  sink: device u32 [bytes / (8192 * loads_per_lane)], owned by the
+ *   caller; word b is set to 1 only if some thread's XOR of the 32-bit words
+ *   it read equals 0x5EC0DE42, and is otherwise left as it was.
+ * Both need skinny_init on the current device.  Errors: SKINNY_EINVAL,
+ * SKINNY_ENOTINIT, SKINNY_EDEVICE, SKINNY_ELAUNCH. */
+int skinny_ceiling_empty(void *stream);
+int skinny_ceiling_stream(const void *src, long long bytes, void *sink, int loads_per_lane,
+                          void *stream);
+
 const char *skinny_last_error(void);
 
 /* Library ABI version: major * 100 + minor. */

@@ -475,3 +475,20 @@ def test_binding_keeps_every_argument_on_one_device(sk):
         sk._common_device(("x", OnDevice("cuda:0")), ("W", OnDevice("cuda:1")))
     with pytest.raises(ValueError, match="stream is on"):
         sk._stream(OnDevice("cuda:1"), torch.device("cuda:0"))
+
+
+def test_ceiling_stream_argument_checks(sk):
+    """The stream reference rejects bad sizes, load counts and pointers before
+    touching a device."""
+    lib = ctypes.CDLL(sk.LIB_PATH)
+    fn = lib.skinny_ceiling_stream
+    fn.argtypes = [ctypes.c_void_p, ctypes.c_longlong, ctypes.c_void_p, ctypes.c_int,
+                   ctypes.c_void_p]
+    fn.restype = ctypes.c_int
+    p = ctypes.c_void_p(4096)
+    cases = [(None, 8192, 1, "null pointer"), (ctypes.c_void_p(4100), 8192, 1, "aligned"),
+             (p, 8192, 3, "loads_per_lane"), (p, 8192, 2, "multiple of 16384"),
+             (p, 0, 1, "positive"), (p, 1 << 31, 1, "below 2^31")]
+    for src, nbytes, lpl, needle in cases:
+        assert fn(src, nbytes, p, lpl, None) == sk.SKINNY_EINVAL, needle
+        assert needle in sk.skinny_last_error(), (needle, sk.skinny_last_error())

@@ -1,0 +1,34 @@
+"""The measurement reference kernels (include/skinny.h, skinny_ceiling_*):
+the stream reference reads exactly the bytes its layout says, once."""
+import numpy as np
+import pytest
+
+pytestmark = pytest.mark.gpu
+
+PATTERN = 0x5EC0DE42
+
+
+@pytest.mark.parametrize("L", [1, 2, 4, 8])
+def test_stream_reference_reads_its_layout(gpu_lib, L):
+    """Two threads get data whose XOR is the sink pattern; the sink words of
+    exactly the workgroups that hold such a thread (by the documented layout:
+    load i of thread t of workgroup b at b*8192L + 8192i + 16t) are set."""
+    import torch
+
+    print(f"ceiling stream L={L}", flush=True)
+    nwg = 6
+    rng = np.random.default_rng(70 + L)
+    data = rng.integers(0, 2 ** 32, 2048 * L * nwg, dtype=np.uint64).astype(np.uint32)
+    view = data.reshape(nwg, L, 512, 4)  # [b][i][t][j]: word b*2048L + 2048i + 4t + j
+    for b, t in ((2, 37), (5, 500)):
+        x = np.bitwise_xor.reduce(view[b, :, t, :].ravel())
+        view[b, 0, t, 0] ^= x ^ np.uint32(PATTERN)
+    hit = (np.bitwise_xor.reduce(np.bitwise_xor.reduce(view, axis=3), axis=1) == PATTERN)
+    expected = np.where(hit.any(axis=1), 1, 7).astype(np.int32)
+    assert list(expected) == [7, 7, 1, 7, 7, 1]
+    src = torch.from_numpy(data.view(np.int32)).to("cuda")
+    sink = torch.full((nwg,), 7, dtype=torch.int32, device="cuda")
+    gpu_lib.skinny_ceiling_stream(src, sink, L)
+    gpu_lib.skinny_ceiling_empty(0)
+    torch.cuda.synchronize()
+    assert np.array_equal(sink.cpu().numpy(), expected)
