@@ -260,62 +260,77 @@ def ring_timing(sk, synthetic, dev, stream, ring, reps: int = 10):
                         f"{RING}-layer weight ring", "per_m": out}
 
 
-def ceiling_timing(sk, dev, stream, ring, reps: int = 10):
-    """What one launch on this device reaches by itself, measured as the calls
-    are (graphs of 60 launches over the same 60-layer weight ring): an empty
-    kernel, and the library's stream reference reading each 8 MiB weight
-    matrix once (best of 1, 2, 4, 8 loads per lane)."""
+def _graph_us(fn, stream, reps: int = 10) -> float:
+    """us per launch of fn() (RING launches) from replays of its graph."""
     import torch
 
-    def timed(fn):
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g, stream=stream):
-            fn()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=stream):
+        fn()
+    g.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(reps):
         g.replay()
-        torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record(stream)
-        for _ in range(reps):
-            g.replay()
-        e1.record(stream)
-        torch.cuda.synchronize()
-        return e0.elapsed_time(e1) * 1e3 / (reps * RING)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) * 1e3 / (reps * RING)
 
-    empty = timed(lambda: [sk.skinny_ceiling_empty(dev) for _ in range(RING)])
+
+def stream_ceiling(sk, dev, stream, ring) -> dict:
+    """The library's stream reference (skinny_ceiling_stream) reading each
+    weight of a ring once per launch, graphs of RING launches as the calls
+    are timed; best of 1, 2, 4, 8 loads per lane."""
+    import torch
+
     nbytes = ring[0].numel() * ring[0].element_size()
     by_l = {}
     for L in (1, 2, 4, 8):
         sinks = [torch.zeros(nbytes // (8192 * L), dtype=torch.int32, device=dev) for _ in ring]
-        by_l[L] = timed(lambda: [sk.skinny_ceiling_stream(w, s, L) for w, s in zip(ring, sinks)])
+        by_l[L] = _graph_us(lambda: [sk.skinny_ceiling_stream(w, s, L)
+                                     for w, s in zip(ring, sinks)], stream)
+        del sinks
     L = min(by_l, key=by_l.get)
     us = by_l[L]
-    return {"workload": f"one launch per weight of the {RING}-layer unpooler ring "
-                        f"({nbytes} bytes each)",
-            "empty_launch_us": round(empty, 3), "stream_us": round(us, 3),
+    return {"bytes": nbytes, "stream_us": round(us, 3),
             "stream_GBs": round(nbytes / (us * 1e-6) / 1e9, 1),
             "stream_pct_peak": round(100 * nbytes / (us * 1e-6) / 1e9 / PEAK_GBS, 2),
             "stream_loads_per_lane": L, "stream_workgroups": nbytes // (8192 * L),
             "stream_us_by_loads_per_lane": {str(k): round(v, 3) for k, v in by_l.items()}}
 
 
+def ceiling_timing(sk, dev, stream, ring):
+    """What one launch on this device reaches by itself, measured as the calls
+    are (graphs of 60 launches over the same 60-layer weight ring): an empty
+    kernel, and the stream reference reading each 8 MiB weight once."""
+    empty = _graph_us(lambda: [sk.skinny_ceiling_empty(dev) for _ in range(RING)], stream)
+    return {"workload": f"one launch per weight of the {RING}-layer unpooler ring",
+            "empty_launch_us": round(empty, 3), **stream_ceiling(sk, dev, stream, ring)}
+
+
 def oproj_timing(sk, synthetic, dev, stream, reps: int = 10):
     """The o_proj shard (N=8192, K=1024, 16 MiB of weights) on its own
     60-layer ring: us per single call (graph of 60 calls) and per ring item
     (one 60-item launch), M = 1..16."""
-    out = shard_timing(sk, synthetic, dev, stream, 8192, 1024, MS, 7000, 950, reps)
+    out, ceiling = shard_timing(sk, synthetic, dev, stream, 8192, 1024, MS, 7000, 950, reps)
     return {"workload": f"o_proj shard GEMM M=1,2,4,8,16, N=8192, K=1024, {RING}-layer weight "
-                        "ring: single calls and one ring launch per M", "per_m": out}
+                        "ring: single calls and one ring launch per M", "per_m": out,
+            "stream_ceiling": ceiling}
 
 
 def pooler_timing(sk, synthetic, dev, stream, reps: int = 5):
     """The pooler shard (N=512, K=8192) and the single-GPU full pooler
     (N=4096, K=8192, 64 MiB of weights), each on its own 60-layer ring, at
     M = 1, 8, 16: us per single call and per ring item."""
-    shard = shard_timing(sk, synthetic, dev, stream, 512, 8192, (1, 8, 16), 7100, 960, reps)
-    full = shard_timing(sk, synthetic, dev, stream, 4096, 8192, (1, 8, 16), 7200, 970, reps)
+    shard, shard_ceiling = shard_timing(sk, synthetic, dev, stream, 512, 8192, (1, 8, 16), 7100,
+                                        960, reps)
+    full, full_ceiling = shard_timing(sk, synthetic, dev, stream, 4096, 8192, (1, 8, 16), 7200,
+                                      970, reps)
     return {"workload": f"pooler shard N=512, K=8192 and full pooler N=4096, K=8192 at "
                         f"M=1,8,16, {RING}-layer weight rings: single calls and one ring "
-                        "launch per M", "shard": shard, "full": full}
+                        "launch per M", "shard": shard, "full": full,
+            "stream_ceiling": {"shard": shard_ceiling, "full": full_ceiling}}
 
 
 def shard_timing(sk, synthetic, dev, stream, N2, K2, ms, wseed, xseed, reps):
@@ -338,6 +353,7 @@ def shard_timing(sk, synthetic, dev, stream, N2, K2, ms, wseed, xseed, reps):
         return e0.elapsed_time(e1) * 1e3 / (reps * per)
 
     out = {}
+    ceiling = stream_ceiling(sk, dev, stream, ring)
     for M in ms:
         xs = [synthetic.to_device(synthetic.gemm_inputs(N=16, K=K2, seed=xseed + i)[0][:M], dev)
               for i in range(RING)]
@@ -347,13 +363,14 @@ def shard_timing(sk, synthetic, dev, stream, N2, K2, ms, wseed, xseed, reps):
         item = timed(lambda: sk.skinny_gemm_bf16_ring(xs, ring, ys), RING)
         b = algorithmic_bytes(M, N2, K2)
         out[str(M)] = {"walk": walk_record(sk, M, N2, K2), "us_per_call": round(single, 3),
+                       "fraction_of_stream_ceiling": round(ceiling["stream_us"] / single, 4),
                        "pct_peak_call": round(100 * b / (single * 1e-6) / 1e9 / PEAK_GBS, 2),
                        "ring_us_per_item": round(item, 3),
                        "pct_peak_ring": round(100 * b / (item * 1e-6) / 1e9 / PEAK_GBS, 2)}
         del xs, ys
     del ring
     torch.cuda.empty_cache()
-    return out
+    return out, ceiling
 
 
 def main():
@@ -472,6 +489,7 @@ def main():
     detail = {str(M): {"launch": dict(launches[M]._asdict()),
                        "walk": walk_record(sk, M, N, K),
                        "us_per_call": round(per_kernel[M], 3),
+                       "fraction_of_stream_ceiling": round(ceiling["stream_us"] / per_kernel[M], 4),
                        "GBs": round(algorithmic_bytes(M) / (per_kernel[M] * 1e-6) / 1e9, 1),
                        "pct_peak": round(100 * algorithmic_bytes(M) / (per_kernel[M] * 1e-6)
                                          / 1e9 / PEAK_GBS, 2)}
