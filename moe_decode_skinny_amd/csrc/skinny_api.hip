@@ -184,7 +184,8 @@ static const TableEntry kTable[] = {
     {1024, 4096, 9, 16, {SKINNY_PATH_MFMA_4X4, 1, 8, 4, 1, 4}, {}},
     // o_proj shard
     {8192, 1024, 1, 1, {SKINNY_PATH_DOT2, 1, 1, 2, 1, 2}, {}},
-    {8192, 1024, 2, 4, {SKINNY_PATH_DOT2, 1, 1, 2, 1, 4}, {2, 1024}},
+    {8192, 1024, 2, 2, {SKINNY_PATH_DOT2, 1, 1, 2, 1, 4}, {2, 1024}},
+    {8192, 1024, 3, 4, {SKINNY_PATH_DOT2, 1, 2, 1, 1, 4}, {}},
     {8192, 1024, 5, 16, {SKINNY_PATH_MFMA, 1, 2, 16, 2, 16}, {2, 256, true}},
     // pooler shard
     {512, 8192, 1, 4, {SKINNY_PATH_DOT2, 1, 4, 4, 1, 2}, {}},
