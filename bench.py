@@ -85,9 +85,10 @@ def ring_source_digest() -> str:
     return h.hexdigest()[:16]
 
 
-def ring_traffic(M: int):
+def ring_traffic(M: int, sk=None):
     """HBM bytes per ring item from the committed counter summary, or None if
-    the ring kernels changed since the counters were taken."""
+    the ring kernels, or the launch the ring chooser picks, changed since the
+    counters were taken."""
     path = os.path.join(HERE, "profiles", "hbm_traffic_ring_unpooler.json")
     try:
         with open(path) as f:
@@ -97,7 +98,15 @@ def ring_traffic(M: int):
     if rec.get("kernel_source_digest") != ring_source_digest():
         return None
     e = rec["per_m"].get(str(M))
-    return None if e is None else e["hbm_bytes_per_item"]
+    if e is None:
+        return None
+    if sk is not None:
+        r = sk.skinny_ring_choose(M, N, K, RING)
+        now = {**dict(r.gemm._asdict()), "segment": r.segment, "workgroups": r.workgroups,
+               "order": r.order}
+        if e.get("launch") != now:
+            return None
+    return e["hbm_bytes_per_item"]
 
 
 def measured_traffic(M: int, sk=None):
@@ -250,10 +259,10 @@ def ring_timing(sk, synthetic, dev, stream, ring, reps: int = 10):
         gbs = algorithmic_bytes(M) / (us * 1e-6) / 1e9
         r = sk.skinny_ring_choose(M, N, K, RING)
         out[str(M)] = {"launch": {**dict(r.gemm._asdict()), "segment": r.segment,
-                                  "workgroups": r.workgroups},
+                                  "workgroups": r.workgroups, "order": r.order},
                        "us_per_item": round(us, 3), "GBs": round(gbs, 1),
                        "pct_peak": round(100 * gbs / PEAK_GBS, 2),
-                       "hbm_bytes_per_item": ring_traffic(M)}
+                       "hbm_bytes_per_item": ring_traffic(M, sk)}
         del g
     return {"workload": f"unpooler shard GEMM M=1,2,4,8,16, N=1024, K=4096: one "
                         f"{RING}-item skinny_gemm_bf16_ring launch per M over the "

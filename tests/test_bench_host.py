@@ -39,8 +39,15 @@ def test_traffic_lookup_follows_the_digest(tmp_path, monkeypatch):
     None once the recorded digest no longer matches the sources."""
     rec = {"kernel_source_digest": bench.kernel_source_digest(),
            "per_m": {"16": {"hbm_bytes_per_launch": 123, "walk": None}}}
+    import moe_decode_skinny_amd as sk
+
+    r = sk.skinny_ring_choose(16, bench.N, bench.K, bench.RING)
+    now = {**dict(r.gemm._asdict()), "segment": r.segment, "workgroups": r.workgroups,
+           "order": r.order}
+    other = {**now, "segment": now["segment"] + 1}
     ring = {"kernel_source_digest": bench.ring_source_digest(),
-            "per_m": {"16": {"hbm_bytes_per_item": 456}}}
+            "per_m": {"16": {"hbm_bytes_per_item": 456, "launch": now},
+                      "8": {"hbm_bytes_per_item": 789, "launch": other}}}
     (tmp_path / "profiles").mkdir()
     (tmp_path / "profiles" / "hbm_traffic_unpooler_sweep.json").write_text(json.dumps(rec))
     (tmp_path / "profiles" / "hbm_traffic_ring_unpooler.json").write_text(json.dumps(ring))
@@ -52,6 +59,9 @@ def test_traffic_lookup_follows_the_digest(tmp_path, monkeypatch):
     assert bench.measured_traffic(16) == 123
     assert bench.measured_traffic(8) is None
     assert bench.ring_traffic(16) == 456
+    assert bench.ring_traffic(16, sk) == 456
+    # counters taken at another ring launch than the chooser's are not used
+    assert bench.ring_traffic(8, sk) is None
     # a changed kernel source voids both
     src = tmp_path / "moe_decode_skinny_amd" / "csrc" / "device.h"
     src.write_bytes(src.read_bytes() + b"\n")
