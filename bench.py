@@ -288,16 +288,18 @@ def _graph_us(fn, stream, reps: int = 10) -> float:
 
 
 def stream_ceiling(sk, dev, stream, ring) -> dict:
-    """The library's stream reference (skinny_ceiling_stream) reading each
+    """The stream reference (skinny_ceiling_stream of libskinny_ceiling) reading each
     weight of a ring once per launch, graphs of RING launches as the calls
     are timed; best of 1, 2, 4, 8 loads per lane."""
     import torch
+
+    from moe_decode_skinny_amd import ceiling as cl
 
     nbytes = ring[0].numel() * ring[0].element_size()
     by_l = {}
     for L in (1, 2, 4, 8):
         sinks = [torch.zeros(nbytes // (8192 * L), dtype=torch.int32, device=dev) for _ in ring]
-        by_l[L] = _graph_us(lambda: [sk.skinny_ceiling_stream(w, s, L)
+        by_l[L] = _graph_us(lambda: [cl.skinny_ceiling_stream(w, s, L)
                                      for w, s in zip(ring, sinks)], stream)
         del sinks
     L = min(by_l, key=by_l.get)
@@ -313,7 +315,9 @@ def ceiling_timing(sk, dev, stream, ring):
     """What one launch on this device reaches by itself, measured as the calls
     are (graphs of 60 launches over the same 60-layer weight ring): an empty
     kernel, and the stream reference reading each 8 MiB weight once."""
-    empty = _graph_us(lambda: [sk.skinny_ceiling_empty(dev) for _ in range(RING)], stream)
+    from moe_decode_skinny_amd import ceiling as cl
+
+    empty = _graph_us(lambda: [cl.skinny_ceiling_empty(dev) for _ in range(RING)], stream)
     return {"workload": f"one launch per weight of the {RING}-layer unpooler ring",
             "empty_launch_us": round(empty, 3), **stream_ceiling(sk, dev, stream, ring)}
 

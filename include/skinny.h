@@ -87,10 +87,13 @@ typedef struct skinny_launch {
                  MFMA_4X4 4, 8                                                */
 } skinny_launch;
 
-/* Prepare `device` (a HIP ordinal) for the compute calls: checks that it is a
- * gfx950 GPU, allocates the library's split-K workspace on it (8 MiB of FP32
- * partials, enough for S * M * N <= 2^21) and the dual norm's buffer (512 KiB
- * of per-slice sums) and sets the kernels' LDS limits.
+/* Prepare `device` (a HIP ordinal) for the compute calls (unpooler page,
+ * Unpooler: everything is prepared at build, before graph capture, so that
+ * run is graph-capturable and allocates nothing; pooler_gather page, Pooler:
+ * the same for the pooler): checks that it is a gfx950 GPU, allocates the
+ * library's split-K workspace on it (8 MiB of FP32 partials, enough for
+ * S * M * N <= 2^21) and the dual norm's buffer (512 KiB of per-slice sums)
+ * and sets the kernels' LDS limits.
  * Call it before any graph capture.  Idempotent.  Returns SKINNY_OK,
  * SKINNY_EDEVICE or SKINNY_ELAUNCH (allocation failure). */
 int skinny_init(int device);
@@ -123,23 +126,33 @@ int skinny_init(int device);
 int skinny_gemm_bf16(const void *x, const void *W, void *y, int M, int N,
                      int K, int splits, void *stream);
 
-/* The same GEMM at an explicit launch shape (for sweeps and tests). */
+/* The same GEMM at an explicit launch shape (unpooler page, compile_unpooler:
+ * one kernel per shape and launch parameters -- splits, K per wave,
+ * accumulators -- shared by every layer of that shape).  For sweeps and
+ * tests; arguments and errors as skinny_gemm_bf16. */
 int skinny_gemm_bf16_launch(const void *x, const void *W, void *y, int M,
                             int N, int K, const skinny_launch *launch,
                             void *stream);
 
-/* The chooser: the launch shape skinny_gemm_bf16 uses for (M, N, K, splits).
- * Pure host function of its arguments.  Returns SKINNY_OK and fills *out, or
- * SKINNY_EINVAL / SKINNY_EUNSUPPORTED with the reason in skinny_last_error(). */
+/* The chooser: the launch shape skinny_gemm_bf16 uses for (M, N, K, splits)
+ * (unpooler page, Unpooler and compile_unpooler: a layer is built with one
+ * launch shape, UNPOOLER by default, whose splits, kw and accs select the
+ * compiled kernel; pooler_gather page, PoolerGemmShape: the pooler GEMM's
+ * block size, outputs per block and K unroll).  Here the shape is measured
+ * per (M, N, K) instead of fixed per layer.  Pure host function of its
+ * arguments.  Returns SKINNY_OK and fills *out, or SKINNY_EINVAL /
+ * SKINNY_EUNSUPPORTED with the reason in skinny_last_error(). */
 int skinny_choose(int M, int N, int K, int splits, skinny_launch *out);
 
 /* Why there is no launch for (M, N, K, splits): the status the GEMM would
- * return for valid pointers (the unpooler page's Unpooler.unsupported and
+ * return for valid pointers (unpooler page, Unpooler.unsupported and
  * launch_unsupported).  SKINNY_OK when supported; the reason otherwise in
  * skinny_last_error().  Host only. */
 int skinny_gemm_unsupported(int M, int N, int K, int splits);
 
-/* Why (M, N, K) cannot run at `launch`; SKINNY_OK when it can.  Host only. */
+/* Why (M, N, K) cannot run at `launch` (unpooler page, launch_unsupported:
+ * the reason the kernel has no launch for a weight shape at given splits, K
+ * per wave and accumulators); SKINNY_OK when it can.  Host only. */
 int skinny_launch_unsupported(int M, int N, int K, const skinny_launch *launch);
 
 /* The next boundary's mailbox for a zero-copy publish (unpooler page, module
@@ -165,7 +178,8 @@ typedef struct skinny_mailbox {
   int tp, rank, capacity, width;
 } skinny_mailbox;
 
-/* The GEMM with its zero-copy publish: y as skinny_gemm_bf16 computes it, and
+/* The GEMM with its zero-copy publish (unpooler page, module description,
+ * zero-copy epilogue and ticket stage): y as skinny_gemm_bf16 computes it, and
  * the same M rows into mailbox->data[stage][rank][0..M) with each bf16 -0.0
  * stored as +0.0 (-0.0 is the mailbox's "not yet written" sentinel); without a
  * ticket, stage_state[1] is set to the stage.  The other slots, rows >= M
@@ -232,18 +246,23 @@ int skinny_gemm_bf16_ring(const void *const *x, const void *const *W,
                           void *const *y, int count, int M, int N, int K,
                           void *stream);
 
-/* The ring at an explicit launch (see skinny_ring_launch). */
+/* The ring at an explicit launch (see skinny_ring_launch; unpooler page,
+ * module description and compile_unpooler, as for skinny_gemm_bf16_ring and
+ * skinny_gemm_bf16_launch).  Arguments and errors as skinny_gemm_bf16_ring. */
 int skinny_gemm_bf16_ring_launch(const void *const *x, const void *const *W,
                                  void *const *y, int count, int M, int N,
                                  int K, const skinny_ring_launch *launch,
                                  void *stream);
 
 /* The ring's chooser: the launch skinny_gemm_bf16_ring uses for (M, N, K,
- * count).  Host only.  SKINNY_OK, or SKINNY_EINVAL / SKINNY_EUNSUPPORTED with
- * the reason in skinny_last_error(). */
+ * count) (unpooler page, Unpooler and compile_unpooler, as for
+ * skinny_choose).  Host only.  SKINNY_OK, or SKINNY_EINVAL /
+ * SKINNY_EUNSUPPORTED with the reason in skinny_last_error(). */
 int skinny_ring_choose(int M, int N, int K, int count, skinny_ring_launch *out);
 
-/* Why (M, N, K, count) cannot run at `launch`; SKINNY_OK when it can. */
+/* Why (M, N, K, count) cannot run at the ring launch `launch` (unpooler
+ * page, launch_unsupported, as for skinny_launch_unsupported); SKINNY_OK
+ * when it can.  Host only. */
 int skinny_ring_launch_unsupported(int M, int N, int K, int count,
                                    const skinny_ring_launch *launch);
 
@@ -252,10 +271,10 @@ int skinny_ring_launch_unsupported(int M, int N, int K, int count,
  * launch skinny_choose returns); otherwise the call is exactly
  * skinny_gemm_bf16_ring_launch with one item at *out (out->gemm then has the
  * same arithmetic as skinny_choose's launch; SKINNY_PATH_MFMA_LDS stands for
- * SKINNY_PATH_MFMA with the ring's staged weight loads).  The unpooler
- * page's module description orders a kernel's weight loads ahead of its
- * activations; the walk keeps one block's weights in flight while the
- * previous block is finished.  Pure host function; errors as skinny_choose. */
+ * SKINNY_PATH_MFMA with the ring's staged weight loads).  Weight loads go
+ * ahead of the activations (unpooler page, module description); the walk
+ * keeps one block's weights in flight while the previous block is
+ * finished.  Pure host function; errors as skinny_choose. */
 int skinny_choose_walk(int M, int N, int K, int splits, skinny_ring_launch *out);
 
 /* The NVFP4 expert input (pooler_gather page, module description and
@@ -314,32 +333,13 @@ int skinny_dual_norm(const void *partial, float *residual, const void *post_w,
                      float pre_gain_center, float pre_eps, void *out, int M, int H,
                      void *stream);
 
-/* The reason for the last non-OK status on this thread ("" if none). */
-/* Measurement references (not steps of the method).  The weight stream is
- * the decode GEMM's dominant cost (unpooler page, module description); these
- * two calls measure, on the caller's device and stream, what one launch costs
- * by itself and how fast one launch can stream a buffer the way the GEMM
- * kernels stream weights, so that a GEMM call's time can be set against the
- * ceiling a single launch reaches.
- *
- * skinny_ceiling_empty: launches one empty 64-thread workgroup.
- * skinny_ceiling_stream: reads the `bytes` bytes at src (16-byte aligned,
- *   a positive multiple of 8192 * loads_per_lane, below 2^31) once, with
- *   bytes / (8192 * loads_per_lane) workgroups of 512 threads; thread t of
- *   workgroup b issues loads_per_lane (1, 2, 4 or 8) 16-byte loads, load i at
- *   byte b * 8192 * loads_per_lane + 8192 * i + 16 t, all before the first
- *   use.  sink: device u32 [bytes / (8192 * loads_per_lane)], owned by the
- *   caller; word b is set to 1 only if some thread's XOR of the 32-bit words
- *   it read equals 0x5EC0DE42, and is otherwise left as it was.
- * Both need skinny_init on the current device.  Errors: SKINNY_EINVAL,
- * SKINNY_ENOTINIT, SKINNY_EDEVICE, SKINNY_ELAUNCH. */
-int skinny_ceiling_empty(void *stream);
-int skinny_ceiling_stream(const void *src, long long bytes, void *sink, int loads_per_lane,
-                          void *stream);
-
+/* The reason for the last non-OK status on this thread, "" if none
+ * (unpooler page, Unpooler.unsupported: the reason string a call that
+ * cannot run gives, which Unpooler raises as ValueError(reason)).  The
+ * string is thread-local and valid until this thread's next call. */
 const char *skinny_last_error(void);
 
-/* Library ABI version: major * 100 + minor. */
+/* Not a step of the method: the library's ABI version, major * 100 + minor. */
 int skinny_version(void);
 
 #ifdef __cplusplus

@@ -13,8 +13,9 @@ Same names as the C ABI:
   skinny_gemm_bf16_ring,
   skinny_gemm_bf16_ring_launch, skinny_ring_choose, skinny_ring_launch_unsupported,
   skinny_rmsnorm_nvfp4, skinny_rmsnorm_bf16, skinny_dual_norm, skinny_last_error,
-  skinny_version, and the measurement references skinny_ceiling_empty and
-  skinny_ceiling_stream
+  skinny_version
+The benchmark's measurement references (a library of their own, not part of
+this ABI) are in ``moe_decode_skinny_amd.ceiling``.
 Status codes map to exceptions as on the unpooler page (Unpooler.run /
 Unpooler.unsupported): EINVAL and EUNSUPPORTED raise ValueError, the others
 RuntimeError.
@@ -118,8 +119,6 @@ _sig = {
     "skinny_rmsnorm_nvfp4": ([_vp, _vp, _f, _f, _vp, _vp, _vp, _i, _i, _vp], _i),
     "skinny_rmsnorm_bf16": ([_vp, _vp, _f, _f, _vp, _i, _i, _vp], _i),
     "skinny_dual_norm": ([_vp, _vp, _vp, _f, _f, _vp, _f, _vp, _vp, _f, _f, _vp, _i, _i, _vp], _i),
-    "skinny_ceiling_empty": ([_vp], _i),
-    "skinny_ceiling_stream": ([_vp, ctypes.c_longlong, _vp, _i, _vp], _i),
     "skinny_last_error": ([], ctypes.c_char_p),
     "skinny_version": ([], _i),
 }
@@ -424,33 +423,6 @@ def skinny_dual_norm(partial, residual, post_w, post_gain_center: float, post_ep
     return out
 
 
-def skinny_ceiling_empty(device=0, stream=None) -> None:
-    """Measurement reference: one launch of an empty kernel."""
-    import torch
-
-    dev = torch.device("cuda", device) if isinstance(device, int) else torch.device(device)
-    with _on(dev):
-        _check(_lib.skinny_ceiling_empty(_stream(stream, dev)))
-
-
-def skinny_ceiling_stream(src, sink, loads_per_lane: int = 4, stream=None) -> None:
-    """Measurement reference: one launch that streams the bytes of src (a
-    contiguous device tensor) as the GEMM kernels stream weights; sink is
-    int32 [src bytes / (8192 * loads_per_lane)] (see include/skinny.h)."""
-    import torch
-
-    if not isinstance(src, torch.Tensor) or not src.is_cuda or not src.is_contiguous():
-        raise ValueError("src must be a contiguous device tensor")
-    kp = _dev_tensor(sink, "sink", torch.int32)
-    nbytes = src.numel() * src.element_size()
-    if loads_per_lane in (1, 2, 4, 8) and sink.numel() * 8192 * loads_per_lane != nbytes:
-        raise ValueError("sink must hold one word per 8192 * loads_per_lane bytes of src")
-    _common_device(("src", src), ("sink", sink))
-    with _on(src.device):
-        _check(_lib.skinny_ceiling_stream(src.data_ptr(), nbytes, kp, int(loads_per_lane),
-                                          _stream(stream, src.device)))
-
-
 __all__ = [
     "Launch", "RingLaunch", "init", "skinny_init", "skinny_gemm_bf16", "skinny_gemm_bf16_launch",
     "skinny_choose", "skinny_gemm_unsupported", "skinny_launch_unsupported",
@@ -458,6 +430,5 @@ __all__ = [
     "skinny_ring_choose",
     "skinny_ring_launch_unsupported",
     "skinny_rmsnorm_nvfp4", "skinny_rmsnorm_bf16", "skinny_dual_norm", "skinny_last_error", "skinny_version",
-    "skinny_ceiling_empty", "skinny_ceiling_stream",
     "LIB_PATH",
 ]

@@ -1,6 +1,7 @@
-// Measurement reference kernels for the small-M decode GEMM (unpooler page,
-// module description: the weight stream is the call's dominant cost).  They
-// compute nothing of the method: one launches an empty kernel, the other
+// libskinny_ceiling: measurement reference kernels for the small-M decode
+// GEMM's benchmark (unpooler page, module description: the weight stream is
+// the call's dominant cost), built as a library of their own beside
+// libskinny (include/skinny_ceiling.h).  They compute nothing of the method: one launches an empty kernel, the other
 // streams a buffer the way the GEMM kernels stream weights (16-byte loads
 // with the streaming cache policy, each load instruction 1 KiB of contiguous
 // memory, every load issued before the first use), so that the time of a
@@ -12,12 +13,17 @@
 // 8192 i + 16 t of that range.  Each thread XORs the dwords it read and
 // writes 1 to sink[b] only if the result equals kCeilingPattern, which keeps
 // the loads live; with any other data the sink is not written.
-#include "internal.h"
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include "device.h"
+#include "skinny_ceiling.h"
 
 namespace skinny {
 namespace {
 
-constexpr unsigned kCeilingPattern = 0x5EC0DE42u;  // the sink trigger (include/skinny.h)
+constexpr unsigned kCeilingPattern = 0x5EC0DE42u;  // the sink trigger (include/skinny_ceiling.h)
 
 __global__ void ceiling_empty_kernel() {}
 
@@ -38,24 +44,76 @@ __global__ __launch_bounds__(512) void ceiling_stream_kernel(const uint8_t *__re
   if (x == kCeilingPattern) sink[blockIdx.x] = 1u;
 }
 
+thread_local char g_error[256] = "";
+
+int fail(int status, const char *fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_error, sizeof g_error, fmt, ap);
+  va_end(ap);
+  return status;
+}
+
+// The current device is a gfx950 GPU (the kernels are built for it only).
+int check_device() {
+  int dev = -1;
+  hipDeviceProp_t prop;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0)
+    return fail(SKINNY_EDEVICE, "no current HIP device");
+  if (hipGetDeviceProperties(&prop, dev) != hipSuccess)
+    return fail(SKINNY_EDEVICE, "cannot query device %d", dev);
+  if (strncmp(prop.gcnArchName, "gfx950", 6) != 0)
+    return fail(SKINNY_EDEVICE, "device %d is %s; the kernels are built for gfx950", dev,
+                prop.gcnArchName);
+  return SKINNY_OK;
+}
+
+int launched(hipError_t e) {
+  if (e != hipSuccess) return fail(SKINNY_ELAUNCH, "launch failed: %s", hipGetErrorString(e));
+  g_error[0] = 0;
+  return SKINNY_OK;
+}
+
 }  // namespace
-
-hipError_t launch_ceiling_empty(hipStream_t stream) {
-  hipLaunchKernelGGL(ceiling_empty_kernel, dim3(1), dim3(64), 0, stream);
-  return hipGetLastError();
-}
-
-hipError_t launch_ceiling_stream(const uint8_t *src, unsigned bytes, unsigned *sink, int L,
-                                 hipStream_t stream) {
-  const dim3 grid(bytes / (8192u * L)), block(512);
-  switch (L) {
-    case 1: hipLaunchKernelGGL(ceiling_stream_kernel<1>, grid, block, 0, stream, src, bytes, sink); break;
-    case 2: hipLaunchKernelGGL(ceiling_stream_kernel<2>, grid, block, 0, stream, src, bytes, sink); break;
-    case 4: hipLaunchKernelGGL(ceiling_stream_kernel<4>, grid, block, 0, stream, src, bytes, sink); break;
-    case 8: hipLaunchKernelGGL(ceiling_stream_kernel<8>, grid, block, 0, stream, src, bytes, sink); break;
-    default: return hipErrorInvalidValue;
-  }
-  return hipGetLastError();
-}
-
 }  // namespace skinny
+
+using namespace skinny;
+
+extern "C" {
+
+int skinny_ceiling_empty(void *stream) {
+  if (int st = check_device()) return st;
+  hipLaunchKernelGGL(ceiling_empty_kernel, dim3(1), dim3(64), 0,
+                     static_cast<hipStream_t>(stream));
+  return launched(hipGetLastError());
+}
+
+int skinny_ceiling_stream(const void *src, long long bytes, void *sink, int loads_per_lane,
+                          void *stream) {
+  if (!src || !sink) return fail(SKINNY_EINVAL, "null pointer");
+  if ((uintptr_t)src % 16 || (uintptr_t)sink % 4)
+    return fail(SKINNY_EINVAL, "src must be 16-byte and sink 4-byte aligned");
+  if (loads_per_lane != 1 && loads_per_lane != 2 && loads_per_lane != 4 && loads_per_lane != 8)
+    return fail(SKINNY_EINVAL, "loads_per_lane=%d: needs 1, 2, 4 or 8", loads_per_lane);
+  const long long unit = 8192LL * loads_per_lane;
+  if (bytes <= 0 || bytes % unit || bytes > 0x7FFFF000LL)
+    return fail(SKINNY_EINVAL, "bytes=%lld: needs a positive multiple of %lld below 2^31", bytes,
+                unit);
+  if (int st = check_device()) return st;
+  const uint8_t *s = static_cast<const uint8_t *>(src);
+  unsigned *k = static_cast<unsigned *>(sink);
+  const unsigned n = (unsigned)bytes;
+  const dim3 grid(n / (8192u * loads_per_lane)), block(512);
+  hipStream_t h = static_cast<hipStream_t>(stream);
+  switch (loads_per_lane) {
+    case 1: hipLaunchKernelGGL(ceiling_stream_kernel<1>, grid, block, 0, h, s, n, k); break;
+    case 2: hipLaunchKernelGGL(ceiling_stream_kernel<2>, grid, block, 0, h, s, n, k); break;
+    case 4: hipLaunchKernelGGL(ceiling_stream_kernel<4>, grid, block, 0, h, s, n, k); break;
+    default: hipLaunchKernelGGL(ceiling_stream_kernel<8>, grid, block, 0, h, s, n, k); break;
+  }
+  return launched(hipGetLastError());
+}
+
+const char *skinny_ceiling_last_error(void) { return g_error; }
+
+}  // extern "C"

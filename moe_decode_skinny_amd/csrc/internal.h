@@ -43,9 +43,6 @@ hipError_t launch_dual_norm(const uint16_t *partial, float *residual, const uint
                             float alpha_scalar, const uint16_t *beta, const uint16_t *next_w,
                             float pre_gc, float pre_eps, uint16_t *out, int M, int H,
                             DeviceState &st, hipStream_t stream);
-hipError_t launch_ceiling_empty(hipStream_t stream);
-hipError_t launch_ceiling_stream(const uint8_t *src, unsigned bytes, unsigned *sink, int L,
-                                 hipStream_t stream);
 hipError_t launch_rmsnorm(const uint16_t *r, const uint16_t *w, float gain_center,
                           float eps, const float *global_scale, uint8_t *a,
                           uint8_t *a_sf, uint16_t *y, int M, int P, bool quant,

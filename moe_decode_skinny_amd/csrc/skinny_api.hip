@@ -3,7 +3,7 @@
 //
 // The checks restate, for gfx950, the unpooler page's Unpooler.unsupported,
 // Unpooler.run and launch_unsupported: N % 16 == 0, 16-byte aligned
-// contiguous BF16 operands, 1 <= M <= 16, splits in {1, 2, 4, 8}, and a K that
+// contiguous BF16 operands, 1 <= M <= 16, splits in {1, 2, 4, 8, 16}, and a K that
 // divides into splits x waves x kw with at most a workgroup's worth of waves.
 // Their reasons come back as strings through skinny_last_error(), like the
 // pages' ValueError(reason).
@@ -671,35 +671,7 @@ using namespace skinny;
 
 extern "C" {
 
-int skinny_version(void) { return 105; }
-
-int skinny_ceiling_empty(void *stream) {
-  int st = SKINNY_OK;
-  if (!current_state(&st)) return st;
-  hipError_t e = launch_ceiling_empty(static_cast<hipStream_t>(stream));
-  if (e != hipSuccess) return fail(SKINNY_ELAUNCH, "launch failed: %s", hipGetErrorString(e));
-  return SKINNY_OK;
-}
-
-int skinny_ceiling_stream(const void *src, long long bytes, void *sink, int loads_per_lane,
-                          void *stream) {
-  if (!src || !sink) return fail(SKINNY_EINVAL, "null pointer");
-  if (!aligned(src, 16) || !aligned(sink, 4))
-    return fail(SKINNY_EINVAL, "src must be 16-byte and sink 4-byte aligned");
-  if (loads_per_lane != 1 && loads_per_lane != 2 && loads_per_lane != 4 && loads_per_lane != 8)
-    return fail(SKINNY_EINVAL, "loads_per_lane=%d: needs 1, 2, 4 or 8", loads_per_lane);
-  const long long unit = 8192LL * loads_per_lane;
-  if (bytes <= 0 || bytes % unit || bytes > 0x7FFFF000LL)
-    return fail(SKINNY_EINVAL, "bytes=%lld: needs a positive multiple of %lld below 2^31", bytes,
-                unit);
-  int st = SKINNY_OK;
-  if (!current_state(&st)) return st;
-  hipError_t e = launch_ceiling_stream(static_cast<const uint8_t *>(src), (unsigned)bytes,
-                                       static_cast<unsigned *>(sink), loads_per_lane,
-                                       static_cast<hipStream_t>(stream));
-  if (e != hipSuccess) return fail(SKINNY_ELAUNCH, "launch failed: %s", hipGetErrorString(e));
-  return SKINNY_OK;
-}
+int skinny_version(void) { return 106; }
 
 const char *skinny_last_error(void) { return g_error; }
 

@@ -1,7 +1,9 @@
-"""Host-only checks of the C ABI: the library loads, exports every entry point
-that include/skinny.h declares, and its host logic (argument checks, the
-launch-shape chooser, error reasons) behaves as documented.  No compute call
-is made here: these tests run without a GPU.
+"""Host-only checks of the C ABI: the libraries load, export every entry point
+that include/*.h declares (include/skinny.h: libskinny; include/skinny_ceiling.h:
+the benchmark's measurement references, libskinny_ceiling), every declaration
+cites the passage of the pages that defines it, and the host logic (argument
+checks, the launch-shape chooser, error reasons) behaves as documented.  No
+compute call is made here: these tests run without a GPU.
 """
 import ctypes
 import os
@@ -10,16 +12,63 @@ import re
 import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+PRODUCT_HEADER = "skinny.h"
+CEILING_HEADER = "skinny_ceiling.h"
+
+# The pages' sections a declaration may cite (page title tail, then section).
+PAGES = {
+    "unpooler": ["module description", "Unpooler.run", "Unpooler.unsupported", "Unpooler",
+                 "compile_unpooler", "launch_unsupported"],
+    "pooler_gather": ["module description", "Pooler", "PoolerGemmShape", "PoolerLayer",
+                      "compile_norm_quant", "compile_gather", "compile_pooler_gemm",
+                      "cvt_e2m1x8_f32", "cvt_f32_to_e4m3", "nvfp4_compute_output_scale"],
+    "oproj.batt": ["module description", "AttentionBoundary", "OProjection"],
+}
+# Declarations that are not steps of the method say so instead of citing.
+NOT_A_STEP = ("Not a step of the method", "For callers that cannot allocate")
 
 
-def _declared_symbols():
+def _header_text(header):
+    return open(os.path.join(ROOT, "include", header)).read()
+
+
+def _declarations(header):
+    """[(name, comment)] for every function the header declares; the comment
+    is the last comment between the previous declaration and this one (a
+    declaration right after another shares that one's comment)."""
+    text = _header_text(header)
+    out, prev_end, prev_comment = [], 0, ""
+    for m in re.finditer(r"^(?:int|const char \*|void)\s*(skinny_\w+)\s*\(", text, flags=re.M):
+        between = text[prev_end:m.start()]
+        comments = re.findall(r"/\*.*?\*/", between, flags=re.S)
+        comment = comments[-1] if comments else prev_comment
+        out.append((m.group(1), comment))
+        prev_end = text.index(";", m.end()) + 1
+        prev_comment = comment
+    return out
+
+
+def _declared_symbols(header=None):
+    headers = [header] if header else [h for h in os.listdir(os.path.join(ROOT, "include"))
+                                       if h.endswith(".h")]
     names = set()
-    for fn in os.listdir(os.path.join(ROOT, "include")):
-        if fn.endswith(".h"):
-            text = open(os.path.join(ROOT, "include", fn)).read()
-            text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-            names |= set(re.findall(r"\b(skinny_\w+)\s*\(", text))
+    for h in headers:
+        text = re.sub(r"/\*.*?\*/", "", _header_text(h), flags=re.S)
+        names |= set(re.findall(r"\b(skinny_\w+)\s*\(", text))
     return sorted(names)
+
+
+def _cites_a_passage(comment):
+    body = re.sub(r"^\s*/?\*+/?", "", comment, flags=re.M).replace("*/", "")
+    flat = " ".join(body.split())
+    if any(tag in flat for tag in NOT_A_STEP):
+        return True
+    for page, sections in PAGES.items():
+        for m in re.finditer(re.escape(page) + r" page[,:]? ", flat):
+            tail = flat[m.end():m.end() + 200]
+            if any(tail.startswith(sec) or f" {sec}" in tail[:120] for sec in sections):
+                return True
+    return False
 
 
 @pytest.fixture(scope="module")
@@ -29,21 +78,55 @@ def sk():
     return sk
 
 
+def test_headers_are_the_two_libraries():
+    assert sorted(h for h in os.listdir(os.path.join(ROOT, "include")) if h.endswith(".h")) == \
+        [PRODUCT_HEADER, CEILING_HEADER]
+
+
 def test_header_declares_the_entry_points():
-    names = _declared_symbols()
+    names = _declared_symbols(PRODUCT_HEADER)
     for n in ["skinny_init", "skinny_gemm_bf16", "skinny_rmsnorm_nvfp4", "skinny_choose",
               "skinny_last_error"]:
         assert n in names
+    assert not [n for n in names if n.startswith("skinny_ceiling")]
+
+
+@pytest.mark.parametrize("header", [PRODUCT_HEADER, CEILING_HEADER])
+def test_every_declaration_cites_its_passage(header):
+    """Each declared call's comment names a page and one of its sections, or
+    says that it is not a step of the method."""
+    decls = _declarations(header)
+    assert sorted(n for n, _ in decls) == _declared_symbols(header)
+    bad = [n for n, c in decls if not _cites_a_passage(c)]
+    assert not bad, bad
+
+
+def test_citation_check_rejects_uncited_comments():
+    assert not _cites_a_passage("/* The same GEMM at an explicit launch. */")
+    assert not _cites_a_passage("/* the unpooler page */")
+    assert _cites_a_passage("/* (unpooler page,\n * launch_unsupported) */")
 
 
 def test_library_exports_every_declared_symbol(sk):
     lib = ctypes.CDLL(sk.LIB_PATH)
-    missing = [n for n in _declared_symbols() if not hasattr(lib, n)]
+    missing = [n for n in _declared_symbols(PRODUCT_HEADER) if not hasattr(lib, n)]
     assert not missing, missing
+    # the measurement references live only in their own library
+    assert not hasattr(lib, "skinny_ceiling_stream") and not hasattr(lib, "skinny_ceiling_empty")
+
+
+def test_ceiling_library_exports_its_symbols():
+    from moe_decode_skinny_amd import ceiling
+
+    lib = ctypes.CDLL(ceiling.LIB_PATH)
+    missing = [n for n in _declared_symbols(CEILING_HEADER) if not hasattr(lib, n)]
+    assert not missing, missing
+    for n in _declared_symbols(CEILING_HEADER):
+        assert hasattr(ceiling, n), n
 
 
 def test_binding_has_the_same_names(sk):
-    for n in _declared_symbols():
+    for n in _declared_symbols(PRODUCT_HEADER):
         assert hasattr(sk, n), n
 
 
@@ -480,7 +563,9 @@ def test_binding_keeps_every_argument_on_one_device(sk):
 def test_ceiling_stream_argument_checks(sk):
     """The stream reference rejects bad sizes, load counts and pointers before
     touching a device."""
-    lib = ctypes.CDLL(sk.LIB_PATH)
+    from moe_decode_skinny_amd import ceiling
+
+    lib = ctypes.CDLL(ceiling.LIB_PATH)
     fn = lib.skinny_ceiling_stream
     fn.argtypes = [ctypes.c_void_p, ctypes.c_longlong, ctypes.c_void_p, ctypes.c_int,
                    ctypes.c_void_p]
@@ -491,4 +576,5 @@ def test_ceiling_stream_argument_checks(sk):
              (p, 0, 1, "positive"), (p, 1 << 31, 1, "below 2^31")]
     for src, nbytes, lpl, needle in cases:
         assert fn(src, nbytes, p, lpl, None) == sk.SKINNY_EINVAL, needle
-        assert needle in sk.skinny_last_error(), (needle, sk.skinny_last_error())
+        msg = ceiling.skinny_ceiling_last_error()
+        assert needle in msg, (needle, msg)

@@ -1,5 +1,6 @@
-"""The measurement reference kernels (include/skinny.h, skinny_ceiling_*):
-the stream reference reads exactly the bytes its layout says, once."""
+"""The benchmark's measurement reference kernels (libskinny_ceiling,
+include/skinny_ceiling.h): the stream reference reads exactly the bytes its
+layout says, once."""
 import numpy as np
 import pytest
 
@@ -9,11 +10,13 @@ PATTERN = 0x5EC0DE42
 
 
 @pytest.mark.parametrize("L", [1, 2, 4, 8])
-def test_stream_reference_reads_its_layout(gpu_lib, L):
+def test_stream_reference_reads_its_layout(L):
     """Two threads get data whose XOR is the sink pattern; the sink words of
     exactly the workgroups that hold such a thread (by the documented layout:
     load i of thread t of workgroup b at b*8192L + 8192i + 16t) are set."""
     import torch
+
+    from moe_decode_skinny_amd import ceiling
 
     print(f"ceiling stream L={L}", flush=True)
     nwg = 6
@@ -28,7 +31,7 @@ def test_stream_reference_reads_its_layout(gpu_lib, L):
     assert list(expected) == [7, 7, 1, 7, 7, 1]
     src = torch.from_numpy(data.view(np.int32)).to("cuda")
     sink = torch.full((nwg,), 7, dtype=torch.int32, device="cuda")
-    gpu_lib.skinny_ceiling_stream(src, sink, L)
-    gpu_lib.skinny_ceiling_empty(0)
+    ceiling.skinny_ceiling_stream(src, sink, L)
+    ceiling.skinny_ceiling_empty(0)
     torch.cuda.synchronize()
     assert np.array_equal(sink.cpu().numpy(), expected)

@@ -4,10 +4,10 @@ post_attn_norm, gated add into the FP32 residual stream in place,
 pre_ffn_norm into BF16; the formula is a reading, see the oracle source).
 
 Both sides compute in binary64 with one rounding per narrowing; only the
-order of the two sums of squares differs, which moves the reciprocal roots by
-an ulp of binary64, so results are expected bit for bit.  The test allows
-1 ulp (bf16 out; the residual's value moved by beta times 1 bf16 ulp of h) on
-at most 0.1% of the elements.
+order of the two sums of squares differs, which can move a reciprocal root by
+an ulp of binary64 and a rounded result only when the exact value lies within
+about 2^-53 (relative) of a bfloat16 or binary32 midpoint.  The test asks
+for the output and the updated residual bit for bit.
 """
 import sys
 
@@ -53,14 +53,11 @@ def _run(sk, partial, residual, post_w, alpha, beta, next_w, consts):
 
 
 def _compare(out, res, want_out, want_res, tag):
-    d_out = np.abs(out.astype(np.int32) - want_out.astype(np.int32))  # bf16 ulps (same sign)
-    bad_out = np.count_nonzero(d_out)
+    bad_out = np.count_nonzero(out != want_out)
     bad_res = np.count_nonzero(res.view(np.uint32) != want_res.view(np.uint32))
     _say(f"{tag}: out differs at {bad_out}, residual at {bad_res} of {out.size}")
-    assert np.all(np.isfinite(res)) and d_out.max() <= 1, tag
-    assert bad_out <= 0.001 * out.size and bad_res <= 0.001 * out.size, tag
-    rel = np.abs(res.astype(np.float64) - want_res) / np.maximum(np.abs(want_res), 1e-30)
-    assert np.all(rel <= 2.0 ** -7), tag
+    assert np.all(np.isfinite(res)), tag
+    assert bad_out == 0 and bad_res == 0, tag
 
 
 CONSTS = (1.0, 1e-6, 1.0, 1e-6)  # post gain center, post eps, pre gain center, pre eps
@@ -138,4 +135,3 @@ def test_dual_norm_in_place_across_graph_replays(gpu_lib):
                                                  beta, next_w, 1.0, 1e-6)
         got = r.cpu().numpy()
         _compare(from_dev(out), got, want_out, want_res, f"replay {rep}")
-        want_res = got  # continue from the GPU's state (any 1-ulp step stays local)

@@ -1,11 +1,15 @@
 """GPU parity of the norm kernels against the oracle, through the C ABI.
 
-skinny_rmsnorm_nvfp4 (pooler_gather page, module description): codes and
-scales bit-exact except where the oracle's pre-quantization value lies within
-one bfloat16 ulp (scaled) of a rounding boundary (tests/helpers.py); the
-number of exempt positions must stay below 1%.
-skinny_rmsnorm_bf16 (same page, "BF16 edge layers"): within one bfloat16 ulp
-of the oracle, with fewer than 1% of elements off by that ulp.
+skinny_rmsnorm_nvfp4 (pooler_gather page, module description;
+cvt_e2m1x8_f32, cvt_f32_to_e4m3, nvfp4_compute_output_scale): the kernel
+computes in binary64 with one rounding per narrowing, as the oracle does, so
+codes and scales must be bit-exact on every case (no boundary exemption).
+The cases include rows built to land exactly on every e2m1 midpoint and every
+e4m3 midpoint (tests/norm_cases.py), blocks whose scales are e4m3
+subnormals, zero-scale blocks and signed zeros.  The boundary-exemption
+rule of tests/helpers.py only explains a failure (which codes differ, and
+whether they sit on a rounding boundary); it no longer accepts one.
+skinny_rmsnorm_bf16 (same page, "BF16 edge layers"): bit-exact.
 
 The full-pooler case feeds the GPU GEMM output (M=8, x[8, 8192] @ W[4096,
 8192]^T) to both sides, with global_scale = 448 * 6 / amax(yn_oracle).
@@ -18,7 +22,8 @@ import pytest
 
 import oracle
 import synthetic
-from tests.helpers import bf16_ulp, compare_nvfp4, from_dev, to_dev
+from tests import norm_cases
+from tests.helpers import compare_nvfp4, from_dev, to_dev
 
 pytestmark = pytest.mark.gpu
 THREADS = min(16, os.cpu_count() or 1)
@@ -43,6 +48,23 @@ def _nvfp4_gpu(sk, r_bits, w_bits, gc, eps, gs):
     return a.cpu().numpy(), sf.cpu().numpy()
 
 
+def _assert_exact(r_bits, w_bits, gc, eps, gs, a, sf, tag=""):
+    """Codes and scales equal to the oracle's, byte for byte.  On a mismatch
+    the boundary rule names the first difference and whether it lies on a
+    rounding boundary."""
+    ref = oracle.rmsnorm_nvfp4(r_bits, w_bits, gc, eps, gs)
+    if np.array_equal(a, ref["a"]) and np.array_equal(sf, ref["a_sf"]):
+        return ref
+    n_a = int(np.count_nonzero(a != ref["a"]))
+    n_sf = int(np.count_nonzero(sf != ref["a_sf"]))
+    try:
+        exempt, total = compare_nvfp4(r_bits, w_bits, gc, eps, gs, a, sf)
+        why = f"all {exempt} differing codes of {total} on a rounding boundary"
+    except AssertionError as e:
+        why = str(e)
+    raise AssertionError(f"{tag}: {n_a} code bytes and {n_sf} scales differ; {why}")
+
+
 def _gs_for(r_bits, w_bits, gc, eps):
     yn = oracle.bf16_value(oracle.rmsnorm_bf16(r_bits, w_bits, gc, eps))
     return oracle.f32(448.0 * 6.0 / np.abs(yn).max())
@@ -63,9 +85,7 @@ def test_full_pooler_expert_input(gpu_lib):
     gc, eps = 1.0, 1e-6
     gs = _gs_for(r_bits, nw, gc, eps)
     a, sf = _nvfp4_gpu(gpu_lib, r_bits, nw, gc, eps, gs)
-    exempt, total = compare_nvfp4(r_bits, nw, gc, eps, gs, a, sf)
-    _say(f"exempt {exempt} of {total}")
-    assert exempt < 0.01 * total
+    _assert_exact(r_bits, nw, gc, eps, gs, a, sf, "full pooler")
     # the block with the largest |yn| reaches the largest scale
     assert (sf == 0x7E).any()
 
@@ -77,10 +97,9 @@ def test_nvfp4_shapes(gpu_lib, M, P, gc, eps):
     _say(f"nvfp4 M={M} P={P}")
     r = synthetic.rows_normal(M, P, seed=M * 7 + P)
     nw = synthetic.norm_weight(P, seed=P)
-    for gs in (_gs_for(r, nw, gc, eps), 1.0, 3.0e4):
+    for gs in (_gs_for(r, nw, gc, eps), 1.0, 3.0e4, 1.0e-3):
         a, sf = _nvfp4_gpu(gpu_lib, r, nw, gc, eps, gs)
-        exempt, total = compare_nvfp4(r, nw, gc, eps, gs, a, sf)
-        assert exempt <= max(2, 0.01 * total)
+        _assert_exact(r, nw, gc, eps, gs, a, sf, f"M={M} P={P} gs={gs}")
 
 
 def test_nvfp4_zero_and_tiny_rows(gpu_lib):
@@ -94,8 +113,42 @@ def test_nvfp4_zero_and_tiny_rows(gpu_lib):
     nw = synthetic.norm_weight(P, seed=1)
     a, sf = _nvfp4_gpu(gpu_lib, r_bits, nw, 1.0, 1e-6, 500.0)
     assert np.all(sf[0] == 0) and np.all(a[0] == 0)
-    exempt, _ = compare_nvfp4(r_bits, nw, 1.0, 1e-6, 500.0, a, sf)
-    assert exempt <= 2
+    _assert_exact(r_bits, nw, 1.0, 1e-6, 500.0, a, sf, "zero and tiny rows")
+
+
+def test_nvfp4_e2m1_midpoints(gpu_lib):
+    """Normed values exactly on every e2m1 midpoint {0.25, 0.75, 1.25, 1.75,
+    2.5, 3.5, 5} of both signs (ties to the even code), one bfloat16 step on
+    either side of each, output scales 1 and 2, saturation above 6, signed
+    zeros and negative values that round to code 0x8, zero-scale blocks."""
+    r, w, gc, eps, gs = norm_cases.e2m1_tie_case()
+    _say(f"e2m1 ties P={w.size}")
+    a, sf = _nvfp4_gpu(gpu_lib, r, w, gc, eps, gs)
+    _assert_exact(r, w, gc, eps, gs, a, sf, "e2m1 midpoints")
+
+
+def test_nvfp4_e4m3_midpoints(gpu_lib):
+    """Block scales exactly on every e4m3fn midpoint, subnormal ones
+    included (ties to the even code), on every finite e4m3fn value, and past
+    448 (saturation to 0x7E)."""
+    r, w, gc, eps, gs = norm_cases.e4m3_tie_case()
+    _say(f"e4m3 ties P={w.size}")
+    a, sf = _nvfp4_gpu(gpu_lib, r, w, gc, eps, gs)
+    _assert_exact(r, w, gc, eps, gs, a, sf, "e4m3 midpoints")
+    assert sorted(set(sf[0].tolist())) == list(range(0x7F))
+
+
+@pytest.mark.parametrize("target", [2.0 ** -6, 2.0 ** -8])
+def test_nvfp4_subnormal_scales(gpu_lib, target):
+    """Normal rows with a global scale small enough that the block scales
+    are e4m3 subnormals (codes 0x01..0x07) and zero, the largest block at or
+    near the smallest normal 0x08."""
+    r, w, gc, eps, gs_of = norm_cases.subnormal_scale_case(gs_target=target)
+    gs = gs_of(oracle.bf16_value(oracle.rmsnorm_bf16(r, w, gc, eps)))
+    _say(f"subnormal scales target={target} gs={gs}")
+    a, sf = _nvfp4_gpu(gpu_lib, r, w, gc, eps, gs)
+    _assert_exact(r, w, gc, eps, gs, a, sf, f"subnormal scales {target}")
+    assert np.count_nonzero((sf >= 1) & (sf <= 7)) > 0.5 * sf.size
 
 
 def test_golden_worked_block_on_gpu(gpu_lib):
@@ -114,14 +167,26 @@ def test_rmsnorm_bf16(gpu_lib, M, P):
     _say(f"rmsnorm_bf16 M={M} P={P}")
     r_bits = synthetic.rows_normal(M, P, seed=P + M)
     nw = synthetic.norm_weight(P, seed=P)
-    ref = oracle.bf16_value(oracle.rmsnorm_bf16(r_bits, nw, 1.0, 1e-6))
+    ref_bits = oracle.rmsnorm_bf16(r_bits, nw, 1.0, 1e-6)
     y = torch.empty((M, P), dtype=torch.bfloat16, device="cuda")
     gpu_lib.skinny_rmsnorm_bf16(to_dev(r_bits), to_dev(nw), 1.0, 1e-6, y)
     torch.cuda.synchronize()
-    got = oracle.bf16_value(from_dev(y))
-    diff = np.abs(got - ref)
-    assert np.all(diff <= bf16_ulp(ref))
-    assert (diff > 0).sum() <= max(2, 0.01 * ref.size)
+    got = from_dev(y)
+    bad = int(np.count_nonzero(got != ref_bits))
+    assert bad == 0, f"{bad} of {ref_bits.size} differ"
+
+
+def test_rmsnorm_bf16_signed_zeros_and_exact_rows(gpu_lib):
+    """The constructed +-1 rows (normed value exactly r * (w + 0)), with
+    -0.0 and +0.0 weights: bit for bit, signs of zero included."""
+    import torch
+
+    r_bits, nw, gc, eps, _ = norm_cases.e2m1_tie_case()
+    ref_bits = oracle.rmsnorm_bf16(r_bits, nw, gc, eps)
+    y = torch.empty(r_bits.shape, dtype=torch.bfloat16, device="cuda")
+    gpu_lib.skinny_rmsnorm_bf16(to_dev(r_bits), to_dev(nw), gc, eps, y)
+    torch.cuda.synchronize()
+    assert np.array_equal(from_dev(y), ref_bits)
 
 
 def test_norm_deterministic(gpu_lib):
