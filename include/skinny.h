@@ -92,8 +92,9 @@ typedef struct skinny_launch {
  * run is graph-capturable and allocates nothing; pooler_gather page, Pooler:
  * the same for the pooler): checks that it is a gfx950 GPU, allocates the
  * library's split-K workspace on it (8 MiB of FP32 partials, enough for
- * S * M * N <= 2^21) and the dual norm's buffer (512 KiB of per-slice sums)
- * and sets the kernels' LDS limits.
+ * S * M * N <= 2^21) and the dual norm's buffer (512 KiB of per-slice sums),
+ * sets the kernels' LDS limits and looks up the device's address of the
+ * static scratch array of skinny_gemm_bf16_noalloc.
  * Call it before any graph capture.  Idempotent.  Returns SKINNY_OK,
  * SKINNY_EDEVICE or SKINNY_ELAUNCH (allocation failure). */
 int skinny_init(int device);
@@ -125,6 +126,21 @@ int skinny_init(int device);
  * Errors: SKINNY_EINVAL, SKINNY_EUNSUPPORTED, SKINNY_ENOTINIT, SKINNY_ELAUNCH. */
 int skinny_gemm_bf16(const void *x, const void *W, void *y, int M, int N,
                      int K, int splits, void *stream);
+
+/* For callers that cannot allocate (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc): skinny_gemm_bf16 with the
+ * same arguments, chooser, kernels and bits, except that a launch with
+ * splits > 1 keeps its FP32 partials in a static device array of the library
+ * (1 MiB, 2^18 floats, one per device, held until the process ends; its
+ * address is looked up by skinny_init) instead of the workspace skinny_init
+ * allocates.  The call allocates and frees nothing.  The array needs no
+ * clearing: each call writes every partial it reads.  Every call on a
+ * device shares that device's array: calls that overlap on one device
+ * (different streams, or host threads without ordering) race.
+ * Errors: as skinny_gemm_bf16, and SKINNY_EUNSUPPORTED when the chosen
+ * launch's splits x M x N exceeds 2^18 (skinny_gemm_bf16 takes up to 2^21). */
+int skinny_gemm_bf16_noalloc(const void *x, const void *W, void *y, int M, int N,
+                             int K, int splits, void *stream);
 
 /* The same GEMM at an explicit launch shape (unpooler page, compile_unpooler:
  * one kernel per shape and launch parameters -- splits, K per wave,

@@ -8,7 +8,8 @@ library has not been built this module raises ImportError; there is no
 fallback.
 
 Same names as the C ABI:
-  skinny_init, skinny_gemm_bf16, skinny_gemm_bf16_launch, skinny_choose,
+  skinny_init, skinny_gemm_bf16, skinny_gemm_bf16_noalloc, skinny_gemm_bf16_launch,
+  skinny_choose,
   skinny_gemm_unsupported, skinny_launch_unsupported, skinny_gemm_bf16_publish,
   skinny_gemm_bf16_ring,
   skinny_gemm_bf16_ring_launch, skinny_ring_choose, skinny_ring_launch_unsupported,
@@ -104,6 +105,7 @@ _f = ctypes.c_float
 _sig = {
     "skinny_init": ([_i], _i),
     "skinny_gemm_bf16": ([_vp, _vp, _vp, _i, _i, _i, _i, _vp], _i),
+    "skinny_gemm_bf16_noalloc": ([_vp, _vp, _vp, _i, _i, _i, _i, _vp], _i),
     "skinny_gemm_bf16_launch": ([_vp, _vp, _vp, _i, _i, _i, ctypes.POINTER(_CLaunch), _vp], _i),
     "skinny_choose": ([_i, _i, _i, _i, ctypes.POINTER(_CLaunch)], _i),
     "skinny_gemm_unsupported": ([_i, _i, _i, _i], _i),
@@ -240,6 +242,18 @@ def skinny_gemm_bf16(x, w, y, splits: int = 0, stream=None):
     xp, wp, yp, M, N, K = _gemm_args(x, w, y)
     with _on(x.device):
         _check(_lib.skinny_gemm_bf16(xp, wp, yp, M, N, K, splits, _stream(stream, x.device)))
+    return y
+
+
+def skinny_gemm_bf16_noalloc(x, w, y, splits: int = 0, stream=None):
+    """skinny_gemm_bf16 with its split-K partials in the library's static
+    scratch array instead of the workspace skinny_init allocated (splits x M
+    x N <= 2^18 floats); for callers that cannot allocate.  Calls that overlap
+    on one device race on that array.  Returns y."""
+    xp, wp, yp, M, N, K = _gemm_args(x, w, y)
+    with _on(x.device):
+        _check(_lib.skinny_gemm_bf16_noalloc(xp, wp, yp, M, N, K, splits,
+                                             _stream(stream, x.device)))
     return y
 
 
@@ -425,6 +439,7 @@ def skinny_dual_norm(partial, residual, post_w, post_gain_center: float, post_ep
 
 __all__ = [
     "Launch", "RingLaunch", "init", "skinny_init", "skinny_gemm_bf16", "skinny_gemm_bf16_launch",
+    "skinny_gemm_bf16_noalloc",
     "skinny_choose", "skinny_gemm_unsupported", "skinny_launch_unsupported",
     "skinny_gemm_bf16_publish", "skinny_gemm_bf16_ring", "skinny_gemm_bf16_ring_launch",
     "skinny_ring_choose",

@@ -25,6 +25,9 @@ constexpr int kMaxSplits = 16;
 // Split-K workspace owned by the library (per device, from skinny_init):
 // FP32 partials [split][token][feature], S * M * N floats at most.
 constexpr size_t kWorkspaceFloats = size_t(2) << 20;  // 8 MiB
+// The same partials for skinny_gemm_bf16_noalloc, in a static device array of
+// the library (no allocation): S * M * N floats at most.
+constexpr size_t kScratchFloats = size_t(1) << 18;  // 1 MiB
 
 constexpr size_t kMaxDynamicLds = 160 * 1024;  // all of a gfx950 CU's LDS
 

@@ -144,16 +144,16 @@ bool blocks_variant_exists(int rows, int chunks, int q, int waves) {
 }
 
 hipError_t launch_gemm_blocks(const uint16_t *x, const uint16_t *w, uint16_t *y, int M,
-                              int N, int K, const skinny_launch &l, DeviceState &st,
+                              int N, int K, const skinny_launch &l, float *partials,
                               const Publish &pub, hipStream_t stream) {
   BlocksKernel k = pick(l.rows, l.chunks, blocks_token_sets(M), l.waves);
   const int groups = N / l.rows;
   dim3 grid(groups * l.splits), block(64 * l.waves);
-  hipLaunchKernelGGL(k, grid, block, 0, stream, x, w, y, st.partials, M, N, K, l.splits,
+  hipLaunchKernelGGL(k, grid, block, 0, stream, x, w, y, partials, M, N, K, l.splits,
                      groups, kBlockK * l.chunks, pub);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || l.splits == 1) return e;
-  return launch_split_reduce(st.partials, y, M, N, l.splits, pub, stream);
+  return launch_split_reduce(partials, y, M, N, l.splits, pub, stream);
 }
 
 }  // namespace skinny

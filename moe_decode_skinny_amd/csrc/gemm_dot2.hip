@@ -196,15 +196,15 @@ int dot2_max_waves() { return 16; }
 
 hipError_t launch_gemm_dot2(const uint16_t *x, const uint16_t *w, uint16_t *y,
                             int M, int N, int K, const skinny_launch &l,
-                            DeviceState &st, const Publish &pub, hipStream_t stream) {
+                            float *partials, const Publish &pub, hipStream_t stream) {
   Dot2Kernel k = pick(l.rows, l.chunks, dot2_token_tile(M), l.waves);
   const int groups = N / l.rows;
   dim3 grid(groups * l.splits), block(64 * l.waves);
-  hipLaunchKernelGGL(k, grid, block, 0, stream, x, w, y, st.partials, M, N, K, l.splits,
+  hipLaunchKernelGGL(k, grid, block, 0, stream, x, w, y, partials, M, N, K, l.splits,
                      groups, kDot2K * l.chunks, pub);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || l.splits == 1) return e;
-  return launch_split_reduce(st.partials, y, M, N, l.splits, pub, stream);
+  return launch_split_reduce(partials, y, M, N, l.splits, pub, stream);
 }
 
 }  // namespace skinny

@@ -217,16 +217,16 @@ size_t mfma_lds_bytes(int M, const skinny_launch &l) {
 
 hipError_t launch_gemm_mfma(const uint16_t *x, const uint16_t *w, uint16_t *y,
                             int M, int N, int K, const skinny_launch &l,
-                            DeviceState &st, const Publish &pub, hipStream_t stream) {
+                            float *partials, const Publish &pub, hipStream_t stream) {
   MfmaKernel k = pick(l.chunks, l.accs);
   const int F = l.rows / kTileN;
   const int groups = N / l.rows;
   dim3 grid(groups * l.splits), block(64 * l.waves);
-  hipLaunchKernelGGL(k, grid, block, mfma_lds_bytes(M, l), stream, x, w, y, st.partials, M, N,
+  hipLaunchKernelGGL(k, grid, block, mfma_lds_bytes(M, l), stream, x, w, y, partials, M, N,
                      K, l.splits, groups, F, kMfmaK * l.chunks, pub);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || l.splits == 1) return e;
-  return launch_split_reduce(st.partials, y, M, N, l.splits, pub, stream);
+  return launch_split_reduce(partials, y, M, N, l.splits, pub, stream);
 }
 
 }  // namespace skinny

@@ -16,6 +16,9 @@ struct DeviceState {
   std::atomic<bool> ready{false};
   float *partials = nullptr;         // kWorkspaceFloats
   double *norm_partials = nullptr;   // kNormPartials
+  // This device's address of the library's static scratch array
+  // (kScratchFloats, skinny_gemm_bf16_noalloc), from hipGetSymbolAddress.
+  float *scratch = nullptr;
 };
 
 // The state of the current HIP device, or nullptr (and a reason) if the
@@ -25,15 +28,16 @@ DeviceState *current_state(int *status);
 
 // ------------------------------------------------------------- launchers
 // Each returns hipSuccess or the launch error; arguments are already valid.
+// `partials`: the split-K workspace (S * M * N floats), used when l.splits > 1.
 hipError_t launch_gemm_mfma(const uint16_t *x, const uint16_t *w, uint16_t *y,
                             int M, int N, int K, const skinny_launch &l,
-                            DeviceState &st, const Publish &pub, hipStream_t stream);
+                            float *partials, const Publish &pub, hipStream_t stream);
 hipError_t launch_gemm_dot2(const uint16_t *x, const uint16_t *w, uint16_t *y,
                             int M, int N, int K, const skinny_launch &l,
-                            DeviceState &st, const Publish &pub, hipStream_t stream);
+                            float *partials, const Publish &pub, hipStream_t stream);
 hipError_t launch_gemm_blocks(const uint16_t *x, const uint16_t *w, uint16_t *y,
                               int M, int N, int K, const skinny_launch &l,
-                              DeviceState &st, const Publish &pub, hipStream_t stream);
+                              float *partials, const Publish &pub, hipStream_t stream);
 hipError_t launch_gemm_ring(const RingItems &items, int count, int M, int N, int K,
                             const skinny_ring_launch &r, hipStream_t stream);
 hipError_t launch_split_reduce(const float *partials, uint16_t *y, int M, int N, int S,

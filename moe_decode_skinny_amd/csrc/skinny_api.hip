@@ -21,6 +21,13 @@ namespace {
 
 thread_local char g_error[512] = "";
 
+// Split-K partials of skinny_gemm_bf16_noalloc: a static array of the code
+// object, so that the call needs no allocation.  Each device holds its own
+// copy until the process ends; in host code this name is only a handle for
+// hipGetSymbolAddress (skinny_init keeps each device's address in its
+// DeviceState), never a device address to pass to a kernel.
+__device__ __align__(256) float scratch[kScratchFloats];
+
 constexpr int kMaxDevices = 64;
 DeviceState g_state[kMaxDevices];
 std::mutex g_init_mutex;
@@ -576,23 +583,27 @@ static int gemm_pointers(const void *x, const void *W, const void *y, int M, int
   return SKINNY_OK;
 }
 
+// `use_scratch`: the split-K partials go to the device's static scratch array
+// instead of the workspace skinny_init allocated (skinny_gemm_bf16_noalloc).
 static int gemm_common(const void *x, const void *W, void *y, int M, int N, int K,
-                       const skinny_launch &l, void *stream, const Publish &pub = Publish{}) {
+                       const skinny_launch &l, void *stream, const Publish &pub = Publish{},
+                       bool use_scratch = false) {
   int st = gemm_pointers(x, W, y, M, N, K);
   if (st) return st;
   DeviceState *ds = current_state(&st);
   if (!ds) return st;
+  float *partials = use_scratch ? ds->scratch : ds->partials;
   const uint16_t *xp = static_cast<const uint16_t *>(x);
   const uint16_t *wp = static_cast<const uint16_t *>(W);
   uint16_t *yp = static_cast<uint16_t *>(y);
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t e;
   if (l.path == SKINNY_PATH_MFMA)
-    e = launch_gemm_mfma(xp, wp, yp, M, N, K, l, *ds, pub, s);
+    e = launch_gemm_mfma(xp, wp, yp, M, N, K, l, partials, pub, s);
   else if (l.path == SKINNY_PATH_MFMA_4X4)
-    e = launch_gemm_blocks(xp, wp, yp, M, N, K, l, *ds, pub, s);
+    e = launch_gemm_blocks(xp, wp, yp, M, N, K, l, partials, pub, s);
   else
-    e = launch_gemm_dot2(xp, wp, yp, M, N, K, l, *ds, pub, s);
+    e = launch_gemm_dot2(xp, wp, yp, M, N, K, l, partials, pub, s);
   if (e != hipSuccess) return fail(SKINNY_ELAUNCH, "launch failed: %s", hipGetErrorString(e));
   return SKINNY_OK;
 }
@@ -671,7 +682,7 @@ using namespace skinny;
 
 extern "C" {
 
-int skinny_version(void) { return 106; }
+int skinny_version(void) { return 107; }
 
 const char *skinny_last_error(void) { return g_error; }
 
@@ -696,12 +707,15 @@ int skinny_init(int device) {
   int status = SKINNY_OK;
   if (hipMalloc(&st.partials, kWorkspaceFloats * sizeof(float)) != hipSuccess ||
       hipMalloc(&st.norm_partials, kNormPartials * sizeof(double)) != hipSuccess ||
+      hipGetSymbolAddress(reinterpret_cast<void **>(&st.scratch), HIP_SYMBOL(scratch)) !=
+          hipSuccess || !st.scratch ||
       mfma_prepare() != hipSuccess || ring_prepare() != hipSuccess ||
       hipDeviceSynchronize() != hipSuccess) {
     status = fail(SKINNY_ELAUNCH, "workspace allocation failed on device %d", device);
     // leave the device as it was: a later skinny_init may try again
     if (st.partials && hipFree(st.partials) == hipSuccess) st.partials = nullptr;
     if (st.norm_partials && hipFree(st.norm_partials) == hipSuccess) st.norm_partials = nullptr;
+    st.scratch = nullptr;
   } else {
     st.ready.store(true, std::memory_order_release);
   }
@@ -742,6 +756,25 @@ int skinny_gemm_bf16(const void *x, const void *W, void *y, int M, int N, int K,
   int st = choose(M, N, K, splits, &l, &w);
   if (st) return st;
   if (!w.segment) return gemm_common(x, W, y, M, N, K, l, stream);
+  st = gemm_pointers(x, W, y, M, N, K);
+  if (st) return st;
+  const void *xs[1] = {x}, *ws[1] = {W};
+  void *ys[1] = {y};
+  return ring_common(xs, ws, ys, 1, M, N, K, walk_launch(l, w), stream);
+}
+
+int skinny_gemm_bf16_noalloc(const void *x, const void *W, void *y, int M, int N, int K,
+                             int splits, void *stream) {
+  skinny_launch l;
+  Walk w;
+  int st = choose(M, N, K, splits, &l, &w);
+  if (st) return st;
+  if (l.splits > 1 && (size_t)l.splits * M * N > kScratchFloats)
+    return fail(SKINNY_EUNSUPPORTED, "splits=%d x M=%d x N=%d = %zu partials exceed the "
+                "static scratch of %zu floats (skinny_gemm_bf16 has a larger workspace)",
+                l.splits, M, N, (size_t)l.splits * M * N, kScratchFloats);
+  if (!w.segment) return gemm_common(x, W, y, M, N, K, l, stream, Publish{}, true);
+  // a walk is the ring kernel, which needs no partials
   st = gemm_pointers(x, W, y, M, N, K);
   if (st) return st;
   const void *xs[1] = {x}, *ws[1] = {W};
