@@ -28,6 +28,21 @@ constexpr size_t kWorkspaceFloats = size_t(2) << 20;  // 8 MiB
 // The same partials for skinny_gemm_bf16_noalloc, in a static device array of
 // the library (no allocation): S * M * N floats at most.
 constexpr size_t kScratchFloats = size_t(1) << 18;  // 1 MiB
+// Counter words of the 16-block path's in-kernel split hand-off, one per
+// output group, each on its own 256-byte stretch (arrivals of different
+// groups then do not contend for one cache line); zero between calls.
+constexpr int kMaxHandoffGroups = 2048;
+constexpr int kCounterStride = 64;  // words
+constexpr size_t kCounterWords = (size_t)kMaxHandoffGroups * kCounterStride;  // 512 KiB
+
+// Where a GEMM call's split-K scratch lives (the skinny_init workspace, or
+// the static scratch array of skinny_gemm_bf16_noalloc).
+struct Workspace {
+  float *partials = nullptr;     // FP32 partials
+  size_t partial_floats = 0;     // their capacity
+  unsigned *counters = nullptr;  // kCounterWords hand-off counters, zero between calls
+  bool force_recompute = false;  // test hook: the hand-off always recomputes the splits
+};
 
 constexpr size_t kMaxDynamicLds = 160 * 1024;  // all of a gfx950 CU's LDS
 
@@ -91,6 +106,9 @@ __device__ __forceinline__ float bf16_lo(unsigned u) { return __uint_as_float(u 
 constexpr unsigned kBufferFlags = 0x00020000u;  // gfx9 dword3: 32-bit data format
 constexpr int kOutOfRange = 0x7FFFF000;         // an offset past any resource used here
 constexpr int kCacheNT = 2;                     // nontemporal (streaming) load policy
+// s_getreg operand of the XCC_ID hardware register, bits 3..0 (the XCD a
+// wave runs on).
+constexpr int kHwRegXccId = 20 | (0 << 6) | ((4 - 1) << 11);
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void *base, unsigned bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes,

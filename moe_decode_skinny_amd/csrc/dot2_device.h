@@ -114,17 +114,17 @@ __device__ __forceinline__ void xor4_step(float *v, int lane) {
   }
 }
 
-// Reduce-scatter of R values per lane (R a power of two, <= 32) over the 16
+// Reduce-scatter of R values per lane (R a power of two, <= 64) over the 16
 // lanes that share bits 1..0 of their index (the 16 blocks of a
 // v_mfma_f32_4x4x4_16b_bf16 result; bits 1..0 index a block's column).
 // Steps pair lane l with l ^ 32, l ^ 16 (permlane swaps), l ^ 8 (DPP
 // row_ror:8) and l ^ 4, halving the values while more than one is left, as
 // in wave_reduce_scatter; afterwards a lane holds the full 16-lane sums of
-// value index lane >> (6 - log2 R) for R <= 16, and of indices
-// 2 (lane >> 2) and 2 (lane >> 2) + 1 in v[0], v[1] for R = 32.
+// value index lane >> (6 - log2 R) for R <= 16, and for R = 32 or 64 of
+// indices U (lane >> 2) + u in v[u], u < U = R / 16.
 template <int R>
 __device__ __forceinline__ void block_reduce_scatter(float *v, int lane) {
-  static_assert(R >= 1 && R <= 32 && (R & (R - 1)) == 0, "R must be a power of two <= 32");
+  static_assert(R >= 1 && R <= 64 && (R & (R - 1)) == 0, "R must be a power of two <= 64");
   constexpr int c0 = R, c1 = halve(c0), c2 = halve(c1), c3 = halve(c2);
   swap_step<c0, 32>(v);
   swap_step<c1, 16>(v);

@@ -4,13 +4,23 @@
 // lane layout and the order of the sums are in blocks_device.h).
 //   wave w of workgroup (group, s) owns K range (s * waves + w) * kw,
 //   kw = 128 * CHUNKS (CHUNKS 4 or 8: whole 512-K load groups), of the
-//   workgroup's 4 * R4 weight rows, and all M tokens in Q sets of 4; weights
-//   are loaded first, then activations, then both are transposed into the
-//   MFMA layout inside each 4-lane group.
+//   workgroup's 4 * R4 weight rows, and all M tokens in Q sets of 4; the
+//   activations are loaded first, then the weights, and both are transposed
+//   into the MFMA layout inside each 4-lane group, activations first.
+// Load order: the pages load weights ahead of the activations so that the
+// weight stream can start before the previous kernel ends.  Inside one
+// launch on gfx950 the activations (L2 hits after the first compute unit of
+// an XCD fetched them) are issued first instead: vector loads complete in
+// issue order, so their transposes, four VALU instructions per loaded dword
+// and most of a wave's VALU work at 9..16 tokens, then run while the weights
+// are still streaming from HBM instead of after them.  The arithmetic and
+// its order are the same either way.
 // Reduction in an order fixed by the launch shape (module description): the
 // 16 blocks across lanes, waves 0..waves-1 in order through LDS, and with
-// S > 1 an FP32 partial per split that split_reduce.hip sums s = 0..S-1 in
-// order.
+// S > 1 an FP32 partial per split, the splits summed s = 0..S-1 in order by
+// the last of the group's S workgroups to finish (see block_handoff), or,
+// for launches with more groups than the hand-off counters cover, by the
+// split_reduce kernel; both give the same bits.
 //
 // Against DOT2 this replaces 4 VALU instructions per (row, token, 8 K) and a
 // 64-lane reduce-scatter with one MFMA per (row set, token set, 4 K x 16
@@ -24,20 +34,104 @@ namespace {
 
 using namespace blocks;
 
+// One wave's K slice of split s: wave v of the workgroup covers K from
+// (s * waves + v) * kw.  Loads (activations first), transposes and products,
+// then the 16-block sum into red[v] (kOutputs values).
+template <int R4, int CHUNKS, int Q>
+__device__ __forceinline__ void wave_slice(const uint16_t *__restrict__ x,
+                                           const uint16_t *__restrict__ w, int M, int K, int f0,
+                                           int s, int v, int waves, int kw, int lane,
+                                           float *red) {
+  constexpr int ROWS = 4 * R4;
+  const int k0 = (s * waves + v) * kw + lane * 8;
+  u32x4 wv[R4][CHUNKS], xv[Q][CHUNKS];
+  load_sets<Q, CHUNKS, 0>(xv, buffer_rsrc(x, (unsigned)(M * K * 2)), K, k0);
+  __builtin_amdgcn_sched_barrier(0);
+  load_sets<R4, CHUNKS, kCacheNT>(wv, buffer_rsrc(w + (size_t)f0 * K, (unsigned)(ROWS * K * 2)),
+                                  K, k0);
+  __builtin_amdgcn_sched_barrier(0);
+  transpose_sets<Q, CHUNKS>(xv, lane);
+  __builtin_amdgcn_sched_barrier(0);
+  transpose_sets<R4, CHUNKS>(wv, lane);
+  f32x4 acc[Q][R4];
+  products<R4, CHUNKS, Q>(wv, xv, acc);
+  reduce_to_lds<R4, Q>(acc, red, lane);
+}
+
+// Output o = i * 64 + lane (i < kPer) summed over the waves' slices in wave
+// order.
+template <int kOut, int kPer>
+__device__ __forceinline__ void sum_waves(float (*red)[kOut], int waves, int lane, float *part) {
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) {
+    const int o = i * 64 + lane;
+    float p = 0.f;
+    if (o < kOut) {
+      p = red[0][o];
+      for (int v = 1; v < waves; ++v) p += red[v][o];
+    }
+    part[i] = p;
+  }
+}
+
+// The split hand-off of group `group` (S > 1), in wave 0 of each of its S
+// workgroups: store this split's partial, then mark the arrival in the
+// group's counter word (bit s, and bit 16 + XCD id), one atomic OR whose
+// returned value tells the last arriver.  Returns true in the last one.
+// The S workgroups of a group are dealt to one XCD (ids congruent mod 8, see
+// the kernel), so partials pass through that XCD's L2: plain stores waited
+// for before the atomic, and in the last arriver an L1 invalidate and loads
+// that bypass L1.  *mixed is set when the arrivals came from more than one
+// XCD, whose L2s do not see each other's stores; the caller then recomputes
+// the other splits instead of reading them.  The counter word is reset by
+// the last arriver, so it is zero again for the next call (no memset).
+template <int kPer>
+__device__ __forceinline__ bool block_handoff(float *__restrict__ slots,
+                                              unsigned *__restrict__ counter, int S, int s,
+                                              int kOut, int lane, const float *part,
+                                              bool *mixed) {
+  const __amdgpu_buffer_rsrc_t res = buffer_rsrc(slots, (unsigned)(S * kOut * 4));
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) {
+    const int o = i * 64 + lane;
+    if (o < kOut)
+      __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(part[i]), res, (s * kOut + o) * 4, 0,
+                                            0);
+  }
+  // every lane's stores have reached L2 before the arrival is marked
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  const unsigned xcc = __builtin_amdgcn_s_getreg(kHwRegXccId) & 7u;
+  const unsigned mine = (1u << s) | (1u << (16 + xcc));
+  unsigned old = 0;
+  if (lane == 0)
+    old = __hip_atomic_fetch_or(counter, mine, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  const unsigned all = (unsigned)__builtin_amdgcn_readfirstlane((int)old) | mine;
+  if ((all & 0xFFFFu) != (1u << S) - 1u) return false;
+  *mixed = __builtin_popcount(all >> 16) != 1;
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+  asm volatile("buffer_inv sc0" ::: "memory");  // no stale line in this CU's L1
+  if (lane == 0) __hip_atomic_store(counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  return true;
+}
+
 template <int R4, int CHUNKS, int Q, int THREADS>
 __global__ __launch_bounds__(THREADS) void gemm_blocks_kernel(
     const uint16_t *__restrict__ x, const uint16_t *__restrict__ w,
-    uint16_t *__restrict__ y, float *__restrict__ partials, int M, int N, int K,
-    int S, int groups, int kw, Publish pub) {
-  constexpr int ROWS = 4 * R4;
+    uint16_t *__restrict__ y, float *__restrict__ partials, unsigned *__restrict__ counters,
+    int M, int N, int K, int S, int groups, int kw, int force_recompute, Publish pub) {
+  constexpr int kOut = kOutputs<R4, Q>, kPer = (kOut + 63) / 64;
   const int lane = threadIdx.x & 63;
-  if (S == 1 && blockIdx.x == 0 && threadIdx.x == 0) publish_stage_word(pub);
+  if ((S == 1 || counters) && blockIdx.x == 0 && threadIdx.x == 0) publish_stage_word(pub);
   const int wave = wave_index();
   const int waves = blockDim.x >> 6;
 
+  // Workgroup -> (group, split): workgroups are dealt to the XCDs
+  // round-robin (ids congruent mod 8 share an XCD, also when the part has
+  // fewer XCDs), so with a group count divisible by 8 the S workgroups of a
+  // group share an XCD and its L2.
   int group, s;
   const int b = blockIdx.x;
-  if ((groups & 7) == 0) {  // the S workgroups of a group share an XCD
+  if ((groups & 7) == 0) {
     const int xcd = b & 7, slot = b >> 3;
     group = (slot / S) * 8 + xcd;
     s = slot % S;
@@ -45,46 +139,83 @@ __global__ __launch_bounds__(THREADS) void gemm_blocks_kernel(
     group = b / S;
     s = b % S;
   }
-  const int f0 = group * ROWS;
-  const int k0 = (s * waves + wave) * kw + lane * 8;
+  const int f0 = group * 4 * R4;
 
-  u32x4 wv[R4][CHUNKS], xv[Q][CHUNKS];
-  load_sets<R4, CHUNKS, kCacheNT>(wv, buffer_rsrc(w + (size_t)f0 * K, (unsigned)(ROWS * K * 2)),
-                                  K, k0);
-  __builtin_amdgcn_sched_barrier(0);
-  load_sets<Q, CHUNKS, 0>(xv, buffer_rsrc(x, (unsigned)(M * K * 2)), K, k0);
-  __builtin_amdgcn_sched_barrier(0);
-  transpose_sets<R4, CHUNKS>(wv, lane);
-  transpose_sets<Q, CHUNKS>(xv, lane);
-  f32x4 acc[Q][R4];
-  products<R4, CHUNKS, Q>(wv, xv, acc);
-
-  constexpr int kOut = kOutputs<R4, Q>;
   __shared__ float red[THREADS / 64][kOut];
-  reduce_to_lds<R4, Q>(acc, red[wave], lane);
+  wave_slice<R4, CHUNKS, Q>(x, w, M, K, f0, s, wave, waves, kw, lane, red[wave]);
   __syncthreads();
   if (wave != 0) return;
+  float part[kPer];
+  sum_waves<kOut, kPer>(red, waves, lane, part);
+
+  if (S > 1 && !counters) {  // FP32 partial of split s for split_reduce: [s][token][feature]
 #pragma unroll
-  for (int o0 = 0; o0 < kOut; o0 += 64) {
-    const int o = o0 + lane;
+    for (int i = 0; i < kPer; ++i) {
+      const int o = i * 64 + lane;
+      if (o >= kOut) break;
+      const int t = output_token(o, R4), r = output_row(o, R4);
+      if (t < M) partials[((size_t)s * M + t) * N + f0 + r] = part[i];
+    }
+    return;
+  }
+  if (S > 1) {
+    bool mixed = false;
+    if (!block_handoff<kPer>(partials + (size_t)group * S * kOut,
+                             counters + (size_t)group * kCounterStride, S, s, kOut, lane, part,
+                             &mixed))
+      return;
+    float sum[kPer];
+    if (!mixed && !force_recompute) {
+      const __amdgpu_buffer_rsrc_t res =
+          buffer_rsrc(partials + (size_t)group * S * kOut, (unsigned)(S * kOut * 4));
+#pragma unroll
+      for (int i = 0; i < kPer; ++i) {
+        const int o = i * 64 + lane;
+        for (int s2 = 0; s2 < S; ++s2) {
+          // bit 0 of the cache policy (sc0): served from L2, not this CU's L1
+          const float v = s2 == s ? part[i]
+                                  : __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
+                                        res, (s2 * kOut + (o < kOut ? o : 0)) * 4, 0, 1));
+          sum[i] = s2 == 0 ? v : sum[i] + v;
+        }
+      }
+    } else {
+      // Splits on several XCDs: this wave recomputes every other split's
+      // wave slices itself (the other waves have left; their LDS rows are
+      // free), with the instructions the other workgroups ran, and sums
+      // them in the same orders: the same bits.
+      for (int s2 = 0; s2 < S; ++s2) {
+        float p2[kPer];
+        if (s2 == s) {
+#pragma unroll
+          for (int i = 0; i < kPer; ++i) p2[i] = part[i];
+        } else {
+          for (int v = 0; v < waves; ++v)
+            wave_slice<R4, CHUNKS, Q>(x, w, M, K, f0, s2, v, waves, kw, lane, red[v]);
+          sum_waves<kOut, kPer>(red, waves, lane, p2);
+        }
+#pragma unroll
+        for (int i = 0; i < kPer; ++i) sum[i] = s2 == 0 ? p2[i] : sum[i] + p2[i];
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) part[i] = sum[i];
+  }
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) {
+    const int o = i * 64 + lane;
     if (o >= kOut) break;
-    float part = red[0][o];
-    for (int v2 = 1; v2 < waves; ++v2) part += red[v2][o];
     const int t = output_token(o, R4), r = output_row(o, R4);
     if (t >= M) continue;
-    if (S == 1) {
-      const unsigned bits = f32_to_bf16(part);
-      y[(size_t)t * N + f0 + r] = (uint16_t)bits;
-      if (uint16_t *slot = publish_slot(pub, N))
-        slot[(size_t)t * N + f0 + r] = (uint16_t)publish_bits(bits);
-    } else {  // FP32 partial of split s: partials[s][token][feature]
-      partials[((size_t)s * M + t) * N + f0 + r] = part;
-    }
+    const unsigned bits = f32_to_bf16(part[i]);
+    y[(size_t)t * N + f0 + r] = (uint16_t)bits;
+    if (uint16_t *slot = publish_slot(pub, N))
+      slot[(size_t)t * N + f0 + r] = (uint16_t)publish_bits(bits);
   }
 }
 
-using BlocksKernel = void (*)(const uint16_t *, const uint16_t *, uint16_t *, float *, int,
-                              int, int, int, int, int, Publish);
+using BlocksKernel = void (*)(const uint16_t *, const uint16_t *, uint16_t *, float *,
+                              unsigned *, int, int, int, int, int, int, int, Publish);
 
 // Register budget per lane: weights 4 * R4 * CHUNKS, activations
 // 4 * Q * CHUNKS, sums 4 * Q * R4 (160 at 512 threads, 112 at 1024).
@@ -144,16 +275,22 @@ bool blocks_variant_exists(int rows, int chunks, int q, int waves) {
 }
 
 hipError_t launch_gemm_blocks(const uint16_t *x, const uint16_t *w, uint16_t *y, int M,
-                              int N, int K, const skinny_launch &l, float *partials,
+                              int N, int K, const skinny_launch &l, const Workspace &ws,
                               const Publish &pub, hipStream_t stream) {
   BlocksKernel k = pick(l.rows, l.chunks, blocks_token_sets(M), l.waves);
   const int groups = N / l.rows;
+  // the in-kernel hand-off when the counters cover the groups and the
+  // partial slots fit; otherwise the two-kernel split (same sums, same order)
+  const bool handoff = l.splits > 1 && ws.counters && groups <= kMaxHandoffGroups &&
+                       (size_t)groups * l.splits * 16 * blocks_token_sets(M) * (l.rows / 4) <=
+                           ws.partial_floats;
   dim3 grid(groups * l.splits), block(64 * l.waves);
-  hipLaunchKernelGGL(k, grid, block, 0, stream, x, w, y, partials, M, N, K, l.splits,
-                     groups, kBlockK * l.chunks, pub);
+  hipLaunchKernelGGL(k, grid, block, 0, stream, x, w, y, ws.partials,
+                     handoff ? ws.counters : nullptr, M, N, K, l.splits, groups,
+                     kBlockK * l.chunks, ws.force_recompute ? 1 : 0, pub);
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess || l.splits == 1) return e;
-  return launch_split_reduce(partials, y, M, N, l.splits, pub, stream);
+  if (e != hipSuccess || l.splits == 1 || handoff) return e;
+  return launch_split_reduce(ws.partials, y, M, N, l.splits, pub, stream);
 }
 
 }  // namespace skinny

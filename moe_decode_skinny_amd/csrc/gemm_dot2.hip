@@ -196,7 +196,8 @@ int dot2_max_waves() { return 16; }
 
 hipError_t launch_gemm_dot2(const uint16_t *x, const uint16_t *w, uint16_t *y,
                             int M, int N, int K, const skinny_launch &l,
-                            float *partials, const Publish &pub, hipStream_t stream) {
+                            const Workspace &ws, const Publish &pub, hipStream_t stream) {
+  float *partials = ws.partials;
   Dot2Kernel k = pick(l.rows, l.chunks, dot2_token_tile(M), l.waves);
   const int groups = N / l.rows;
   dim3 grid(groups * l.splits), block(64 * l.waves);

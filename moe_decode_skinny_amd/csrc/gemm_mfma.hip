@@ -217,7 +217,8 @@ size_t mfma_lds_bytes(int M, const skinny_launch &l) {
 
 hipError_t launch_gemm_mfma(const uint16_t *x, const uint16_t *w, uint16_t *y,
                             int M, int N, int K, const skinny_launch &l,
-                            float *partials, const Publish &pub, hipStream_t stream) {
+                            const Workspace &ws, const Publish &pub, hipStream_t stream) {
+  float *partials = ws.partials;
   MfmaKernel k = pick(l.chunks, l.accs);
   const int F = l.rows / kTileN;
   const int groups = N / l.rows;

@@ -15,10 +15,16 @@ struct DeviceState {
   // on other threads read it (acquire) without taking the init lock.
   std::atomic<bool> ready{false};
   float *partials = nullptr;         // kWorkspaceFloats
+  unsigned *counters = nullptr;      // kCounterWords, zeroed by skinny_init
   double *norm_partials = nullptr;   // kNormPartials
   // This device's address of the library's static scratch array
-  // (kScratchFloats, skinny_gemm_bf16_noalloc), from hipGetSymbolAddress.
+  // (skinny_gemm_bf16_noalloc: kScratchFloats partials, then kCounterWords
+  // counters), from hipGetSymbolAddress.
   float *scratch = nullptr;
+  // Test hook, from the environment at skinny_init
+  // (SKINNY_FORCE_SPLIT_RECOMPUTE=1): the 16-block split hand-off takes its
+  // cross-XCD path (recompute every split) on every call.
+  bool force_recompute = false;
 };
 
 // The state of the current HIP device, or nullptr (and a reason) if the
@@ -28,16 +34,16 @@ DeviceState *current_state(int *status);
 
 // ------------------------------------------------------------- launchers
 // Each returns hipSuccess or the launch error; arguments are already valid.
-// `partials`: the split-K workspace (S * M * N floats), used when l.splits > 1.
+// `ws`: the split-K scratch, used when l.splits > 1.
 hipError_t launch_gemm_mfma(const uint16_t *x, const uint16_t *w, uint16_t *y,
                             int M, int N, int K, const skinny_launch &l,
-                            float *partials, const Publish &pub, hipStream_t stream);
+                            const Workspace &ws, const Publish &pub, hipStream_t stream);
 hipError_t launch_gemm_dot2(const uint16_t *x, const uint16_t *w, uint16_t *y,
                             int M, int N, int K, const skinny_launch &l,
-                            float *partials, const Publish &pub, hipStream_t stream);
+                            const Workspace &ws, const Publish &pub, hipStream_t stream);
 hipError_t launch_gemm_blocks(const uint16_t *x, const uint16_t *w, uint16_t *y,
                               int M, int N, int K, const skinny_launch &l,
-                              float *partials, const Publish &pub, hipStream_t stream);
+                              const Workspace &ws, const Publish &pub, hipStream_t stream);
 hipError_t launch_gemm_ring(const RingItems &items, int count, int M, int N, int K,
                             const skinny_ring_launch &r, hipStream_t stream);
 hipError_t launch_split_reduce(const float *partials, uint16_t *y, int M, int N, int S,

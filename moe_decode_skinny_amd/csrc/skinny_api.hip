@@ -21,12 +21,14 @@ namespace {
 
 thread_local char g_error[512] = "";
 
-// Split-K partials of skinny_gemm_bf16_noalloc: a static array of the code
-// object, so that the call needs no allocation.  Each device holds its own
-// copy until the process ends; in host code this name is only a handle for
+// Split-K scratch of skinny_gemm_bf16_noalloc: a static array of the code
+// object, so that the call needs no allocation: kScratchFloats FP32
+// partials, then kCounterWords hand-off counters (zeroed by skinny_init,
+// zero again after every call).  Each device holds its own copy until the
+// process ends; in host code this name is only a handle for
 // hipGetSymbolAddress (skinny_init keeps each device's address in its
 // DeviceState), never a device address to pass to a kernel.
-__device__ __align__(256) float scratch[kScratchFloats];
+__device__ __align__(256) float scratch[kScratchFloats + kCounterWords];
 
 constexpr int kMaxDevices = 64;
 DeviceState g_state[kMaxDevices];
@@ -187,7 +189,7 @@ static const TableEntry kTable[] = {
     {1024, 4096, 1, 1, {SKINNY_PATH_DOT2, 1, 2, 4, 1, 2}, {}},
     {1024, 4096, 2, 2, {SKINNY_PATH_DOT2, 1, 2, 4, 1, 2}, {2, 256}},
     {1024, 4096, 3, 4, {SKINNY_PATH_DOT2, 1, 4, 2, 1, 2}, {2, 256}},
-    {1024, 4096, 5, 8, {SKINNY_PATH_DOT2, 1, 4, 2, 1, 4}, {}},
+    {1024, 4096, 5, 8, {SKINNY_PATH_MFMA_4X4, 1, 4, 8, 1, 4}, {}},
     {1024, 4096, 9, 16, {SKINNY_PATH_MFMA_4X4, 1, 8, 4, 1, 4}, {}},
     // o_proj shard
     {8192, 1024, 1, 1, {SKINNY_PATH_DOT2, 1, 1, 2, 1, 2}, {}},
@@ -197,11 +199,11 @@ static const TableEntry kTable[] = {
     // pooler shard
     {512, 8192, 1, 4, {SKINNY_PATH_DOT2, 1, 4, 4, 1, 2}, {}},
     {512, 8192, 5, 8, {SKINNY_PATH_DOT2, 1, 8, 2, 1, 2}, {}},
-    {512, 8192, 9, 16, {SKINNY_PATH_DOT2, 1, 16, 1, 1, 2}, {}},
+    {512, 8192, 9, 16, {SKINNY_PATH_MFMA_4X4, 4, 4, 4, 1, 4}, {}},
     // full pooler
     {4096, 8192, 1, 1, {SKINNY_PATH_DOT2, 1, 8, 2, 1, 2}, {}},
     {4096, 8192, 2, 2, {SKINNY_PATH_DOT2, 1, 8, 2, 1, 8}, {}},
-    {4096, 8192, 3, 4, {SKINNY_PATH_MFMA_4X4, 1, 16, 4, 1, 8}, {}},
+    {4096, 8192, 3, 4, {SKINNY_PATH_MFMA_4X4, 1, 8, 8, 1, 8}, {}},
     {4096, 8192, 5, 8, {SKINNY_PATH_MFMA_4X4, 1, 8, 8, 1, 4}, {4, 256}},
     {4096, 8192, 9, 16, {SKINNY_PATH_MFMA_4X4, 1, 16, 4, 1, 4}, {4, 256}},
 };
@@ -592,18 +594,23 @@ static int gemm_common(const void *x, const void *W, void *y, int M, int N, int 
   if (st) return st;
   DeviceState *ds = current_state(&st);
   if (!ds) return st;
-  float *partials = use_scratch ? ds->scratch : ds->partials;
+  Workspace ws;
+  ws.partials = use_scratch ? ds->scratch : ds->partials;
+  ws.partial_floats = use_scratch ? kScratchFloats : kWorkspaceFloats;
+  ws.counters = use_scratch ? reinterpret_cast<unsigned *>(ds->scratch + kScratchFloats)
+                            : ds->counters;
+  ws.force_recompute = ds->force_recompute;
   const uint16_t *xp = static_cast<const uint16_t *>(x);
   const uint16_t *wp = static_cast<const uint16_t *>(W);
   uint16_t *yp = static_cast<uint16_t *>(y);
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t e;
   if (l.path == SKINNY_PATH_MFMA)
-    e = launch_gemm_mfma(xp, wp, yp, M, N, K, l, partials, pub, s);
+    e = launch_gemm_mfma(xp, wp, yp, M, N, K, l, ws, pub, s);
   else if (l.path == SKINNY_PATH_MFMA_4X4)
-    e = launch_gemm_blocks(xp, wp, yp, M, N, K, l, partials, pub, s);
+    e = launch_gemm_blocks(xp, wp, yp, M, N, K, l, ws, pub, s);
   else
-    e = launch_gemm_dot2(xp, wp, yp, M, N, K, l, partials, pub, s);
+    e = launch_gemm_dot2(xp, wp, yp, M, N, K, l, ws, pub, s);
   if (e != hipSuccess) return fail(SKINNY_ELAUNCH, "launch failed: %s", hipGetErrorString(e));
   return SKINNY_OK;
 }
@@ -682,7 +689,7 @@ using namespace skinny;
 
 extern "C" {
 
-int skinny_version(void) { return 107; }
+int skinny_version(void) { return 108; }
 
 const char *skinny_last_error(void) { return g_error; }
 
@@ -705,16 +712,22 @@ int skinny_init(int device) {
   if (hipGetDevice(&prev) != hipSuccess) prev = device;
   if (hipSetDevice(device) != hipSuccess) return fail(SKINNY_EDEVICE, "cannot select device %d", device);
   int status = SKINNY_OK;
+  const char *force = getenv("SKINNY_FORCE_SPLIT_RECOMPUTE");
+  st.force_recompute = force && force[0] == '1';
   if (hipMalloc(&st.partials, kWorkspaceFloats * sizeof(float)) != hipSuccess ||
+      hipMalloc(&st.counters, kCounterWords * sizeof(unsigned)) != hipSuccess ||
+      hipMemset(st.counters, 0, kCounterWords * sizeof(unsigned)) != hipSuccess ||
       hipMalloc(&st.norm_partials, kNormPartials * sizeof(double)) != hipSuccess ||
       hipGetSymbolAddress(reinterpret_cast<void **>(&st.scratch), HIP_SYMBOL(scratch)) !=
           hipSuccess || !st.scratch ||
+      hipMemset(st.scratch + kScratchFloats, 0, kCounterWords * sizeof(unsigned)) != hipSuccess ||
       mfma_prepare() != hipSuccess || ring_prepare() != hipSuccess ||
       hipDeviceSynchronize() != hipSuccess) {
     status = fail(SKINNY_ELAUNCH, "workspace allocation failed on device %d", device);
     // leave the device as it was: a later skinny_init may try again
     if (st.partials && hipFree(st.partials) == hipSuccess) st.partials = nullptr;
     if (st.norm_partials && hipFree(st.norm_partials) == hipSuccess) st.norm_partials = nullptr;
+    if (st.counters && hipFree(st.counters) == hipSuccess) st.counters = nullptr;
     st.scratch = nullptr;
   } else {
     st.ready.store(true, std::memory_order_release);

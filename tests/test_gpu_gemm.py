@@ -321,3 +321,86 @@ def test_random_shapes_through_the_choosers(gpu_lib):
         for i in (0, count - 1):
             ref_i = oracle.gemm_bf16(from_dev(xs[i]), from_dev(ws[i]), THREADS)
             assert_gemm_close(from_dev(ys[i]), ref_i, f"case {case} ring item {i}")
+
+
+def test_blocks_split_in_kernel_equals_the_two_kernel_split(gpu_lib):
+    """The 16-block path sums its splits inside the kernel (the last of a
+    group's workgroups to finish) when the hand-off counters cover the
+    groups (2048), else with the split-reduce kernel; both sum s = 0..S-1
+    in order, so output blocks computed either way are equal bit for bit.
+    N = 16384 at 4 rows is 4096 groups (two kernels); its first 8192
+    columns as their own call are 2048 groups (in-kernel)."""
+    import torch
+
+    M, K = 16, 2048
+    x_bits, w_bits = synthetic.gemm_inputs(N=16384, K=K, seed=41)
+    x, w = to_dev(x_bits[:M]), to_dev(w_bits)
+    for splits in (2, 4):
+        launch = gpu_lib.Launch(3, splits, -(-K // (splits * 512)), 4, 1, 4)
+        _say(f"16-block split S={splits}: 4096 groups against 2048")
+        y_two = torch.empty((M, 16384), dtype=torch.bfloat16, device="cuda")
+        y_one = torch.empty((M, 8192), dtype=torch.bfloat16, device="cuda")
+        gpu_lib.skinny_gemm_bf16_launch(x, w, y_two, launch)
+        gpu_lib.skinny_gemm_bf16_launch(x, w[:8192], y_one, launch)
+        torch.cuda.synchronize()
+        assert np.array_equal(from_dev(y_one), from_dev(y_two)[:, :8192])
+        cols = np.arange(0, 16384, 97)
+        rows = np.arange(M).repeat(cols.size)
+        ref, _ = oracle.gemm_bf16_sampled(x_bits[:M], w_bits, rows, np.tile(cols, M))
+        assert_gemm_close(from_dev(y_two)[:, cols].ravel(), ref, f"S={splits} sampled")
+
+
+_RECOMPUTE_CHILD = r"""
+import sys, numpy as np, torch
+sys.path.insert(0, sys.argv[1])
+import moe_decode_skinny_amd as sk, synthetic
+from tests.helpers import to_dev, from_dev
+sk.init(0)
+out = {}
+for i, (M, N, K, S) in enumerate(CASES):
+    x, w = synthetic.gemm_inputs(N=N, K=K, seed=50 + i)
+    y = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+    launch = sk.Launch(3, S, -(-K // (S * 512)), 4, 1, 4)
+    sk.skinny_gemm_bf16_launch(to_dev(x[:M]), to_dev(w), y, launch)
+    if S == 2:
+        y2 = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+        sk.skinny_gemm_bf16(to_dev(x[:M]), to_dev(w), y2, 0)
+        torch.cuda.synchronize()
+        out[f"chooser{i}"] = from_dev(y2)
+    torch.cuda.synchronize()
+    out[f"case{i}"] = from_dev(y)
+np.savez(sys.argv[2], **out)
+print("child done", flush=True)
+"""
+_RECOMPUTE_CASES = [(16, 512, 8192, 2), (9, 1024, 4096, 4), (16, 48, 1000, 2), (5, 256, 6000, 8)]
+
+
+def test_blocks_split_recompute_path_is_bitwise_the_handoff(gpu_lib, tmp_path):
+    """When a group's split workgroups ran on more than one XCD, the last of
+    them recomputes every split itself (same instructions, same order)
+    instead of reading partials another XCD's L2 holds.  A child process
+    with SKINNY_FORCE_SPLIT_RECOMPUTE=1 takes that path on every call; its
+    outputs must equal this process's bit for bit."""
+    import subprocess
+
+    import torch
+
+    out = tmp_path / "child.npz"
+    env = dict(os.environ, SKINNY_FORCE_SPLIT_RECOMPUTE="1")
+    code = _RECOMPUTE_CHILD.replace("CASES", repr(_RECOMPUTE_CASES))
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    _say("child process with SKINNY_FORCE_SPLIT_RECOMPUTE=1")
+    res = subprocess.run([sys.executable, "-c", code, root, str(out)], env=env,
+                         capture_output=True, text=True, timeout=300)
+    assert res.returncode == 0, res.stdout[-2000:] + res.stderr[-2000:]
+    child = np.load(out)
+    for i, (M, N, K, S) in enumerate(_RECOMPUTE_CASES):
+        x, w = synthetic.gemm_inputs(N=N, K=K, seed=50 + i)
+        launch = gpu_lib.Launch(3, S, -(-K // (S * 512)), 4, 1, 4)
+        y = _run(gpu_lib, x, w, M, launch=launch)
+        _say(f"recompute case {i}: M={M} N={N} K={K} S={S}")
+        assert np.array_equal(child[f"case{i}"], y), f"case {i}"
+        assert_gemm_close(y, oracle.gemm_bf16(x[:M], w, THREADS), f"case {i}")
+        if S == 2:
+            assert np.array_equal(child[f"chooser{i}"], _run(gpu_lib, x, w, M)), f"chooser {i}"
+    torch.cuda.synchronize()
