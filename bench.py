@@ -85,55 +85,423 @@ def ring_source_digest() -> str:
     return h.hexdigest()[:16]
 
 
-def ring_traffic(M: int, sk=None):
-    """HBM bytes per ring item from the committed counter summary, or None if
-    the ring kernels, or the launch the ring chooser picks, changed since the
-    counters were taken."""
-    path = os.path.join(HERE, "profiles", "hbm_traffic_ring_unpooler.json")
+def _summary(name: str):
     try:
-        with open(path) as f:
-            rec = json.load(f)
-    except OSError:
+        with open(os.path.join(HERE, "profiles", name)) as f:
+            return json.load(f)
+    except (OSError, ValueError):
         return None
-    if rec.get("kernel_source_digest") != ring_source_digest():
-        return None
-    e = rec["per_m"].get(str(M))
-    if e is None:
-        return None
-    if sk is not None:
-        r = sk.skinny_ring_choose(M, N, K, RING)
-        now = {**dict(r.gemm._asdict()), "segment": r.segment, "workgroups": r.workgroups,
-               "order": r.order}
-        if e.get("launch") != now:
-            return None
-    return e["hbm_bytes_per_item"]
 
 
-def measured_traffic(M: int, sk=None):
-    """HBM bytes per launch of the M=<M> sweep kernel from the committed
+def _ring_launch_record(sk, M: int, n: int = N, k: int = K) -> dict:
+    r = sk.skinny_ring_choose(M, n, k, RING)
+    return {**dict(r.gemm._asdict()), "segment": r.segment, "workgroups": r.workgroups,
+            "order": r.order}
+
+
+def ring_traffic(M: int, sk=None):
+    """HBM bytes per ring item (unpooler shard) from the committed counter
+    summary, or None if the ring kernels, or the launch the ring chooser
+    picks, changed since the counters were taken."""
+    rec = _summary("hbm_traffic_shapes.json")
+    if not rec or rec.get("ring_source_digest") != ring_source_digest():
+        return None
+    for e in rec["entries"]:
+        if e["ring"] and e["shape"] == "unpooler" and e["M"] == M:
+            if sk is not None and e["launch"] != _ring_launch_record(sk, M):
+                return None
+            return e["hbm_bytes_per_item"]
+    return None
+
+
+def measured_traffic(M: int, sk=None, shape: str = "unpooler"):
+    """HBM bytes per call of the shape's chooser call from the committed
     counter summary (FETCH_SIZE + WRITE_SIZE, scaled by the plain-copy
     reference), or None when the kernels, or the launch and walk the chooser
     picks, changed since it was taken."""
-    path = os.path.join(HERE, "profiles", "hbm_traffic_unpooler_sweep.json")
-    try:
-        with open(path) as f:
-            rec = json.load(f)
-    except (OSError, ValueError):
+    rec = _summary("hbm_traffic_shapes.json")
+    if not rec or rec.get("kernel_source_digest") != kernel_source_digest():
         return None
-    if rec.get("kernel_source_digest") != kernel_source_digest():
+    n, k, _ = SHAPES[shape]
+    for e in rec["entries"]:
+        if not e["ring"] and e["shape"] == shape and e["M"] == M:
+            if sk is not None and e["launch"] != walk_record(sk, M, n, k):
+                return None
+            return e["hbm_bytes_per_item"]
+    return None
+
+
+def traced_call(M: int, sk=None, shape: str = "unpooler"):
+    """The kernel-trace figures of the shape's chooser call at M from the
+    committed summary (median / p10 / p90 us per dispatch, dispatches), or
+    None when the kernels or the chooser's launch changed since."""
+    rec = _summary("kernel_trace_shapes.json")
+    if not rec or rec.get("kernel_source_digest") != kernel_source_digest():
         return None
-    per_m = rec.get("per_m", {}).get(str(M))
-    if per_m is None:
-        return None
-    if sk is not None and per_m.get("walk") != walk_record(sk, M, N, K):
-        return None
-    return per_m.get("hbm_bytes_per_launch")
+    n, k, _ = SHAPES[shape]
+    for e in rec["entries"]:
+        if e["shape"] == shape and e["M"] == M:
+            if sk is not None and e["launch"] != walk_record(sk, M, n, k):
+                return None
+            ks = e["kernels"]
+            return {"median_us": e["call_median_us"],
+                    "p10_us": round(sum(kk["p10"] for kk in ks), 3),
+                    "p90_us": round(sum(kk["p90"] for kk in ks), 3),
+                    "dispatches": min(kk["n"] for kk in ks),
+                    "kernels": [kk["kernel"] for kk in ks],
+                    "source": "profiles/kernel_trace_shapes.json"}
+    return None
 
 
 def walk_record(sk, M: int, n: int, k: int) -> dict:
     """The launch and walk skinny_gemm_bf16 runs (segment 0: the plain kernel)."""
     w = sk.skinny_choose_walk(M, n, k, 0)
     return {**dict(w.gemm._asdict()), "segment": w.segment, "workgroups": w.workgroups}
+
+
+# ---------------------------------------------------------------- profiling
+# Shapes profiled one per rocprofv3 run, so that rows of a kernel trace or a
+# counter collection belong to exactly one (shape, M): the pages' shards, each
+# on its own 60-layer weight ring (weight seeds as in the timing below).
+SHAPES = {"unpooler": (1024, 4096, 1000), "oproj": (8192, 1024, 7000),
+          "pooler_shard": (512, 8192, 7100), "pooler_full": (4096, 8192, 7200)}
+TRACE_SET = ([("unpooler", m) for m in MS] + [("oproj", m) for m in (1, 8, 16)]
+             + [("pooler_shard", m) for m in (1, 8, 16)] + [("pooler_full", m) for m in (1, 8, 16)])
+COUNTER_SET = [("unpooler", m) for m in MS] + [("oproj", 16), ("pooler_shard", 16),
+                                                ("pooler_full", 8)]
+RING_COUNTER_SET = [("unpooler", m) for m in MS]
+# rocprofv3 --pmc passes (each within one run's counter limits: <= 4 TCC).
+COUNTER_PASSES = {
+    "fetch": ["FETCH_SIZE"],
+    "write": ["WRITE_SIZE"],
+    "rdreq": ["TCC_EA0_RDREQ_32B_sum", "TCC_EA0_RDREQ_64B_sum", "TCC_EA0_RDREQ_128B_sum",
+              "TCC_EA0_RDREQ_sum"],
+    "dram": ["TCC_EA0_RDREQ_DRAM_32B_sum", "TCC_EA0_WRREQ_WRITE_DRAM_32B_sum"],
+    "util": ["MfmaUtil", "VALUBusy"],
+}
+TRACE_PASSES = 12  # ring passes timed per trace run: 12 x 60 = 720 dispatches of the call
+COPY_MIB = 64      # the plain device copy that scales byte counters
+
+
+def profile_runs(root="gpurun_out/prof"):
+    """(run directory, rocprofv3 arguments, bench.py arguments) of every
+    profiling run, in order."""
+    runs = []
+    for name, M in TRACE_SET:
+        d = f"{root}/trace_{name}_m{M}"
+        runs.append((d, ["--kernel-trace", "--stats"],
+                     ["--profile-shape", f"{name}:{M}", "--passes", str(TRACE_PASSES)]))
+    for pas in ("fetch", "write", "rdreq", "dram"):
+        for name, M in COUNTER_SET:
+            d = f"{root}/{pas}_{name}_m{M}"
+            runs.append((d, ["--pmc", *COUNTER_PASSES[pas]],
+                         ["--profile-shape", f"{name}:{M}", "--passes", "1",
+                          "--copy-mib", str(COPY_MIB)]))
+        if pas in ("fetch", "write"):
+            for name, M in RING_COUNTER_SET:
+                d = f"{root}/{pas}_ring_{name}_m{M}"
+                runs.append((d, ["--pmc", *COUNTER_PASSES[pas]],
+                             ["--profile-shape", f"ring:{name}:{M}", "--passes", "1",
+                              "--copy-mib", str(COPY_MIB)]))
+    for name, M in [("unpooler", m) for m in MS] + [("pooler_shard", 16)]:
+        d = f"{root}/util_{name}_m{M}"
+        runs.append((d, ["--pmc", *COUNTER_PASSES["util"]],
+                     ["--profile-shape", f"{name}:{M}", "--passes", "1"]))
+    return runs
+
+
+def profile_command(d, prof_args, bench_args) -> str:
+    return (f"timeout -s KILL 120 rocprofv3 {' '.join(prof_args)} --output-format csv -d {d} "
+            f"-o run -- python3 -u bench.py {' '.join(bench_args)} --profile-out {d}")
+
+
+def profile_shape(spec: str, passes: int, out_dir: str, copy_mib: int) -> None:
+    """One shape's calls for a profiler run: the chooser's call (skinny_gemm_bf16)
+    or, for ring:<shape>:<M>, one 60-item ring launch (skinny_gemm_bf16_ring),
+    over the shape's 60-layer weight ring: an eager warm-up, then graphs of
+    one ring pass replayed 3 + `passes` times.  Writes out_dir/shape.json."""
+    import torch
+
+    import moe_decode_skinny_amd as sk
+    import synthetic
+
+    parts = spec.split(":")
+    ring_launch = parts[0] == "ring"
+    name, M = parts[-2], int(parts[-1])
+    n, k, wseed = SHAPES[name]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    sk.skinny_init(0)
+    if copy_mib:
+        src = torch.empty(copy_mib << 20, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+    ring = synthetic.device_weight_ring(RING, n, k, dev, base_seed=wseed)
+    if ring_launch:
+        xs = [synthetic.to_device(synthetic.gemm_inputs(N=16, K=k, seed=900 + i)[0][:M], dev)
+              for i in range(RING)]
+        ys = [torch.empty((M, n), dtype=torch.bfloat16, device=dev) for _ in range(RING)]
+        fn = lambda: sk.skinny_gemm_bf16_ring(xs, ring, ys)
+    else:
+        x = synthetic.to_device(synthetic.gemm_inputs(N=16, K=k, seed=0)[0][:M], dev)
+        y = torch.empty((M, n), dtype=torch.bfloat16, device=dev)
+        fn = lambda: [sk.skinny_gemm_bf16(x, w, y, 0) for w in ring]
+    stream = torch.cuda.Stream(dev)
+    with torch.cuda.stream(stream):
+        fn()
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=stream):
+            fn()
+        for _ in range(3):
+            g.replay()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(passes):
+            g.replay()
+        e1.record(stream)
+        torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / (passes * RING)
+    if ring_launch:
+        r = sk.skinny_ring_choose(M, n, k, RING)
+        launch = {**dict(r.gemm._asdict()), "segment": r.segment, "workgroups": r.workgroups,
+                  "order": r.order}
+    else:
+        launch = walk_record(sk, M, n, k)
+    rec = {"shape": name, "ring": ring_launch, "M": M, "N": n, "K": k, "launch": launch,
+           "calls": (4 + passes) * (1 if ring_launch else RING),
+           "items_per_call": RING if ring_launch else 1,
+           "us_per_item_replay": round(us, 3), "copy_mib": copy_mib,
+           "kernel_source_digest": kernel_source_digest(),
+           "ring_source_digest": ring_source_digest()}
+    os.makedirs(out_dir, exist_ok=True)
+    with open(os.path.join(out_dir, "shape.json"), "w") as f:
+        json.dump(rec, f)
+    print(json.dumps(rec), flush=True)
+    del g, ring
+    torch.cuda.synchronize()
+
+
+def _short_kernel(name: str) -> str:
+    """'void skinny::(anonymous namespace)::gemm_x<1, 2>(args)' -> 'gemm_x<1, 2>'."""
+    head = name.split("(", 1)[0] if "(anonymous namespace)" not in name else \
+        name.replace("(anonymous namespace)::", "").split("(", 1)[0]
+    head = head.replace("void ", "").replace("skinny::", "").strip()
+    return head
+
+
+def _quantiles(vals):
+    v = sorted(vals)
+    q = lambda p: v[min(len(v) - 1, max(0, int(round(p * (len(v) - 1)))))]
+    return {"n": len(v), "mean": sum(v) / len(v), "median": q(0.5), "p10": q(0.1), "p90": q(0.9)}
+
+
+def _is_library_kernel(short: str) -> bool:
+    return short.startswith(("gemm_", "split_reduce"))
+
+
+def summarize_profiles(root: str, out_dir: str) -> None:
+    """Reduce the rocprofv3 CSVs of the profiling runs under `root` (one run
+    directory per shape and pass, each holding shape.json) to the committed
+    summaries under `out_dir`: kernel_trace_shapes.{json,txt} and
+    hbm_traffic_shapes.{json,txt}."""
+    import csv
+    import glob
+
+    runs = {os.path.basename(d): d for d, _, _ in profile_runs(root)
+            if os.path.exists(os.path.join(d, "shape.json"))}
+    cmds = {os.path.basename(d): profile_command(d, p, b) for d, p, b in profile_runs(root)}
+
+    def shape_of(d):
+        with open(os.path.join(d, "shape.json")) as f:
+            return json.load(f)
+
+    def csv_rows(d, suffix):
+        files = glob.glob(os.path.join(d, "**", f"*{suffix}"), recursive=True)
+        if not files:
+            raise FileNotFoundError(f"no *{suffix} under {d}")
+        with open(files[0]) as f:
+            return list(csv.DictReader(f))
+
+    # ---- kernel traces
+    trace = []
+    for key, d in runs.items():
+        if not key.startswith("trace_"):
+            continue
+        sh = shape_of(d)
+        durs = {}
+        for r in csv_rows(d, "kernel_trace.csv"):
+            short = _short_kernel(r["Kernel_Name"])
+            if not _is_library_kernel(short):
+                continue
+            grid = int(r["Grid_Size_X"]) * int(r["Grid_Size_Y"]) * int(r["Grid_Size_Z"])
+            us = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1000.0
+            durs.setdefault((short, grid), []).append(us)
+        kernels = [{"kernel": kname, "grid": grid, **{q: round(v, 3) if q != "n" else v
+                                                      for q, v in _quantiles(ds).items()}}
+                   for (kname, grid), ds in sorted(durs.items())]
+        trace.append({"shape": sh["shape"], "M": sh["M"], "N": sh["N"], "K": sh["K"],
+                      "launch": sh["launch"], "kernels": kernels,
+                      "call_median_us": round(sum(kk["median"] for kk in kernels), 3),
+                      "replay_us_per_call": sh["us_per_item_replay"], "command": cmds[key]})
+    # the digests the runs recorded on the GPU box (all runs share one tree)
+    digests = {shape_of(d)["kernel_source_digest"] for d in runs.values()
+               if os.path.exists(os.path.join(d, "shape.json"))}
+    ring_digests = {shape_of(d)["ring_source_digest"] for d in runs.values()
+                    if os.path.exists(os.path.join(d, "shape.json"))}
+    if len(digests) != 1 or len(ring_digests) != 1:
+        raise ValueError(f"runs from different kernel sources: {digests} {ring_digests}")
+    digest, ring_digest = digests.pop(), ring_digests.pop()
+    with open(os.path.join(out_dir, "kernel_trace_shapes.json"), "w") as f:
+        json.dump({"kernel_source_digest": digest, "entries": trace}, f, indent=1)
+    lines = ["rocprofv3 kernel traces, one run per shape: the chooser's call over the shape's",
+             f"{RING}-layer weight ring (an eager warm-up, then graph replays of one ring pass,",
+             f"3 + {TRACE_PASSES} passes: {(4 + TRACE_PASSES) * RING} dispatches of each kernel of "
+             "the call); per library kernel and grid: dispatches, mean / median / p10 / p90",
+             "duration in us; call = sum of the medians of the call's kernels; replay = event-timed",
+             "us per call of the same graph replays in the run (profiler on).",
+             "Reduced with: python bench.py --summarize gpurun_out/prof",
+             f"kernel sources digest {digest}", ""]
+    for e in trace:
+        lines.append(f"{e['shape']} M={e['M']} N={e['N']} K={e['K']}  launch {e['launch']}")
+        lines.append(f"  command: {e['command']}")
+        for kk in e["kernels"]:
+            lines.append(f"  {kk['kernel']:<44} grid {kk['grid']:>8}  n {kk['n']:>4}  mean "
+                         f"{kk['mean']:7.3f}  median {kk['median']:7.3f}  p10 {kk['p10']:7.3f}  "
+                         f"p90 {kk['p90']:7.3f}")
+        lines.append(f"  call median {e['call_median_us']:.3f} us  (replay {e['replay_us_per_call']:.3f}"
+                     f" us/call)  {algorithmic_bytes(e['M'], e['N'], e['K']) / e['call_median_us'] / 1e3:.1f}"
+                     " GB/s")
+        lines.append("")
+    with open(os.path.join(out_dir, "kernel_trace_shapes.txt"), "w") as f:
+        f.write("\n".join(lines))
+
+    # ---- counters
+    def counter_medians(d):
+        """{(kernel, grid): {counter: median per dispatch}}, and the copy
+        kernel's per-dispatch values."""
+        per = {}
+        for r in csv_rows(d, "counter_collection.csv"):
+            short = _short_kernel(r["Kernel_Name"])
+            key = (short, int(r["Grid_Size"]))
+            per.setdefault(key, {}).setdefault(r["Counter_Name"], []).append(
+                float(r["Counter_Value"]))
+        out, copy = {}, None
+        for (kname, grid), cs in per.items():
+            med = {c: _quantiles(v)["median"] for c, v in cs.items()}
+            if "copyBuffer" in kname:
+                copy = med
+            elif _is_library_kernel(kname):
+                out[(kname, grid)] = med
+        return out, copy
+
+    traffic = []
+    copy_bytes = COPY_MIB << 20
+    for key, d in runs.items():
+        if not key.startswith("fetch_"):
+            continue
+        base = key[len("fetch_"):]
+        sh = shape_of(d)
+        fetch, fcopy = counter_medians(d)
+        write, wcopy = counter_medians(runs["write_" + base])
+        fscale = copy_bytes / (fcopy["FETCH_SIZE"] * 1024)
+        wscale = copy_bytes / (wcopy["WRITE_SIZE"] * 1024)
+        rec = {"shape": sh["shape"], "ring": sh["ring"], "M": sh["M"], "N": sh["N"], "K": sh["K"],
+               "launch": sh["launch"], "items_per_dispatch": sh["items_per_call"],
+               "fetch_scale": round(fscale, 4), "write_scale": round(wscale, 4),
+               "kernels": [], "commands": [cmds[key], cmds["write_" + base]]}
+        fetch_b = sum(v["FETCH_SIZE"] for v in fetch.values()) * 1024 * fscale
+        write_b = sum(v["WRITE_SIZE"] for v in write.values()) * 1024 * wscale
+        for kk in sorted(fetch):
+            rec["kernels"].append({"kernel": kk[0], "grid": kk[1],
+                                   "fetch_kib": fetch[kk]["FETCH_SIZE"],
+                                   "write_kib": write.get(kk, {}).get("WRITE_SIZE")})
+        items = sh["items_per_call"]
+        rec["hbm_bytes_per_item"] = int(round((fetch_b + write_b) / items))
+        if ("rdreq_" + base) in runs:
+            rq, rcopy = counter_medians(runs["rdreq_" + base])
+            dr, dcopy = counter_medians(runs["dram_" + base])
+            req = {c: sum(v.get(c, 0.0) for v in rq.values()) for c in COUNTER_PASSES["rdreq"]}
+            rd_bytes = (32 * req["TCC_EA0_RDREQ_32B_sum"] + 64 * req["TCC_EA0_RDREQ_64B_sum"]
+                        + 128 * req["TCC_EA0_RDREQ_128B_sum"])
+            dram_rd = 32 * sum(v.get("TCC_EA0_RDREQ_DRAM_32B_sum", 0.0) for v in dr.values())
+            dram_wr = 32 * sum(v.get("TCC_EA0_WRREQ_WRITE_DRAM_32B_sum", 0.0) for v in dr.values())
+            rec["read_requests"] = {c.replace("TCC_EA0_", "").replace("_sum", ""): v
+                                    for c, v in req.items()}
+            rec["read_bytes_from_request_sizes"] = int(round(rd_bytes))
+            rec["dram_read_bytes"] = int(round(dram_rd))
+            rec["dram_write_bytes"] = int(round(dram_wr))
+            rec["copy_reference"] = {
+                "bytes_each_way": copy_bytes,
+                "read_bytes_from_request_sizes": int(round(
+                    32 * rcopy["TCC_EA0_RDREQ_32B_sum"] + 64 * rcopy["TCC_EA0_RDREQ_64B_sum"]
+                    + 128 * rcopy["TCC_EA0_RDREQ_128B_sum"])),
+                "dram_read_bytes": int(round(32 * dcopy["TCC_EA0_RDREQ_DRAM_32B_sum"])),
+                "dram_write_bytes": int(round(32 * dcopy["TCC_EA0_WRREQ_WRITE_DRAM_32B_sum"]))}
+            rec["commands"] += [cmds["rdreq_" + base], cmds["dram_" + base]]
+        rec["algorithmic_bytes_per_item"] = algorithmic_bytes(sh["M"], sh["N"], sh["K"])
+        rec["ratio"] = round(rec["hbm_bytes_per_item"] / rec["algorithmic_bytes_per_item"], 4)
+        traffic.append(rec)
+    util = []
+    for key, d in runs.items():
+        if key.startswith("util_"):
+            sh = shape_of(d)
+            med, _ = counter_medians(d)
+            util.append({"shape": sh["shape"], "M": sh["M"], "launch": sh["launch"],
+                         "kernels": [{"kernel": kk[0], "grid": kk[1], **{c: round(v, 2)
+                                                                         for c, v in cs.items()}}
+                                     for kk, cs in sorted(med.items())],
+                         "command": cmds[key]})
+    with open(os.path.join(out_dir, "hbm_traffic_shapes.json"), "w") as f:
+        json.dump({"kernel_source_digest": digest, "ring_source_digest": ring_digest,
+                   "entries": traffic, "utilization": util}, f, indent=1)
+    lines = ["HBM traffic per call (per item for ring launches), one rocprofv3 --pmc run per shape",
+             "and counter set (program: bench.py --profile-shape; medians over the dispatches):",
+             f"  fetch/write: FETCH_SIZE, WRITE_SIZE (KiB per dispatch) scaled by a plain {COPY_MIB} MiB",
+             "    device copy in the same run (scale = copy bytes / what the counter reads for it);",
+             "  rdreq: read bytes from the request-size counters 32*RDREQ_32B + 64*RDREQ_64B +",
+             "    128*RDREQ_128B (TCC_EA0_*_sum), no scale factor;",
+             "  dram: 32*TCC_EA0_RDREQ_DRAM_32B_sum and 32*TCC_EA0_WRREQ_WRITE_DRAM_32B_sum;",
+             "  util: MfmaUtil and VALUBusy (percent).",
+             "Reduced with: python bench.py --summarize gpurun_out/prof",
+             f"kernel sources digest {digest}, ring sources digest {ring_digest}", ""]
+    for r in traffic:
+        tag = "ring item" if r["ring"] else "call"
+        lines.append(f"{'ring ' if r['ring'] else ''}{r['shape']} M={r['M']} N={r['N']} K={r['K']}  "
+                     f"launch {r['launch']}")
+        for kk in r["kernels"]:
+            lines.append(f"  {kk['kernel']:<44} grid {kk['grid']:>8}  fetch {kk['fetch_kib']:9.1f} KiB"
+                         f"  write {kk['write_kib'] if kk['write_kib'] is not None else float('nan'):8.1f} KiB")
+        lines.append(f"  per {tag}: FETCH x{r['fetch_scale']} + WRITE x{r['write_scale']} = "
+                     f"{r['hbm_bytes_per_item']} B, algorithmic {r['algorithmic_bytes_per_item']} B, "
+                     f"ratio {r['ratio']}")
+        if "read_requests" in r:
+            rr = r["read_requests"]
+            lines.append(f"  read requests 32B {rr['RDREQ_32B']:.0f}  64B {rr['RDREQ_64B']:.0f}  "
+                         f"128B {rr['RDREQ_128B']:.0f}  all {rr['RDREQ']:.0f}: "
+                         f"{r['read_bytes_from_request_sizes']} B read; DRAM read "
+                         f"{r['dram_read_bytes']} B, DRAM write {r['dram_write_bytes']} B")
+            c = r["copy_reference"]
+            lines.append(f"  copy reference ({c['bytes_each_way']} B each way): request sizes "
+                         f"{c['read_bytes_from_request_sizes']} B read, DRAM {c['dram_read_bytes']} B"
+                         f" read / {c['dram_write_bytes']} B write")
+        for cmd in r["commands"]:
+            lines.append(f"  command: {cmd}")
+        lines.append("")
+    for u in util:
+        lines.append(f"utilization {u['shape']} M={u['M']} launch {u['launch']}")
+        for kk in u["kernels"]:
+            lines.append(f"  {kk['kernel']:<44} grid {kk['grid']:>8}  MfmaUtil {kk.get('MfmaUtil')}"
+                         f"  VALUBusy {kk.get('VALUBusy')}")
+        lines.append(f"  command: {u['command']}")
+        lines.append("")
+    with open(os.path.join(out_dir, "hbm_traffic_shapes.txt"), "w") as f:
+        f.write("\n".join(lines))
+    print(f"wrote {out_dir}/kernel_trace_shapes.* ({len(trace)} shapes) and "
+          f"hbm_traffic_shapes.* ({len(traffic)} shapes, {len(util)} utilization runs)")
 
 
 def _cpu_model() -> str:
@@ -150,11 +518,13 @@ def _cpu_model() -> str:
 def cpu_baseline(budget_s: float = 12.0):
     """The oracle (plain C, binary64) on the host cores for a bounded sample of
     the same sweep: whole steps until the budget is spent, with every host
-    thread it may use (at most 16) and then with one thread."""
+    thread it may use (at most 16) and then with one thread; and per M the
+    median us per call over 3 runs on each thread count."""
     import oracle
     import synthetic
 
-    threads = min(16, len(os.sched_getaffinity(0)))
+    affinity = len(os.sched_getaffinity(0))
+    threads = min(16, affinity)
     x, w = synthetic.gemm_inputs(N=N, K=K, seed=0)
     oracle.gemm_bf16(x[:1], w[:16], threads)  # load the library
     step_bytes = sum(algorithmic_bytes(M) for M in MS)
@@ -169,6 +539,19 @@ def cpu_baseline(budget_s: float = 12.0):
             if el >= budget or steps >= 200:
                 return steps, el
 
+    def per_m(nthreads, runs=3):
+        out = {}
+        for M in MS:
+            ts = []
+            for _ in range(runs):
+                t0 = time.perf_counter()
+                oracle.gemm_bf16(x[:M], w, nthreads)
+                ts.append(time.perf_counter() - t0)
+            us = sorted(ts)[len(ts) // 2] * 1e6
+            out[str(M)] = {"median_us_per_call": round(us, 1),
+                           "GBs": round(algorithmic_bytes(M) / (us * 1e-6) / 1e9, 4)}
+        return out
+
     steps, el = run(threads, budget_s)
     steps1, el1 = run(1, budget_s / 3)
     per_step, per_step1 = el / steps, el1 / steps1
@@ -178,7 +561,9 @@ def cpu_baseline(budget_s: float = 12.0):
                       f"({el:.1f} s, {per_step * 1e3:.1f} ms/step)",
             "value_1_thread": round(step_bytes / per_step1 / 1e9, 4),
             "sample_1_thread": f"{steps1} steps ({el1:.1f} s, {per_step1 * 1e3:.1f} ms/step)",
-            "cpu_model": _cpu_model()}
+            "per_m": {"threads": threads, **per_m(threads)},
+            "per_m_1_thread": per_m(1),
+            "host": {"nproc": os.cpu_count(), "affinity": affinity, "cpu_model": _cpu_model()}}
 
 
 def epilogue_timing(sk, synthetic, dev, stream, reps: int = 50):
@@ -397,11 +782,33 @@ def main():
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="first run one plain device copy of this many MiB (the reference "
                          "kernel that scales hardware byte counters in a counter run)")
+    ap.add_argument("--profile-shape", default="",
+                    help="profiling run: <shape>:<M> (shapes: " + ", ".join(SHAPES) +
+                         ") runs that shape's chooser call over its weight ring; "
+                         "ring:<shape>:<M> its 60-item ring launch")
+    ap.add_argument("--passes", type=int, default=TRACE_PASSES,
+                    help="profiling run: ring passes replayed after 3 warm ones")
+    ap.add_argument("--profile-out", default="", help="profiling run: directory for shape.json")
+    ap.add_argument("--profile-commands", action="store_true",
+                    help="print the rocprofv3 command of every profiling run and exit")
+    ap.add_argument("--summarize", default="",
+                    help="reduce the profiling runs under this directory to profiles/*_shapes.*")
     args = ap.parse_args()
+    if args.profile_commands:
+        for d, p, b in profile_runs():
+            print(profile_command(d, p, b))
+        return
+    if args.summarize:
+        summarize_profiles(args.summarize, os.path.join(HERE, "profiles"))
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py runs on one GPU only: this GEMM is one GPU's shard and the "
               "build has no multi-GPU path (use --gpus 1)", file=sys.stderr)
         sys.exit(2)
+
+    if args.profile_shape:
+        profile_shape(args.profile_shape, args.passes, args.profile_out or ".", args.copy_mib)
+        return
 
     import torch
 
@@ -528,7 +935,8 @@ def main():
                      "traffic": measured_traffic(dom, sk),
                      "kernel": f"M={dom} {walk_record(sk, dom, N, K)}",
                      "bytes_per_launch": algorithmic_bytes(dom),
-                     "us_per_launch": round(per_kernel[dom], 3)},
+                     "us_per_launch": round(per_kernel[dom], 3),
+                     "traced": traced_call(dom, sk)},
         "per_m": detail,
         "ceiling": {**ceiling,
                     "dominant_call_fraction": round(ceiling["stream_us"] / per_kernel[dom], 4)},
@@ -536,8 +944,14 @@ def main():
         "ring": ring_out,
         "oproj": oproj_out,
         "pooler": pooler_out,
-        "wall_s": round(wall, 3),
+        "wall_s": round(wall, 6),
+        "timed_region_s": round(ms_step * args.steps * 1e-3, 6),
     }
+    # Release the device before the host-only part, so nothing holds the GPU
+    # while the CPU baseline runs and the process ends with nothing pending.
+    del full, tails, ring, xs, ys
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
     if not args.no_cpu:
         log("timing the CPU oracle baseline")
         out["cpu_baseline"] = cpu_baseline()
