@@ -7,8 +7,8 @@
  *   - "vllm.models.muse_spark.nvidia.specialized_decode.cutedsl.gemm.unpooler"
  *     (module description; Unpooler.run; Unpooler.unsupported;
  *     launch_unsupported): y[M, N] = x[M, K] @ W[N, K]^T, BF16 in and out,
- *     FP32 accumulation, 1 <= M <= 16, split-K partials summed in an order
- *     fixed by the launch shape so that runs are bitwise reproducible.
+ *     FP32 accumulation, 1 <= M <= 16, split-K partials added in an order
+ *     that only the launch shape decides, so repeated runs give equal bits.
  *   - "vllm.models.muse_spark.nvidia.specialized_decode.cutedsl.moe.pooler_gather"
  *     (module description; compile_norm_quant; cvt_e2m1x8_f32;
  *     cvt_f32_to_e4m3; nvfp4_compute_output_scale): RMSNorm with a gain
@@ -75,8 +75,9 @@ enum {
  *         chunks 4 or 8: whole groups of 512 K, loaded as 1 KiB row pieces)
  *         and all tokens in sets of 4; waves = ceil(K / (splits * kw)) <= 16.
  * In all three, wave partials are summed in LDS in wave order; with splits > 1
- * each workgroup writes an FP32 partial and a second kernel on the same
- * stream sums splits 0..S-1 in order. */
+ * each workgroup writes an FP32 partial and splits 0..S-1 are summed in that
+ * order: by the last workgroup of the output block to finish (MFMA_4X4) or by
+ * a second kernel on the same stream (the others). */
 typedef struct skinny_launch {
   int path;   /* SKINNY_PATH_MFMA, SKINNY_PATH_DOT2 or SKINNY_PATH_MFMA_4X4 */
   int splits; /* S in {1, 2, 4, 8, 16}: workgroups along K per output block   */
@@ -88,9 +89,9 @@ typedef struct skinny_launch {
 } skinny_launch;
 
 /* Prepare `device` (a HIP ordinal) for the compute calls (unpooler page,
- * Unpooler: everything is prepared at build, before graph capture, so that
- * run is graph-capturable and allocates nothing; pooler_gather page, Pooler:
- * the same for the pooler): checks that it is a gfx950 GPU, allocates the
+ * Unpooler: the layer is set up ahead of time, outside graph capture, after
+ * which its run call may be recorded into a graph and needs no allocation;
+ * pooler_gather page, Pooler: the same for the pooler): checks that it is a gfx950 GPU, allocates the
  * library's split-K workspace on it (8 MiB of FP32 partials, enough for
  * S * M * N <= 2^21) and the dual norm's buffer (512 KiB of per-slice sums),
  * sets the kernels' LDS limits and looks up the device's address of the
@@ -116,9 +117,13 @@ int skinny_init(int device);
  *           (longer K: SKINNY_EUNSUPPORTED)
  *   splits  0 = let the chooser pick; otherwise S in {1, 2, 4, 8, 16}
  * x, W and y must not overlap.  The result is bitwise identical for the same
- * (M, N, K, launch) on one device.  A launch with S > 1 enqueues two kernels
- * and uses the device's workspace: two such calls must not run concurrently
- * on different streams of one device (calls on one stream are ordered).
+ * (M, N, K, launch) on one device.  A launch with S > 1 uses the device's
+ * workspace: the 16-block path (SKINNY_PATH_MFMA_4X4) adds the splits inside
+ * its one kernel (the last of each output block's workgroups to finish, with
+ * self-resetting counters), the other paths enqueue a second kernel for it;
+ * the splits are added in the order s = 0..S-1 either way.  Two such calls
+ * must not run concurrently on different streams of one device (calls on one
+ * stream are ordered).
  * For some measured shapes the chosen launch runs as a persistent walk over
  * the output blocks (the layer-ring kernel with one item, see
  * skinny_choose_walk); the result is still bitwise that of
@@ -242,9 +247,9 @@ typedef struct skinny_ring_launch {
 
 /* The layer ring: `count` independent GEMMs y_i = bf16(x_i @ W_i^T) of one
  * shape (M, N, K) in one persistent launch (unpooler page, module
- * description: the weights are loaded before the dependency wait and the
- * activations after it, so that a layer's weight stream overlaps the end of
- * the previous layer).  Each workgroup has the weights of its next tile in
+ * description: weight loads are issued ahead of the wait on the previous
+ * kernel and activation loads after it, which overlaps one layer's weight
+ * stream with the tail of the layer before).  Each workgroup has the weights of its next tile in
  * flight while it multiplies, reduces and stores the current one.
  *   x, W, y   HOST arrays of `count` device pointers, read during the call
  *             only; x[i] bf16 [M, K], W[i] bf16 [N, K], y[i] bf16 [M, N], all

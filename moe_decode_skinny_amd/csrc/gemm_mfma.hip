@@ -11,8 +11,9 @@
 // so a lane's four results are four consecutive features of one token: one
 // 8-byte store of y.
 //
-// Work split (unpooler page, module description: CTA (t, s) owns features
-// [16 t, 16 t + 16) and the K slice s; each warp owns consecutive K):
+// Work split (unpooler page, module description: there a thread block is a
+// 16-feature tile and one of S slices of K, and its warps divide the slice
+// into consecutive runs of K):
 //   workgroup (group, s), s < S, owns F = rows / 16 tiles of 16 features and
 //   the K slice s of length kslice = KW * kw; its waves are (tile f, quarter
 //   q), q < KW, and wave (f, q) owns K [s kslice + q kw, + kw), kw = 32 CHUNKS.
@@ -21,8 +22,9 @@
 //   along K, into LDS, where the F tiles share it (activation traffic is
 //   M / (16 F) of the weight traffic); then each wave runs its MFMAs, chunk i
 //   into accumulator i % ACCS, with B fragments read from LDS.
-// Reduction, in an order fixed by the launch shape (module description:
-// partials summed in a fixed order, so runs are bitwise reproducible):
+// Reduction, in an order fixed by the launch shape (module description: the
+// partials are added in one fixed order, so repeated runs give the same
+// bits):
 //   accumulators 0..ACCS-1 in order -> waves q = 0..KW-1 of a tile in order
 //   through LDS -> with S = 1 the BF16 store; with S > 1 an FP32 partial per
 //   split, which a second kernel (split_reduce.hip) sums s = 0..S-1 in order.

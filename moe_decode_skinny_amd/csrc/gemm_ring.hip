@@ -4,9 +4,9 @@
 // kernel families: DOT2 (VALU dot products, lanes along K), MFMA 16x16x32
 // and the 16-block MFMA 4x4x4 (lanes along K, products on the matrix cores).
 //
-// The unpooler page's module description loads the weights before the
-// dependency wait and the activations after it, so that one layer's weight
-// stream overlaps the end of the previous kernel.  Within one launch the same
+// On the unpooler page (module description) a kernel issues its weight loads
+// ahead of the wait on the previous kernel and reads activations only after
+// it, so one layer's weight stream overlaps the tail of the layer before.  Within one launch the same
 // ordering becomes a software pipeline per workgroup: while one tile (item,
 // output block) is multiplied, reduced and stored, the weight loads of the
 // workgroup's next tile are already in flight.  Activations are loaded when a

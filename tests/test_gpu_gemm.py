@@ -7,7 +7,8 @@ Workloads (synthetic, seeded; the shard shapes of the three API pages):
                   (pooler_gather page, module description)
 x ~ N(0, 1), W ~ N(0, 1/K).  Acceptance: |err| <= 2^-7 |ref| + 2^-10 rms(ref)
 per element (tests/helpers.py), bitwise determinism per launch shape
-(unpooler page: the summation order depends only on the launch shape), and
+(unpooler page, module description: the order of the partial sums is a
+function of the launch shape alone), and
 bit-exactness on integer inputs whose sums are exact in any order.
 """
 import os

@@ -1,11 +1,13 @@
 """Pins of the oracle's zero-copy publish (mailbox stand-in).
 
 What the pages fix: the unpooler page's module description (zero-copy
-epilogue: y goes into this rank's slot of the next boundary's mailbox at the
-publish stage, -0.0 stored as +0.0, and the active-stage word is set; ticket
-stage: the stage is the upper 16 bits of the ticket word and no stage word is
-stored) and the pooler_gather page (the mailbox is BF16 [3, tp, capacity,
-hidden / tp]; -0.0 is its "not yet written" sentinel).  The checks below are
+epilogue: the GEMM also writes its output into the slot this rank owns in
+the following boundary's mailbox, at the publish stage, with negative zero
+replaced by positive zero, and then sets the active-stage word; with a
+ticket, the ticket word's high half selects the stage and the call leaves
+the stage word alone) and the pooler_gather page (a mailbox holds BF16
+[3, tp, capacity, hidden / tp]; negative zero marks an entry not yet
+written).  The checks below are
 a hand-worked case and properties that hold for any input, not a second copy
 of the oracle's loop.
 """
