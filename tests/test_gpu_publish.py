@@ -86,14 +86,17 @@ def _plain(sk, x_bits, w_bits, M, launch):
 
 def _launches(sk, M, N, K):
     """The chooser's launch and one launch per store site: DOT2, MFMA and
-    MFMA 4x4 with one split (the GEMM kernel stores y) and with splits (the
-    reduce does)."""
+    MFMA 4x4 with one split (the GEMM kernel stores y), DOT2 and MFMA with
+    splits (the split-reduce kernel does), and MFMA 4x4 with 2 and 4 splits
+    (the last workgroup of each output group to finish does)."""
     out = [None,
            sk.Launch(0, 1, -(-K // 1024), 2, 1, 4),
            sk.Launch(1, 1, -(-K // 256), 8, 1, 16),
            sk.Launch(3, 1, -(-K // 512), 4, 1, 4),
            sk.Launch(0, 4, -(-K // (4 * 512)), 1, 1, 4),
-           sk.Launch(1, 2, 2 * -(-K // (2 * 32 * 8)), 8, 2, 32)]
+           sk.Launch(1, 2, 2 * -(-K // (2 * 32 * 8)), 8, 2, 32),
+           sk.Launch(3, 2, -(-K // (2 * 512)), 4, 1, 4),
+           sk.Launch(3, 4, -(-K // (4 * 512)), 4, 1, 8)]
     return [l for l in out if l is None or sk.skinny_launch_unsupported(M, N, K, l) is None]
 
 
@@ -103,7 +106,7 @@ def test_publish_every_store_site(gpu_lib, M):
     x, w = synthetic.gemm_inputs(N=N, K=K, seed=40)
     ref = oracle.gemm_bf16(x[:M], w, THREADS)
     launches = _launches(gpu_lib, M, N, K)
-    assert len(launches) >= 5
+    assert len(launches) >= 7
     for l in launches:
         _say(f"publish M={M} {l}")
         y, used = _publish(gpu_lib, x, w, M, launch=l, stage=[1, 7])
