@@ -405,3 +405,45 @@ def test_blocks_split_recompute_path_is_bitwise_the_handoff(gpu_lib, tmp_path):
         if S == 2:
             assert np.array_equal(child[f"chooser{i}"], _run(gpu_lib, x, w, M)), f"chooser {i}"
     torch.cuda.synchronize()
+
+
+def test_in_kernel_split_across_graph_replays(gpu_lib):
+    """The pooler shard at 16 tokens runs the 16-block launch with 4 splits
+    summed inside the kernel; its hand-off counters must be back at zero
+    after every call. A captured call replayed with new inputs, eager calls
+    of other shapes on the same workspace between replays: every replay
+    equals the eager call bit for bit (same x) or the oracle (new x)."""
+    import torch
+
+    M, N, K = 16, 512, 8192
+    launch = gpu_lib.skinny_choose(M, N, K, 0)
+    assert launch.path == gpu_lib.SKINNY_PATH_MFMA_4X4 and launch.splits > 1
+    x_bits, w_bits = synthetic.gemm_inputs(N=N, K=K, seed=61)
+    x2_bits, _ = synthetic.gemm_inputs(N=16, K=K, seed=62)
+    xo, wo = synthetic.gemm_inputs(N=1024, K=4096, seed=63)
+    x, w = to_dev(x_bits[:M]), to_dev(w_bits)
+    y = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+    yo = torch.empty((9, 1024), dtype=torch.bfloat16, device="cuda")
+    gpu_lib.skinny_gemm_bf16(x, w, y, 0)
+    torch.cuda.synchronize()
+    eager = from_dev(y).copy()
+    assert_gemm_close(eager, oracle.gemm_bf16(x_bits[:M], w_bits, THREADS), "eager")
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            gpu_lib.skinny_gemm_bf16(x, w, y, 0)
+    torch.cuda.synchronize()
+    other = gpu_lib.Launch(3, 2, 4, 4, 1, 4)  # another in-kernel split in between
+    ref2 = oracle.gemm_bf16(x2_bits[:M], w_bits, THREADS)
+    for rep in range(6):
+        _say(f"in-kernel split graph replay {rep}")
+        y.fill_(3.0)
+        x.copy_(to_dev((x_bits if rep % 2 == 0 else x2_bits)[:M]))
+        gpu_lib.skinny_gemm_bf16_launch(to_dev(xo[:9]), to_dev(wo), yo, other)
+        g.replay()
+        torch.cuda.synchronize()
+        if rep % 2 == 0:
+            assert np.array_equal(from_dev(y), eager), f"replay {rep}"
+        else:
+            assert_gemm_close(from_dev(y), ref2, f"replay {rep}")
