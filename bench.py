@@ -61,14 +61,24 @@ KERNEL_SOURCES = ["moe_decode_skinny_amd/csrc/gemm_mfma.hip", "moe_decode_skinny
                   "moe_decode_skinny_amd/csrc/split_reduce.hip", "moe_decode_skinny_amd/csrc/device.h"]
 
 
-def kernel_source_digest() -> str:
+def _code_digest(sources) -> str:
+    """sha256 of the sources' code: comments and whitespace removed, so an
+    edit of a comment does not mark the profiles of the kernels as stale."""
     import hashlib
+    import re
 
     h = hashlib.sha256()
-    for rel in KERNEL_SOURCES:
-        with open(os.path.join(HERE, rel), "rb") as f:
-            h.update(f.read())
+    for rel in sources:
+        with open(os.path.join(HERE, rel)) as f:
+            text = f.read()
+        text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", " ", text)
+        h.update(" ".join(text.split()).encode())
     return h.hexdigest()[:16]
+
+
+def kernel_source_digest() -> str:
+    return _code_digest(KERNEL_SOURCES)
 
 
 RING_SOURCES = ["moe_decode_skinny_amd/csrc/gemm_ring.hip", "moe_decode_skinny_amd/csrc/dot2_device.h",
@@ -76,13 +86,7 @@ RING_SOURCES = ["moe_decode_skinny_amd/csrc/gemm_ring.hip", "moe_decode_skinny_a
 
 
 def ring_source_digest() -> str:
-    import hashlib
-
-    h = hashlib.sha256()
-    for rel in RING_SOURCES:
-        with open(os.path.join(HERE, rel), "rb") as f:
-            h.update(f.read())
-    return h.hexdigest()[:16]
+    return _code_digest(RING_SOURCES)
 
 
 def _summary(name: str):
@@ -124,7 +128,8 @@ def measured_traffic(M: int, sk=None, shape: str = "unpooler"):
         return None
     n, k, _ = SHAPES[shape]
     for e in rec["entries"]:
-        if not e["ring"] and e["shape"] == shape and e["M"] == M:
+        if (not e["ring"] and not e.get("explicit_launch") and not e.get("l1_only")
+                and e["shape"] == shape and e["M"] == M):
             if sk is not None and e["launch"] != walk_record(sk, M, n, k):
                 return None
             return e["hbm_bytes_per_item"]
@@ -178,7 +183,14 @@ COUNTER_PASSES = {
               "TCC_EA0_RDREQ_sum"],
     "dram": ["TCC_EA0_RDREQ_DRAM_32B_sum", "TCC_EA0_WRREQ_WRITE_DRAM_32B_sum"],
     "util": ["MfmaUtil", "VALUBusy"],
+    # L1 (TCP) -> L2 read requests and L1 tag accesses: the activation
+    # re-reads every workgroup pulls through its compute unit
+    "tcp": ["TCP_TCC_READ_REQ_sum", "TCP_TOTAL_CACHE_ACCESSES_sum", "TCP_TOTAL_READ_sum"],
 }
+# An explicit launch profiled beside the chooser's, to compare the load
+# traffic: the pooler shard's 16-token launch before the 16-block in-kernel
+# split (DOT2, 2 rows, 16 waves of 1 chunk) and after it.
+COMPARE_LAUNCHES = [("pooler_shard", 16, "0,1,16,1,1,2")]
 TRACE_PASSES = 12  # ring passes timed per trace run: 12 x 60 = 720 dispatches of the call
 COPY_MIB = 64      # the plain device copy that scales byte counters
 
@@ -207,6 +219,17 @@ def profile_runs(root="gpurun_out/prof"):
         d = f"{root}/util_{name}_m{M}"
         runs.append((d, ["--pmc", *COUNTER_PASSES["util"]],
                      ["--profile-shape", f"{name}:{M}", "--passes", "1"]))
+    for name, M in [("unpooler", 16), ("pooler_shard", 16)]:
+        d = f"{root}/tcp_{name}_m{M}"
+        runs.append((d, ["--pmc", *COUNTER_PASSES["tcp"]],
+                     ["--profile-shape", f"{name}:{M}", "--passes", "1"]))
+    for name, M, launch in COMPARE_LAUNCHES:
+        tag = launch.replace(",", "")
+        for pas in ("fetch", "write", "tcp"):
+            d = f"{root}/{pas}_{name}_m{M}_l{tag}"
+            runs.append((d, ["--pmc", *COUNTER_PASSES[pas]],
+                         ["--profile-shape", f"{name}:{M}", "--launch", launch, "--passes", "1",
+                          "--copy-mib", str(COPY_MIB)]))
     return runs
 
 
@@ -215,11 +238,13 @@ def profile_command(d, prof_args, bench_args) -> str:
             f"-o run -- python3 -u bench.py {' '.join(bench_args)} --profile-out {d}")
 
 
-def profile_shape(spec: str, passes: int, out_dir: str, copy_mib: int) -> None:
+def profile_shape(spec: str, passes: int, out_dir: str, copy_mib: int, launch: str = "") -> None:
     """One shape's calls for a profiler run: the chooser's call (skinny_gemm_bf16)
     or, for ring:<shape>:<M>, one 60-item ring launch (skinny_gemm_bf16_ring),
     over the shape's 60-layer weight ring: an eager warm-up, then graphs of
-    one ring pass replayed 3 + `passes` times.  Writes out_dir/shape.json."""
+    one ring pass replayed 3 + `passes` times; with `launch` ("path,splits,
+    waves,chunks,accs,rows") the GEMM at that explicit launch instead of the
+    chooser's.  Writes out_dir/shape.json."""
     import torch
 
     import moe_decode_skinny_amd as sk
@@ -247,7 +272,11 @@ def profile_shape(spec: str, passes: int, out_dir: str, copy_mib: int) -> None:
     else:
         x = synthetic.to_device(synthetic.gemm_inputs(N=16, K=k, seed=0)[0][:M], dev)
         y = torch.empty((M, n), dtype=torch.bfloat16, device=dev)
-        fn = lambda: [sk.skinny_gemm_bf16(x, w, y, 0) for w in ring]
+        if launch:
+            explicit = sk.Launch(*[int(v) for v in launch.split(",")])
+            fn = lambda: [sk.skinny_gemm_bf16_launch(x, w, y, explicit) for w in ring]
+        else:
+            fn = lambda: [sk.skinny_gemm_bf16(x, w, y, 0) for w in ring]
     stream = torch.cuda.Stream(dev)
     with torch.cuda.stream(stream):
         fn()
@@ -267,11 +296,14 @@ def profile_shape(spec: str, passes: int, out_dir: str, copy_mib: int) -> None:
     us = e0.elapsed_time(e1) * 1e3 / (passes * RING)
     if ring_launch:
         r = sk.skinny_ring_choose(M, n, k, RING)
-        launch = {**dict(r.gemm._asdict()), "segment": r.segment, "workgroups": r.workgroups,
-                  "order": r.order}
+        rec_launch = {**dict(r.gemm._asdict()), "segment": r.segment,
+                      "workgroups": r.workgroups, "order": r.order}
+    elif launch:
+        rec_launch = {**dict(explicit._asdict()), "segment": 0, "workgroups": 0}
     else:
-        launch = walk_record(sk, M, n, k)
-    rec = {"shape": name, "ring": ring_launch, "M": M, "N": n, "K": k, "launch": launch,
+        rec_launch = walk_record(sk, M, n, k)
+    rec = {"shape": name, "ring": ring_launch, "M": M, "N": n, "K": k, "launch": rec_launch,
+           "explicit_launch": bool(launch),
            "calls": (4 + passes) * (1 if ring_launch else RING),
            "items_per_call": RING if ring_launch else 1,
            "us_per_item_replay": round(us, 3), "copy_mib": copy_mib,
@@ -412,7 +444,8 @@ def summarize_profiles(root: str, out_dir: str) -> None:
         fscale = copy_bytes / (fcopy["FETCH_SIZE"] * 1024)
         wscale = copy_bytes / (wcopy["WRITE_SIZE"] * 1024)
         rec = {"shape": sh["shape"], "ring": sh["ring"], "M": sh["M"], "N": sh["N"], "K": sh["K"],
-               "launch": sh["launch"], "items_per_dispatch": sh["items_per_call"],
+               "launch": sh["launch"], "explicit_launch": sh.get("explicit_launch", False),
+               "items_per_dispatch": sh["items_per_call"],
                "fetch_scale": round(fscale, 4), "write_scale": round(wscale, 4),
                "kernels": [], "commands": [cmds[key], cmds["write_" + base]]}
         fetch_b = sum(v["FETCH_SIZE"] for v in fetch.values()) * 1024 * fscale
@@ -423,6 +456,11 @@ def summarize_profiles(root: str, out_dir: str) -> None:
                                    "write_kib": write.get(kk, {}).get("WRITE_SIZE")})
         items = sh["items_per_call"]
         rec["hbm_bytes_per_item"] = int(round((fetch_b + write_b) / items))
+        if ("tcp_" + base) in runs:
+            tq, _ = counter_medians(runs["tcp_" + base])
+            rec["l1"] = {c.replace("_sum", ""): sum(v.get(c, 0.0) for v in tq.values())
+                         for c in COUNTER_PASSES["tcp"]}
+            rec["commands"].append(cmds["tcp_" + base])
         if ("rdreq_" + base) in runs:
             rq, rcopy = counter_medians(runs["rdreq_" + base])
             dr, dcopy = counter_medians(runs["dram_" + base])
@@ -447,6 +485,17 @@ def summarize_profiles(root: str, out_dir: str) -> None:
         rec["algorithmic_bytes_per_item"] = algorithmic_bytes(sh["M"], sh["N"], sh["K"])
         rec["ratio"] = round(rec["hbm_bytes_per_item"] / rec["algorithmic_bytes_per_item"], 4)
         traffic.append(rec)
+    # L1 -> L2 traffic of runs that have no fetch pass of their own
+    for key, d in runs.items():
+        if key.startswith("tcp_") and ("fetch_" + key[len("tcp_"):]) not in runs:
+            sh = shape_of(d)
+            tq, _ = counter_medians(d)
+            traffic.append({"shape": sh["shape"], "ring": False, "M": sh["M"], "N": sh["N"],
+                            "K": sh["K"], "launch": sh["launch"], "l1_only": True,
+                            "explicit_launch": sh.get("explicit_launch", False),
+                            "l1": {c.replace("_sum", ""): sum(v.get(c, 0.0) for v in tq.values())
+                                   for c in COUNTER_PASSES["tcp"]},
+                            "commands": [cmds[key]]})
     util = []
     for key, d in runs.items():
         if key.startswith("util_"):
@@ -467,13 +516,25 @@ def summarize_profiles(root: str, out_dir: str) -> None:
              "  rdreq: read bytes from the request-size counters 32*RDREQ_32B + 64*RDREQ_64B +",
              "    128*RDREQ_128B (TCC_EA0_*_sum), no scale factor;",
              "  dram: 32*TCC_EA0_RDREQ_DRAM_32B_sum and 32*TCC_EA0_WRREQ_WRITE_DRAM_32B_sum;",
-             "  util: MfmaUtil and VALUBusy (percent).",
+             "  util: MfmaUtil and VALUBusy (percent);",
+             "  tcp: TCP_TCC_READ_REQ (L1 -> L2 read requests), TCP_TOTAL_CACHE_ACCESSES (L1 tag",
+             "    accesses) and TCP_TOTAL_READ, per call: the activation re-reads the workgroups pull.",
              "Reduced with: python bench.py --summarize gpurun_out/prof",
              f"kernel sources digest {digest}, ring sources digest {ring_digest}", ""]
     for r in traffic:
         tag = "ring item" if r["ring"] else "call"
         lines.append(f"{'ring ' if r['ring'] else ''}{r['shape']} M={r['M']} N={r['N']} K={r['K']}  "
-                     f"launch {r['launch']}")
+                     f"{'explicit ' if r.get('explicit_launch') else ''}launch {r['launch']}")
+        if "l1" in r:
+            l1 = r["l1"]
+            lines.append(f"  L1 -> L2 read requests {l1['TCP_TCC_READ_REQ']:.0f}, L1 tag accesses "
+                         f"{l1['TCP_TOTAL_CACHE_ACCESSES']:.0f}, reads from TA {l1['TCP_TOTAL_READ']:.0f}"
+                         " (per call)")
+        if r.get("l1_only"):
+            for cmd in r["commands"]:
+                lines.append(f"  command: {cmd}")
+            lines.append("")
+            continue
         for kk in r["kernels"]:
             lines.append(f"  {kk['kernel']:<44} grid {kk['grid']:>8}  fetch {kk['fetch_kib']:9.1f} KiB"
                          f"  write {kk['write_kib'] if kk['write_kib'] is not None else float('nan'):8.1f} KiB")
@@ -791,6 +852,8 @@ def main():
     ap.add_argument("--passes", type=int, default=TRACE_PASSES,
                     help="profiling run: ring passes replayed after 3 warm ones")
     ap.add_argument("--profile-out", default="", help="profiling run: directory for shape.json")
+    ap.add_argument("--launch", default="",
+                    help="profiling run: an explicit launch path,splits,waves,chunks,accs,rows")
     ap.add_argument("--profile-commands", action="store_true",
                     help="print the rocprofv3 command of every profiling run and exit")
     ap.add_argument("--summarize", default="",
@@ -809,7 +872,8 @@ def main():
         sys.exit(2)
 
     if args.profile_shape:
-        profile_shape(args.profile_shape, args.passes, args.profile_out or ".", args.copy_mib)
+        profile_shape(args.profile_shape, args.passes, args.profile_out or ".", args.copy_mib,
+                      args.launch)
         return
 
     import torch

@@ -80,9 +80,12 @@ def test_summary_lookups_follow_the_digest_and_the_launch(tmp_path, monkeypatch)
     t = bench.traced_call(16, sk)
     assert t["median_us"] == 5.0 and t["dispatches"] == 901 and t["p90_us"] == 5.2
     assert bench.traced_call(8, sk) is None
-    # a changed kernel source voids all three
+    # a comment or whitespace edit keeps them
     src = tmp_path / "moe_decode_skinny_amd" / "csrc" / "device.h"
-    src.write_bytes(src.read_bytes() + b"\n")
+    src.write_bytes(src.read_bytes() + b"\n// a comment\n/* another */\n")
+    assert bench.measured_traffic(16) == 123 and bench.traced_call(16) is not None
+    # a changed kernel source voids all three
+    src.write_bytes(src.read_bytes() + b"\nconstexpr int kSomething = 1;\n")
     assert bench.measured_traffic(16) is None
     assert bench.ring_traffic(16) is None
     assert bench.traced_call(16) is None
