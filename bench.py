@@ -187,10 +187,13 @@ COUNTER_PASSES = {
     # re-reads every workgroup pulls through its compute unit
     "tcp": ["TCP_TCC_READ_REQ_sum", "TCP_TOTAL_CACHE_ACCESSES_sum", "TCP_TOTAL_READ_sum"],
 }
-# An explicit launch profiled beside the chooser's, to compare the load
-# traffic: the pooler shard's 16-token launch before the 16-block in-kernel
-# split (DOT2, 2 rows, 16 waves of 1 chunk) and after it.
-COMPARE_LAUNCHES = [("pooler_shard", 16, "0,1,16,1,1,2")]
+# Explicit launches profiled beside the chooser's, to compare the load
+# traffic of the 16-token calls: the pooler shard at DOT2 (2 rows, 16 waves
+# of 1 chunk) and at the 16-block launch with 4 splits summed in the kernel,
+# and the unpooler at the 16-block launch of 4 rows with all tokens in each
+# workgroup; the chooser's launches take two token groups instead.
+COMPARE_LAUNCHES = [("pooler_shard", 16, "0,1,16,1,1,2"), ("pooler_shard", 16, "3,4,4,4,1,4"),
+                    ("unpooler", 16, "3,1,8,4,1,4")]
 TRACE_PASSES = 12  # ring passes timed per trace run: 12 x 60 = 720 dispatches of the call
 COPY_MIB = 64      # the plain device copy that scales byte counters
 

@@ -73,7 +73,12 @@ enum {
  *   MFMA_4X4: a workgroup owns rows = 4 or 8 output features; each wave owns
  *         kw = 128 * chunks consecutive K (16 blocks x 8 bf16 per chunk,
  *         chunks 4 or 8: whole groups of 512 K, loaded as 1 KiB row pieces)
- *         and all tokens in sets of 4; waves = ceil(K / (splits * kw)) <= 16.
+ *         and the workgroup's tokens in sets of 4; waves = ceil(K / (splits *
+ *         kw)) <= 16.  `accs` = H token groups (1, 2 or 4; a tile
+ *         decomposition along M): group h takes tokens 4Qh .. 4Qh + 4Q - 1,
+ *         Q = ceil(ceil(M / H) / 4) rounded up to 1, 2 or 4 sets, and every
+ *         group must get a token (ceil(M / 4Q) == H); H = 1 is all M tokens
+ *         in each workgroup.  A token's sums do not depend on H.
  * In all three, wave partials are summed in LDS in wave order; with splits > 1
  * each workgroup writes an FP32 partial and splits 0..S-1 are summed in that
  * order: by the last workgroup of the output block to finish (MFMA_4X4) or by
@@ -83,7 +88,8 @@ typedef struct skinny_launch {
   int splits; /* S in {1, 2, 4, 8, 16}: workgroups along K per output block   */
   int waves;  /* waves per workgroup (see above)                             */
   int chunks; /* K chunks per wave: MFMA 1..16, DOT2 1, 2, 4, MFMA_4X4 4, 8  */
-  int accs;   /* MFMA: accumulators per wave, 1, 2 or 4; others: 1           */
+  int accs;   /* MFMA: accumulators per wave, 1, 2 or 4; MFMA_4X4: token
+                 groups, 1, 2 or 4; DOT2: 1                                  */
   int rows;   /* features per workgroup: MFMA 16, 32, 64; DOT2 2..16;
                  MFMA_4X4 4, 8                                                */
 } skinny_launch;
@@ -223,7 +229,8 @@ int skinny_gemm_bf16_publish(const void *x, const void *W, void *y, int M,
  *               or MFMA_LDS (as MFMA with chunks 2..16, and the staging
  *               regions, waves x 16 x (64 chunks + 16) bytes, plus 2 KiB per
  *               wave, within the 160 KiB of LDS) or MFMA_4X4 (rows 4 or 8,
- *               chunks 4 or 8, waves = ceil(K / (128 chunks)) <= 16)
+ *               chunks 4 or 8, waves = ceil(K / (128 chunks)) <= 16, accs 1:
+ *               a ring tile takes all M tokens)
  *   segment     consecutive output blocks of one item a workgroup takes in a
  *               row, keeping that item's activations in registers; it
  *               divides N / gemm.rows

@@ -57,8 +57,9 @@ class _CLaunch(ctypes.Structure):
 
 
 class Launch(NamedTuple):
-    """skinny_launch: path (0 DOT2, 1 MFMA, 2 MFMA_LDS: ring only), splits, waves,
-    chunks, accs, rows."""
+    """skinny_launch: path (0 DOT2, 1 MFMA, 2 MFMA_LDS: ring only, 3 MFMA_4X4),
+    splits, waves, chunks, accs (MFMA: accumulators; MFMA_4X4: token groups),
+    rows."""
     path: int
     splits: int
     waves: int

@@ -2,11 +2,18 @@
 // (unpooler page, module description): lanes run along K as in the DOT2
 // path, the products go to the matrix cores (v_mfma_f32_4x4x4_16b_bf16; the
 // lane layout and the order of the sums are in blocks_device.h).
-//   wave w of workgroup (group, s) owns K range (s * waves + w) * kw,
+//   wave w of workgroup (group, h, s) owns K range (s * waves + w) * kw,
 //   kw = 128 * CHUNKS (CHUNKS 4 or 8: whole 512-K load groups), of the
-//   workgroup's 4 * R4 weight rows, and all M tokens in Q sets of 4; the
-//   activations are loaded first, then the weights, and both are transposed
-//   into the MFMA layout inside each 4-lane group, activations first.
+//   workgroup's 4 * R4 weight rows, and tokens 4 Q h .. 4 Q h + 4 Q - 1 (Q
+//   sets of 4; with H = 1 token group, all M tokens); the activations are
+//   loaded first, then the weights, and both are transposed into the MFMA
+//   layout inside each 4-lane group, activations first.
+// Token groups (H > 1) split the activations instead of K: each workgroup
+// pulls 1 / H of them through its compute unit and all of its rows'
+// weights, which the H workgroups of a row group (dealt to one XCD) share
+// through that XCD's L2, so HBM still streams W once.  No partials and no
+// hand-off: a token's sums are the same instructions in the same order as
+// with H = 1, so the bits are too.
 // Load order: the pages load weights ahead of the activations so that the
 // weight stream can start before the previous kernel ends.  Inside one
 // launch on gfx950 the activations (L2 hits after the first compute unit of
@@ -118,31 +125,37 @@ template <int R4, int CHUNKS, int Q, int THREADS>
 __global__ __launch_bounds__(THREADS) void gemm_blocks_kernel(
     const uint16_t *__restrict__ x, const uint16_t *__restrict__ w,
     uint16_t *__restrict__ y, float *__restrict__ partials, unsigned *__restrict__ counters,
-    int M, int N, int K, int S, int groups, int kw, int force_recompute, Publish pub) {
+    int M, int N, int K, int S, int H, int groups, int kw, int force_recompute, Publish pub) {
   constexpr int kOut = kOutputs<R4, Q>, kPer = (kOut + 63) / 64;
   const int lane = threadIdx.x & 63;
   if ((S == 1 || counters) && blockIdx.x == 0 && threadIdx.x == 0) publish_stage_word(pub);
   const int wave = wave_index();
   const int waves = blockDim.x >> 6;
 
-  // Workgroup -> (group, split): workgroups are dealt to the XCDs
-  // round-robin (ids congruent mod 8 share an XCD, also when the part has
-  // fewer XCDs), so with a group count divisible by 8 the S workgroups of a
-  // group share an XCD and its L2.
-  int group, s;
+  // Workgroup -> (row group, token group h, split s): workgroups are dealt
+  // to the XCDs round-robin (ids congruent mod 8 share an XCD, also when the
+  // part has fewer XCDs), so with a row-group count divisible by 8 the H * S
+  // workgroups of a row group share an XCD and its L2.
+  const int per = H * S;
+  int group, j;
   const int b = blockIdx.x;
   if ((groups & 7) == 0) {
     const int xcd = b & 7, slot = b >> 3;
-    group = (slot / S) * 8 + xcd;
-    s = slot % S;
+    group = (slot / per) * 8 + xcd;
+    j = slot % per;
   } else {
-    group = b / S;
-    s = b % S;
+    group = b / per;
+    j = b % per;
   }
+  const int h = j / S, s = j % S;
   const int f0 = group * 4 * R4;
+  const int t0 = 4 * Q * h;           // first token of this workgroup
+  const int Mh = min(4 * Q, M - t0);  // its token count, >= 1
+  const uint16_t *xh = x + (size_t)t0 * K;
+  const int ob = group * H + h;       // output block (row group, token group)
 
   __shared__ float red[THREADS / 64][kOut];
-  wave_slice<R4, CHUNKS, Q>(x, w, M, K, f0, s, wave, waves, kw, lane, red[wave]);
+  wave_slice<R4, CHUNKS, Q>(xh, w, Mh, K, f0, s, wave, waves, kw, lane, red[wave]);
   __syncthreads();
   if (wave != 0) return;
   float part[kPer];
@@ -154,20 +167,20 @@ __global__ __launch_bounds__(THREADS) void gemm_blocks_kernel(
       const int o = i * 64 + lane;
       if (o >= kOut) break;
       const int t = output_token(o, R4), r = output_row(o, R4);
-      if (t < M) partials[((size_t)s * M + t) * N + f0 + r] = part[i];
+      if (t < Mh) partials[((size_t)s * M + t0 + t) * N + f0 + r] = part[i];
     }
     return;
   }
   if (S > 1) {
     bool mixed = false;
-    if (!block_handoff<kPer>(partials + (size_t)group * S * kOut,
-                             counters + (size_t)group * kCounterStride, S, s, kOut, lane, part,
+    if (!block_handoff<kPer>(partials + (size_t)ob * S * kOut,
+                             counters + (size_t)ob * kCounterStride, S, s, kOut, lane, part,
                              &mixed))
       return;
     float sum[kPer];
     if (!mixed && !force_recompute) {
       const __amdgpu_buffer_rsrc_t res =
-          buffer_rsrc(partials + (size_t)group * S * kOut, (unsigned)(S * kOut * 4));
+          buffer_rsrc(partials + (size_t)ob * S * kOut, (unsigned)(S * kOut * 4));
 #pragma unroll
       for (int i = 0; i < kPer; ++i) {
         const int o = i * 64 + lane;
@@ -191,7 +204,7 @@ __global__ __launch_bounds__(THREADS) void gemm_blocks_kernel(
           for (int i = 0; i < kPer; ++i) p2[i] = part[i];
         } else {
           for (int v = 0; v < waves; ++v)
-            wave_slice<R4, CHUNKS, Q>(x, w, M, K, f0, s2, v, waves, kw, lane, red[v]);
+            wave_slice<R4, CHUNKS, Q>(xh, w, Mh, K, f0, s2, v, waves, kw, lane, red[v]);
           sum_waves<kOut, kPer>(red, waves, lane, p2);
         }
 #pragma unroll
@@ -206,16 +219,16 @@ __global__ __launch_bounds__(THREADS) void gemm_blocks_kernel(
     const int o = i * 64 + lane;
     if (o >= kOut) break;
     const int t = output_token(o, R4), r = output_row(o, R4);
-    if (t >= M) continue;
+    if (t >= Mh) continue;
     const unsigned bits = f32_to_bf16(part[i]);
-    y[(size_t)t * N + f0 + r] = (uint16_t)bits;
+    y[(size_t)(t0 + t) * N + f0 + r] = (uint16_t)bits;
     if (uint16_t *slot = publish_slot(pub, N))
-      slot[(size_t)t * N + f0 + r] = (uint16_t)publish_bits(bits);
+      slot[(size_t)(t0 + t) * N + f0 + r] = (uint16_t)publish_bits(bits);
   }
 }
 
 using BlocksKernel = void (*)(const uint16_t *, const uint16_t *, uint16_t *, float *,
-                              unsigned *, int, int, int, int, int, int, int, Publish);
+                              unsigned *, int, int, int, int, int, int, int, int, Publish);
 
 // Register budget per lane: weights 4 * R4 * CHUNKS, activations
 // 4 * Q * CHUNKS, sums 4 * Q * R4 (160 at 512 threads, 112 at 1024).
@@ -270,6 +283,12 @@ int blocks_token_sets(int M) {
   return 0;
 }
 
+int blocks_group_token_sets(int M, int H) {
+  if (H != 1 && H != 2 && H != 4) return 0;
+  const int q = blocks_token_sets((M + H - 1) / H);
+  return q && (M + 4 * q - 1) / (4 * q) == H ? q : 0;
+}
+
 bool blocks_variant_exists(int rows, int chunks, int q, int waves) {
   return waves >= 1 && waves <= kBlocksMaxWaves && pick(rows, chunks, q, waves) != nullptr;
 }
@@ -277,16 +296,19 @@ bool blocks_variant_exists(int rows, int chunks, int q, int waves) {
 hipError_t launch_gemm_blocks(const uint16_t *x, const uint16_t *w, uint16_t *y, int M,
                               int N, int K, const skinny_launch &l, const Workspace &ws,
                               const Publish &pub, hipStream_t stream) {
-  BlocksKernel k = pick(l.rows, l.chunks, blocks_token_sets(M), l.waves);
+  const int H = l.accs;  // token groups
+  const int q = blocks_group_token_sets(M, H);
+  BlocksKernel k = pick(l.rows, l.chunks, q, l.waves);
   const int groups = N / l.rows;
-  // the in-kernel hand-off when the counters cover the groups and the
-  // partial slots fit; otherwise the two-kernel split (same sums, same order)
-  const bool handoff = l.splits > 1 && ws.counters && groups <= kMaxHandoffGroups &&
-                       (size_t)groups * l.splits * 16 * blocks_token_sets(M) * (l.rows / 4) <=
-                           ws.partial_floats;
-  dim3 grid(groups * l.splits), block(64 * l.waves);
+  const long blocks = (long)groups * H;
+  // the in-kernel hand-off when the counters cover the output blocks and
+  // the partial slots fit; otherwise the two-kernel split (same sums, same
+  // order)
+  const bool handoff = l.splits > 1 && ws.counters && blocks <= kMaxHandoffGroups &&
+                       (size_t)blocks * l.splits * 16 * q * (l.rows / 4) <= ws.partial_floats;
+  dim3 grid(groups * H * l.splits), block(64 * l.waves);
   hipLaunchKernelGGL(k, grid, block, 0, stream, x, w, y, ws.partials,
-                     handoff ? ws.counters : nullptr, M, N, K, l.splits, groups,
+                     handoff ? ws.counters : nullptr, M, N, K, l.splits, H, groups,
                      kBlockK * l.chunks, ws.force_recompute ? 1 : 0, pub);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || l.splits == 1 || handoff) return e;

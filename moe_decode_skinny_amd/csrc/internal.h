@@ -67,6 +67,9 @@ bool dot2_variant_exists(int rows, int chunks, int mt, int waves);
 int dot2_token_tile(int M);  // smallest compiled token count >= M, 0 if none
 int dot2_max_waves();        // waves per DOT2 workgroup (the 16-wave form's bound)
 int blocks_token_sets(int M);  // 4-token sets of the 16-block MFMA path (1, 2, 4), 0 if none
+// 4-token sets per workgroup of a 16-block launch with H token groups (1, 2
+// or 4); 0 unless every group gets at least one of the M tokens
+int blocks_group_token_sets(int M, int H);
 bool blocks_variant_exists(int rows, int chunks, int q, int waves);
 bool ring_variant_exists(int rows, int chunks, int mt, int waves);  // DOT2 ring (<= 16 waves)
 bool blocks_ring_variant_exists(int rows, int chunks, int q, int waves);  // MFMA 4x4 ring

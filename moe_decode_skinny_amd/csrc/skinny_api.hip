@@ -66,6 +66,14 @@ int check_problem(int M, int N, int K) {
 
 int ceil_div(long a, long b) { return (int)((a + b - 1) / b); }
 
+// A kernel's grid counts its work-items in 32 bits.
+int grid_check(long workgroups, int waves) {
+  if (workgroups * waves * 64 > 0xFFFFFFFFL)
+    return fail(SKINNY_EUNSUPPORTED, "%ld workgroups of %d waves exceed the 2^32 work-items of "
+                "one grid", workgroups, waves);
+  return SKINNY_OK;
+}
+
 }  // namespace
 
 DeviceState *current_state(int *status) {
@@ -115,7 +123,7 @@ static int launch_check(int M, int N, int K, const skinny_launch &l) {
     if (mfma_lds_bytes(M, l) > kMaxDynamicLds)
       return fail(SKINNY_EUNSUPPORTED, "K slice of %ld per workgroup needs %zu bytes of LDS "
                   "(max %zu)", (long)(l.waves / F) * kw, mfma_lds_bytes(M, l), kMaxDynamicLds);
-    return SKINNY_OK;
+    return grid_check((long)(N / l.rows) * l.splits, l.waves);
   }
   if (l.path == SKINNY_PATH_DOT2) {
     const int mt = dot2_token_tile(M);
@@ -135,12 +143,15 @@ static int launch_check(int M, int N, int K, const skinny_launch &l) {
       return fail(SKINNY_EUNSUPPORTED, "no DOT2 kernel with rows=%d chunks=%d tokens=%d at %d "
                   "waves (more than 8 waves: only the register-light variants)", l.rows,
                   l.chunks, mt, l.waves);
-    return SKINNY_OK;
+    return grid_check((long)(N / l.rows) * l.splits, l.waves);
   }
   if (l.path == SKINNY_PATH_MFMA_4X4) {
-    const int q = blocks_token_sets(M);
-    if (q == 0) return fail(SKINNY_EUNSUPPORTED, "MFMA 4x4 path takes M <= 16, got %d", M);
-    if (l.accs != 1) return fail(SKINNY_EUNSUPPORTED, "MFMA 4x4 launch has accs=1");
+    if (blocks_token_sets(M) == 0)
+      return fail(SKINNY_EUNSUPPORTED, "MFMA 4x4 path takes M <= 16, got %d", M);
+    const int q = blocks_group_token_sets(M, l.accs);
+    if (q == 0)
+      return fail(SKINNY_EUNSUPPORTED, "MFMA 4x4 accs=%d token groups for M=%d: needs 1, 2 or "
+                  "4 groups of whole 4-token sets, each with at least one token", l.accs, M);
     if (l.rows != 4 && l.rows != 8)
       return fail(SKINNY_EUNSUPPORTED, "MFMA 4x4 rows=%d: needs 4 or 8", l.rows);
     if (l.chunks != 4 && l.chunks != 8)
@@ -159,7 +170,7 @@ static int launch_check(int M, int N, int K, const skinny_launch &l) {
     if (!blocks_variant_exists(l.rows, l.chunks, q, l.waves))
       return fail(SKINNY_EUNSUPPORTED, "no MFMA 4x4 kernel with rows=%d chunks=%d tokens=%d "
                   "at %d waves", l.rows, l.chunks, 4 * q, l.waves);
-    return SKINNY_OK;
+    return grid_check((long)(N / l.rows) * l.accs * l.splits, l.waves);
   }
   return fail(SKINNY_EUNSUPPORTED, "unknown path %d", l.path);
 }
@@ -190,7 +201,7 @@ static const TableEntry kTable[] = {
     {1024, 4096, 2, 2, {SKINNY_PATH_DOT2, 1, 2, 4, 1, 2}, {2, 256}},
     {1024, 4096, 3, 4, {SKINNY_PATH_DOT2, 1, 4, 2, 1, 2}, {2, 256}},
     {1024, 4096, 5, 8, {SKINNY_PATH_MFMA_4X4, 1, 4, 8, 1, 4}, {}},
-    {1024, 4096, 9, 16, {SKINNY_PATH_MFMA_4X4, 1, 8, 4, 1, 4}, {}},
+    {1024, 4096, 9, 16, {SKINNY_PATH_MFMA_4X4, 1, 8, 4, 2, 8}, {}},
     // o_proj shard
     {8192, 1024, 1, 1, {SKINNY_PATH_DOT2, 1, 1, 2, 1, 2}, {}},
     {8192, 1024, 2, 2, {SKINNY_PATH_DOT2, 1, 1, 2, 1, 4}, {2, 1024}},
@@ -199,7 +210,7 @@ static const TableEntry kTable[] = {
     // pooler shard
     {512, 8192, 1, 4, {SKINNY_PATH_DOT2, 1, 4, 4, 1, 2}, {}},
     {512, 8192, 5, 8, {SKINNY_PATH_DOT2, 1, 8, 2, 1, 2}, {}},
-    {512, 8192, 9, 16, {SKINNY_PATH_MFMA_4X4, 4, 4, 4, 1, 4}, {}},
+    {512, 8192, 9, 16, {SKINNY_PATH_MFMA_4X4, 1, 8, 8, 2, 4}, {}},
     // full pooler
     {4096, 8192, 1, 1, {SKINNY_PATH_DOT2, 1, 8, 2, 1, 2}, {}},
     {4096, 8192, 2, 2, {SKINNY_PATH_DOT2, 1, 8, 2, 1, 8}, {}},
@@ -208,11 +219,54 @@ static const TableEntry kTable[] = {
     {4096, 8192, 9, 16, {SKINNY_PATH_MFMA_4X4, 1, 16, 4, 1, 4}, {4, 256}},
 };
 
+// The 16-block launch of the rule for 9..16 tokens on K = 4096..8192 (4
+// chunks a wave; one split of at most 16 waves covers K).
+//   No split count: of 4 or 8 rows and 1 or 2 token groups, the launch with
+//   the most workgroups up to one per compute unit (and at least half of
+//   them: 128..256), ties to the fewer rows + tokens per workgroup (the
+//   bytes per K it pulls through its compute unit).  Measured against the
+//   former 4-row, one-group rule and DOT2 on N = 512..2048: 4-35% faster.
+//   A split count S > 1: 8 rows, 2 token groups up to N = 1024 (1 above),
+//   the splits summed inside the kernel, when that is at most 2048
+//   workgroups.  Measured against the DOT2 and MFMA split launches (whose
+//   splits a second kernel sums) on N = 512..8192: faster in 17 of 20
+//   cases, the others within 2%, except 4 splits of N = 8192 (4096
+//   workgroups: slower, so not taken).
+static skinny_launch blocks_rule(int M, int N, int K, int splits) {
+  if (M <= 8 || K < 4096 || K > 16 * kGroupK) return skinny_launch{};
+  if (splits > 1) {
+    const int H = N <= 1024 ? 2 : 1;
+    const skinny_launch l{SKINNY_PATH_MFMA_4X4, splits, ceil_div(K, (long)splits * kGroupK), 4,
+                          H, 8};
+    // at most 2048 workgroups, so also at most 2048 output blocks: the
+    // hand-off counters cover them
+    if ((long)(N / 8) * H * splits <= 2048 && launch_check(M, N, K, l) == SKINNY_OK) return l;
+    return skinny_launch{};
+  }
+  skinny_launch best{};
+  long best_wgs = 0;
+  int best_per = 0;
+  for (int rows : {4, 8})
+    for (int H : {1, 2}) {
+      const skinny_launch l{SKINNY_PATH_MFMA_4X4, 1, ceil_div(K, (long)kGroupK), 4, H, rows};
+      const long wgs = (long)(N / rows) * H;
+      const int per = rows + ceil_div(M, H);
+      if (wgs < 128 || wgs > 256 || launch_check(M, N, K, l) != SKINNY_OK) continue;
+      if (wgs > best_wgs || (wgs == best_wgs && per < best_per)) {
+        best = l;
+        best_wgs = wgs;
+        best_per = per;
+      }
+    }
+  return best;
+}
+
 // The general rule the table follows (used for any other shape, or when an
 // explicit split count is asked for):
-//   the 16-block MFMA for 9..16 tokens when one split of at most 16 waves
+//   the 16-block MFMA for 9..16 tokens as blocks_rule gives it; else, for
+//   9..16 tokens with no split count, when one split of at most 16 waves
 //   covers K = 4096..8192 and N gives every compute unit a 4-row block
-//   (N / 4 >= 256): 4 rows, 4 chunks per wave;
+//   (N / 4 >= 256): 4 rows, 4 chunks per wave (a walk from 512 blocks);
 //   DOT2 (lanes along K; activation traffic M / rows of the weight traffic;
 //   no split-K) for M <= 8, and for M <= 16 on narrow shards (< 256 MFMA
 //   tiles); 2 rows per workgroup for M <= 2, else 4, and 2 rows when that
@@ -225,6 +279,8 @@ static const TableEntry kTable[] = {
 static skinny_launch rule(int M, int N, int K, int splits) {
   const long tiles = N / kTileN;
   const long units = ceil_div(K, kDot2K);
+  const skinny_launch b = blocks_rule(M, N, K, splits);
+  if (b.waves) return b;
   if (M > 8 && splits <= 1 && N / 4 >= 256 && K >= 4096 && K <= 16 * kGroupK) {
     const skinny_launch l{SKINNY_PATH_MFMA_4X4, 1, ceil_div(K, (long)kGroupK), 4, 1, 4};
     if (launch_check(M, N, K, l) == SKINNY_OK) return l;
@@ -308,7 +364,7 @@ static skinny_ring_launch walk_launch(const skinny_launch &l, const Walk &w) {
 // block). Measured against the plain launch: 8-46% faster on
 // N = 2048..8192, K = 4096..8192.
 static void blocks_walk(int M, int N, int K, const skinny_launch &l, Walk *w) {
-  if (l.path != SKINNY_PATH_MFMA_4X4 || l.splits != 1) return;
+  if (l.path != SKINNY_PATH_MFMA_4X4 || l.splits != 1 || l.accs != 1) return;
   const int groups = N / l.rows;
   int seg = 1;
   while (groups / (2 * seg) >= 256 && groups % (2 * seg) == 0) seg *= 2;
@@ -394,7 +450,8 @@ static int ring_check(int count, int M, int N, int K, const skinny_ring_launch &
                   "waves (more than 8 waves: only the register-light variants)", l.rows,
                   l.chunks, dot2_token_tile(M), l.waves);
   } else if (l.path == SKINNY_PATH_MFMA_4X4) {
-    if (l.accs != 1) return fail(SKINNY_EUNSUPPORTED, "MFMA 4x4 launch has accs=1");
+    if (l.accs != 1)
+      return fail(SKINNY_EUNSUPPORTED, "the ring's MFMA 4x4 tiles take all M tokens (accs=1)");
     if (l.rows != 4 && l.rows != 8)
       return fail(SKINNY_EUNSUPPORTED, "MFMA 4x4 rows=%d: needs 4 or 8", l.rows);
     if (l.chunks != 4 && l.chunks != 8)

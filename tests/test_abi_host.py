@@ -250,41 +250,91 @@ def test_off_table_16_block_walks(sk):
     workgroups; fewer blocks run the plain kernel."""
     P3 = sk.SKINNY_PATH_MFMA_4X4
     for M, N, K, seg, wgs in [(16, 2048, 8192, 2, 256), (12, 8192, 8192, 8, 256),
-                              (9, 2048, 4096, 2, 256), (16, 2064, 4096, 2, 258)]:
+                              (9, 3072, 6144, 2, 384), (16, 2064, 4096, 2, 258)]:
         w = sk.skinny_choose_walk(M, N, K, 0)
         assert (w.gemm.path, w.segment, w.workgroups) == (P3, seg, wgs), (M, N, K, w)
         assert tuple(w.gemm) == tuple(sk.skinny_choose(M, N, K, 0))
-    for M, N, K in [(16, 1040, 6000), (16, 1024, 8192), (12, 2032, 4096)]:
+        assert w.gemm.accs == 1 and w.gemm.rows == 4
+    for M, N, K in [(16, 1040, 6000), (16, 1024, 8192), (12, 2032, 4096), (9, 2048, 4096)]:
         w = sk.skinny_choose_walk(M, N, K, 0)
         assert w.gemm.path == P3 and w.segment == 0, (M, N, K, w)
 
 
 def test_rule_takes_the_16_block_path_for_many_tokens_on_long_k(sk):
-    """The chooser's rule outside the table: the 16-block MFMA (4 rows, 4
-    chunks, one split) for 9..16 tokens when N / 4 >= 256 and 4096 <= K <=
-    8192; DOT2 or the 16x16 MFMA otherwise (fewer tokens, narrow N, short or
-    very long K, or an explicit split count)."""
+    """The chooser outside the table for 9..16 tokens and 4096 <= K <= 8192:
+    the 16-block MFMA with one split, 4 chunks, and the rows (4 or 8) and
+    token groups (1 or 2) that give the most workgroups in 128..256, ties
+    to fewer rows + tokens a workgroup; with none in that range, 4 rows and
+    one group when N / 4 >= 256; DOT2 or the 16x16 MFMA otherwise (fewer
+    tokens, narrow N, short or very long K)."""
     P3 = sk.SKINNY_PATH_MFMA_4X4
-    for M, N, K in [(9, 1024, 4096), (12, 2048, 4096), (16, 1040, 6000), (16, 2048, 8192)]:
+    for M, N, K, rows, H in [(9, 1024, 4096, 8, 2), (12, 2048, 4096, 8, 1),
+                             (16, 1040, 6000, 4, 1), (16, 2048, 8192, 4, 1),
+                             (16, 512, 4096, 4, 2), (12, 768, 8192, 8, 2),
+                             (9, 1536, 4096, 8, 1), (12, 1008, 4096, 8, 2)]:
         l = sk.skinny_choose(M, N, K, 0)
-        assert (l.path, l.splits, l.chunks, l.rows) == (P3, 1, 4, 4), (M, N, K, l)
+        assert (l.path, l.splits, l.chunks, l.rows, l.accs) == (P3, 1, 4, rows, H), (M, N, K, l)
         assert l.waves == -(-K // 512)
-    for M, N, K, splits in [(8, 2048, 4096, 0), (12, 1008, 4096, 0), (12, 2048, 2048, 0),
-                            (12, 2048, 8200, 0), (12, 2048, 4096, 2)]:
+    for M, N, K, splits in [(8, 2048, 4096, 0), (12, 240, 4096, 0), (12, 2048, 2048, 0),
+                            (12, 2048, 8200, 0), (8, 1024, 4096, 2)]:
         assert sk.skinny_choose(M, N, K, splits).path != P3, (M, N, K, splits)
 
 
+def test_rule_sums_requested_splits_inside_the_16_block_kernel(sk):
+    """An explicit split count S > 1 for 9..16 tokens and 4096 <= K <= 8192:
+    the 16-block launch of 8 rows, 4 chunks, two token groups up to
+    N = 1024 (one above), whose splits the last workgroup of each output
+    block sums, when that is at most 2048 workgroups; else the DOT2 or MFMA
+    split launch."""
+    P3 = sk.SKINNY_PATH_MFMA_4X4
+    for M, N, K, S, H in [(16, 512, 8192, 4, 2), (9, 1024, 4096, 2, 2), (12, 2048, 4096, 2, 1),
+                          (16, 4096, 8192, 4, 1), (16, 8192, 8192, 2, 1)]:
+        l = sk.skinny_choose(M, N, K, S)
+        assert tuple(l) == (P3, S, -(-K // (S * 512)), 4, H, 8), (M, N, K, S, l)
+        assert N // 8 * H * S <= 2048
+    for M, N, K, S in [(16, 8192, 8192, 4), (16, 8192, 1024, 2), (8, 512, 8192, 4)]:
+        assert sk.skinny_choose(M, N, K, S).path != P3, (M, N, K, S)
+
+
+def test_mfma_4x4_token_groups(sk):
+    """Token groups (accs = H) of the 16-block path: group h takes tokens
+    4Qh .. 4Qh + 4Q - 1 with Q the token sets of ceil(M / H) (1, 2 or 4),
+    and every group needs a token (ceil(M / 4Q) == H). The ring and the
+    chooser's walks keep all tokens in one workgroup, and a grid over 2^32
+    work-items is refused."""
+    L, P = sk.Launch, sk.SKINNY_PATH_MFMA_4X4
+    ok = {(M, H) for M in range(1, 17) for H in (1, 2, 4)
+          if sk.skinny_launch_unsupported(M, 1024, 4096, L(P, 1, 8, 4, H, 4)) is None}
+    # H = 1: every M; H = 2: M = 5..16 (4 or 8 tokens a group); H = 4: M = 13..16
+    assert ok == ({(M, 1) for M in range(1, 17)} | {(M, 2) for M in range(5, 17)}
+                  | {(M, 4) for M in range(13, 17)})
+    for M, H in [(4, 2), (12, 4), (9, 4), (16, 3), (16, 0), (16, 8)]:
+        why = sk.skinny_launch_unsupported(M, 1024, 4096, L(P, 1, 8, 4, H, 4))
+        assert why is not None and f"accs={H}" in why, (M, H, why)
+    # token groups with splits: valid, the splits' workspace as without them
+    assert sk.skinny_launch_unsupported(16, 512, 8192, L(P, 2, 8, 4, 2, 4)) is None
+    assert sk.skinny_launch_unsupported(13, 512, 8192, L(P, 4, 4, 4, 4, 4)) is None
+    ring = sk.RingLaunch(L(P, 1, 8, 4, 2, 4), 1, 256, 0)
+    assert "all M tokens" in sk.skinny_ring_launch_unsupported(16, 1024, 4096, 1, ring)
+    # 2^22 blocks of 4 rows x 4 token groups x 16 waves: 2^34 work-items
+    why = sk.skinny_launch_unsupported(16, 1 << 24, 8192, L(P, 1, 16, 4, 4, 4))
+    assert why is not None and "2^32 work-items" in why, why
+    assert "2^32 work-items" in sk.skinny_launch_unsupported(16, 1 << 24, 8192,
+                                                             L(P, 1, 16, 4, 1, 4))
+
+
 def test_mfma_4x4_launch_reasons(sk):
-    """The 16-block MFMA path: rows 4 or 8, accs 1, chunks 4 or 8 (whole
-    512-K load groups), waves = ceil(K / (S * 128 chunks)) <= 16, and only the
-    register-budgeted variants."""
+    """The 16-block MFMA path: rows 4 or 8, accs = token groups 1, 2 or 4
+    (each with a token), chunks 4 or 8 (whole 512-K load groups),
+    waves = ceil(K / (S * 128 chunks)) <= 16, and only the register-budgeted
+    variants."""
     L, P = sk.Launch, sk.SKINNY_PATH_MFMA_4X4
     assert sk.skinny_launch_unsupported(16, 1024, 4096, L(P, 1, 8, 4, 1, 4)) is None
     assert sk.skinny_launch_unsupported(16, 1024, 4096, L(P, 2, 4, 4, 1, 8)) is None
     assert sk.skinny_launch_unsupported(1, 512, 8192, L(P, 1, 16, 4, 1, 4)) is None
     assert "rows=2" in sk.skinny_launch_unsupported(16, 1024, 4096, L(P, 1, 8, 4, 1, 2))
     assert "rows=16" in sk.skinny_launch_unsupported(16, 1024, 4096, L(P, 1, 8, 4, 1, 16))
-    assert "accs" in sk.skinny_launch_unsupported(16, 1024, 4096, L(P, 1, 8, 4, 2, 4))
+    assert "accs=3" in sk.skinny_launch_unsupported(16, 1024, 4096, L(P, 1, 8, 4, 3, 4))
     assert "needs 8 waves" in sk.skinny_launch_unsupported(16, 1024, 4096, L(P, 1, 4, 4, 1, 4))
     assert "MFMA 4x4: 1..16" in sk.skinny_launch_unsupported(16, 1024, 16384,
                                                             L(P, 1, 32, 4, 1, 4))

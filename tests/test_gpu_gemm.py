@@ -351,6 +351,60 @@ def test_blocks_split_in_kernel_equals_the_two_kernel_split(gpu_lib):
         assert_gemm_close(from_dev(y_two)[:, cols].ravel(), ref, f"S={splits} sampled")
 
 
+@pytest.mark.parametrize("N,K", [(1024, 4096), (512, 8192), (48, 1000)])
+def test_token_groups_are_bitwise_one_group(gpu_lib, N, K):
+    """The 16-block path's token groups (accs = H: each workgroup takes 4Q of
+    the M tokens over all of its K range) compute every token with the same
+    instructions in the same order as H = 1, so the outputs are equal bit
+    for bit, with and without splits, also when the last group holds fewer
+    than 4Q tokens. N = 48 gives 12 or 6 row groups (not a multiple of 8:
+    the plain workgroup order), K = 1000 a ragged last chunk."""
+    x_bits, w_bits = synthetic.gemm_inputs(N=N, K=K, seed=71)
+    n = 0
+    for M in (2, 5, 8, 9, 12, 13, 16):
+        checked = False
+        for rows in (4, 8):
+            for chunks in (4, 8):
+                for S in (1, 2):
+                    one = gpu_lib.Launch(3, S, -(-K // (S * 128 * chunks)), chunks, 1, rows)
+                    if gpu_lib.skinny_launch_unsupported(M, N, K, one) is not None:
+                        continue
+                    y1 = _run(gpu_lib, x_bits, w_bits, M, launch=one)
+                    if not checked:
+                        assert_gemm_close(y1, oracle.gemm_bf16(x_bits[:M], w_bits, THREADS),
+                                          f"M={M} {one}")
+                        checked = True
+                    for H in (2, 4):
+                        l = one._replace(accs=H)
+                        if gpu_lib.skinny_launch_unsupported(M, N, K, l) is not None:
+                            continue
+                        _say(f"token groups M={M} N={N} K={K} {l}")
+                        y2 = _run(gpu_lib, x_bits, w_bits, M, launch=l)
+                        assert np.array_equal(y2, y1), f"M={M} {l}"
+                        n += 1
+    assert n >= 20
+
+
+def test_token_groups_through_the_two_kernel_split(gpu_lib):
+    """Token groups multiply the output blocks: N = 8192 at 4 rows is 2048
+    blocks at H = 1 (splits summed inside the kernel) and 4096 or 8192 at
+    H = 2 or 4, past the 2048 hand-off counters (splits summed by the
+    split-reduce kernel). Both add s = 0..S-1 in order: equal bit for bit."""
+    M, N, K = 16, 8192, 2048
+    x_bits, w_bits = synthetic.gemm_inputs(N=N, K=K, seed=72)
+    for S in (2, 4):
+        one = gpu_lib.Launch(3, S, -(-K // (S * 512)), 4, 1, 4)
+        y1 = _run(gpu_lib, x_bits, w_bits, M, launch=one)
+        for H in (2, 4):
+            _say(f"token groups H={H} S={S}: two-kernel split against the in-kernel one")
+            assert np.array_equal(_run(gpu_lib, x_bits, w_bits, M, launch=one._replace(accs=H)),
+                                  y1), f"S={S} H={H}"
+        cols = np.arange(0, N, 61)
+        rows = np.arange(M).repeat(cols.size)
+        ref, _ = oracle.gemm_bf16_sampled(x_bits[:M], w_bits, rows, np.tile(cols, M))
+        assert_gemm_close(y1[:, cols].ravel(), ref, f"S={S} sampled")
+
+
 _RECOMPUTE_CHILD = r"""
 import sys, numpy as np, torch
 sys.path.insert(0, sys.argv[1])
@@ -358,10 +412,10 @@ import moe_decode_skinny_amd as sk, synthetic
 from tests.helpers import to_dev, from_dev
 sk.init(0)
 out = {}
-for i, (M, N, K, S) in enumerate(CASES):
+for i, (M, N, K, S, H) in enumerate(CASES):
     x, w = synthetic.gemm_inputs(N=N, K=K, seed=50 + i)
     y = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
-    launch = sk.Launch(3, S, -(-K // (S * 512)), 4, 1, 4)
+    launch = sk.Launch(3, S, -(-K // (S * 512)), 4, H, 4)
     sk.skinny_gemm_bf16_launch(to_dev(x[:M]), to_dev(w), y, launch)
     if S == 2:
         y2 = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
@@ -373,7 +427,10 @@ for i, (M, N, K, S) in enumerate(CASES):
 np.savez(sys.argv[2], **out)
 print("child done", flush=True)
 """
-_RECOMPUTE_CASES = [(16, 512, 8192, 2), (9, 1024, 4096, 4), (16, 48, 1000, 2), (5, 256, 6000, 8)]
+# (M, N, K, S, token groups H)
+_RECOMPUTE_CASES = [(16, 512, 8192, 2, 1), (9, 1024, 4096, 4, 1), (16, 48, 1000, 2, 1),
+                    (5, 256, 6000, 8, 1), (16, 512, 8192, 2, 2), (13, 1024, 4096, 4, 4),
+                    (9, 48, 1000, 2, 2)]
 
 
 def test_blocks_split_recompute_path_is_bitwise_the_handoff(gpu_lib, tmp_path):
@@ -395,11 +452,11 @@ def test_blocks_split_recompute_path_is_bitwise_the_handoff(gpu_lib, tmp_path):
                          capture_output=True, text=True, timeout=300)
     assert res.returncode == 0, res.stdout[-2000:] + res.stderr[-2000:]
     child = np.load(out)
-    for i, (M, N, K, S) in enumerate(_RECOMPUTE_CASES):
+    for i, (M, N, K, S, H) in enumerate(_RECOMPUTE_CASES):
         x, w = synthetic.gemm_inputs(N=N, K=K, seed=50 + i)
-        launch = gpu_lib.Launch(3, S, -(-K // (S * 512)), 4, 1, 4)
+        launch = gpu_lib.Launch(3, S, -(-K // (S * 512)), 4, H, 4)
         y = _run(gpu_lib, x, w, M, launch=launch)
-        _say(f"recompute case {i}: M={M} N={N} K={K} S={S}")
+        _say(f"recompute case {i}: M={M} N={N} K={K} S={S} H={H}")
         assert np.array_equal(child[f"case{i}"], y), f"case {i}"
         assert_gemm_close(y, oracle.gemm_bf16(x[:M], w, THREADS), f"case {i}")
         if S == 2:
@@ -408,23 +465,23 @@ def test_blocks_split_recompute_path_is_bitwise_the_handoff(gpu_lib, tmp_path):
 
 
 def test_in_kernel_split_across_graph_replays(gpu_lib):
-    """The pooler shard at 16 tokens runs the 16-block launch with 4 splits
+    """The pooler shard at 16 tokens in the 16-block launch with 4 splits
     summed inside the kernel; its hand-off counters must be back at zero
     after every call. A captured call replayed with new inputs, eager calls
-    of other shapes on the same workspace between replays: every replay
-    equals the eager call bit for bit (same x) or the oracle (new x)."""
+    of other split launches (one with token groups) on the same workspace
+    between replays: every replay equals the eager call bit for bit (same
+    x) or the oracle (new x)."""
     import torch
 
     M, N, K = 16, 512, 8192
-    launch = gpu_lib.skinny_choose(M, N, K, 0)
-    assert launch.path == gpu_lib.SKINNY_PATH_MFMA_4X4 and launch.splits > 1
+    launch = gpu_lib.Launch(3, 4, 4, 4, 1, 4)
     x_bits, w_bits = synthetic.gemm_inputs(N=N, K=K, seed=61)
     x2_bits, _ = synthetic.gemm_inputs(N=16, K=K, seed=62)
     xo, wo = synthetic.gemm_inputs(N=1024, K=4096, seed=63)
     x, w = to_dev(x_bits[:M]), to_dev(w_bits)
     y = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
     yo = torch.empty((9, 1024), dtype=torch.bfloat16, device="cuda")
-    gpu_lib.skinny_gemm_bf16(x, w, y, 0)
+    gpu_lib.skinny_gemm_bf16_launch(x, w, y, launch)
     torch.cuda.synchronize()
     eager = from_dev(y).copy()
     assert_gemm_close(eager, oracle.gemm_bf16(x_bits[:M], w_bits, THREADS), "eager")
@@ -432,15 +489,17 @@ def test_in_kernel_split_across_graph_replays(gpu_lib):
     s = torch.cuda.Stream()
     with torch.cuda.stream(s):
         with torch.cuda.graph(g, stream=s):
-            gpu_lib.skinny_gemm_bf16(x, w, y, 0)
+            gpu_lib.skinny_gemm_bf16_launch(x, w, y, launch)
     torch.cuda.synchronize()
-    other = gpu_lib.Launch(3, 2, 4, 4, 1, 4)  # another in-kernel split in between
+    # other in-kernel splits in between: the same blocks' counters, and
+    # twice as many output blocks with two token groups
+    others = [gpu_lib.Launch(3, 2, 4, 4, 1, 4), gpu_lib.Launch(3, 2, 4, 4, 2, 4)]
     ref2 = oracle.gemm_bf16(x2_bits[:M], w_bits, THREADS)
     for rep in range(6):
         _say(f"in-kernel split graph replay {rep}")
         y.fill_(3.0)
         x.copy_(to_dev((x_bits if rep % 2 == 0 else x2_bits)[:M]))
-        gpu_lib.skinny_gemm_bf16_launch(to_dev(xo[:9]), to_dev(wo), yo, other)
+        gpu_lib.skinny_gemm_bf16_launch(to_dev(xo[:9]), to_dev(wo), yo, others[rep % 2])
         g.replay()
         torch.cuda.synchronize()
         if rep % 2 == 0:

@@ -88,7 +88,8 @@ def _launches(sk, M, N, K):
     """The chooser's launch and one launch per store site: DOT2, MFMA and
     MFMA 4x4 with one split (the GEMM kernel stores y), DOT2 and MFMA with
     splits (the split-reduce kernel does), and MFMA 4x4 with 2 and 4 splits
-    (the last workgroup of each output group to finish does)."""
+    (the last workgroup of each output group to finish does), and MFMA 4x4
+    with two token groups, without and with splits (from M = 5)."""
     out = [None,
            sk.Launch(0, 1, -(-K // 1024), 2, 1, 4),
            sk.Launch(1, 1, -(-K // 256), 8, 1, 16),
@@ -96,7 +97,9 @@ def _launches(sk, M, N, K):
            sk.Launch(0, 4, -(-K // (4 * 512)), 1, 1, 4),
            sk.Launch(1, 2, 2 * -(-K // (2 * 32 * 8)), 8, 2, 32),
            sk.Launch(3, 2, -(-K // (2 * 512)), 4, 1, 4),
-           sk.Launch(3, 4, -(-K // (4 * 512)), 4, 1, 8)]
+           sk.Launch(3, 4, -(-K // (4 * 512)), 4, 1, 8),
+           sk.Launch(3, 1, -(-K // 512), 4, 2, 4),
+           sk.Launch(3, 2, -(-K // (2 * 512)), 4, 2, 4)]
     return [l for l in out if l is None or sk.skinny_launch_unsupported(M, N, K, l) is None]
 
 

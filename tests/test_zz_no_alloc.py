@@ -49,9 +49,10 @@ def _pair(sk, M, N, K, splits, seed):
     ((16, 2048, 2048, 8, 3), (1, 1024, 4096, 16, 4)),
     # the chooser's own launches (no split: the kernel or its walk)
     ((16, 1024, 4096, 0, 5), (3, 8192, 1024, 0, 6)),
-    # the chooser's 16-block launch with 4 splits summed inside the kernel
-    # (partials and hand-off counters in the static array), then a smaller one
-    ((16, 512, 8192, 0, 7), (9, 512, 4096, 2, 8)),
+    # 4 splits asked for: the chooser's 16-block launch sums them inside the
+    # kernel (partials and hand-off counters in the static array), then a
+    # smaller one with 2 splits
+    ((16, 512, 8192, 4, 7), (9, 512, 4096, 2, 8)),
 ])
 def test_noalloc_matches_the_allocating_call_twice(gpu_lib, first, second):
     l1 = _pair(gpu_lib, *first)
@@ -61,6 +62,7 @@ def test_noalloc_matches_the_allocating_call_twice(gpu_lib, first, second):
         assert first[3] * first[0] * first[1] > second[3] * second[0] * second[1]
     if first[4] == 7:
         assert l1.path == gpu_lib.SKINNY_PATH_MFMA_4X4 and l1.splits == 4
+        assert l2.path == gpu_lib.SKINNY_PATH_MFMA_4X4 and l2.splits == 2
 
 
 def test_noalloc_refuses_partials_beyond_the_array(gpu_lib):
