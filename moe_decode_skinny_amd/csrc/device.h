@@ -82,6 +82,25 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
+// The in-order sum term(0) + term(1) + ... + term(n - 1) of 1 <= n <= N
+// terms, n known only at run time (a wave or split count).  A plain loop
+// with a run-time bound waits for each term's load before it issues the
+// next; here every load is issued first and the adds follow in index
+// order, so the result is the plain loop's and the loads cost one round
+// trip instead of n.  term(i) is evaluated for every i < N, with no
+// branch: the caller makes that safe (a row of a static LDS array, a buffer
+// load, which returns zero past its range); terms from n on are not added.
+template <int N, typename T, typename Term>
+__device__ __forceinline__ T sum_in_order(int n, Term term) {
+  T v[N];
+#pragma unroll
+  for (int i = 0; i < N; ++i) v[i] = term(i);
+  T sum = v[0];
+#pragma unroll
+  for (int i = 1; i < N; ++i) sum = i < n ? sum + v[i] : sum;
+  return sum;
+}
+
 // FP32 -> bfloat16 bits, round to nearest even; NaN stays a quiet NaN.
 __device__ __forceinline__ unsigned f32_to_bf16(float f) {
   unsigned u = __float_as_uint(f);

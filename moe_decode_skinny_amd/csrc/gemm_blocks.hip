@@ -66,18 +66,26 @@ __device__ __forceinline__ void wave_slice(const uint16_t *__restrict__ x,
 }
 
 // Output o = i * 64 + lane (i < kPer) summed over the waves' slices in wave
-// order.
-template <int kOut, int kPer>
+// order (waves <= kWaves).
+template <int kOut, int kPer, int kWaves>
 __device__ __forceinline__ void sum_waves(float (*red)[kOut], int waves, int lane, float *part) {
 #pragma unroll
   for (int i = 0; i < kPer; ++i) {
-    const int o = i * 64 + lane;
-    float p = 0.f;
-    if (o < kOut) {
-      p = red[0][o];
-      for (int v = 1; v < waves; ++v) p += red[v][o];
-    }
-    part[i] = p;
+    const int o = i * 64 + lane, oc = o < kOut ? o : 0;
+    const float p = sum_in_order<kWaves, float>(waves, [&](int v) { return red[v][oc]; });
+    part[i] = o < kOut ? p : 0.f;
+  }
+}
+
+// Splits 0..S-1 summed in order (S = 2, 4, 8 or 16), with the S terms
+// loaded before the first add and no load past S.
+template <typename Term>
+__device__ __forceinline__ float sum_splits(int S, Term term) {
+  switch (S) {
+    case 2: return sum_in_order<2, float>(2, term);
+    case 4: return sum_in_order<4, float>(4, term);
+    case 8: return sum_in_order<8, float>(8, term);
+    default: return sum_in_order<16, float>(16, term);
   }
 }
 
@@ -159,7 +167,7 @@ __global__ __launch_bounds__(THREADS) void gemm_blocks_kernel(
   __syncthreads();
   if (wave != 0) return;
   float part[kPer];
-  sum_waves<kOut, kPer>(red, waves, lane, part);
+  sum_waves<kOut, kPer, THREADS / 64>(red, waves, lane, part);
 
   if (S > 1 && !counters) {  // FP32 partial of split s for split_reduce: [s][token][feature]
 #pragma unroll
@@ -183,14 +191,13 @@ __global__ __launch_bounds__(THREADS) void gemm_blocks_kernel(
           buffer_rsrc(partials + (size_t)ob * S * kOut, (unsigned)(S * kOut * 4));
 #pragma unroll
       for (int i = 0; i < kPer; ++i) {
-        const int o = i * 64 + lane;
-        for (int s2 = 0; s2 < S; ++s2) {
+        const int oc = i * 64 + lane < kOut ? i * 64 + lane : 0;
+        sum[i] = sum_splits(S, [&](int s2) {
           // bit 0 of the cache policy (sc0): served from L2, not this CU's L1
-          const float v = s2 == s ? part[i]
-                                  : __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
-                                        res, (s2 * kOut + (o < kOut ? o : 0)) * 4, 0, 1));
-          sum[i] = s2 == 0 ? v : sum[i] + v;
-        }
+          return s2 == s ? part[i]
+                         : __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
+                               res, (s2 * kOut + oc) * 4, 0, 1));
+        });
       }
     } else {
       // Splits on several XCDs: this wave recomputes every other split's
@@ -205,7 +212,7 @@ __global__ __launch_bounds__(THREADS) void gemm_blocks_kernel(
         } else {
           for (int v = 0; v < waves; ++v)
             wave_slice<R4, CHUNKS, Q>(xh, w, Mh, K, f0, s2, v, waves, kw, lane, red[v]);
-          sum_waves<kOut, kPer>(red, waves, lane, p2);
+          sum_waves<kOut, kPer, THREADS / 64>(red, waves, lane, p2);
         }
 #pragma unroll
         for (int i = 0; i < kPer; ++i) sum[i] = s2 == 0 ? p2[i] : sum[i] + p2[i];
