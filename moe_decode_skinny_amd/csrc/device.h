@@ -101,6 +101,19 @@ __device__ __forceinline__ T sum_in_order(int n, Term term) {
   return sum;
 }
 
+// sum_in_order over the rows of a workgroup's waves (1 <= waves <= MAXW):
+// reads the next power of two >= waves rows, not MAXW, so a one-wave launch
+// reads one.
+template <int MAXW, typename T, typename Term>
+__device__ __forceinline__ T sum_waves_in_order(int waves, Term term) {
+  static_assert(MAXW == 8 || MAXW == 16, "8 or 16 waves at most");
+  if (waves == 1) return term(0);
+  if (waves <= 2) return sum_in_order<2, T>(waves, term);
+  if (waves <= 4) return sum_in_order<4, T>(waves, term);
+  if (MAXW == 8 || waves <= 8) return sum_in_order<8, T>(waves, term);
+  return sum_in_order<MAXW, T>(waves, term);
+}
+
 // FP32 -> bfloat16 bits, round to nearest even; NaN stays a quiet NaN.
 __device__ __forceinline__ unsigned f32_to_bf16(float f) {
   unsigned u = __float_as_uint(f);

@@ -105,10 +105,8 @@ __global__ __launch_bounds__(THREADS) void gemm_dot2_kernel(
   const int r = lane / MT, t = lane % MT;
   const bool live = lane < kOut && t < M;
   float part = 0.f;
-  if (lane < kOut) {
-    part = red[0][lane];
-    for (int v2 = 1; v2 < waves; ++v2) part += red[v2][lane];
-  }
+  if (lane < kOut)
+    part = sum_waves_in_order<THREADS / 64, float>(waves, [&](int v2) { return red[v2][lane]; });
 
   if (!live) return;
   if (S == 1) {

@@ -166,8 +166,8 @@ __device__ __forceinline__ bool dot2_ring_tile(const RingItems &items, const Dot
   __syncthreads();
   if (wave == 0 && lane < kOut) {
     const int r = lane / MT, t = lane % MT;
-    float part = red[P][0][lane];
-    for (int v2 = 1; v2 < waves; ++v2) part += red[P][v2][lane];
+    const float part =
+        sum_waves_in_order<WAVES, float>(waves, [&](int v2) { return red[P][v2][lane]; });
     if (t < a.M) items.y[item][(size_t)t * a.N + f0 + r] = (uint16_t)f32_to_bf16(part);
   }
   s = ns;
@@ -311,8 +311,8 @@ __device__ __forceinline__ bool blocks_ring_tile(const RingItems &items, const D
     for (int o0 = 0; o0 < kOut; o0 += 64) {
       const int o = o0 + lane;
       if (o < kOut) {
-        float part = red[P][0][o];
-        for (int v2 = 1; v2 < waves; ++v2) part += red[P][v2][o];
+        const float part =
+            sum_in_order<WAVES, float>(waves, [&](int v2) { return red[P][v2][o]; });
         const int t = blocks::output_token(o, R4), r = blocks::output_row(o, R4);
         if (t < a.M) items.y[item][(size_t)t * a.N + f0 + r] = (uint16_t)f32_to_bf16(part);
       }
