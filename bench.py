@@ -739,33 +739,48 @@ def _graph_us(fn, stream, reps: int = 10) -> float:
 
 
 def stream_ceiling(sk, dev, stream, ring) -> dict:
-    """The stream reference (skinny_ceiling_stream of libskinny_ceiling) reading each
-    weight of a ring once per launch, graphs of RING launches as the calls
-    are timed; best of 1, 2, 4, 8 loads per lane."""
+    """The stream references of libskinny_ceiling reading each weight of a
+    ring once per launch, graphs of RING launches as the calls are timed;
+    best of 1, 2, 4, 8 loads per lane: skinny_ceiling_stream (loads only) and
+    skinny_ceiling_stream_store (the loads, then the cross-wave combine and
+    store a GEMM workgroup ends with)."""
     import torch
 
     from moe_decode_skinny_amd import ceiling as cl
 
     nbytes = ring[0].numel() * ring[0].element_size()
-    by_l = {}
+    by_l, by_l_store = {}, {}
     for L in (1, 2, 4, 8):
         sinks = [torch.zeros(nbytes // (8192 * L), dtype=torch.int32, device=dev) for _ in ring]
         by_l[L] = _graph_us(lambda: [cl.skinny_ceiling_stream(w, s, L)
                                      for w, s in zip(ring, sinks)], stream)
         del sinks
+        outs = [torch.zeros(64 * nbytes // (8192 * L), dtype=torch.int32, device=dev)
+                for _ in ring]
+        by_l_store[L] = _graph_us(lambda: [cl.skinny_ceiling_stream_store(w, o, L)
+                                           for w, o in zip(ring, outs)], stream)
+        del outs
     L = min(by_l, key=by_l.get)
     us = by_l[L]
+    Ls = min(by_l_store, key=by_l_store.get)
+    us_s = by_l_store[Ls]
     return {"bytes": nbytes, "stream_us": round(us, 3),
             "stream_GBs": round(nbytes / (us * 1e-6) / 1e9, 1),
             "stream_pct_peak": round(100 * nbytes / (us * 1e-6) / 1e9 / PEAK_GBS, 2),
             "stream_loads_per_lane": L, "stream_workgroups": nbytes // (8192 * L),
-            "stream_us_by_loads_per_lane": {str(k): round(v, 3) for k, v in by_l.items()}}
+            "stream_us_by_loads_per_lane": {str(k): round(v, 3) for k, v in by_l.items()},
+            "stream_store_us": round(us_s, 3),
+            "stream_store_pct_peak": round(100 * nbytes / (us_s * 1e-6) / 1e9 / PEAK_GBS, 2),
+            "stream_store_loads_per_lane": Ls,
+            "stream_store_us_by_loads_per_lane": {str(k): round(v, 3)
+                                                  for k, v in by_l_store.items()}}
 
 
 def ceiling_timing(sk, dev, stream, ring):
     """What one launch on this device reaches by itself, measured as the calls
     are (graphs of 60 launches over the same 60-layer weight ring): an empty
-    kernel, and the stream reference reading each 8 MiB weight once."""
+    kernel, and the stream references reading each 8 MiB weight once (loads
+    only, and loads then a GEMM workgroup's combine and store)."""
     from moe_decode_skinny_amd import ceiling as cl
 
     empty = _graph_us(lambda: [cl.skinny_ceiling_empty(dev) for _ in range(RING)], stream)
@@ -828,6 +843,8 @@ def shard_timing(sk, synthetic, dev, stream, N2, K2, ms, wseed, xseed, reps):
         b = algorithmic_bytes(M, N2, K2)
         out[str(M)] = {"walk": walk_record(sk, M, N2, K2), "us_per_call": round(single, 3),
                        "fraction_of_stream_ceiling": round(ceiling["stream_us"] / single, 4),
+                       "fraction_of_stream_store_ceiling": round(
+                           ceiling["stream_store_us"] / single, 4),
                        "pct_peak_call": round(100 * b / (single * 1e-6) / 1e9 / PEAK_GBS, 2),
                        "ring_us_per_item": round(item, 3),
                        "pct_peak_ring": round(100 * b / (item * 1e-6) / 1e9 / PEAK_GBS, 2)}
@@ -979,6 +996,8 @@ def main():
                        "walk": walk_record(sk, M, N, K),
                        "us_per_call": round(per_kernel[M], 3),
                        "fraction_of_stream_ceiling": round(ceiling["stream_us"] / per_kernel[M], 4),
+                       "fraction_of_stream_store_ceiling": round(
+                           ceiling["stream_store_us"] / per_kernel[M], 4),
                        "GBs": round(algorithmic_bytes(M) / (per_kernel[M] * 1e-6) / 1e9, 1),
                        "pct_peak": round(100 * algorithmic_bytes(M) / (per_kernel[M] * 1e-6)
                                          / 1e9 / PEAK_GBS, 2)}
@@ -1008,7 +1027,9 @@ def main():
                      "traced": traced_call(dom, sk)},
         "per_m": detail,
         "ceiling": {**ceiling,
-                    "dominant_call_fraction": round(ceiling["stream_us"] / per_kernel[dom], 4)},
+                    "dominant_call_fraction": round(ceiling["stream_us"] / per_kernel[dom], 4),
+                    "dominant_call_fraction_of_stream_store": round(
+                        ceiling["stream_store_us"] / per_kernel[dom], 4)},
         "epilogue": epi,
         "ring": ring_out,
         "oproj": oproj_out,

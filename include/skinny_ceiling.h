@@ -7,10 +7,12 @@
  * The decode GEMM's dominant cost is streaming its weight once ("unpooler"
  * page, vllm.models.muse_spark.nvidia.specialized_decode.cutedsl.gemm.unpooler,
  * module description: weights are loaded first, and the call is one pass over
- * them).  These two calls measure, on the caller's device and stream, what
- * one launch costs by itself and how fast one launch can stream a buffer the
- * way the GEMM kernels stream weights, so that a GEMM call's time can be set
- * against the ceiling a single launch reaches.
+ * them).  These calls measure, on the caller's device and stream, what one
+ * launch costs by itself, how fast one launch can stream a buffer the way the
+ * GEMM kernels stream weights, and how fast when it also ends as a GEMM
+ * workgroup does (words combined across its waves through LDS, then stored),
+ * so that a GEMM call's time can be set against the ceiling a single launch
+ * reaches.
  *
  * Conventions: pointers are device pointers owned by the caller; `stream` is
  * a hipStream_t (NULL = the default stream) of the calling thread's current
@@ -45,6 +47,19 @@ int skinny_ceiling_empty(void *stream);
  * Errors: -1 (bad pointer, alignment or size), -3, -4. */
 int skinny_ceiling_stream(const void *src, long long bytes, void *sink, int loads_per_lane,
                           void *stream);
+
+/* Measurement reference (unpooler page, module description: the cost of one
+ * call is its weight stream, and the call ends by storing its result): the
+ * loads of skinny_ceiling_stream, same layout and sizes, then each
+ * workgroup b stores 64 words:
+ *   out[b * 64 + l] = XOR over waves w = 0..7 and loads i of the four 32-bit
+ *                     words thread 64 w + l read in load i
+ *   out   device u32 [64 * bytes / (8192 * loads_per_lane)], 4-byte aligned
+ * Each wave's words pass through LDS and wave 0 combines them after a
+ * barrier, as a GEMM workgroup sums its waves' partials before its store.
+ * Errors: -1 (bad pointer, alignment or size), -3, -4. */
+int skinny_ceiling_stream_store(const void *src, long long bytes, void *out, int loads_per_lane,
+                                void *stream);
 
 /* The reason for this thread's last non-zero status, "" if none (as
  * skinny_last_error does for libskinny; unpooler page,

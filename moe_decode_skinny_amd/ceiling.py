@@ -1,8 +1,9 @@
 """Binding of libskinny_ceiling.so (include/skinny_ceiling.h): the benchmark's
 measurement references, a library of their own beside libskinny.  Not steps
-of the method: one empty launch, and one launch that streams a buffer the way
+of the method: one empty launch, one launch that streams a buffer the way
 the GEMM kernels stream weights (unpooler page, module description: a decode
-GEMM call is one pass over its weight).  Argument marshalling only; raises
+GEMM call is one pass over its weight), and that stream ended as a GEMM
+workgroup ends (a cross-wave combine through LDS, then a store).  Argument marshalling only; raises
 ImportError when the library is not built (there is no fallback).
 """
 from __future__ import annotations
@@ -24,6 +25,8 @@ _lib.skinny_ceiling_empty.argtypes = [_vp]
 _lib.skinny_ceiling_empty.restype = _i
 _lib.skinny_ceiling_stream.argtypes = [_vp, ctypes.c_longlong, _vp, _i, _vp]
 _lib.skinny_ceiling_stream.restype = _i
+_lib.skinny_ceiling_stream_store.argtypes = [_vp, ctypes.c_longlong, _vp, _i, _vp]
+_lib.skinny_ceiling_stream_store.restype = _i
 _lib.skinny_ceiling_last_error.argtypes = []
 _lib.skinny_ceiling_last_error.restype = ctypes.c_char_p
 
@@ -68,5 +71,23 @@ def skinny_ceiling_stream(src, sink, loads_per_lane: int = 4, stream=None) -> No
                                           _stream(stream, src.device)))
 
 
-__all__ = ["skinny_ceiling_empty", "skinny_ceiling_stream", "skinny_ceiling_last_error",
-           "LIB_PATH"]
+def skinny_ceiling_stream_store(src, out, loads_per_lane: int = 1, stream=None) -> None:
+    """The loads of skinny_ceiling_stream, then 64 words per workgroup combined
+    across its waves through LDS and stored; out is int32 [64 * src bytes /
+    (8192 * loads_per_lane)] (include/skinny_ceiling.h)."""
+    import torch
+
+    if not isinstance(src, torch.Tensor) or not src.is_cuda or not src.is_contiguous():
+        raise ValueError("src must be a contiguous device tensor")
+    op = _dev_tensor(out, "out", torch.int32)
+    nbytes = src.numel() * src.element_size()
+    if loads_per_lane in (1, 2, 4, 8) and out.numel() * 8192 * loads_per_lane != 64 * nbytes:
+        raise ValueError("out must hold 64 words per 8192 * loads_per_lane bytes of src")
+    _common_device(("src", src), ("out", out))
+    with _on(src.device):
+        _check(_lib.skinny_ceiling_stream_store(src.data_ptr(), nbytes, op, int(loads_per_lane),
+                                                _stream(stream, src.device)))
+
+
+__all__ = ["skinny_ceiling_empty", "skinny_ceiling_stream", "skinny_ceiling_stream_store",
+           "skinny_ceiling_last_error", "LIB_PATH"]

@@ -113,6 +113,7 @@ def test_library_exports_every_declared_symbol(sk):
     assert not missing, missing
     # the measurement references live only in their own library
     assert not hasattr(lib, "skinny_ceiling_stream") and not hasattr(lib, "skinny_ceiling_empty")
+    assert not hasattr(lib, "skinny_ceiling_stream_store")
 
 
 def test_ceiling_library_exports_its_symbols():
@@ -610,13 +611,14 @@ def test_binding_keeps_every_argument_on_one_device(sk):
         sk._stream(OnDevice("cuda:1"), torch.device("cuda:0"))
 
 
-def test_ceiling_stream_argument_checks(sk):
-    """The stream reference rejects bad sizes, load counts and pointers before
+@pytest.mark.parametrize("name", ["skinny_ceiling_stream", "skinny_ceiling_stream_store"])
+def test_ceiling_stream_argument_checks(sk, name):
+    """The stream references reject bad sizes, load counts and pointers before
     touching a device."""
     from moe_decode_skinny_amd import ceiling
 
     lib = ctypes.CDLL(ceiling.LIB_PATH)
-    fn = lib.skinny_ceiling_stream
+    fn = getattr(lib, name)
     fn.argtypes = [ctypes.c_void_p, ctypes.c_longlong, ctypes.c_void_p, ctypes.c_int,
                    ctypes.c_void_p]
     fn.restype = ctypes.c_int
@@ -628,3 +630,4 @@ def test_ceiling_stream_argument_checks(sk):
         assert fn(src, nbytes, p, lpl, None) == sk.SKINNY_EINVAL, needle
         msg = ceiling.skinny_ceiling_last_error()
         assert needle in msg, (needle, msg)
+    assert fn(p, 8192, ctypes.c_void_p(4098), 1, None) == sk.SKINNY_EINVAL

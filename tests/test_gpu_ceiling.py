@@ -1,6 +1,7 @@
 """The benchmark's measurement reference kernels (libskinny_ceiling,
-include/skinny_ceiling.h): the stream reference reads exactly the bytes its
-layout says, once."""
+include/skinny_ceiling.h): the stream references read exactly the bytes
+their layout says, once, and the stream-and-store reference stores the
+documented XOR of them."""
 import numpy as np
 import pytest
 
@@ -35,3 +36,24 @@ def test_stream_reference_reads_its_layout(L):
     ceiling.skinny_ceiling_empty(0)
     torch.cuda.synchronize()
     assert np.array_equal(sink.cpu().numpy(), expected)
+
+
+@pytest.mark.parametrize("L", [1, 2, 4, 8])
+def test_stream_store_reference_stores_its_xor(L):
+    """out[b * 64 + l] is the XOR of every word threads 64 w + l (w < 8) of
+    workgroup b read, by the documented layout."""
+    import torch
+
+    from moe_decode_skinny_amd import ceiling
+
+    print(f"ceiling stream-and-store L={L}", flush=True)
+    nwg = 5
+    rng = np.random.default_rng(90 + L)
+    data = rng.integers(0, 2 ** 32, 2048 * L * nwg, dtype=np.uint64).astype(np.uint32)
+    view = data.reshape(nwg, L, 8, 64, 4)  # [b][i][wave][lane][j]
+    want = np.bitwise_xor.reduce(view.transpose(0, 3, 1, 2, 4).reshape(nwg, 64, -1), axis=2)
+    src = torch.from_numpy(data.view(np.int32)).to("cuda")
+    out = torch.full((nwg * 64,), 7, dtype=torch.int32, device="cuda")
+    ceiling.skinny_ceiling_stream_store(src, out, L)
+    torch.cuda.synchronize()
+    assert np.array_equal(out.cpu().numpy().view(np.uint32), want.ravel())
