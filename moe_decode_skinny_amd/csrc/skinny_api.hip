@@ -746,7 +746,7 @@ using namespace skinny;
 
 extern "C" {
 
-int skinny_version(void) { return 108; }
+int skinny_version(void) { return 109; }
 
 const char *skinny_last_error(void) { return g_error; }
 
