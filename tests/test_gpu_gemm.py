@@ -169,6 +169,19 @@ def test_exact_integer_inputs_bit_exact(gpu_lib, M):
         assert np.array_equal(y, ref), f"{l} not bit-exact at M={M}"
 
 
+@pytest.mark.parametrize("N,K", [(1024, 4096), (512, 8192), (4096, 8192), (8192, 1024)])
+@pytest.mark.parametrize("M", [9, 16])
+def test_exact_integer_inputs_at_the_shard_launches(gpu_lib, N, K, M):
+    """The chooser's launch on each shard shape, the one the benchmark times
+    (at 9..16 tokens the unpooler and pooler shards take token groups, the
+    full pooler a walk), reproduces the oracle bit for bit on integer inputs
+    whose every partial sum is exact in FP32."""
+    x, w = synthetic.exact_integer_inputs(M=16, N=N, K=K, seed=M)
+    _say(f"exact integers at the chooser's launch: M={M} N={N} K={K} "
+         f"{tuple(gpu_lib.skinny_choose(M, N, K, 0))}")
+    assert np.array_equal(_run(gpu_lib, x, w, M), oracle.gemm_bf16(x[:M], w, THREADS))
+
+
 @pytest.mark.parametrize("M,N,K", [(1, 16, 8), (16, 16, 8), (2, 16, 32), (5, 80, 8), (16, 16, 4104),
                                    (1, 16, 65536), (16, 32, 65536), (4, 65536, 64),
                                    (16, 49152, 520), (12, 2048, 4096), (9, 1024, 8192),
