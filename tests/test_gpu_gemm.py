@@ -337,6 +337,26 @@ def test_random_shapes_through_the_choosers(gpu_lib):
             assert_gemm_close(from_dev(ys[i]), ref_i, f"case {case} ring item {i}")
 
 
+@pytest.mark.parametrize("M,N,K,splits", [
+    (9, 512, 4096, 0), (16, 768, 8192, 0), (12, 1008, 4096, 0), (16, 1536, 4096, 0),
+    (13, 2032, 4096, 0), (10, 512, 6000, 0),
+    (16, 512, 8192, 4), (9, 1024, 4096, 2), (12, 2048, 4096, 2), (16, 768, 8192, 8),
+    (13, 1024, 6144, 4)])
+def test_rule_launches_for_many_tokens(gpu_lib, M, N, K, splits):
+    """Off the measured table, 9..16 tokens on K = 4096..8192 take the
+    16-block launch: without a split count the rows and token groups the rule
+    picks, with one its in-kernel split (8 rows, two token groups up to
+    N = 1024). Each against the oracle, and bitwise equal on a second run."""
+    x, w = synthetic.gemm_inputs(N=N, K=K, seed=5000 + M + N + K)
+    launch = gpu_lib.skinny_choose(M, N, K, splits)
+    _say(f"rule launch M={M} N={N} K={K} splits={splits}: {tuple(launch)}")
+    assert launch.path == gpu_lib.SKINNY_PATH_MFMA_4X4
+    assert launch.splits == max(splits, 1)
+    y = _run(gpu_lib, x, w, M, splits=splits)
+    assert_gemm_close(y, oracle.gemm_bf16(x[:M], w, THREADS), f"M={M} N={N} K={K} S={splits}")
+    assert np.array_equal(_run(gpu_lib, x, w, M, splits=splits, poison=False), y)
+
+
 def test_blocks_split_in_kernel_equals_the_two_kernel_split(gpu_lib):
     """The 16-block path sums its splits inside the kernel (the last of a
     group's workgroups to finish) when the hand-off counters cover the
