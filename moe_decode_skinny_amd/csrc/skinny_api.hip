@@ -198,9 +198,9 @@ struct TableEntry {
 static const TableEntry kTable[] = {
     // unpooler shard
     {1024, 4096, 1, 1, {SKINNY_PATH_DOT2, 1, 2, 4, 1, 2}, {}},
-    {1024, 4096, 2, 2, {SKINNY_PATH_DOT2, 1, 2, 4, 1, 2}, {2, 256}},
+    {1024, 4096, 2, 2, {SKINNY_PATH_DOT2, 1, 8, 1, 1, 2}, {}},
     {1024, 4096, 3, 4, {SKINNY_PATH_DOT2, 1, 4, 2, 1, 2}, {2, 256}},
-    {1024, 4096, 5, 8, {SKINNY_PATH_MFMA_4X4, 1, 4, 8, 1, 4}, {}},
+    {1024, 4096, 5, 8, {SKINNY_PATH_MFMA_4X4, 1, 8, 4, 1, 4}, {}},
     {1024, 4096, 9, 16, {SKINNY_PATH_MFMA_4X4, 1, 8, 4, 2, 8}, {}},
     // o_proj shard
     {8192, 1024, 1, 1, {SKINNY_PATH_DOT2, 1, 1, 2, 1, 2}, {}},
