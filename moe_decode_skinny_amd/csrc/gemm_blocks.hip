@@ -25,9 +25,9 @@
 // Reduction in an order fixed by the launch shape (module description): the
 // 16 blocks across lanes, waves 0..waves-1 in order through LDS, and with
 // S > 1 an FP32 partial per split, the splits summed s = 0..S-1 in order by
-// the last of the group's S workgroups to finish (see block_handoff), or,
-// for launches with more groups than the hand-off counters cover, by the
-// split_reduce kernel; both give the same bits.
+// the last of an output block's S workgroups to finish (see block_handoff),
+// or, for launches with more output blocks than the hand-off counters
+// cover, by the split_reduce kernel; both give the same bits.
 //
 // Against DOT2 this replaces 4 VALU instructions per (row, token, 8 K) and a
 // 64-lane reduce-scatter with one MFMA per (row set, token set, 4 K x 16
@@ -89,11 +89,11 @@ __device__ __forceinline__ float sum_splits(int S, Term term) {
   }
 }
 
-// The split hand-off of group `group` (S > 1), in wave 0 of each of its S
+// The split hand-off of one output block (S > 1), in wave 0 of each of its S
 // workgroups: store this split's partial, then mark the arrival in the
-// group's counter word (bit s, and bit 16 + XCD id), one atomic OR whose
+// block's counter word (bit s, and bit 16 + XCD id), one atomic OR whose
 // returned value tells the last arriver.  Returns true in the last one.
-// The S workgroups of a group are dealt to one XCD (ids congruent mod 8, see
+// The S workgroups of a block are dealt to one XCD (ids congruent mod 8, see
 // the kernel), so partials pass through that XCD's L2: plain stores waited
 // for before the atomic, and in the last arriver an L1 invalidate and loads
 // that bypass L1.  *mixed is set when the arrivals came from more than one
