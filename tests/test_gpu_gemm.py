@@ -497,6 +497,43 @@ def test_blocks_split_recompute_path_is_bitwise_the_handoff(gpu_lib, tmp_path):
     torch.cuda.synchronize()
 
 
+def test_handoff_split_counts_interleaved_on_the_same_blocks(gpu_lib):
+    """The in-kernel hand-off's counter word and partial slots of an output
+    block are shared by every split count: each call must leave the counter
+    at zero and read only partials its own workgroups stored, never those an
+    earlier call (another split count, other inputs) left behind.  The
+    pooler shard at 16 tokens on 4-row blocks with 2, 4, 8 and 16 splits
+    (the same 128 output blocks) and four activation sets, called in
+    rotating orders: every output equals its first call's bits and the
+    oracle."""
+    import torch
+
+    M, N, K = 16, 512, 8192
+    _, w_bits = synthetic.gemm_inputs(N=N, K=K, seed=71)
+    xs = [synthetic.gemm_inputs(N=16, K=K, seed=72 + j)[0][:M] for j in range(4)]
+    w = to_dev(w_bits)
+    xd = [to_dev(xb) for xb in xs]
+    launches = {S: gpu_lib.Launch(3, S, K // (S * 512), 4, 1, 4) for S in (2, 4, 8, 16)}
+    y = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+    first = {}
+    for rnd in range(3):
+        order = [(S, j) for j in range(4) for S in (2, 4, 8, 16)]
+        order = order[5 * rnd:] + order[:5 * rnd]
+        if rnd == 2:
+            order.reverse()
+        for S, j in order:
+            _say(f"interleaved hand-off round {rnd}: S={S} x{j}")
+            y.fill_(7.0)
+            gpu_lib.skinny_gemm_bf16_launch(xd[j], w, y, launches[S])
+            torch.cuda.synchronize()
+            got = from_dev(y).copy()
+            if (S, j) not in first:
+                assert_gemm_close(got, oracle.gemm_bf16(xs[j], w_bits, THREADS), f"S={S} x{j}")
+                first[(S, j)] = got
+            else:
+                assert np.array_equal(got, first[(S, j)]), f"round {rnd} S={S} x{j}"
+
+
 def test_in_kernel_split_across_graph_replays(gpu_lib):
     """The pooler shard at 16 tokens in the 16-block launch with 4 splits
     summed inside the kernel; its hand-off counters must be back at zero
