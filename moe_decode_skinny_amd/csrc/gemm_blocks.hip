@@ -129,16 +129,24 @@ __device__ __forceinline__ bool block_handoff(float *__restrict__ slots,
   return true;
 }
 
+// mode: bit 0 the splits are summed in the kernel (counters and partial
+// slots valid), bit 1 that hand-off always recomputes (test hook).  The
+// arguments the main loop needs come first and include the wave count, so
+// the start reads no implicit argument (blockDim).  Unlike the other GEMM
+// kernels this one is built without argument preloading: its 16-token
+// launch measured slower with it.
+constexpr int kModeHandoff = 1, kModeRecompute = 2;
+
 template <int R4, int CHUNKS, int Q, int THREADS>
 __global__ __launch_bounds__(THREADS) void gemm_blocks_kernel(
-    const uint16_t *__restrict__ x, const uint16_t *__restrict__ w,
-    uint16_t *__restrict__ y, float *__restrict__ partials, unsigned *__restrict__ counters,
-    int M, int N, int K, int S, int H, int groups, int kw, int force_recompute, Publish pub) {
+    const uint16_t *__restrict__ x, const uint16_t *__restrict__ w, int M, int N, int K,
+    int S, int H, int groups, int kw, int waves, int mode, uint16_t *__restrict__ y,
+    float *__restrict__ partials, unsigned *__restrict__ counters, Publish pub) {
   constexpr int kOut = kOutputs<R4, Q>, kPer = (kOut + 63) / 64;
   const int lane = threadIdx.x & 63;
-  if ((S == 1 || counters) && blockIdx.x == 0 && threadIdx.x == 0) publish_stage_word(pub);
+  if ((S == 1 || (mode & kModeHandoff)) && blockIdx.x == 0 && threadIdx.x == 0)
+    publish_stage_word(pub);
   const int wave = wave_index();
-  const int waves = blockDim.x >> 6;
 
   // Workgroup -> (row group, token group h, split s): workgroups are dealt
   // to the XCDs round-robin (ids congruent mod 8 share an XCD, also when the
@@ -169,7 +177,7 @@ __global__ __launch_bounds__(THREADS) void gemm_blocks_kernel(
   float part[kPer];
   sum_waves<kOut, kPer, THREADS / 64>(red, waves, lane, part);
 
-  if (S > 1 && !counters) {  // FP32 partial of split s for split_reduce: [s][token][feature]
+  if (S > 1 && !(mode & kModeHandoff)) {  // FP32 partial of split s for split_reduce: [s][token][feature]
 #pragma unroll
     for (int i = 0; i < kPer; ++i) {
       const int o = i * 64 + lane;
@@ -186,7 +194,7 @@ __global__ __launch_bounds__(THREADS) void gemm_blocks_kernel(
                              &mixed))
       return;
     float sum[kPer];
-    if (!mixed && !force_recompute) {
+    if (!mixed && !(mode & kModeRecompute)) {
       const __amdgpu_buffer_rsrc_t res =
           buffer_rsrc(partials + (size_t)ob * S * kOut, (unsigned)(S * kOut * 4));
 #pragma unroll
@@ -234,8 +242,8 @@ __global__ __launch_bounds__(THREADS) void gemm_blocks_kernel(
   }
 }
 
-using BlocksKernel = void (*)(const uint16_t *, const uint16_t *, uint16_t *, float *,
-                              unsigned *, int, int, int, int, int, int, int, int, Publish);
+using BlocksKernel = void (*)(const uint16_t *, const uint16_t *, int, int, int, int, int, int,
+                              int, int, int, uint16_t *, float *, unsigned *, Publish);
 
 // Register budget per lane: weights 4 * R4 * CHUNKS, activations
 // 4 * Q * CHUNKS, sums 4 * Q * R4 (160 at 512 threads, 112 at 1024).
@@ -314,9 +322,10 @@ hipError_t launch_gemm_blocks(const uint16_t *x, const uint16_t *w, uint16_t *y,
   const bool handoff = l.splits > 1 && ws.counters && blocks <= kMaxHandoffGroups &&
                        (size_t)blocks * l.splits * 16 * q * (l.rows / 4) <= ws.partial_floats;
   dim3 grid(groups * H * l.splits), block(64 * l.waves);
-  hipLaunchKernelGGL(k, grid, block, 0, stream, x, w, y, ws.partials,
-                     handoff ? ws.counters : nullptr, M, N, K, l.splits, H, groups,
-                     kBlockK * l.chunks, ws.force_recompute ? 1 : 0, pub);
+  const int mode = (handoff ? kModeHandoff : 0) | (ws.force_recompute ? kModeRecompute : 0);
+  hipLaunchKernelGGL(k, grid, block, 0, stream, x, w, M, N, K, l.splits, H, groups,
+                     kBlockK * l.chunks, l.waves, mode, y, ws.partials,
+                     handoff ? ws.counters : nullptr, pub);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || l.splits == 1 || handoff) return e;
   return launch_split_reduce(ws.partials, y, M, N, l.splits, pub, stream);

@@ -22,16 +22,18 @@ namespace {
 using namespace dot2;
 
 // THREADS: the launch bound, 512, or 1024 for the register-light variants
-// that run 16 waves (long K at one chunk per wave).
+// that run 16 waves (long K at one chunk per wave).  The arguments the main
+// loop needs come first, the workgroup's wave count among them: the first
+// 14 argument dwords arrive preloaded in SGPRs, so the loads issue without
+// waiting for a kernel-argument fetch (blockDim would be one).
 template <int ROWS, int CHUNKS, int MT, int THREADS>
 __global__ __launch_bounds__(THREADS) void gemm_dot2_kernel(
-    const uint16_t *__restrict__ x, const uint16_t *__restrict__ w,
-    uint16_t *__restrict__ y, float *__restrict__ partials, int M, int N, int K,
-    int S, int groups, int kw, Publish pub) {
+    const uint16_t *__restrict__ x, const uint16_t *__restrict__ w, int M, int N, int K,
+    int S, int groups, int kw, int waves, uint16_t *__restrict__ y,
+    float *__restrict__ partials, Publish pub) {
   const int lane = threadIdx.x & 63;
   if (S == 1 && blockIdx.x == 0 && threadIdx.x == 0) publish_stage_word(pub);
   const int wave = wave_index();
-  const int waves = blockDim.x >> 6;
 
   int group, s;
   const int b = blockIdx.x;
@@ -117,8 +119,8 @@ __global__ __launch_bounds__(THREADS) void gemm_dot2_kernel(
     partials[((size_t)s * M + t) * N + f0 + r] = part;
 }
 
-using Dot2Kernel = void (*)(const uint16_t *, const uint16_t *, uint16_t *,
-                            float *, int, int, int, int, int, int, Publish);
+using Dot2Kernel = void (*)(const uint16_t *, const uint16_t *, int, int, int, int, int, int,
+                            int, uint16_t *, float *, Publish);
 
 // Register budget per lane: weights 4 * ROWS * CHUNKS, activations
 // 4 * MT * CHUNKS, sums ROWS * MT: at most 160 for 8 waves, 112 for the
@@ -199,8 +201,8 @@ hipError_t launch_gemm_dot2(const uint16_t *x, const uint16_t *w, uint16_t *y,
   Dot2Kernel k = pick(l.rows, l.chunks, dot2_token_tile(M), l.waves);
   const int groups = N / l.rows;
   dim3 grid(groups * l.splits), block(64 * l.waves);
-  hipLaunchKernelGGL(k, grid, block, 0, stream, x, w, y, partials, M, N, K, l.splits,
-                     groups, kDot2K * l.chunks, pub);
+  hipLaunchKernelGGL(k, grid, block, 0, stream, x, w, M, N, K, l.splits, groups,
+                     kDot2K * l.chunks, l.waves, y, partials, pub);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || l.splits == 1) return e;
   return launch_split_reduce(partials, y, M, N, l.splits, pub, stream);

@@ -40,14 +40,17 @@ namespace {
 constexpr int mfma_max_threads(int chunks) { return chunks >= 16 ? 512 : 1024; }
 
 template <int CHUNKS, int ACCS>
+// The arguments the main loop needs come first, the workgroup's wave count
+// among them (the first 14 argument dwords arrive preloaded in SGPRs;
+// blockDim would be a kernel-argument fetch).
 __global__ __launch_bounds__(mfma_max_threads(CHUNKS)) void gemm_mfma_kernel(
-    const uint16_t *__restrict__ x, const uint16_t *__restrict__ w,
-    uint16_t *__restrict__ y, float *__restrict__ partials, int M, int N, int K,
-    int S, int groups, int F, int kw, Publish pub) {
+    const uint16_t *__restrict__ x, const uint16_t *__restrict__ w, int M, int N, int K,
+    int S, int groups, int F, int kw, int waves, uint16_t *__restrict__ y,
+    float *__restrict__ partials, Publish pub) {
   const int lane = threadIdx.x & 63;
   if (S == 1 && blockIdx.x == 0 && threadIdx.x == 0) publish_stage_word(pub);
   const int wave = wave_index();
-  const int waves = blockDim.x >> 6;
+  const int threads = waves * 64;
   const int KW = waves / F;
   const int f = wave / KW, q = wave - f * KW;
   const int row = lane & 15;  // weight row (A) / token (B) of this lane
@@ -101,12 +104,12 @@ __global__ __launch_bounds__(mfma_max_threads(CHUNKS)) void gemm_mfma_kernel(
   const int xstride = kslice + 8;
   const int seg_row = kslice / 8;
   const int segs = M * seg_row;
-  const int iters = (segs + (int)blockDim.x - 1) / (int)blockDim.x;
+  const int iters = (segs + threads - 1) / threads;
   u32x4 xv[CHUNKS];
 #pragma unroll
   for (int i = 0; i < CHUNKS; ++i) {
     if (i < iters) {
-      const int j = threadIdx.x + i * blockDim.x;
+      const int j = threadIdx.x + i * threads;
       const int t = j / seg_row, k = kbase + (j - t * seg_row) * 8;
       xv[i] = __builtin_amdgcn_raw_buffer_load_b128(
           xres, (j < segs && k < K) ? (t * K + k) * 2 : kOutOfRange, 0, 0);
@@ -116,7 +119,7 @@ __global__ __launch_bounds__(mfma_max_threads(CHUNKS)) void gemm_mfma_kernel(
 #pragma unroll
   for (int i = 0; i < CHUNKS; ++i) {
     if (i < iters) {
-      const int j = threadIdx.x + i * blockDim.x;
+      const int j = threadIdx.x + i * threads;
       const int t = j / seg_row, c = j - t * seg_row;
       if (j < segs) *reinterpret_cast<u32x4 *>(xs + t * xstride + c * 8) = xv[i];
     }
@@ -166,8 +169,8 @@ __global__ __launch_bounds__(mfma_max_threads(CHUNKS)) void gemm_mfma_kernel(
   }
 }
 
-using MfmaKernel = void (*)(const uint16_t *, const uint16_t *, uint16_t *,
-                            float *, int, int, int, int, int, int, int, Publish);
+using MfmaKernel = void (*)(const uint16_t *, const uint16_t *, int, int, int, int, int, int,
+                            int, int, uint16_t *, float *, Publish);
 
 template <int C>
 MfmaKernel pick_accs(int accs) {
@@ -225,8 +228,8 @@ hipError_t launch_gemm_mfma(const uint16_t *x, const uint16_t *w, uint16_t *y,
   const int F = l.rows / kTileN;
   const int groups = N / l.rows;
   dim3 grid(groups * l.splits), block(64 * l.waves);
-  hipLaunchKernelGGL(k, grid, block, mfma_lds_bytes(M, l), stream, x, w, y, partials, M, N,
-                     K, l.splits, groups, F, kMfmaK * l.chunks, pub);
+  hipLaunchKernelGGL(k, grid, block, mfma_lds_bytes(M, l), stream, x, w, M, N, K, l.splits,
+                     groups, F, kMfmaK * l.chunks, l.waves, y, partials, pub);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || l.splits == 1) return e;
   return launch_split_reduce(partials, y, M, N, l.splits, pub, stream);

@@ -79,6 +79,17 @@ struct RingWalk {
   }
 };
 
+// The ring kernels' arguments: the first item's weights, the sizes, the wave
+// count and the walk come first, the item table last.  The first 14
+// argument dwords arrive preloaded in SGPRs, so a workgroup whose first tile
+// belongs to item 0 (every tile of a single GEMM run as a walk) starts its
+// weight stream without a kernel-argument fetch; the table is read as the
+// walk goes on.
+__device__ __forceinline__ const uint16_t *first_weights(const RingItems &items,
+                                                         const uint16_t *w_first, int item) {
+  return item == 0 ? w_first : items.w[item];
+}
+
 // ------------------------------------------------------------------ DOT2 ring
 // Issue the loads of ROWS weight rows of one tile (or of nothing: bytes = 0
 // turns every load into a zero read that touches no memory).
@@ -179,10 +190,11 @@ __device__ __forceinline__ bool dot2_ring_tile(const RingItems &items, const Dot
 // fit 16 waves (long K at one chunk per wave).
 template <int ROWS, int CHUNKS, int MT, int THREADS>
 __global__ __launch_bounds__(THREADS) void gemm_dot2_ring_kernel(
-    RingItems items, int M, int N, int K, RingWalk walk, int kw) {
+    const uint16_t *w_first, int M, int N, int K, int kw, int waves, int groups, int seg,
+    int spi, int segs, int local, RingItems items) {
   const int lane = threadIdx.x & 63;
   const int wave = wave_index();
-  const int waves = blockDim.x >> 6;
+  const RingWalk walk{groups, seg, spi, segs, local};
   const Dot2Args a{M, N, K};
   const int k0 = wave * kw + lane * 8;
   __shared__ float red[2][THREADS / 64][ROWS * MT];
@@ -190,8 +202,9 @@ __global__ __launch_bounds__(THREADS) void gemm_dot2_ring_kernel(
   // gridDim.x <= walk.segs, so every workgroup has a first tile.
   int s = blockIdx.x, sub = 0;
   u32x4 wa[ROWS][CHUNKS], wb[ROWS][CHUNKS], xv[MT][CHUNKS];
-  load_weights<ROWS, CHUNKS>(wa, items.w[walk.item(s)] + (size_t)walk.block(s, 0) * ROWS * K,
-                             (unsigned)(ROWS * K * 2), K, k0);
+  load_weights<ROWS, CHUNKS>(
+      wa, first_weights(items, w_first, walk.item(s)) + (size_t)walk.block(s, 0) * ROWS * K,
+      (unsigned)(ROWS * K * 2), K, k0);
   for (;;) {
     if (!dot2_ring_tile<ROWS, CHUNKS, MT, THREADS / 64, 0>(items, a, walk, s, sub, wa, wb, xv,
                                                             red, lane, wave, waves, k0))
@@ -202,7 +215,8 @@ __global__ __launch_bounds__(THREADS) void gemm_dot2_ring_kernel(
   }
 }
 
-using Dot2RingKernel = void (*)(RingItems, int, int, int, RingWalk, int);
+using Dot2RingKernel = void (*)(const uint16_t *, int, int, int, int, int, int, int, int, int,
+                                int, RingItems);
 
 // Register budget per lane: two weight buffers 8 * ROWS * CHUNKS,
 // activations 4 * MT * CHUNKS, sums ROWS * MT: at most 160 for 8 waves, 112
@@ -325,11 +339,12 @@ __device__ __forceinline__ bool blocks_ring_tile(const RingItems &items, const D
 
 template <int R4, int CHUNKS, int Q, int THREADS>
 __global__ __launch_bounds__(THREADS) void gemm_blocks_ring_kernel(
-    RingItems items, int M, int N, int K, RingWalk walk, int kw) {
+    const uint16_t *w_first, int M, int N, int K, int kw, int waves, int groups, int seg,
+    int spi, int segs, int local, RingItems items) {
   constexpr int ROWS = 4 * R4;
   const int lane = threadIdx.x & 63;
   const int wave = wave_index();
-  const int waves = blockDim.x >> 6;
+  const RingWalk walk{groups, seg, spi, segs, local};
   const Dot2Args a{M, N, K};
   const int k0 = wave * kw + lane * 8;
   __shared__ float red[2][THREADS / 64][blocks::kOutputs<R4, Q>];
@@ -338,7 +353,8 @@ __global__ __launch_bounds__(THREADS) void gemm_blocks_ring_kernel(
   int s = blockIdx.x, sub = 0;
   u32x4 wa[R4][CHUNKS], wb[R4][CHUNKS], xv[Q][CHUNKS];
   blocks::load_sets<R4, CHUNKS, kCacheNT>(
-      wa, buffer_rsrc(items.w[walk.item(s)] + (size_t)walk.block(s, 0) * ROWS * K,
+      wa, buffer_rsrc(first_weights(items, w_first, walk.item(s)) +
+                          (size_t)walk.block(s, 0) * ROWS * K,
                       (unsigned)(ROWS * K * 2)),
       K, k0);
   for (;;) {
@@ -551,10 +567,11 @@ __device__ __forceinline__ bool mfma_ring_tile(const RingItems &items, const Mfm
 // buffers of waves x 64 lanes x 16 bytes.
 template <int CHUNKS, int ACCS, bool STAGED>
 __global__ __launch_bounds__(mfma_ring_threads(CHUNKS)) void gemm_mfma_ring_kernel(
-    RingItems items, int M, int N, int K, RingWalk walk, int F, int kw) {
+    const uint16_t *w_first, int M, int N, int K, int kw, int waves, int F, int groups,
+    int seg, int spi, int segs, int local, RingItems items) {
   const int lane = threadIdx.x & 63;
   const int wave = wave_index();
-  const int waves = blockDim.x >> 6;
+  const RingWalk walk{groups, seg, spi, segs, local};
   const int KW = waves / F;
   const int f = wave / KW, q = wave - f * KW;
   const MfmaArgs a{M, N, K, F, KW, waves};
@@ -567,7 +584,8 @@ __global__ __launch_bounds__(mfma_ring_threads(CHUNKS)) void gemm_mfma_ring_kern
   int s = blockIdx.x, sub = 0;  // gridDim.x <= walk.segs
   u32x4 wa[CHUNKS], wb[CHUNKS], xv[CHUNKS];
   {
-    const uint16_t *w0 = items.w[walk.item(s)] + (size_t)(walk.block(s, 0) * F + f) * kTileN * K;
+    const uint16_t *w0 = first_weights(items, w_first, walk.item(s)) +
+                         (size_t)(walk.block(s, 0) * F + f) * kTileN * K;
     if constexpr (STAGED)
       load_tile_rows<CHUNKS>(wa, w0, (unsigned)(kTileN * K * 2), K, kq, lane);
     else
@@ -584,7 +602,8 @@ __global__ __launch_bounds__(mfma_ring_threads(CHUNKS)) void gemm_mfma_ring_kern
   }
 }
 
-using MfmaRingKernel = void (*)(RingItems, int, int, int, RingWalk, int, int);
+using MfmaRingKernel = void (*)(const uint16_t *, int, int, int, int, int, int, int, int, int,
+                                int, int, RingItems);
 
 template <int C, bool STAGED>
 MfmaRingKernel mfma_ring_pick_accs(int accs) {
@@ -669,19 +688,20 @@ hipError_t launch_gemm_ring(const RingItems &items, int count, int M, int N, int
   // XCD-local slots only when the workgroups divide evenly over the 8 XCDs.
   const int local =
       r.order == SKINNY_RING_XCD_LOCAL && r.workgroups % 8 == 0 ? (count / 8) * 8 * spi : 0;
-  const RingWalk walk{groups, r.segment, spi, count * spi, local};
+  const int segs = count * spi;
   if (l.path == SKINNY_PATH_MFMA || l.path == SKINNY_PATH_MFMA_LDS) {
     hipLaunchKernelGGL(mfma_ring_pick(l.chunks, l.accs, l.path == SKINNY_PATH_MFMA_LDS),
                        dim3(r.workgroups), dim3(64 * l.waves), mfma_ring_lds_bytes(l), stream,
-                       items, M, N, K, walk, l.rows / kTileN, kMfmaK * l.chunks);
+                       items.w[0], M, N, K, kMfmaK * l.chunks, l.waves, l.rows / kTileN, groups,
+                       r.segment, spi, segs, local, items);
   } else if (l.path == SKINNY_PATH_MFMA_4X4) {
     hipLaunchKernelGGL(blocks_ring_pick(l.rows, l.chunks, blocks_token_sets(M), l.waves),
-                       dim3(r.workgroups), dim3(64 * l.waves), 0, stream, items, M, N, K, walk,
-                       kBlockK * l.chunks);
+                       dim3(r.workgroups), dim3(64 * l.waves), 0, stream, items.w[0], M, N, K,
+                       kBlockK * l.chunks, l.waves, groups, r.segment, spi, segs, local, items);
   } else {
     hipLaunchKernelGGL(dot2_ring_pick(l.rows, l.chunks, dot2_token_tile(M), l.waves),
-                       dim3(r.workgroups),
-                       dim3(64 * l.waves), 0, stream, items, M, N, K, walk, kDot2K * l.chunks);
+                       dim3(r.workgroups), dim3(64 * l.waves), 0, stream, items.w[0], M, N, K,
+                       kDot2K * l.chunks, l.waves, groups, r.segment, spi, segs, local, items);
   }
   return hipGetLastError();
 }

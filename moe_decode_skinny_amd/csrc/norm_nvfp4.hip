@@ -70,11 +70,13 @@ __device__ __forceinline__ unsigned e2m1_rn_satfinite(double v) {
 
 constexpr int kQuantBlocks = kNormThreads / 4;  // 16-column blocks a workgroup quantises
 
+// The sizes come right after the inputs: the first 14 argument dwords
+// arrive preloaded in SGPRs, and the row index needs `parts` at once.
 template <bool QUANT>
 __global__ __launch_bounds__(kNormThreads) void rmsnorm_kernel(
-    const uint16_t *__restrict__ r, const uint16_t *__restrict__ w, float gain_center,
-    float eps, const float *__restrict__ global_scale, uint8_t *__restrict__ a,
-    uint8_t *__restrict__ a_sf, uint16_t *__restrict__ y, int P, int parts) {
+    const uint16_t *__restrict__ r, const uint16_t *__restrict__ w, int P, int parts,
+    float gain_center, float eps, const float *__restrict__ global_scale,
+    uint8_t *__restrict__ a, uint8_t *__restrict__ a_sf, uint16_t *__restrict__ y) {
   const int row = blockIdx.x / parts, part = blockIdx.x - row * parts;
   const int tid = threadIdx.x;
   const int blocks = P / 16;
@@ -142,11 +144,11 @@ hipError_t launch_rmsnorm(const uint16_t *r, const uint16_t *w, float gain_cente
   const int parts = (P / 16 + kQuantBlocks - 1) / kQuantBlocks;
   dim3 grid(parts * M), block(kNormThreads);
   if (quant)
-    hipLaunchKernelGGL(rmsnorm_kernel<true>, grid, block, 0, stream, r, w, gain_center,
-                       eps, global_scale, a, a_sf, y, P, parts);
+    hipLaunchKernelGGL(rmsnorm_kernel<true>, grid, block, 0, stream, r, w, P, parts,
+                       gain_center, eps, global_scale, a, a_sf, y);
   else
-    hipLaunchKernelGGL(rmsnorm_kernel<false>, grid, block, 0, stream, r, w, gain_center,
-                       eps, global_scale, a, a_sf, y, P, parts);
+    hipLaunchKernelGGL(rmsnorm_kernel<false>, grid, block, 0, stream, r, w, P, parts,
+                       gain_center, eps, global_scale, a, a_sf, y);
   return hipGetLastError();
 }
 
