@@ -199,7 +199,7 @@ static const TableEntry kTable[] = {
     // unpooler shard
     {1024, 4096, 1, 1, {SKINNY_PATH_DOT2, 1, 2, 4, 1, 2}, {}},
     {1024, 4096, 2, 2, {SKINNY_PATH_DOT2, 1, 8, 1, 1, 2}, {}},
-    {1024, 4096, 3, 4, {SKINNY_PATH_DOT2, 1, 4, 2, 1, 2}, {2, 256}},
+    {1024, 4096, 3, 4, {SKINNY_PATH_DOT2, 1, 8, 1, 1, 4}, {}},
     {1024, 4096, 5, 8, {SKINNY_PATH_MFMA_4X4, 1, 8, 4, 1, 4}, {}},
     {1024, 4096, 9, 16, {SKINNY_PATH_MFMA_4X4, 1, 8, 4, 2, 8}, {}},
     // o_proj shard
@@ -214,8 +214,7 @@ static const TableEntry kTable[] = {
     // full pooler
     {4096, 8192, 1, 1, {SKINNY_PATH_DOT2, 1, 8, 2, 1, 2}, {}},
     {4096, 8192, 2, 2, {SKINNY_PATH_DOT2, 1, 8, 2, 1, 8}, {}},
-    {4096, 8192, 3, 4, {SKINNY_PATH_MFMA_4X4, 1, 8, 8, 1, 8}, {}},
-    {4096, 8192, 5, 8, {SKINNY_PATH_MFMA_4X4, 1, 8, 8, 1, 4}, {4, 256}},
+    {4096, 8192, 3, 8, {SKINNY_PATH_DOT2, 1, 8, 2, 1, 2}, {8, 256}},
     {4096, 8192, 9, 16, {SKINNY_PATH_MFMA_4X4, 1, 16, 4, 1, 4}, {4, 256}},
 };
 
