@@ -602,7 +602,7 @@ def cpu_baseline(budget_s: float = 12.0):
                 oracle.gemm_bf16(x[:M], w, nthreads)
             steps += 1
             el = time.perf_counter() - t0
-            if el >= budget or steps >= 200:
+            if el >= budget or steps >= 5000:
                 return steps, el
 
     def per_m(nthreads, runs=3):
