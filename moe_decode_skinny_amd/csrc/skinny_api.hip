@@ -357,6 +357,41 @@ static skinny_ring_launch walk_launch(const skinny_launch &l, const Walk &w) {
   return r;
 }
 
+// The DOT2 walk for 3..8 tokens on wide shards: 2 chunks a wave and K / 1024
+// waves (one pass over K, 4096 <= K <= 8192; at 3-4 tokens only K = 4096 or
+// 8192), 4 rows up to K = 4096 and 2 above, 256 workgroups each taking one
+// or two segments of 2, 4 or 8 output blocks (the longest such segment; no
+// walk when the blocks do not split that evenly). Measured against the
+// rule's plain DOT2 launch (60-call graphs over a weight ring): on 13
+// off-table shapes (N = 2048..16384, K = 4096 and 8192) at 4 and 8 tokens
+// 3-17% faster wherever it applies, while where the segments would not split
+// evenly (3 a workgroup, or fewer blocks) the plain launch was as fast or
+// faster, and at 1-2 tokens the gain was at most 1-8% and not general; then,
+// with this rule, on 9 shapes at 3-8 tokens 2-23% faster at K = 4096, 8192
+// and at 5-8 tokens on K = 5120 and 6144 (N = 2048, K = 6144: within 1.2%),
+// but 1-2.5% slower at 3-4 tokens on K = 5120 and 6144.
+static bool dot2_walk(int M, int N, int K, int splits, skinny_launch *out, Walk *w) {
+  if (M < 3 || M > 8 || splits > 1 || K < 4096 || K > 8192 || K % 1024) return false;
+  if (M <= 4 && K % 4096) return false;
+  const int rows = K <= 4096 ? 4 : 2;
+  if (N % rows) return false;
+  const int groups = N / rows;
+  int seg = 0;
+  for (int s : {8, 4, 2})
+    if (groups % (s * 256) == 0 && groups / (s * 256) <= 2) {
+      seg = s;
+      break;
+    }
+  if (!seg) return false;
+  const skinny_launch l{SKINNY_PATH_DOT2, 1, K / 1024, 2, 1, rows};
+  const Walk walk{seg, 256, false};
+  if (launch_check(M, N, K, l) != SKINNY_OK || ring_check(1, M, N, K, walk_launch(l, walk)))
+    return false;
+  *out = l;
+  *w = walk;
+  return true;
+}
+
 // A 16-block launch of the rule on 512 or more output blocks runs as a walk
 // of one segment per workgroup, the segment as long as keeps 256 or more
 // workgroups (the activations loaded once per segment instead of once per
@@ -373,9 +408,10 @@ static void blocks_walk(int M, int N, int K, const skinny_launch &l, Walk *w) {
 }
 
 // The chooser: a pure function of (M, N, K, splits): the measured table for
-// the shard shapes, the staged walk or the rule above otherwise; *walk (if
-// asked for) says how the launch runs (a table entry's walk, the staged walk,
-// or the rule's 16-block walk, each only if valid; else the plain kernel).
+// the shard shapes, the staged walk, the DOT2 walk or the rule above
+// otherwise; *walk (if asked for) says how the launch runs (a table entry's
+// walk, the staged walk, the DOT2 walk or the rule's 16-block walk, each only
+// if valid; else the plain kernel).
 static int choose(int M, int N, int K, int splits, skinny_launch *out, Walk *walk = nullptr) {
   int st = check_problem(M, N, K);
   if (st) return st;
@@ -391,7 +427,7 @@ static int choose(int M, int N, int K, int splits, skinny_launch *out, Walk *wal
         w = e.walk;
       break;
     }
-  if (!l.waves && !staged_walk(M, N, K, splits, &l, &w)) {
+  if (!l.waves && !staged_walk(M, N, K, splits, &l, &w) && !dot2_walk(M, N, K, splits, &l, &w)) {
     l = rule(M, N, K, splits);
     blocks_walk(M, N, K, l, &w);
   }

@@ -284,14 +284,15 @@ def test_split_k_handoff_alternating_inputs(gpu_lib, path, splits):
 
 @pytest.mark.parametrize("N,K", [(1024, 4096), (8192, 1024), (512, 8192), (4096, 8192),
                                  (2048, 1000), (8192, 3072), (16384, 1024), (2064, 4096),
-                                 (2048, 6144)])
+                                 (2048, 6144), (4096, 4096)])
 def test_chooser_walk_is_bitwise_the_plain_launch(gpu_lib, N, K):
     """skinny_gemm_bf16 runs some shapes as a persistent walk (the ring kernel
     with one item): bit for bit the plain kernel at skinny_choose's launch,
     within tolerance of the oracle, and no write outside y (the four shard
     shapes, and off-table shapes whose 9-16 token calls run the staged walk,
     one segment a workgroup, up to 4 output blocks a segment, a ragged K, or
-    a 16-block walk of 2-block segments)."""
+    a 16-block walk of 2-block segments, and whose 3-8 token calls run the
+    DOT2 walk of 2- or 4-block segments)."""
     x, w = synthetic.gemm_inputs(N=N, K=K, seed=31)
     ref16 = oracle.gemm_bf16(x[:16], w, THREADS)  # rows are independent
     for M in (1, 2, 3, 4, 5, 8, 9, 16):
