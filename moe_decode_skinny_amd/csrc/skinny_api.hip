@@ -357,9 +357,10 @@ static skinny_ring_launch walk_launch(const skinny_launch &l, const Walk &w) {
   return r;
 }
 
-// The DOT2 walk for 3..8 tokens on wide shards: 2 chunks a wave and K / 1024
-// waves (one pass over K, 4096 <= K <= 8192; at 3-4 tokens only K = 4096 or
-// 8192), 4 rows up to K = 4096 and 2 above, 256 workgroups each taking one
+// The DOT2 walk for 3..8 tokens (2 tokens at K = 8192) on wide shards: 2
+// chunks a wave and K / 1024 waves (one pass over K, 4096 <= K <= 8192; at
+// 3-4 tokens only K = 4096 or 8192), 4 rows up to K = 4096 and 2 above, 256
+// workgroups each taking one
 // or two segments of 2, 4 or 8 output blocks (the longest such segment; no
 // walk when the blocks do not split that evenly). Measured against the
 // rule's plain DOT2 launch (60-call graphs over a weight ring): on 13
@@ -369,10 +370,11 @@ static skinny_ring_launch walk_launch(const skinny_launch &l, const Walk &w) {
 // faster, and at 1-2 tokens the gain was at most 1-8% and not general; then,
 // with this rule, on 9 shapes at 3-8 tokens 2-23% faster at K = 4096, 8192
 // and at 5-8 tokens on K = 5120 and 6144 (N = 2048, K = 6144: within 1.2%),
-// but 1-2.5% slower at 3-4 tokens on K = 5120 and 6144.
+// but 1-2.5% slower at 3-4 tokens on K = 5120 and 6144; at 2 tokens and
+// K = 8192 (N = 2048, 8192) 8-9% faster, at 1 token within 1%.
 static bool dot2_walk(int M, int N, int K, int splits, skinny_launch *out, Walk *w) {
-  if (M < 3 || M > 8 || splits > 1 || K < 4096 || K > 8192 || K % 1024) return false;
-  if (M <= 4 && K % 4096) return false;
+  if (M < 2 || M > 8 || splits > 1 || K < 4096 || K > 8192 || K % 1024) return false;
+  if ((M == 2 && K != 8192) || (M <= 4 && K % 4096)) return false;
   const int rows = K <= 4096 ? 4 : 2;
   if (N % rows) return false;
   const int groups = N / rows;

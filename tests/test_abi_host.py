@@ -263,16 +263,18 @@ def test_off_table_16_block_walks(sk):
 
 
 def test_off_table_dot2_walks(sk):
-    """3-8 tokens on wide off-table shards run the DOT2 walk: 2 chunks a wave,
-    K / 1024 waves, 4 rows up to K = 4096 and 2 above, 256 workgroups of one
-    or two segments of 2, 4 or 8 blocks; skinny_choose returns the walk's
-    launch. No walk when the blocks do not split that evenly, at 1-2 tokens,
-    at 3-4 tokens unless K is a multiple of 4096, or outside 4096..8192."""
+    """3-8 tokens (and 2 at K = 8192) on wide off-table shards run the DOT2
+    walk: 2 chunks a wave, K / 1024 waves, 4 rows up to K = 4096 and 2
+    above, 256 workgroups of one or two segments of 2, 4 or 8 blocks;
+    skinny_choose returns the walk's launch. No walk when the blocks do not
+    split that evenly, at 1 token, at 2 tokens below K = 8192, at 3-4 tokens
+    unless K is a multiple of 4096, or outside 4096..8192."""
     P0 = sk.SKINNY_PATH_DOT2
     for M, N, K, seg, rows in [(3, 2048, 4096, 2, 4), (8, 4096, 4096, 4, 4),
                                (4, 8192, 4096, 8, 4), (6, 16384, 4096, 8, 4),
                                (5, 2048, 8192, 4, 2), (8, 8192, 8192, 8, 2),
-                               (5, 2048, 6144, 4, 2), (8, 4096, 5120, 8, 2)]:
+                               (5, 2048, 6144, 4, 2), (8, 4096, 5120, 8, 2),
+                               (2, 2048, 8192, 4, 2), (2, 8192, 8192, 8, 2)]:
         w = sk.skinny_choose_walk(M, N, K, 0)
         assert (w.gemm.path, w.segment, w.workgroups) == (P0, seg, 256), (M, N, K, w)
         assert (w.gemm.waves, w.gemm.chunks, w.gemm.rows) == (K // 1024, 2, rows), (M, N, K, w)

@@ -284,7 +284,7 @@ def test_split_k_handoff_alternating_inputs(gpu_lib, path, splits):
 
 @pytest.mark.parametrize("N,K", [(1024, 4096), (8192, 1024), (512, 8192), (4096, 8192),
                                  (2048, 1000), (8192, 3072), (16384, 1024), (2064, 4096),
-                                 (2048, 6144), (4096, 4096)])
+                                 (2048, 6144), (4096, 4096), (2048, 8192)])
 def test_chooser_walk_is_bitwise_the_plain_launch(gpu_lib, N, K):
     """skinny_gemm_bf16 runs some shapes as a persistent walk (the ring kernel
     with one item): bit for bit the plain kernel at skinny_choose's launch,
