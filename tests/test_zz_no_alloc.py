@@ -52,7 +52,9 @@ def _pair(sk, M, N, K, splits, seed):
     # 4 splits asked for: the chooser's 16-block launch sums them inside the
     # kernel (partials and hand-off counters in the static array), then a
     # smaller one with 2 splits
-    ((16, 512, 8192, 4, 7), (9, 512, 4096, 2, 8)),
+    ((16, 512, 8192, 4, 7), (9, 512, 4096, 2, 8)),    # calls the chooser runs as walks (the ring kernel, no scratch): the full
+    # pooler's DOT2 walk, then a smaller off-table DOT2 walk
+    ((8, 4096, 8192, 0, 9), (4, 2048, 4096, 0, 10)),
 ])
 def test_noalloc_matches_the_allocating_call_twice(gpu_lib, first, second):
     l1 = _pair(gpu_lib, *first)
@@ -63,6 +65,9 @@ def test_noalloc_matches_the_allocating_call_twice(gpu_lib, first, second):
     if first[4] == 7:
         assert l1.path == gpu_lib.SKINNY_PATH_MFMA_4X4 and l1.splits == 4
         assert l2.path == gpu_lib.SKINNY_PATH_MFMA_4X4 and l2.splits == 2
+    if first[4] == 9:
+        for M, N, K, splits, _ in (first, second):
+            assert gpu_lib.skinny_choose_walk(M, N, K, splits).segment > 0, (M, N, K)
 
 
 def test_noalloc_refuses_partials_beyond_the_array(gpu_lib):
