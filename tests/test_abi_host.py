@@ -658,3 +658,34 @@ def test_ceiling_stream_argument_checks(sk, name):
         msg = ceiling.skinny_ceiling_last_error()
         assert needle in msg, (needle, msg)
     assert fn(p, 8192, ctypes.c_void_p(4098), 1, None) == sk.SKINNY_EINVAL
+
+
+def test_last_error_is_per_thread(sk):
+    """skinny_last_error is thread-local (include/skinny.h): two threads that
+    fail differently, interleaved so that each failure lands between the
+    other thread's failure and its read, each read back their own reason."""
+    import threading
+
+    lib = sk._lib
+    step = threading.Barrier(2)
+    got = {}
+
+    def worker(name, M):
+        out = sk.Launch(0, 0, 0, 0, 0, 0)._c()
+        step.wait()
+        if name == "a":
+            assert lib.skinny_choose(M, 1024, 4096, 0, ctypes.byref(out)) == sk.SKINNY_EINVAL
+            step.wait()  # b fails now
+            step.wait()
+        else:
+            step.wait()
+            assert lib.skinny_choose(M, 1024, 4096, 0, ctypes.byref(out)) == sk.SKINNY_EINVAL
+            step.wait()
+        got[name] = lib.skinny_last_error().decode()
+
+    ts = [threading.Thread(target=worker, args=("a", 17)), threading.Thread(target=worker, args=("b", 0))]
+    for t in ts:
+        t.start()
+    for t in ts:
+        t.join(timeout=30)
+    assert "M=17" in got["a"] and "M=0" in got["b"], got
