@@ -39,10 +39,10 @@ namespace {
 // activations need 128 VGPRs of operands, so that variant gets 8 waves.
 constexpr int mfma_max_threads(int chunks) { return chunks >= 16 ? 512 : 1024; }
 
-template <int CHUNKS, int ACCS>
 // The arguments the main loop needs come first, the workgroup's wave count
 // among them (the first 14 argument dwords arrive preloaded in SGPRs;
 // blockDim would be a kernel-argument fetch).
+template <int CHUNKS, int ACCS>
 __global__ __launch_bounds__(mfma_max_threads(CHUNKS)) void gemm_mfma_kernel(
     const uint16_t *__restrict__ x, const uint16_t *__restrict__ w, int M, int N, int K,
     int S, int groups, int F, int kw, int waves, uint16_t *__restrict__ y,
