@@ -541,7 +541,7 @@ static const RingEntry kRingTable[] = {
     {1024, 4096, 2, 2, DOT2_RING(8, 1, 8, 2, 2048, I)},
     {1024, 4096, 3, 4, DOT2_RING(8, 1, 4, 4, 2048, X)},
     {1024, 4096, 5, 8, MFMA4X4_RING(8, 4, 8, 32, 240, I)},
-    {1024, 4096, 9, 16, LDS_RING(8, 16, 1, 16, 16, 240, X)},
+    {1024, 4096, 9, 16, MFMA4X4_RING(8, 4, 8, 32, 240, X)},
     // o_proj shard
     {8192, 1024, 1, 1, MFMA4X4_RING(2, 4, 4, 8, 1024, I)},
     {8192, 1024, 2, 2, DOT2_RING(1, 2, 8, 1, 512, X)},
