@@ -382,7 +382,7 @@ def summarize_profiles(root: str, out_dir: str) -> None:
                       "launch": sh["launch"], "kernels": kernels,
                       "call_median_us": round(sum(kk["median"] for kk in kernels), 3),
                       "replay_us_per_call": sh["us_per_item_replay"], "command": cmds[key]})
-    # the digests the runs recorded on the GPU machine (all runs share one tree)
+    # the kernel-source digests the runs recorded (all runs share one tree)
     digests = {shape_of(d)["kernel_source_digest"] for d in runs.values()
                if os.path.exists(os.path.join(d, "shape.json"))}
     ring_digests = {shape_of(d)["ring_source_digest"] for d in runs.values()
@@ -398,7 +398,7 @@ def summarize_profiles(root: str, out_dir: str) -> None:
              "the call); per library kernel and grid: dispatches, mean / median / p10 / p90",
              "duration in us; call = sum of the medians of the call's kernels; replay = event-timed",
              "us per call of the same graph replays in the run (profiler on).",
-             "Reduced with: python bench.py --summarize gpurun_out/prof",
+             f"Reduced with: python bench.py --summarize {root}",
              f"kernel sources digest {digest}", ""]
     for e in trace:
         lines.append(f"{e['shape']} M={e['M']} N={e['N']} K={e['K']}  launch {e['launch']}")
@@ -522,7 +522,7 @@ def summarize_profiles(root: str, out_dir: str) -> None:
              "  util: MfmaUtil and VALUBusy (percent);",
              "  tcp: TCP_TCC_READ_REQ (L1 -> L2 read requests), TCP_TOTAL_CACHE_ACCESSES (L1 tag",
              "    accesses) and TCP_TOTAL_READ, per call: the activation re-reads the workgroups pull.",
-             "Reduced with: python bench.py --summarize gpurun_out/prof",
+             f"Reduced with: python bench.py --summarize {root}",
              f"kernel sources digest {digest}, ring sources digest {ring_digest}", ""]
     for r in traffic:
         tag = "ring item" if r["ring"] else "call"
@@ -888,7 +888,7 @@ def main():
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py runs on one GPU only: this GEMM is one GPU's shard and the "
-              "build has no multi-GPU path (use --gpus 1)", file=sys.stderr)
+              "library has no multi-GPU path (use --gpus 1)", file=sys.stderr)
         sys.exit(2)
 
     if args.profile_shape:

@@ -39,7 +39,7 @@ def _load():
     if _lib is not None:
         return _lib
     # Load what is built (build() in __graft_entry__ rebuilds it after a
-    # change); compile only when nothing is, never while timing on a GPU machine.
+    # change); compile only when nothing is, never inside a timed run.
     if not os.path.exists(_LIB_PATH):
         from . import build as _build  # compiling the checker is not using it
 
