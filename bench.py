@@ -818,18 +818,22 @@ def shard_timing(sk, synthetic, dev, stream, N2, K2, ms, wseed, xseed, reps):
     ring = synthetic.device_weight_ring(RING, N2, K2, dev, base_seed=wseed)
 
     def timed(fn, per):
+        # the median of three timings of `reps` replays each
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g, stream=stream):
             fn()
         g.replay()
         torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record(stream)
-        for _ in range(reps):
-            g.replay()
-        e1.record(stream)
-        torch.cuda.synchronize()
-        return e0.elapsed_time(e1) * 1e3 / (reps * per)
+        runs = []
+        for _ in range(3):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for _ in range(reps):
+                g.replay()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            runs.append(e0.elapsed_time(e1) * 1e3 / (reps * per))
+        return sorted(runs)[1]
 
     out = {}
     ceiling = stream_ceiling(sk, dev, stream, ring)
