@@ -91,8 +91,8 @@ DeviceState *current_state(int *status) {
 }
 
 // Validity of (M, N, K) at an explicit launch shape; the gfx950 restatement
-// of launch_unsupported (splits, K per wave, waves per workgroup) plus this
-// build's own limits (compiled variants, LDS, workspace).
+// of launch_unsupported (splits, K per wave, waves per workgroup) plus the
+// library's own limits (compiled variants, LDS, workspace).
 static int launch_check(int M, int N, int K, const skinny_launch &l) {
   int st = check_problem(M, N, K);
   if (st) return st;
