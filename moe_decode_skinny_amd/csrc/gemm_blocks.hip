@@ -236,7 +236,10 @@ __global__ __launch_bounds__(THREADS) void gemm_blocks_kernel(
     const int t = output_token(o, R4), r = output_row(o, R4);
     if (t >= Mh) continue;
     const unsigned bits = f32_to_bf16(part[i]);
-    y[(size_t)(t0 + t) * N + f0 + r] = (uint16_t)bits;
+    if (S == 1)
+      store_out_device(y + (size_t)(t0 + t) * N + f0 + r, bits);
+    else
+      y[(size_t)(t0 + t) * N + f0 + r] = (uint16_t)bits;
     if (uint16_t *slot = publish_slot(pub, N))
       slot[(size_t)(t0 + t) * N + f0 + r] = (uint16_t)publish_bits(bits);
   }

@@ -36,7 +36,7 @@ __global__ __launch_bounds__(kReduceThreads) void split_reduce_kernel(
   for (int s = 1; s < S; ++s) sum += v[s];
   const unsigned lo = f32_to_bf16(sum[0]) | (f32_to_bf16(sum[1]) << 16);
   const unsigned hi = f32_to_bf16(sum[2]) | (f32_to_bf16(sum[3]) << 16);
-  *reinterpret_cast<uint2 *>(y + (size_t)t * N + n) = make_uint2(lo, hi);
+  store_out_device(y + (size_t)t * N + n, lo, hi);
   if (uint16_t *slot = publish_slot(pub, N))
     *reinterpret_cast<uint2 *>(slot + (size_t)t * N + n) =
         make_uint2(publish_pair(lo), publish_pair(hi));
