@@ -1,8 +1,8 @@
 """Benchmark of the small-M decode GEMM on one MI355X.
 
 Workload: the unpooler shard GEMM sweep y[M, 1024] = x[M, 4096] @ W[1024,
-4096]^T for M = 1, 2, 4, 8, 16 (unpooler page, module description), BF16 in
-and out, FP32 accumulation, at the chooser's launch shapes.  One step is one
+4096]^T for M = 1, 2, 4, 8, 16 (unpooler page, module description), BF16
+operands and result with FP32 sums, at the chooser's launch shapes.  One step is one
 pass of the sweep: five GEMM launches, each on the next weight of a ring of
 distinct layers (60 layers = 480 MiB, twice the 256 MiB Infinity Cache, so no
 call finds its weights in a cache).  Inputs are seeded synthetic tensors

@@ -6,8 +6,8 @@
  * decode:
  *   - "vllm.models.muse_spark.nvidia.specialized_decode.cutedsl.gemm.unpooler"
  *     (module description; Unpooler.run; Unpooler.unsupported;
- *     launch_unsupported): y[M, N] = x[M, K] @ W[N, K]^T, BF16 in and out,
- *     FP32 accumulation, 1 <= M <= 16, split-K partials added in an order
+ *     launch_unsupported): y[M, N] = x[M, K] @ W[N, K]^T for 1 to 16 tokens,
+ *     BF16 operands and result, FP32 sums, split-K partials added in an order
  *     that only the launch shape decides, so repeated runs give equal bits.
  *   - "vllm.models.muse_spark.nvidia.specialized_decode.cutedsl.moe.pooler_gather"
  *     (module description; compile_norm_quant; cvt_e2m1x8_f32;

@@ -1,6 +1,6 @@
 // The MFMA path of the small-M decode GEMM  y[M, N] = x[M, K] @ W[N, K]^T
-// (unpooler page, module description): BF16 in and out, FP32 accumulation,
-// 1 <= M <= 16.
+// (unpooler page, module description): BF16 operands and result, FP32 sums,
+// 1 to 16 tokens.
 //
 // gfx950 design.  The pages' SM100 kernel feeds 16 weight rows x 8 tokens to
 // mma.sync; here one v_mfma_f32_16x16x32_bf16 takes 16 weight rows (A) and 16

@@ -1,7 +1,7 @@
 // The split-K reduction of the small-M decode GEMM: y[t][n] = bf16( sum over
-// s = 0..S-1, in that order, of partials[s][t][n] ) (unpooler page, module
-// description: the partials are summed in a fixed order that depends only on
-// the launch shape, then rounded to BF16 and stored).
+// s = 0..S-1, in that order, of partials[s][t][n] ).  The order is set by the
+// split count alone, so a launch shape always gives the same bits (unpooler
+// page, module description).
 //
 // It runs as the second kernel of a split launch, on the same stream, so the
 // kernel boundary orders it after every partial store of the first: no

@@ -13,13 +13,14 @@
  *
  * Sources (the three vLLM API pages on the Muse Spark specialized decode):
  *   [unpooler]  page "...specialized_decode.cutedsl.gemm.unpooler", module
- *               description: y[M, N] = x[M, K] @ W[N, K]^T, BF16 in and out,
- *               FP32 accumulate, 1 <= M <= 16.
+ *               description: y[M, N] = x[M, K] @ W[N, K]^T for 1 to 16
+ *               tokens, with BF16 operands and result and sums kept in FP32.
  *   [pooler]    page "...specialized_decode.cutedsl.moe.pooler_gather", module
  *               description: y = bf16(x * rsqrt(mean(x**2) + eps) *
- *               (weight + gain_center)), then NVFP4 with block 16: a is uint8
- *               [b, P/2] with the even column in the low nibble, a_sf is
- *               float8_e4m3fn [b, P/16], not swizzled.
+ *               (weight + gain_center)), then NVFP4 over 16-column blocks:
+ *               codes packed two to a byte in a, uint8 [b, P/2], the even
+ *               column's code in bits 0-3; one float8_e4m3fn scale per
+ *               block in a_sf, [b, P/16], row-major (no swizzle).
  *   [cvt]       same page, cvt_e2m1x8_f32 / cvt_f32_to_e4m3: round to nearest
  *               even with saturation to the largest finite value.
  *   [oscale]    same page, nvfp4_compute_output_scale: the output scale is the

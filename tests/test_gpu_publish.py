@@ -1,9 +1,9 @@
 """GPU parity of the zero-copy publish (skinny_gemm_bf16_publish) through the
 C ABI, on one GPU.
 
-The unpooler page's zero-copy epilogue also writes y into this rank's slot of
-the next boundary's mailbox ([3 stages][tp][capacity][width] BF16) with -0.0
-stored as +0.0 (the pooler_gather page: -0.0 is the mailbox's sentinel) and
+In the unpooler page's zero-copy epilogue, the kernel that stores y also
+copies it into the calling rank's slot of the mailbox read at the following
+boundary ([3 stages][tp][capacity][width] BF16), writing -0.0 as +0.0 (the pooler_gather page: -0.0 is the mailbox's sentinel) and
 sets the active-stage word, or takes the stage from a ticket's upper half and
 stores no word.  Here y must match the oracle GEMM within the GEMM tolerance
 and be bitwise equal to the plain call at the same launch; the mailbox and

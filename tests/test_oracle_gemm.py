@@ -1,5 +1,6 @@
 """Pins for the oracle GEMM y = bf16(x @ W^T) (unpooler page, module
-description: BF16 in and out, FP32-or-better accumulation, 1 <= M <= 16).
+description: BF16 operands and result, sums in FP32 or wider, 1 to 16
+tokens).
 
 Pins: exact rational brute force on tiny inputs, closed forms (identity,
 one-hot, power-of-two scaling), numpy's float64 matmul on the exact sums, and
