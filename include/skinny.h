@@ -58,8 +58,8 @@ enum {
 
 /* A launch shape of the GEMM: the counterpart of the unpooler page's
  * UnpoolerShape (splits, kw, accs) and the pooler page's PoolerGemmShape.
- * The launch is fully determined by (M, N, K, skinny_launch); the summation
- * order depends only on it.
+ * (M, N, K, skinny_launch) fixes the launch completely, and with it the order
+ * in which every output's products are added.
  *
  *   MFMA: a workgroup owns rows = 16 F output features (F = 1, 2 or 4 MFMA
  *         tiles sharing one LDS copy of the activations) and one of `splits`
@@ -178,8 +178,8 @@ int skinny_choose(int M, int N, int K, int splits, skinny_launch *out);
 int skinny_gemm_unsupported(int M, int N, int K, int splits);
 
 /* Why (M, N, K) cannot run at `launch` (unpooler page, launch_unsupported:
- * the reason the kernel has no launch for a weight shape at given splits, K
- * per wave and accumulators); SKINNY_OK when it can.  Host only. */
+ * a weight shape that the given splits, K per wave and accumulators cannot
+ * serve is reported with its reason); SKINNY_OK when it can.  Host only. */
 int skinny_launch_unsupported(int M, int N, int K, const skinny_launch *launch);
 
 /* The next boundary's mailbox for a zero-copy publish (unpooler page, module
