@@ -149,12 +149,11 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void *base, 
 __device__ __forceinline__ float bf16_hi(unsigned u) { return __uint_as_float(u & 0xffff0000u); }
 
 // An output store with the device-scope cache policy (a relaxed agent-scope
-// atomic store: the store's sc1 bit).  Used where it measured faster: the
-// 16-block kernel at one split and the split reduce, whose workgroups each
-// store whole 16-byte pieces of y rows, were 1-2.5% faster per call.  Where
-// many workgroups store 2-4 bytes into the same lines (DOT2 at 1-2 tokens,
-// the layer ring, the in-kernel split's last arriver) the same store was
-// 1-13% slower, so those kernels store y with plain stores.
+// atomic store: the store's sc1 bit).  Used only where it measured faster:
+// the 16-block kernel at one split and the split reduce, 1-2.5% per call.
+// With the same store, DOT2 at 1-2 tokens and the layer ring were 3.5-13%
+// slower and the 16-block kernel's in-kernel split 1-3% slower, so those
+// keep plain stores.
 __device__ __forceinline__ void store_out_device(uint16_t *p, unsigned bits) {
   __hip_atomic_store(p, (uint16_t)bits, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
