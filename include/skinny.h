@@ -141,13 +141,16 @@ int skinny_gemm_bf16(const void *x, const void *W, void *y, int M, int N,
 /* For callers that cannot allocate (code under HIP graph capture, tight
  * serving loops, harnesses that forbid hipMalloc): skinny_gemm_bf16 with the
  * same arguments, chooser, kernels and bits, except that a launch with
- * splits > 1 keeps its FP32 partials in a static device array of the library
- * (1 MiB, 2^18 floats, one per device, held until the process ends; its
- * address is looked up by skinny_init) instead of the workspace skinny_init
- * allocates.  The call allocates and frees nothing.  The array needs no
- * clearing: each call writes every partial it reads.  Every call on a
- * device shares that device's array: calls that overlap on one device
- * (different streams, or host threads without ordering) race.
+ * splits > 1 keeps its FP32 partials (2^18 floats at most) and, on the
+ * 16-block path, its split hand-off counters (2048 words, each on its own
+ * 256 bytes) in a static device array of the library (1.5 MiB, one per
+ * device, held until the process ends; its address is looked up by
+ * skinny_init) instead of the workspace skinny_init allocates.  The call
+ * allocates and frees nothing.  skinny_init zeroes the counters and every
+ * hand-off returns its counter to zero, so they are zero between calls; the
+ * partials need no clearing, since each call writes every partial it reads.
+ * Every call on a device shares that device's array: calls that overlap on
+ * one device (different streams, or host threads without ordering) race.
  * Errors: as skinny_gemm_bf16, and SKINNY_EUNSUPPORTED when the chosen
  * launch's splits x M x N exceeds 2^18 (skinny_gemm_bf16 takes up to 2^21). */
 int skinny_gemm_bf16_noalloc(const void *x, const void *W, void *y, int M, int N,
