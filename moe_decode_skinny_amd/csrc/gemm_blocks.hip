@@ -95,11 +95,17 @@ __device__ __forceinline__ float sum_splits(int S, Term term) {
 // returned value tells the last arriver.  Returns true in the last one.
 // The S workgroups of a block are dealt to one XCD (ids congruent mod 8, see
 // the kernel), so partials pass through that XCD's L2: plain stores waited
-// for before the atomic, and in the last arriver an L1 invalidate and loads
-// that bypass L1.  *mixed is set when the arrivals came from more than one
-// XCD, whose L2s do not see each other's stores; the caller then recomputes
-// the other splits instead of reading them.  The counter word is reset by
-// the last arriver, so it is zero again for the next call (no memset).
+// for before the atomic, and in the last arriver plain loads.  Those loads
+// cannot meet a stale line in this CU's L1: a block's slot is read once per
+// launch, by its last arriver, after every store to it; slots of different
+// blocks share no cache line (S * kOut floats with S even and kOut a
+// multiple of 16); and the compute units' L1 caches are invalidated when a
+// launch starts.  (The L1 invalidate below matters only in thread-group-split
+// mode; outside it, measured with polling loads, it does not drop lines.)
+// *mixed is set when the arrivals came from more than one XCD, whose L2s do
+// not see each other's stores; the caller then recomputes the other splits
+// instead of reading them.  The counter word is reset by the last arriver,
+// so it is zero again for the next call (no memset).
 template <int kPer>
 __device__ __forceinline__ bool block_handoff(float *__restrict__ slots,
                                               unsigned *__restrict__ counter, int S, int s,
@@ -124,7 +130,7 @@ __device__ __forceinline__ bool block_handoff(float *__restrict__ slots,
   if ((all & 0xFFFFu) != (1u << S) - 1u) return false;
   *mixed = __builtin_popcount(all >> 16) != 1;
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
-  asm volatile("buffer_inv sc0" ::: "memory");  // no stale line in this CU's L1
+  asm volatile("buffer_inv sc0" ::: "memory");  // see above: thread-group-split mode
   if (lane == 0) __hip_atomic_store(counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   return true;
 }
@@ -201,7 +207,8 @@ __global__ __launch_bounds__(THREADS) void gemm_blocks_kernel(
       for (int i = 0; i < kPer; ++i) {
         const int oc = i * 64 + lane < kOut ? i * 64 + lane : 0;
         sum[i] = sum_splits(S, [&](int s2) {
-          // bit 0 of the cache policy (sc0): served from L2, not this CU's L1
+          // the other splits' partials (sc0 policy; no stale L1 line, see
+          // block_handoff)
           return s2 == s ? part[i]
                          : __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
                                res, (s2 * kOut + oc) * 4, 0, 1));
