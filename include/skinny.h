@@ -99,9 +99,10 @@ typedef struct skinny_launch {
  * which its run call may be recorded into a graph and needs no allocation;
  * pooler_gather page, Pooler: the same for the pooler): checks that it is a gfx950 GPU, allocates the
  * library's split-K workspace on it (8 MiB of FP32 partials, enough for
- * S * M * N <= 2^21) and the dual norm's buffer (512 KiB of per-slice sums),
- * sets the kernels' LDS limits and looks up the device's address of the
- * static scratch array of skinny_gemm_bf16_noalloc.
+ * S * M * N <= 2^21, and 512 KiB of split hand-off counters, zeroed) and the
+ * dual norm's buffer (512 KiB of per-slice sums), sets the kernels' LDS
+ * limits, and looks up the device's address of the static scratch array of
+ * skinny_gemm_bf16_noalloc and zeroes that array's counters.
  * Call it before any graph capture.  Idempotent.  Returns SKINNY_OK,
  * SKINNY_EDEVICE or SKINNY_ELAUNCH (allocation failure). */
 int skinny_init(int device);
