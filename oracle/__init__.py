@@ -126,7 +126,8 @@ def f32(v: float) -> float:
 def bf16_value(bits) -> np.ndarray:
     """Values (float64) of bfloat16 bit patterns."""
     b = np.ascontiguousarray(bits, dtype=np.uint16)
-    return (b.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    with np.errstate(invalid="ignore"):  # signalling-NaN patterns widen to NaN
+        return (b.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
 
 
 def bf16_round(values) -> np.ndarray:

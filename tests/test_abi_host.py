@@ -29,7 +29,8 @@ NOT_A_STEP = ("Not a step of the method", "For callers that cannot allocate")
 
 
 def _header_text(header):
-    return open(os.path.join(ROOT, "include", header)).read()
+    with open(os.path.join(ROOT, "include", header)) as f:
+        return f.read()
 
 
 def _declarations(header):

@@ -38,7 +38,8 @@ def _copy_sources(tmp_path):
     for rel in bench.KERNEL_SOURCES + bench.RING_SOURCES:
         dst = tmp_path / rel
         dst.parent.mkdir(parents=True, exist_ok=True)
-        dst.write_bytes(open(os.path.join(ROOT, rel), "rb").read())
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            dst.write_bytes(f.read())
 
 
 def test_summary_lookups_follow_the_digest_and_the_launch(tmp_path, monkeypatch):

@@ -103,7 +103,8 @@ BATTERY = [
 
 
 def _build(tmp_path, name, text=None, repl=None):
-    src = open(SRC).read()
+    with open(SRC) as f:
+        src = f.read()
     if text is not None:
         assert src.count(text) >= 1, f"mutation {name}: pattern not in the oracle source"
         src = src.replace(text, repl)
